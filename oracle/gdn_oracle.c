@@ -1,0 +1,290 @@
+/*
+ * gdn_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU implementation of the varlen gated delta-rule hot path,
+ * computed in fp64.  Only the test suite, the package smoke check and the CPU-baseline leg of the
+ * benchmark may load it.  It shares no code, header, table or helper with the HIP library: the
+ * element decoders, the offsets check, the gate formulas and the recurrence below are written
+ * out independently from the definitions on the source pages.
+ *
+ * Sources (docs.rs source pages; cited by page and named item):
+ *   [conv]    onnxruntime-ep-mlx 0.31.1, src/ops/paged_ssm.rs -- kernel string CONV and host fn conv()
+ *   [prep]    same page -- kernel string DELTA_PREPARE
+ *   [delta]   same page -- kernel string DELTA and host fn delta()
+ *   [rates]   mlx-c-rust, compile/gated_delta_rate_activation.rs -- the rate-activation graph builder
+ *
+ * Readings taken where the pages are silent (each is listed in the design notes):
+ *   - offsets are valid iff offsets[0]==0, offsets[B]==N and offsets never decrease; an invalid
+ *     call writes nothing at all (the pages' kernels check the endpoints and each sequence's own
+ *     pair per thread; the strict whole-call reading is the plainest one that is deterministic).
+ *   - a NULL initial state means zeros.
+ *   - the epsilon of the q/k L2 norm is added to the sum of squares inside the square root.
+ *   - softplus(x) = max(x,0) + log1p(exp(-|x|)), i.e. logaddexp(x, 0).
+ *   - every value is decoded exactly to double first; nothing is rounded on the way out.
+ *
+ * Dtype codes used by this file: 0 = float32, 1 = bfloat16, 2 = float16 (IEEE binary16).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_F16 2
+
+/* ---- element decoders: bit layouts of IEEE binary32, bfloat16 and IEEE binary16 ---------------- */
+
+static double dec_bf16_bits(uint16_t h) {
+    /* bfloat16 is the upper half of an IEEE binary32 word. */
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double dec_f16_bits(uint16_t h) {
+    /* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 mantissa bits. */
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-14 * 2^-10 */
+    } else if (e == 31) {
+        v = m ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+static double dec(const void *p, int dtype, size_t i) {
+    switch (dtype) {
+    case OR_F32: return (double)((const float *)p)[i];
+    case OR_BF16: return dec_bf16_bits(((const uint16_t *)p)[i]);
+    case OR_F16: return dec_f16_bits(((const uint16_t *)p)[i]);
+    default: return NAN;
+    }
+}
+
+/* Exposed so the tests can pin the decoders against library conversions. */
+double gdn_oracle_decode(const void *p, int dtype, long long i) { return dec(p, dtype, (size_t)i); }
+
+/* ---- offsets ------------------------------------------------------------------------------------ */
+
+/* 1 if offsets[0..B] describe B packed sequences covering tokens [0, N), else 0.
+ * [conv]/[delta]: a sequence is processed only when offsets[0]==0, offsets[B]==N and
+ * 0 <= start <= end <= N; read strictly over the whole call. */
+int gdn_oracle_offsets_valid(const int32_t *offsets, int B, int N) {
+    if (B < 1 || offsets == NULL) return 0;
+    if (offsets[0] != 0 || offsets[B] != N) return 0;
+    for (int i = 0; i < B; ++i) {
+        if (offsets[i] < 0 || offsets[i] > N) return 0;
+        if (offsets[i + 1] < offsets[i]) return 0;
+    }
+    return 1;
+}
+
+/* ---- varlen depthwise causal conv1d with a carried window -------------------------------------- */
+
+/* [conv]: for sequence b, channel c and each token t of the sequence (local index l = t - start),
+ *   y[t,c] = act( bias[c] + sum_{j<W} w[c,j] * xv(l - (W-1-j)*D) ),
+ * where xv(m) is the input token start+m when m >= 0 and the carried window entry
+ * state_in[b,c,L+m] otherwise (L = (W-1)*D, oldest entry first).  act is SiLU z/(1+e^-z) when
+ * silu != 0, else the identity.  The new window is the last L entries of (old window ++ the
+ * sequence's tokens): state_out[b,c,j] = xv(len - L + j).
+ *
+ * Shapes: x, y [N,C]; w [C,W]; bias [C] or NULL; state_in, state_out [B,C,L] (state_in NULL ->
+ * zeros; state_out NULL -> not produced).  x, w and bias use x_dtype, the window uses state_dtype.
+ * Returns 0 on success, 1 when the offsets are malformed (then nothing is written). */
+int gdn_oracle_conv(int B, int N, int C, int W, int D, int x_dtype, int state_dtype, int silu,
+                    const void *x, const void *w, const void *bias, const void *state_in,
+                    const int32_t *offsets, double *y, double *state_out) {
+    if (!gdn_oracle_offsets_valid(offsets, B, N)) return 1;
+    const long long L = (long long)(W - 1) * D;
+    for (int b = 0; b < B; ++b) {
+        const int start = offsets[b];
+        const int len = offsets[b + 1] - start;
+        for (int c = 0; c < C; ++c) {
+            const size_t wbase = (size_t)b * C + c; /* window row of (b, c) */
+            for (int l = 0; l < len; ++l) {
+                double acc = bias ? dec(bias, x_dtype, (size_t)c) : 0.0;
+                for (int j = 0; j < W; ++j) {
+                    long long m = (long long)l - (long long)(W - 1 - j) * D;
+                    double xv;
+                    if (m >= 0)
+                        xv = dec(x, x_dtype, (size_t)(start + m) * C + c);
+                    else
+                        xv = state_in ? dec(state_in, state_dtype, (size_t)(wbase * L + L + m)) : 0.0;
+                    acc += dec(w, x_dtype, (size_t)c * W + j) * xv;
+                }
+                if (silu) acc = acc / (1.0 + exp(-acc));
+                y[(size_t)(start + l) * C + c] = acc;
+            }
+            if (state_out) {
+                for (long long j = 0; j < L; ++j) {
+                    long long m = (long long)len - L + j;
+                    double v;
+                    if (m >= 0)
+                        v = dec(x, x_dtype, (size_t)(start + m) * C + c);
+                    else
+                        v = state_in ? dec(state_in, state_dtype, (size_t)(wbase * L + L + m)) : 0.0;
+                    state_out[wbase * L + j] = v;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* ---- q/k normalisation and the gate / rate activations ----------------------------------------- */
+
+/* [prep], [delta] and [rates]: decay g from the decay input x of head h:
+ *   softplus on: g = exp( -exp(A_log[h]) * softplus(x + dt_bias[h]) )
+ *   softplus off: x is a raw log-decay and g = exp(x). */
+static double decay_gate(double x, int softplus, double a_log, double dtb) {
+    if (softplus) {
+        double z = x + dtb;
+        double sp = (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z)));
+        x = -exp(a_log) * sp;
+    }
+    return exp(x);
+}
+
+/* [prep], [delta] and [rates]: update rate beta = sigmoid(x) = 1/(1+e^-x), or x itself when raw. */
+static double rate_gate(double x, int sigmoid) { return sigmoid ? 1.0 / (1.0 + exp(-x)) : x; }
+
+/* [prep]: for every token t and key head hq, the q and k vectors (packed row [q | k | v], q of head
+ * hq at hq*K, k at HQ*K + hq*K) are scaled by 1/sqrt(sum x^2 + 1e-12) when l2norm != 0 and passed
+ * unchanged otherwise; qk_out is [2,N,HQ,K] (q plane then k plane).  For every token t and value
+ * head h, gb_out[0,t,h] = g (1 when a is NULL) and gb_out[1,t,h] = beta (1 when b is NULL); gb_out
+ * is [2,N,H].  a and b are [N,H] in gate_dtype; A_log and dt_bias are [H] float32 (used only with
+ * softplus).  Either output pointer may be NULL. */
+void gdn_oracle_prepare(int N, int HQ, int H, int K, int V, int qkv_dtype, int gate_dtype, int l2norm,
+                        int softplus, int sigmoid, const void *qkv, const void *a, const void *b,
+                        const float *A_log, const float *dt_bias, double *qk_out, double *gb_out) {
+    const size_t C = (size_t)2 * HQ * K + (size_t)H * V;
+    if (qk_out) {
+        for (int t = 0; t < N; ++t) {
+            for (int plane = 0; plane < 2; ++plane) {
+                for (int hq = 0; hq < HQ; ++hq) {
+                    const size_t src = (size_t)t * C + (size_t)plane * HQ * K + (size_t)hq * K;
+                    double ss = 0.0;
+                    for (int i = 0; i < K; ++i) {
+                        double v = dec(qkv, qkv_dtype, src + i);
+                        ss += v * v;
+                    }
+                    const double r = l2norm ? 1.0 / sqrt(ss + 1e-12) : 1.0;
+                    double *dst = qk_out + (((size_t)plane * N + t) * HQ + hq) * K;
+                    for (int i = 0; i < K; ++i) dst[i] = dec(qkv, qkv_dtype, src + i) * r;
+                }
+            }
+        }
+    }
+    if (gb_out) {
+        for (int t = 0; t < N; ++t) {
+            for (int h = 0; h < H; ++h) {
+                const size_t i = (size_t)t * H + h;
+                double g = 1.0, beta = 1.0;
+                if (a)
+                    g = decay_gate(dec(a, gate_dtype, i), softplus, softplus ? (double)A_log[h] : 0.0,
+                                   softplus ? (double)dt_bias[h] : 0.0);
+                if (b) beta = rate_gate(dec(b, gate_dtype, i), sigmoid);
+                gb_out[i] = g;
+                gb_out[(size_t)N * H + i] = beta;
+            }
+        }
+    }
+}
+
+/* ---- the gated delta-rule recurrence ------------------------------------------------------------ */
+
+/* [delta]: for each sequence b, value head h (key head kh = h / (H/HQ)) and value column v, the
+ * state s = state_in[b,h,v,:] (a K-vector; zeros when state_in is NULL) is carried through the
+ * sequence's tokens in order:
+ *     s <- g * s
+ *     r  = k^ . s
+ *     delta = beta * (v_t - r)
+ *     s <- s + delta * k^
+ *     out[t,h,v] = scale * (q^ . s)
+ * with q^, k^, g, beta as produced by gdn_oracle_prepare.  The final s is state_out[b,h,v,:].
+ * scale <= 0 selects 1/sqrt(K) (host fn delta(): a zero scale attribute means 1/sqrt(K)).
+ * Layouts: qkv [N, 2*HQ*K + H*V]; out [N,H,V]; state [B,H,V,K] float32 in, fp64 out.
+ * Returns 0 on success, 1 when the offsets are malformed (then nothing is written), 2 when out of
+ * memory.  Parallel over independent (b, h) pairs with OpenMP when built with it. */
+int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, int gate_dtype,
+                    int l2norm, int softplus, int sigmoid, double scale, const void *qkv,
+                    const void *a, const void *b, const float *A_log, const float *dt_bias,
+                    const float *state_in, const int32_t *offsets, double *out, double *state_out) {
+    if (!gdn_oracle_offsets_valid(offsets, B, N)) return 1;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)K);
+    const size_t C = (size_t)2 * HQ * K + (size_t)H * V;
+    const int G = H / HQ;
+    double *qk = (double *)malloc(sizeof(double) * ((size_t)2 * N * HQ * K + 1));
+    double *gb = (double *)malloc(sizeof(double) * ((size_t)2 * N * H + 1));
+    if (!qk || !gb) {
+        free(qk);
+        free(gb);
+        return 2;
+    }
+    gdn_oracle_prepare(N, HQ, H, K, V, qkv_dtype, gate_dtype, l2norm, softplus, sigmoid, qkv, a, b,
+                       A_log, dt_bias, qk, gb);
+    int failed = 0;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (long long bh = 0; bh < (long long)B * H; ++bh) {
+        const int bb = (int)(bh / H), h = (int)(bh % H);
+        const int kh = h / G;
+        const int start = offsets[bb], end = offsets[bb + 1];
+        double *s = (double *)malloc(sizeof(double) * (size_t)K);
+        if (!s) {
+            failed = 1;
+            continue;
+        }
+        for (int v = 0; v < V; ++v) {
+            const size_t col = ((size_t)bb * H + h) * V + v;
+            for (int i = 0; i < K; ++i) s[i] = state_in ? (double)state_in[col * K + i] : 0.0;
+            for (int t = start; t < end; ++t) {
+                const double *qh = qk + ((size_t)t * HQ + kh) * K;
+                const double *kk = qk + (((size_t)N + t) * HQ + kh) * K;
+                const double g = gb[(size_t)t * H + h];
+                const double beta = gb[((size_t)N + t) * H + h];
+                const double vt = dec(qkv, qkv_dtype, (size_t)t * C + (size_t)2 * HQ * K + (size_t)h * V + v);
+                for (int i = 0; i < K; ++i) s[i] *= g;
+                double r = 0.0;
+                for (int i = 0; i < K; ++i) r += kk[i] * s[i];
+                const double delta = beta * (vt - r);
+                for (int i = 0; i < K; ++i) s[i] += delta * kk[i];
+                double o = 0.0;
+                for (int i = 0; i < K; ++i) o += qh[i] * s[i];
+                out[((size_t)t * H + h) * V + v] = scale * o;
+            }
+            if (state_out)
+                for (int i = 0; i < K; ++i) state_out[col * K + i] = s[i];
+        }
+        free(s);
+    }
+    free(qk);
+    free(gb);
+    return failed ? 2 : 0;
+}
+
+/* Number of OpenMP threads the scan will use (1 without OpenMP). */
+int gdn_oracle_threads(void) {
+#ifdef _OPENMP
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+#else
+    return 1;
+#endif
+}
