@@ -1,0 +1,231 @@
+"""Benchmark of the varlen gated delta-rule hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of seeded synthetic input, with inputs resident
+in HBM: the varlen causal conv1d (its window updated in place) followed by the gated delta-rule
+recurrence (state updated in place).  The default workload is the decode step (B=256 sequences x 1
+token, HQ=16, H=32, K=V=128, bf16, fp32 state), where the recurrence runs in one fused launch.
+The prefill workload (B=8, lengths ~ U[512, 4096]) is measured too and reported in "also".
+
+Prints ONE JSON line.  The dominant kernel (the recurrence) is timed with HIP events on the stream
+it is launched on; its algorithmic bytes per launch are the fp32 state read and written plus the
+token streams it must read (q, k, v, a, b) and write (out).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+SCAN_SOURCES = ["gated_delta_rule_varlen_amd/csrc/gdn_scan.hip", "gated_delta_rule_varlen_amd/csrc/gdn_device.hpp"]
+
+
+def sizeof(dt: str) -> int:
+    return 4 if dt == "f32" else 2
+
+
+def scan_bytes(w) -> int:
+    """Algorithmic HBM bytes of one recurrence launch: state in + out (fp32), token rows
+    [q|k|v] and the two gate inputs read, outputs written."""
+    state = 2 * w.B * w.H * w.V * w.K * 4
+    tokens = w.N * (w.C * sizeof(w.io) + 2 * w.H * sizeof(w.gate_dtype)) + w.N * w.H * w.V * sizeof(w.io)
+    return state + tokens
+
+
+def src_digest() -> str:
+    h = hashlib.sha256()
+    for p in SCAN_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, only while the kernel source is
+    unchanged since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("src_digest") != src_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Path:
+    """Device-resident inputs of one workload and one step of the hot path."""
+
+    def __init__(self, w, torch, path: str):
+        import gated_delta_rule_varlen_amd as gdn
+
+        self.gdn, self.torch, self.w, self.path = gdn, torch, w, path
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+        def dev(a, d):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(a)
+            t = torch.from_numpy(a if d == "f32" else a.view(np.int16)).cuda()
+            return t if d == "f32" else t.view(dt[d])
+
+        self.x = dev(w.x, w.io)
+        self.conv_w = dev(w.conv_w, w.io)
+        self.conv_b = dev(w.conv_bias, w.io)
+        self.conv_state = dev(w.conv_state, w.conv_state_dtype)
+        if self.conv_state is None and w.L > 0:
+            self.conv_state = torch.zeros((w.B, w.C, w.L), dtype=dt[w.conv_state_dtype], device="cuda")
+        self.offsets = torch.from_numpy(w.offsets).cuda()
+        self.a, self.b = dev(w.a, w.gate_dtype), dev(w.b, w.gate_dtype)
+        self.A_log, self.dt_bias = dev(w.A_log, "f32"), dev(w.dt_bias, "f32")
+        self.state = dev(w.state, "f32")
+        if self.state is None:
+            self.state = torch.zeros((w.B, w.H, w.V, w.K), dtype=torch.float32, device="cuda")
+        self.y = torch.empty_like(self.x)
+        self.out = torch.empty((w.N, w.H, w.V), dtype=self.x.dtype, device="cuda")
+
+    def step(self, ev=None):
+        w, gdn = self.w, self.gdn
+        gdn.conv1d_varlen(self.x, self.conv_w, self.offsets, bias=self.conv_b, state_in=self.conv_state,
+                          dilation=w.D, silu=w.silu, y=self.y, state_out=self.conv_state)
+        if ev is not None:
+            ev[0].record()
+        _, _, used = gdn.scan_varlen(self.y, self.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=self.a, b=self.b,
+                                     A_log=self.A_log, dt_bias=self.dt_bias, state_in=self.state,
+                                     l2norm=w.l2norm, softplus=w.softplus, sigmoid=w.sigmoid, path=self.path,
+                                     out=self.out, state_out=self.state)
+        if ev is not None:
+            ev[1].record()
+        return used
+
+
+def time_path(p: "Path", steps: int, warmup: int):
+    torch = p.torch
+    for _ in range(warmup):
+        used = p.step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        used = p.step(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return total_ms / steps, scan_ms, used, wall
+
+
+def roofline(w, scan_ms: float, workload: str):
+    achieved = scan_bytes(w) / (scan_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(workload),
+            "kernel": "scan_kernel", "algorithmic_bytes_per_launch": scan_bytes(w),
+            "avg_launch_us": round(scan_ms * 1e3, 2)}
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The oracle (conv + scan, fp64, OpenMP) on a bounded sample of the same workload:
+    whole sequences, taken in order until about budget_s seconds of CPU work."""
+    import oracle
+
+    done_tokens = 0
+    seqs = 0
+    t_total = 0.0
+    reps = 0
+    while t_total < budget_s and reps < 64:
+        for b in range(w.B):
+            s, e = int(w.offsets[b]), int(w.offsets[b + 1])
+            off = np.array([0, e - s], np.int32)
+            t0 = time.perf_counter()
+            oracle.conv(np.ascontiguousarray(w.x[s:e]), w.conv_w, off, W=w.W, D=w.D, x_dtype=w.io, bias=w.conv_bias,
+                        state_in=None if w.conv_state is None else np.ascontiguousarray(w.conv_state[b:b + 1]),
+                        state_dtype=w.conv_state_dtype, silu=w.silu)
+            oracle.scan(np.ascontiguousarray(w.qkv[s:e]), off, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io,
+                        gate_dtype=w.gate_dtype, a=None if w.a is None else np.ascontiguousarray(w.a[s:e]),
+                        b=None if w.b is None else np.ascontiguousarray(w.b[s:e]), A_log=w.A_log,
+                        dt_bias=w.dt_bias, state_in=None if w.state is None else np.ascontiguousarray(w.state[b:b + 1]),
+                        l2norm=w.l2norm, softplus=w.softplus, sigmoid=w.sigmoid)
+            t_total += time.perf_counter() - t0
+            done_tokens += e - s
+            seqs += 1
+            if t_total >= budget_s:
+                break
+        reps += 1
+    return {"value": round(done_tokens / t_total, 2), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{seqs} whole sequences ({done_tokens} tokens) of the same workload, conv + scan in fp64, "
+                      f"{t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "long", "edge_fp16", "tiny_fp32"])
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "seq", "chunk"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true", help="skip the secondary prefill measurement")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the path shards with no exchange across sequences or key-head groups; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+
+    torch.cuda.set_device(0)
+    w = workloads.NAMED[args.workload]()
+    p = Path(w, torch, args.path)
+    ms, scan_ms, used, _ = time_path(p, args.steps, args.warmup)
+    tokens_per_s = w.N / (ms * 1e-3)
+    line = {
+        "metric": "gated-delta varlen scan tokens/s + achieved HBM GB/s (decode & prefill)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 I/O, f32 state and arithmetic" if w.io == "bf16" else w.io,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "HQ": w.HQ, "H": w.H, "K": w.K, "V": w.V,
+                   "conv_W": w.W, "conv_D": w.D, "path": used, "parallelism": "single GPU"},
+        "roofline": roofline(w, scan_ms, args.workload),
+    }
+    if not args.no_also and args.workload == "decode":
+        del p
+        torch.cuda.empty_cache()
+        wp = workloads.varlen_prefill()
+        pp = Path(wp, torch, "auto")
+        pms, pscan_ms, pused, _ = time_path(pp, max(3, args.steps // 10), 2)
+        line["also"] = {"prefill": {"workload": wp.name, "N": wp.N, "path": pused,
+                                    "tokens_per_s": round(wp.N / (pms * 1e-3), 1), "ms_per_step": round(pms, 4),
+                                    "scan_ms": round(pscan_ms, 4),
+                                    "scan_tflops_fp32": round(7 * wp.K * wp.V * wp.H * wp.N / (pscan_ms * 1e-3) / 1e12, 2),
+                                    "roofline": roofline(wp, pscan_ms, "prefill")}}
+        del pp
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+// gdn_api.cpp -- the extern "C" entry points of libgdn: argument validation, path selection and
+// dispatch to the kernel launchers.  Every check here runs on the host before anything is queued,
+// so a rejected call launches nothing and writes nothing.  The checks mirror the claim predicates
+// and handler checks of the paged_ssm.rs page (conv_claim, delta_claim, conv(), delta()):
+// positive geometry, H divisible by HQ, key width at most 256, dtype agreement, int32-sized
+// dispatches.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "gdn.h"
+#include "gdn_launch.hpp"
+
+namespace {
+
+bool dtype_ok(int d) { return d == GDN_F32 || d == GDN_BF16 || d == GDN_F16; }
+long long dsize(int d) { return d == GDN_F32 ? 4 : 2; }
+bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+gdn_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return GDN_OK;
+    if (e == hipErrorInvalidConfiguration) return GDN_ERR_OVERFLOW;
+    return GDN_ERR_HIP;
+}
+
+// Shape, dtype and flag checks shared by prepare, scan and the workspace query.
+gdn_status check_scan_desc(const gdn_scan_desc* d) {
+    if (d == nullptr) return GDN_ERR_NULL;
+    if (d->B < 1 || d->N < 0 || d->HQ < 1 || d->H < 1 || d->K < 1 || d->V < 1) return GDN_ERR_SHAPE;
+    if (d->H % d->HQ != 0 || d->K > 256) return GDN_ERR_SHAPE;
+    if (!dtype_ok(d->qkv_dtype)) return GDN_ERR_DTYPE;
+    if (d->gate_dtype != GDN_F32 && d->gate_dtype != d->qkv_dtype) return GDN_ERR_DTYPE;
+    if (d->flags & ~(uint32_t)(GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID)) return GDN_ERR_UNSUPPORTED;
+    const long long C = 2ll * d->HQ * d->K + (long long)d->H * d->V;
+    if (C > INT_MAX) return GDN_ERR_OVERFLOW;
+    if ((long long)d->B * d->H > INT_MAX) return GDN_ERR_OVERFLOW;
+    if (d->K != 32 && d->K != 64 && d->K != 128 && d->K != 256) return GDN_ERR_UNSUPPORTED;
+    if ((C * dsize(d->qkv_dtype)) % 16 != 0) return GDN_ERR_ALIGN;  // token rows must start 16-byte aligned
+    if (d->path < GDN_PATH_AUTO || d->path > GDN_PATH_CHUNK) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+// The chunked path needs every decay strictly positive and finite (it works with log-decays) and
+// normalised keys; it computes gates and norms itself, so it runs on the fused inputs only.
+bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay) {
+    (void)d;
+    (void)prepared;
+    (void)has_decay;
+    return false;  // the chunked kernels are not part of this build yet
+}
+
+int resolve_path(const gdn_scan_desc* d, bool prepared, bool has_decay, size_t ws_bytes) {
+    if (d->path != GDN_PATH_AUTO) return d->path;
+    if ((long long)d->N <= 2ll * d->B) return GDN_PATH_DECODE;
+    if (chunk_eligible(d, prepared, has_decay) &&
+        ws_bytes >= gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
+        return GDN_PATH_CHUNK;
+    return GDN_PATH_SEQ;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "a dimension is out of range or inconsistent";
+        case GDN_ERR_DTYPE: return "unknown or disallowed element type";
+        case GDN_ERR_OVERFLOW: return "a size or launch grid exceeds the index range";
+        case GDN_ERR_ALIGN: return "a tensor pointer or token row is not 16-byte aligned";
+        case GDN_ERR_UNSUPPORTED: return "shape, flag or path not supported by this build";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN_ERR_HIP: return "the HIP runtime rejected a launch";
+        case GDN_ERR_OFFSETS: return "malformed offsets (device-detected; nothing written)";
+    }
+    return "unknown status";
+}
+
+gdn_status gdn_conv1d_varlen(const gdn_conv_desc* d, const void* x, const void* w, const void* bias,
+                             const void* state_in, void* y, void* state_out, const int32_t* offsets,
+                             int32_t* dev_status, hipStream_t stream) {
+    if (d == nullptr || w == nullptr || offsets == nullptr) return GDN_ERR_NULL;
+    if (d->B < 1 || d->N < 0 || d->C < 1 || d->W < 1 || d->D < 1) return GDN_ERR_SHAPE;
+    if (d->N > 0 && (x == nullptr || y == nullptr)) return GDN_ERR_NULL;
+    if (!dtype_ok(d->x_dtype)) return GDN_ERR_DTYPE;
+    if (d->state_dtype != d->x_dtype && d->state_dtype != GDN_F32) return GDN_ERR_DTYPE;
+    if (d->flags & ~(uint32_t)GDN_CONV_SILU) return GDN_ERR_UNSUPPORTED;
+    const long long L = (long long)(d->W - 1) * d->D;
+    if (L > INT_MAX || (long long)d->B * d->C > INT_MAX) return GDN_ERR_OVERFLOW;
+    if (d->W > 8) return GDN_ERR_UNSUPPORTED;
+    if (misaligned(x) || misaligned(w) || misaligned(bias) || misaligned(state_in) || misaligned(y) ||
+        misaligned(state_out))
+        return GDN_ERR_ALIGN;
+    gdn::ConvLaunch a;
+    a.x = x;
+    a.w = w;
+    a.bias = bias;
+    a.state_in = L > 0 ? state_in : nullptr;
+    a.y = y;
+    a.state_out = L > 0 ? state_out : nullptr;
+    a.offsets = offsets;
+    a.dev_status = dev_status;
+    a.B = d->B;
+    a.N = d->N;
+    a.C = d->C;
+    a.W = d->W;
+    a.D = d->D;
+    a.x_dtype = d->x_dtype;
+    a.state_dtype = d->state_dtype;
+    a.silu = (d->flags & GDN_CONV_SILU) != 0;
+    return from_hip(gdn::launch_conv(a, stream));
+}
+
+gdn_status gdn_prepare_qk_gates(const gdn_scan_desc* d, const void* qkv, const void* a, const void* b,
+                                const float* A_log, const float* dt_bias, float* qk_out, float* gb_out,
+                                hipStream_t stream) {
+    const gdn_status st = check_scan_desc(d);
+    if (st != GDN_OK) return st;
+    if (qk_out == nullptr && gb_out == nullptr) return GDN_ERR_NULL;
+    if (d->N > 0 && qkv == nullptr && qk_out != nullptr) return GDN_ERR_NULL;
+    if (a != nullptr && (d->flags & GDN_SOFTPLUS) && (A_log == nullptr || dt_bias == nullptr)) return GDN_ERR_NULL;
+    if (misaligned(qkv) || misaligned(qk_out) || misaligned(gb_out)) return GDN_ERR_ALIGN;
+    if (d->N == 0) return GDN_OK;
+    gdn::PrepareLaunch p;
+    p.qkv = qkv;
+    p.a = a;
+    p.b = b;
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.qk_out = qk_out;
+    p.gb_out = gb_out;
+    p.N = d->N;
+    p.HQ = d->HQ;
+    p.H = d->H;
+    p.K = d->K;
+    p.V = d->V;
+    p.qkv_dtype = d->qkv_dtype;
+    p.gate_dtype = d->gate_dtype;
+    p.flags = d->flags;
+    return from_hip(gdn::launch_prepare(p, stream));
+}
+
+gdn_status gdn_scan_workspace_bytes(const gdn_scan_desc* d, size_t* bytes) {
+    if (bytes == nullptr) return GDN_ERR_NULL;
+    const gdn_status st = check_scan_desc(d);
+    if (st != GDN_OK) return st;
+    // Resolved as AUTO would with an unlimited workspace, assuming fused inputs with a decay input.
+    const int path = resolve_path(d, false, true, SIZE_MAX);
+    *bytes = path == GDN_PATH_CHUNK ? gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V) : 0;
+    return GDN_OK;
+}
+
+gdn_status gdn_scan_varlen(const gdn_scan_desc* d, const void* qkv, const float* qk_prep, const float* gb_prep,
+                           const void* a, const void* b, const float* A_log, const float* dt_bias,
+                           const float* state_in, void* out, float* state_out, const int32_t* offsets,
+                           void* workspace, size_t ws_bytes, int32_t* dev_status, int32_t* path_used,
+                           hipStream_t stream) {
+    const gdn_status st = check_scan_desc(d);
+    if (st != GDN_OK) return st;
+    if (offsets == nullptr) return GDN_ERR_NULL;
+    if (d->N > 0 && (qkv == nullptr || out == nullptr)) return GDN_ERR_NULL;
+    if ((qk_prep == nullptr) != (gb_prep == nullptr)) return GDN_ERR_NULL;
+    const bool prepared = qk_prep != nullptr;
+    if (!prepared && a != nullptr && (d->flags & GDN_SOFTPLUS) && (A_log == nullptr || dt_bias == nullptr))
+        return GDN_ERR_NULL;
+    if (misaligned(qkv) || misaligned(qk_prep) || misaligned(gb_prep) || misaligned(state_in) || misaligned(out) ||
+        misaligned(state_out) || misaligned(workspace))
+        return GDN_ERR_ALIGN;
+    const int path = resolve_path(d, prepared, a != nullptr, workspace ? ws_bytes : 0);
+    if (path == GDN_PATH_CHUNK) {
+        if (!chunk_eligible(d, prepared, a != nullptr)) return GDN_ERR_UNSUPPORTED;
+        if (workspace == nullptr || ws_bytes < gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
+            return GDN_ERR_WORKSPACE;
+    }
+    gdn::ScanLaunch s;
+    s.qkv = qkv;
+    s.qk_prep = qk_prep;
+    s.gb_prep = gb_prep;
+    s.a = prepared ? nullptr : a;
+    s.b = prepared ? nullptr : b;
+    s.A_log = A_log;
+    s.dt_bias = dt_bias;
+    s.state_in = state_in;
+    s.out = out;
+    s.state_out = state_out;
+    s.offsets = offsets;
+    s.dev_status = dev_status;
+    s.workspace = workspace;
+    s.ws_bytes = ws_bytes;
+    s.B = d->B;
+    s.N = d->N;
+    s.HQ = d->HQ;
+    s.H = d->H;
+    s.K = d->K;
+    s.V = d->V;
+    s.qkv_dtype = d->qkv_dtype;
+    s.gate_dtype = d->gate_dtype;
+    s.flags = d->flags;
+    s.scale = (d->scale > 0.0f && std::isfinite(d->scale)) ? d->scale : 1.0f / std::sqrt((float)d->K);
+    s.path = path;
+    const hipError_t e = path == GDN_PATH_CHUNK ? gdn::launch_scan_chunked(s, stream)
+                                                : gdn::launch_scan_recurrent(s, stream);
+    const gdn_status rs = from_hip(e);
+    if (rs == GDN_OK && path_used != nullptr) *path_used = path;
+    return rs;
+}
+
+}  // extern "C"

@@ -1,0 +1,270 @@
+// gdn_conv.hip -- varlen depthwise causal conv1d with a carried window (gfx950).
+//
+// Operation: paged_ssm.rs page, kernel string CONV (see gdn.h for the definition).  The page's
+// kernel runs one thread per (sequence, channel), serial over the sequence.  Here the work is
+// token-parallel instead, which is what fills 256 CUs for a single long sequence:
+//
+//   * a thread owns VEC adjacent channels (16 bytes of a token row: 8 half or 4 fp32 channels), so
+//     every row access of a wave is one contiguous, fully coalesced segment;
+//   * "body" blocks own a tile of TT consecutive packed tokens and compute every token whose local
+//     index is >= L (all taps then fall inside the sequence); for dilation 1 the W taps slide
+//     through registers, so each token row is loaded once;
+//   * "head" blocks own one sequence: they compute its first min(L, len) tokens -- the only ones
+//     whose taps reach into the carried window -- and then write the new window.  The window is
+//     read and written by the same thread in that order, so state_out may alias state_in.
+//
+// Every block checks the whole offsets array first and writes nothing when it is malformed.
+#include <type_traits>
+
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+namespace {
+
+struct ConvArgs {
+    const void* x;
+    const void* w;
+    const void* bias;
+    const void* state_in;  // not restrict: may alias state_out
+    void* y;
+    void* state_out;
+    const int32_t* offsets;
+    int32_t* dev_status;
+    int B, N, C, D, L;
+    int silu;
+    int n_cvec;  // C / VEC
+    int n_cblk;  // channel blocks per item
+    int tile;    // tokens per body block
+};
+
+template <typename T, int VEC>
+__device__ __forceinline__ void load_row(const typename T::storage* p, float (&v)[VEC]) {
+    if constexpr (VEC == 1) {
+        v[0] = to_f32<T>(p[0]);
+    } else {
+        static_assert(VEC * sizeof(typename T::storage) == 16, "one 16-byte vector per thread");
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(p);
+        if constexpr (std::is_same<T, F32>::value) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(raw[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = to_f32<T>((uint16_t)(raw[i] & 0xffffu));
+                v[2 * i + 1] = to_f32<T>((uint16_t)(raw[i] >> 16));
+            }
+        }
+    }
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void store_row(typename T::storage* p, const float (&v)[VEC]) {
+    if constexpr (VEC == 1) {
+        p[0] = from_f32<T>(v[0]);
+    } else {
+        u32x4 raw;
+        if constexpr (std::is_same<T, F32>::value) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) raw[i] = __float_as_uint(v[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                raw[i] = (uint32_t)from_f32<T>(v[2 * i]) | ((uint32_t)from_f32<T>(v[2 * i + 1]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(p) = raw;
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void activate(float (&acc)[VEC], int silu) {
+    if (silu) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] = acc[i] / (1.0f + expf(-acc[i]));
+    }
+}
+
+// T: element type of x, w, bias, y.  S: element type of the window (T or F32).
+template <typename T, typename S, int VEC, int W>
+__global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
+    using TS = typename T::storage;
+    using SS = typename S::storage;
+    const bool malformed = offsets_malformed(p.offsets, p.B, p.N);
+    report_status(p.dev_status, malformed);
+    if (malformed) return;
+
+    const int item = (int)(blockIdx.x / (unsigned)p.n_cblk);
+    const int cvec = (int)(blockIdx.x % (unsigned)p.n_cblk) * (int)blockDim.x + (int)threadIdx.x;
+    if (cvec >= p.n_cvec) return;
+    const int C = p.C, D = p.D, L = p.L;
+    const int c0 = cvec * VEC;
+    const TS* __restrict__ x = static_cast<const TS*>(p.x);
+    TS* __restrict__ y = static_cast<TS*>(p.y);
+
+    float wr[VEC][W];
+    {
+        const TS* wp = static_cast<const TS*>(p.w) + (size_t)c0 * W;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+#pragma unroll
+            for (int j = 0; j < W; ++j) wr[i][j] = to_f32<T>(wp[i * W + j]);
+    }
+    float bias[VEC];
+    if (p.bias != nullptr) {
+        load_row<T, VEC>(static_cast<const TS*>(p.bias) + c0, bias);
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) bias[i] = 0.0f;
+    }
+
+    if (item < p.B) {
+        // ---- head: the first min(L, len) tokens of sequence b, then the new window ----------------
+        const int b = item;
+        const int start = p.offsets[b];
+        const int len = p.offsets[b + 1] - start;
+        const SS* st_in = static_cast<const SS*>(p.state_in);
+        SS* st_out = static_cast<SS*>(p.state_out);
+        const size_t wrow = ((size_t)b * C + c0) * (size_t)L;  // window of channel c0 + i at wrow + i*L
+        const int nh = len < L ? len : L;
+        for (int l = 0; l < nh; ++l) {
+            float acc[VEC];
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] = bias[i];
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                const int m = l - (W - 1 - j) * D;
+                float xv[VEC];
+                if (m >= 0) {
+                    load_row<T, VEC>(x + (size_t)(start + m) * C + c0, xv);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i)
+                        xv[i] = st_in ? to_f32<S>(st_in[wrow + (size_t)i * L + (L + m)]) : 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[i] = fmaf(wr[i][j], xv[i], acc[i]);
+            }
+            activate<VEC>(acc, p.silu);
+            store_row<T, VEC>(y + (size_t)(start + l) * C + c0, acc);
+        }
+        if (st_out != nullptr) {
+            // new window: entry j is xv(len - L + j); reading index len + j >= j of the old window
+            // before writing index j keeps an aliased (in-place) update correct.
+            for (int j = 0; j < L; ++j) {
+                const int m = len - L + j;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    SS v;
+                    if (m >= 0) {
+                        const TS xs = x[(size_t)(start + m) * C + c0 + i];
+                        if constexpr (std::is_same<S, T>::value) v = xs;
+                        else v = to_f32<T>(xs);  // exact widening into an fp32 window
+                    } else {
+                        v = st_in ? st_in[wrow + (size_t)i * L + (L + m)] : (SS)0;
+                    }
+                    st_out[wrow + (size_t)i * L + j] = v;
+                }
+            }
+        }
+        return;
+    }
+
+    // ---- body: tokens [t0, t1) with local index >= L ----------------------------------------------
+    const int t0 = (item - p.B) * p.tile;
+    const int t1 = min(t0 + p.tile, p.N);
+    int b = find_sequence(p.offsets, p.B, t0);
+    int next = p.offsets[b + 1];
+    float ring[W][VEC];  // ring[j] = x[t - (W-1-j)*D]
+    int ring_t = -2;
+    for (int t = t0; t < t1; ++t) {
+        while (next <= t) {
+            ++b;
+            next = p.offsets[b + 1];
+        }
+        const int l = t - p.offsets[b];
+        if (l < L) continue;  // reaches into the window: computed by the head block
+        if (D == 1 && ring_t == t - 1) {
+#pragma unroll
+            for (int j = 0; j + 1 < W; ++j)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) ring[j][i] = ring[j + 1][i];
+            load_row<T, VEC>(x + (size_t)t * C + c0, ring[W - 1]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < W; ++j) load_row<T, VEC>(x + (size_t)(t - (W - 1 - j) * D) * C + c0, ring[j]);
+        }
+        ring_t = t;
+        float acc[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] = bias[i];
+#pragma unroll
+        for (int j = 0; j < W; ++j)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] = fmaf(wr[i][j], ring[j][i], acc[i]);
+        activate<VEC>(acc, p.silu);
+        store_row<T, VEC>(y + (size_t)t * C + c0, acc);
+    }
+}
+
+template <typename T, typename S, int VEC>
+hipError_t launch_vec(const ConvLaunch& a, hipStream_t stream) {
+    ConvArgs p;
+    p.x = a.x;
+    p.w = a.w;
+    p.bias = a.bias;
+    p.state_in = a.state_in;
+    p.y = a.y;
+    p.state_out = a.state_out;
+    p.offsets = a.offsets;
+    p.dev_status = a.dev_status;
+    p.B = a.B;
+    p.N = a.N;
+    p.C = a.C;
+    p.D = a.D;
+    p.L = (a.W - 1) * a.D;
+    p.silu = a.silu ? 1 : 0;
+    p.n_cvec = a.C / VEC;
+    const int threads = p.n_cvec >= 256 ? 256 : ((p.n_cvec + 63) / 64) * 64;
+    p.n_cblk = (p.n_cvec + threads - 1) / threads;
+    p.tile = 16;
+    const long long n_tiles = ((long long)a.N + p.tile - 1) / p.tile;
+    const long long blocks = ((long long)a.B + n_tiles) * p.n_cblk;
+    if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
+    switch (a.W) {
+#define GDN_CONV_CASE(WW)                                                                                    \
+    case WW:                                                                                                 \
+        hipLaunchKernelGGL((conv_kernel<T, S, VEC, WW>), dim3((unsigned)blocks), dim3(threads), 0, stream, p); \
+        break;
+        GDN_CONV_CASE(1)
+        GDN_CONV_CASE(2)
+        GDN_CONV_CASE(3)
+        GDN_CONV_CASE(4)
+        GDN_CONV_CASE(5)
+        GDN_CONV_CASE(6)
+        GDN_CONV_CASE(7)
+        GDN_CONV_CASE(8)
+#undef GDN_CONV_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename S>
+hipError_t launch_typed(const ConvLaunch& a, hipStream_t stream) {
+    constexpr int VEC = 16 / (int)sizeof(typename T::storage);
+    if (a.C % VEC == 0) return launch_vec<T, S, VEC>(a, stream);
+    return launch_vec<T, S, 1>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_conv(const ConvLaunch& a, hipStream_t stream) {
+    const int xs = a.x_dtype, ss = a.state_dtype;
+    if (xs == GDN_F32) return launch_typed<F32, F32>(a, stream);
+    if (xs == GDN_BF16) return ss == GDN_F32 ? launch_typed<BF16, F32>(a, stream) : launch_typed<BF16, BF16>(a, stream);
+    if (xs == GDN_F16) return ss == GDN_F32 ? launch_typed<F16, F32>(a, stream) : launch_typed<F16, F16>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

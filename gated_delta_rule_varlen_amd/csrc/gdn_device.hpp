@@ -1,0 +1,144 @@
+// gdn_device.hpp -- device helpers shared by the libgdn kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+// Storage tags: the kernels are templated on these; values are always widened to fp32.
+struct F32 {
+    using storage = float;
+    static constexpr int code = GDN_F32;
+};
+struct BF16 {
+    using storage = uint16_t;
+    static constexpr int code = GDN_BF16;
+};
+struct F16 {
+    using storage = uint16_t;
+    static constexpr int code = GDN_F16;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even (v_cvt on gfx950)
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(typename T::storage v);
+template <>
+__device__ __forceinline__ float to_f32<F32>(float v) { return v; }
+template <>
+__device__ __forceinline__ float to_f32<BF16>(uint16_t v) { return bf16_bits_to_f32(v); }
+template <>
+__device__ __forceinline__ float to_f32<F16>(uint16_t v) { return f16_bits_to_f32(v); }
+
+template <typename T>
+__device__ __forceinline__ typename T::storage from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<F32>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t from_f32<BF16>(float v) { return f32_to_bf16_bits(v); }
+template <>
+__device__ __forceinline__ uint16_t from_f32<F16>(float v) { return f32_to_f16_bits(v); }
+
+// Load one element of a runtime-typed tensor (gate inputs) as fp32.
+__device__ __forceinline__ float load_any(const void* p, int dtype, size_t i) {
+    if (dtype == GDN_F32) return static_cast<const float*>(p)[i];
+    const uint16_t h = static_cast<const uint16_t*>(p)[i];
+    return dtype == GDN_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+}
+
+// Load 4 consecutive elements (8- or 16-byte aligned) and widen to fp32.
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const typename T::storage* p);
+template <>
+__device__ __forceinline__ f32x4 load4<F32>(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<BF16>(const uint16_t* p) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                 __uint_as_float(w.y & 0xffff0000u)};
+}
+template <>
+__device__ __forceinline__ f32x4 load4<F16>(const uint16_t* p) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    return f32x4{f16_bits_to_f32(w.x & 0xffffu), f16_bits_to_f32(w.x >> 16), f16_bits_to_f32(w.y & 0xffffu),
+                 f16_bits_to_f32(w.y >> 16)};
+}
+
+// DPP lane permutation of a float within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i within each half row
+constexpr int DPP_MIRROR = 0x140;     // lane i <-> 15-i within each row
+
+// Sum over aligned groups of N consecutive lanes (N a power of two <= 64); every lane of a group
+// receives the group's sum.  Within a 16-lane row the butterfly uses DPP; wider groups add
+// cross-row swizzles.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (N >= 2) x += dpp<DPP_QUAD_XOR1>(x);
+    if constexpr (N >= 4) x += dpp<DPP_QUAD_XOR2>(x);
+    if constexpr (N >= 8) x += dpp<DPP_HALF_MIRROR>(x);
+    if constexpr (N >= 16) x += dpp<DPP_MIRROR>(x);
+    if constexpr (N >= 32) x += __shfl_xor(x, 16);
+    if constexpr (N >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Whole-call offsets check, done cooperatively by every thread of a block.  Offsets are valid iff
+// offsets[0] == 0, offsets[B] == N and they never decrease (which keeps every entry in [0, N]).
+// Must be reached by all threads of the block.  Returns true when the offsets are malformed.
+__device__ __forceinline__ bool offsets_malformed(const int32_t* __restrict__ offsets, int B, int N) {
+    int bad = 0;
+    for (int i = threadIdx.x; i <= B; i += blockDim.x) {
+        const int o = offsets[i];
+        if (i == 0) bad |= (o != 0);
+        else bad |= (offsets[i - 1] > o);
+        if (i == B) bad |= (o != N);
+    }
+    return __syncthreads_or(bad) != 0;
+}
+
+// The block with linear index 0 reports the verdict of the offsets check.
+__device__ __forceinline__ void report_status(int32_t* dev_status, bool malformed) {
+    if (dev_status != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        *dev_status = malformed ? GDN_ERR_OFFSETS : GDN_OK;
+}
+
+// Sequence containing token t: the last b in [0, B) with offsets[b] <= t (offsets already valid,
+// t < N).  Zero-length sequences share their start with the next one and are skipped.
+__device__ __forceinline__ int find_sequence(const int32_t* __restrict__ offsets, int B, int t) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offsets[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace gdn

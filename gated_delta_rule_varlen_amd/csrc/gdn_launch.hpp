@@ -1,0 +1,70 @@
+// gdn_launch.hpp -- host-side launchers of the libgdn kernels (internal; not part of the ABI).
+// The entry points in gdn_api.cpp validate every argument and then call exactly one of these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+struct ConvLaunch {
+    const void* x;
+    const void* w;
+    const void* bias;
+    const void* state_in;
+    void* y;
+    void* state_out;
+    const int32_t* offsets;
+    int32_t* dev_status;
+    int B, N, C, W, D;
+    int x_dtype, state_dtype;
+    bool silu;
+};
+hipError_t launch_conv(const ConvLaunch& a, hipStream_t stream);
+
+struct PrepareLaunch {
+    const void* qkv;
+    const void* a;
+    const void* b;
+    const float* A_log;
+    const float* dt_bias;
+    float* qk_out;
+    float* gb_out;
+    int N, HQ, H, K, V;
+    int qkv_dtype, gate_dtype;
+    uint32_t flags;
+};
+hipError_t launch_prepare(const PrepareLaunch& a, hipStream_t stream);
+
+struct ScanLaunch {
+    const void* qkv;
+    const float* qk_prep;  // non-NULL selects the prepared variant
+    const float* gb_prep;
+    const void* a;
+    const void* b;
+    const float* A_log;
+    const float* dt_bias;
+    const float* state_in;
+    void* out;
+    float* state_out;
+    const int32_t* offsets;
+    int32_t* dev_status;
+    void* workspace;
+    size_t ws_bytes;
+    int B, N, HQ, H, K, V;
+    int qkv_dtype, gate_dtype;
+    uint32_t flags;
+    float scale;  // already resolved (> 0)
+    int path;     // resolved: GDN_PATH_DECODE, GDN_PATH_SEQ or GDN_PATH_CHUNK
+};
+hipError_t launch_scan_recurrent(const ScanLaunch& a, hipStream_t stream);  // DECODE and SEQ
+hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream);    // CHUNK
+size_t chunked_workspace_bytes(int B, int N, int HQ, int H, int K, int V);
+
+// Limits of the launch grids (checked by the entry points before launching).
+constexpr long long kMaxBlocks = (1ll << 31) - 1;
+
+}  // namespace gdn

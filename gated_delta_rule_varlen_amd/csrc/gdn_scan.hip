@@ -1,0 +1,334 @@
+// gdn_scan.hip -- gated delta-rule recurrence, token-sequential form (gfx950, wave64).
+//
+// Operation: paged_ssm.rs page, kernel string DELTA (see gdn.h).  Every value column (b, h, v) is an
+// independent recurrence over a K-vector s.  Work mapping:
+//
+//   * a column is owned by a group of LPC adjacent lanes; lane j of the group holds the K-indices
+//     4*(j + LPC*i) + e (i < K/(4*LPC), e < 4), so every 16-byte state access of a group is one
+//     contiguous 16*LPC-byte segment and the state of a block streams with perfectly coalesced
+//     loads and stores;
+//   * a lane group carries CPL columns of the same head, a wave 64/LPC groups, a block NW waves;
+//     blocks are laid out (sequence, head, column tile) and re-mapped so that the blocks of one
+//     head land on one XCD (they read the same q/k rows through that XCD's L2);
+//   * per token the two state dot products k.s and q.s of the OLD state are computed together, then
+//     reduced over the group with a 4-step DPP butterfly (the page's 32-wide simd_sum becomes a
+//     16-lane row reduction).  Using
+//         r = g (k^.s),  delta = beta (v - r),  q^.s' = g (q^.s) + delta (q^.k^)
+//     the readout needs no second reduction after the update, which halves the serial chain;
+//   * "fused" instances normalise q/k and evaluate the gates in-kernel from the raw inputs (one
+//     launch per decode step: no prepare pass, no fp32 q/k round trip through HBM); "prepared"
+//     instances read the fp32 outputs of gdn_prepare_qk_gates;
+//   * the next token's operands are loaded while the current token is computed.
+//
+// DECODE instances stream the state with non-temporal loads/stores (read once, written once).
+#include <type_traits>
+
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+namespace {
+
+struct ScanArgs {
+    const void* qkv;
+    const float* qk_prep;
+    const float* gb_prep;
+    const void* a;
+    const void* b;
+    const float* A_log;
+    const float* dt_bias;
+    const float* state_in;  // not restrict: may alias state_out
+    void* out;
+    float* state_out;
+    const int32_t* offsets;
+    int32_t* dev_status;
+    int B, N, HQ, H, K, V, C, G;
+    int gate_dtype;
+    uint32_t flags;
+    float scale;
+    int n_vtiles;   // column tiles per (sequence, head)
+    int n_blocks;   // grid size
+};
+
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
+
+// Blocks are dispatched round-robin over the 8 XCDs; this makes logical blocks [i*n/8, (i+1)*n/8)
+// run on XCD i, so neighbouring logical blocks (same head) share an L2.
+__device__ __forceinline__ int xcd_remap(int phys, int n) {
+    const int per = n >> 3;
+    if (phys >= per * 8) return phys;
+    return (phys & 7) * per + (phys >> 3);
+}
+
+template <bool NT>
+__device__ __forceinline__ f32x4 ld_state(const float* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    else return *reinterpret_cast<const f32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st_state(float* p, f32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+    else *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// Operands of one token as seen by one lane.
+template <int EPL, int CPL>
+struct TokenOps {
+    float q[EPL];
+    float k[EPL];
+    float v[CPL];
+    float ga;  // prepared: g; fused: raw decay input (0 when absent)
+    float gb;  // prepared: beta; fused: raw rate input (0 when absent)
+};
+
+template <typename T, int K, int LPC, int CPL, bool PREP>
+__device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int kh, int gl, int vbase,
+                                           TokenOps<K / LPC, CPL>& o) {
+    constexpr int EPL = K / LPC;
+    using TS = typename T::storage;
+    if constexpr (PREP) {
+        const float* qp = p.qk_prep + ((size_t)t * p.HQ + kh) * K;
+        const float* kp = p.qk_prep + (((size_t)p.N + t) * p.HQ + kh) * K;
+#pragma unroll
+        for (int i = 0; i < EPL / 4; ++i) {
+            const f32x4 qv = *reinterpret_cast<const f32x4*>(qp + 4 * (gl + LPC * i));
+            const f32x4 kv = *reinterpret_cast<const f32x4*>(kp + 4 * (gl + LPC * i));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o.q[4 * i + e] = qv[e];
+                o.k[4 * i + e] = kv[e];
+            }
+        }
+        o.ga = p.gb_prep[(size_t)t * p.H + h];
+        o.gb = p.gb_prep[((size_t)p.N + t) * p.H + h];
+    } else {
+        const TS* row = static_cast<const TS*>(p.qkv) + (size_t)t * p.C;
+        const TS* qp = row + (size_t)kh * K;
+        const TS* kp = row + (size_t)p.HQ * K + (size_t)kh * K;
+#pragma unroll
+        for (int i = 0; i < EPL / 4; ++i) {
+            const f32x4 qv = load4<T>(qp + 4 * (gl + LPC * i));
+            const f32x4 kv = load4<T>(kp + 4 * (gl + LPC * i));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o.q[4 * i + e] = qv[e];
+                o.k[4 * i + e] = kv[e];
+            }
+        }
+        const size_t gi = (size_t)t * p.H + h;
+        o.ga = p.a ? load_any(p.a, p.gate_dtype, gi) : 0.0f;
+        o.gb = p.b ? load_any(p.b, p.gate_dtype, gi) : 0.0f;
+    }
+    const TS* vp = static_cast<const TS*>(p.qkv) + (size_t)t * p.C + (size_t)2 * p.HQ * K + (size_t)h * p.V + vbase;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o.v[c] = (vbase + c < p.V) ? to_f32<T>(vp[c]) : 0.0f;
+}
+
+template <typename T, int K, int LPC, int CPL, bool PREP, bool NT>
+__global__ __launch_bounds__(64) void scan_kernel(ScanArgs p) {
+    constexpr int EPL = K / LPC;  // state elements per lane per column
+    static_assert(EPL % 4 == 0, "whole 16-byte chunks per lane");
+    constexpr int GPW = 64 / LPC;  // lane groups per wave
+    constexpr int WC = GPW * CPL;  // columns per wave (= per block)
+    using TS = typename T::storage;
+
+    const bool malformed = offsets_malformed(p.offsets, p.B, p.N);
+    report_status(p.dev_status, malformed);
+    if (malformed) return;
+
+    const int blk = xcd_remap((int)blockIdx.x, p.n_blocks);
+    const int vt = blk % p.n_vtiles;
+    const int bh = blk / p.n_vtiles;
+    const int h = bh % p.H;
+    const int b = bh / p.H;
+    const int kh = h / p.G;
+    const int lane = (int)threadIdx.x;
+    const int grp = lane / LPC, gl = lane % LPC;
+    const int vbase = vt * WC + grp * CPL;
+    const size_t col0 = ((size_t)b * p.H + h) * p.V;
+
+    float s[CPL][EPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const bool valid = (vbase + c < p.V) && p.state_in != nullptr;
+        const float* sp = p.state_in + (col0 + vbase + c) * K;
+#pragma unroll
+        for (int i = 0; i < EPL / 4; ++i) {
+            const f32x4 v = valid ? ld_state<NT>(sp + 4 * (gl + LPC * i)) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[c][4 * i + e] = v[e];
+        }
+    }
+
+    const int start = p.offsets[b], end = p.offsets[b + 1];
+    const bool l2 = (p.flags & GDN_L2NORM) != 0;
+    const bool softplus = (p.flags & GDN_SOFTPLUS) != 0;
+    const bool sigmoid = (p.flags & GDN_SIGMOID) != 0;
+    const float a_mul = (!PREP && p.a && softplus) ? -expf(p.A_log[h]) : 0.0f;
+    const float a_bias = (!PREP && p.a && softplus) ? p.dt_bias[h] : 0.0f;
+    TS* outp = static_cast<TS*>(p.out);
+
+    TokenOps<EPL, CPL> cur;
+    if (start < end) load_token<T, K, LPC, CPL, PREP>(p, start, h, kh, gl, vbase, cur);
+    for (int t = start; t < end; ++t) {
+        TokenOps<EPL, CPL> nxt;
+        if (t + 1 < end) load_token<T, K, LPC, CPL, PREP>(p, t + 1, h, kh, gl, vbase, nxt);
+
+        float g, beta;
+        if constexpr (PREP) {
+            g = cur.ga;
+            beta = cur.gb;
+        } else {
+            g = 1.0f;
+            if (p.a) g = softplus ? expf(a_mul * softplus_f(cur.ga + a_bias)) : expf(cur.ga);
+            beta = 1.0f;
+            if (p.b) beta = sigmoid ? 1.0f / (1.0f + expf(-cur.gb)) : cur.gb;
+        }
+
+        float pk[CPL], pq[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            pk[c] = 0.0f;
+            pq[c] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                pk[c] = fmaf(s[c][e], cur.k[e], pk[c]);
+                pq[c] = fmaf(s[c][e], cur.q[e], pq[c]);
+            }
+        }
+        float qk = 0.0f, nq = 0.0f, nk = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            qk = fmaf(cur.q[e], cur.k[e], qk);
+            if constexpr (!PREP) {
+                nq = fmaf(cur.q[e], cur.q[e], nq);
+                nk = fmaf(cur.k[e], cur.k[e], nk);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            pk[c] = group_sum<LPC>(pk[c]);
+            pq[c] = group_sum<LPC>(pq[c]);
+        }
+        qk = group_sum<LPC>(qk);
+        float rq = 1.0f, rk = 1.0f;
+        if constexpr (!PREP) {
+            if (l2) {
+                rq = rsqrtf(group_sum<LPC>(nq) + 1e-12f);
+                rk = rsqrtf(group_sum<LPC>(nk) + 1e-12f);
+            }
+        }
+        const float oscale = p.scale * rq;
+        float mine = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float r = g * rk * pk[c];
+            const float dk = beta * (cur.v[c] - r) * rk;  // delta * rk: coefficient of the raw k
+            const float o = oscale * fmaf(g, pq[c], dk * qk);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) s[c][e] = fmaf(g, s[c][e], dk * cur.k[e]);
+            if (gl == c) mine = o;
+        }
+        if (gl < CPL && vbase + gl < p.V) outp[((size_t)t * p.H + h) * p.V + vbase + gl] = from_f32<T>(mine);
+        cur = nxt;
+    }
+
+    if (p.state_out != nullptr) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            if (vbase + c >= p.V) continue;
+            float* sp = p.state_out + (col0 + vbase + c) * K;
+#pragma unroll
+            for (int i = 0; i < EPL / 4; ++i)
+                st_state<NT>(sp + 4 * (gl + LPC * i),
+                             f32x4{s[c][4 * i], s[c][4 * i + 1], s[c][4 * i + 2], s[c][4 * i + 3]});
+        }
+    }
+}
+
+template <typename T, int K, int LPC, int CPL, bool PREP, bool NT>
+hipError_t launch_tile(ScanArgs p, hipStream_t stream) {
+    constexpr int WC = (64 / LPC) * CPL;
+    p.n_vtiles = (p.V + WC - 1) / WC;
+    const long long blocks = (long long)p.B * p.H * p.n_vtiles;
+    if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
+    p.n_blocks = (int)blocks;
+    hipLaunchKernelGGL((scan_kernel<T, K, LPC, CPL, PREP, NT>), dim3((unsigned)blocks), dim3(64), 0, stream, p);
+    return hipGetLastError();
+}
+
+// Tile choice.  DECODE: 4 columns per lane group (many sequences; streaming).  SEQ: the widest
+// tile that still gives at least two waves per SIMD (2048 waves), down to one column per group.
+template <typename T, int K, bool PREP>
+hipError_t launch_k(const ScanArgs& p, int path, hipStream_t stream) {
+    constexpr int LPC = K >= 64 ? 16 : 8;
+    if (path == GDN_PATH_DECODE) {
+        if constexpr (K >= 256) return launch_tile<T, K, LPC, 2, PREP, true>(p, stream);
+        else return launch_tile<T, K, LPC, 4, PREP, true>(p, stream);
+    }
+    const long long cols = (long long)p.B * p.H * p.V;
+    constexpr int GPW = 64 / LPC;
+    if constexpr (K <= 128) {
+        if (cols / (GPW * 2) >= 2048) return launch_tile<T, K, LPC, 2, PREP, false>(p, stream);
+    }
+    if constexpr (K >= 128) {
+        if (cols / GPW < 2048) return launch_tile<T, K, 32, 1, PREP, false>(p, stream);
+    }
+    return launch_tile<T, K, LPC, 1, PREP, false>(p, stream);
+}
+
+template <typename T, bool PREP>
+hipError_t launch_t(const ScanArgs& p, int path, hipStream_t stream) {
+    switch (p.K) {
+        case 32: return launch_k<T, 32, PREP>(p, path, stream);
+        case 64: return launch_k<T, 64, PREP>(p, path, stream);
+        case 128: return launch_k<T, 128, PREP>(p, path, stream);
+        case 256: return launch_k<T, 256, PREP>(p, path, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool PREP>
+hipError_t launch_p(const ScanArgs& p, int dtype, int path, hipStream_t stream) {
+    switch (dtype) {
+        case GDN_F32: return launch_t<F32, PREP>(p, path, stream);
+        case GDN_BF16: return launch_t<BF16, PREP>(p, path, stream);
+        case GDN_F16: return launch_t<F16, PREP>(p, path, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_scan_recurrent(const ScanLaunch& a, hipStream_t stream) {
+    ScanArgs p;
+    p.qkv = a.qkv;
+    p.qk_prep = a.qk_prep;
+    p.gb_prep = a.gb_prep;
+    p.a = a.a;
+    p.b = a.b;
+    p.A_log = a.A_log;
+    p.dt_bias = a.dt_bias;
+    p.state_in = a.state_in;
+    p.out = a.out;
+    p.state_out = a.state_out;
+    p.offsets = a.offsets;
+    p.dev_status = a.dev_status;
+    p.B = a.B;
+    p.N = a.N;
+    p.HQ = a.HQ;
+    p.H = a.H;
+    p.K = a.K;
+    p.V = a.V;
+    p.C = 2 * a.HQ * a.K + a.H * a.V;
+    p.G = a.H / a.HQ;
+    p.gate_dtype = a.gate_dtype;
+    p.flags = a.flags;
+    p.scale = a.scale;
+    p.n_vtiles = 0;
+    p.n_blocks = 0;
+    if (a.qk_prep != nullptr) return launch_p<true>(p, a.qkv_dtype, a.path, stream);
+    return launch_p<false>(p, a.qkv_dtype, a.path, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,193 @@
+/*
+ * gdn.h -- C ABI of libgdn, the MI355X (gfx950) varlen gated delta-rule hot path.
+ *
+ * Three operations, each one asynchronous launch sequence on the caller's HIP stream:
+ *   gdn_conv1d_varlen     depthwise causal conv1d over offset-packed sequences, with a carried
+ *                         (W-1)*D window per (sequence, channel)
+ *   gdn_prepare_qk_gates  per-token q/k L2 normalisation plus the decay and update-rate gates
+ *   gdn_scan_varlen       the gated delta-rule recurrence with a per-(sequence, head) state
+ *
+ * Sources (docs.rs source pages): "onnxruntime-ep-mlx 0.31.1 src/ops/paged_ssm.rs" -- kernel strings
+ * CONV, DELTA_PREPARE and DELTA, host functions conv(), delta() and the claim predicates; and
+ * "mlx-c-rust compile/gated_delta_rate_activation.rs" -- the rate-activation graph.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library allocates nothing,
+ *     keeps no state between calls and is re-entrant.  Descriptor pointers and path_used are host
+ *     pointers.  Calls return as soon as the work is queued on `stream` (NULL = default stream).
+ *   - Packed tokens: offsets[B+1] (int32, device) delimit sequence b as tokens
+ *     [offsets[b], offsets[b+1]).  Offsets are valid iff offsets[0] == 0, offsets[B] == N and they
+ *     never decrease (zero-length sequences are allowed).  Invalid offsets are detected on the
+ *     device: then NO element of any output is written, and *dev_status (when dev_status is not
+ *     NULL) receives GDN_ERR_OFFSETS; on valid offsets *dev_status receives GDN_OK.  The call
+ *     itself still returns GDN_OK, because detection is asynchronous.
+ *   - Argument errors are detected on the host before anything is launched: the call returns a
+ *     negative gdn_status and writes nothing.
+ *   - Pointers to tensors must be 16-byte aligned (GDN_ERR_ALIGN otherwise).
+ *   - state_out may alias state_in (in-place update); no other aliasing is allowed.
+ *   - Element types: GDN_F32, GDN_BF16 (bfloat16), GDN_F16 (IEEE binary16).  Outputs in a half
+ *     type are rounded to nearest-even from fp32 arithmetic.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = -2,       /* a dimension is out of range or inconsistent */
+    GDN_ERR_DTYPE = -3,       /* unknown or disallowed element type combination */
+    GDN_ERR_OVERFLOW = -4,    /* a size or launch grid does not fit the index types */
+    GDN_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned */
+    GDN_ERR_UNSUPPORTED = -6, /* valid per the op's definition but not built (see each call) */
+    GDN_ERR_WORKSPACE = -7,   /* workspace missing or smaller than gdn_scan_workspace_bytes() */
+    GDN_ERR_HIP = -8,         /* the HIP runtime refused a launch */
+    GDN_ERR_OFFSETS = -9      /* device-detected: malformed offsets (written to *dev_status only) */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
+
+/* ------------------------------------------------------------------------------------------------
+ * gdn_conv1d_varlen -- paged_ssm.rs page, kernel string CONV and host fn conv().
+ *
+ * For sequence b with start = offsets[b], each token t of it (local index l = t - start) and each
+ * channel c:
+ *     y[t,c] = act( bias[c] + sum_{j<W} w[c,j] * xv(l - (W-1-j)*D) )
+ * where xv(m) = x[start+m, c] for m >= 0 and state_in[b, c, L+m] for m < 0 (the carried window,
+ * oldest entry first, L = (W-1)*D).  Tap W-1 multiplies the current token (causal
+ * cross-correlation).  act = SiLU z/(1+e^-z) when GDN_CONV_SILU is set, else identity.  The
+ * arithmetic is fp32.  The new window is the last L entries of (old window ++ the sequence's
+ * tokens), copied bit-exactly (widened exactly when the window type is f32 and x is half):
+ *     state_out[b, c, j] = xv(len - L + j),  j < L.
+ *
+ * Tensors (row-major):
+ *   x          [N, C]     x_dtype                      required unless N == 0
+ *   w          [C, W]     x_dtype                      required
+ *   bias       [C]        x_dtype                      NULL = no bias
+ *   state_in   [B, C, L]  state_dtype                  NULL = zero window
+ *   y          [N, C]     x_dtype                      required unless N == 0
+ *   state_out  [B, C, L]  state_dtype                  NULL = new window not produced; may alias state_in
+ *   offsets    [B+1]      int32                        required
+ *   dev_status [1]        int32                        NULL = no status word
+ * Constraints: B >= 1, N >= 0, C >= 1, 1 <= W <= 8 (GDN_ERR_UNSUPPORTED above 8), D >= 1,
+ * state_dtype is x_dtype or GDN_F32.
+ * ---------------------------------------------------------------------------------------------- */
+#define GDN_CONV_SILU 1u
+
+typedef struct gdn_conv_desc {
+    int32_t B, N, C, W, D;
+    int32_t x_dtype;     /* gdn_dtype of x, w, bias and y */
+    int32_t state_dtype; /* gdn_dtype of the window: x_dtype or GDN_F32 */
+    uint32_t flags;      /* GDN_CONV_SILU */
+} gdn_conv_desc;
+
+gdn_status gdn_conv1d_varlen(const gdn_conv_desc *desc, const void *x, const void *w, const void *bias,
+                             const void *state_in, void *y, void *state_out, const int32_t *offsets,
+                             int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Recurrence descriptor shared by gdn_prepare_qk_gates and gdn_scan_varlen.
+ *
+ * Packed token row (width C = 2*HQ*K + H*V): [q: HQ heads x K | k: HQ heads x K | v: H heads x V]
+ * (paged_ssm.rs page, kernel string DELTA).  Value head h reads key head kh = h / (H/HQ)
+ * (consecutive value heads share a key head).  Flags:
+ *   GDN_L2NORM    q and k are scaled by 1/sqrt(sum x^2 + 1e-12) per (token, key head)
+ *   GDN_SOFTPLUS  decay g = exp(-exp(A_log[h]) * softplus(a + dt_bias[h])); without it a is a raw
+ *                 log-decay and g = exp(a).  softplus(x) = max(x,0) + log1p(exp(-|x|)).
+ *   GDN_SIGMOID   update rate beta = 1/(1+exp(-b)); without it beta = b.
+ * A NULL decay input a means g = 1; a NULL rate input b means beta = 1.  Gate arithmetic is fp32
+ * (gate inputs are widened to fp32 first).  scale <= 0 selects 1/sqrt(K).
+ * Constraints: B >= 1, N >= 0, HQ >= 1, H >= 1, H % HQ == 0, 1 <= K <= 256 (the pages' limit),
+ * V >= 1; this build instantiates K in {32, 64, 128, 256} (GDN_ERR_UNSUPPORTED otherwise).
+ * gate_dtype is GDN_F32 or qkv_dtype.
+ * ---------------------------------------------------------------------------------------------- */
+#define GDN_L2NORM 1u
+#define GDN_SOFTPLUS 2u
+#define GDN_SIGMOID 4u
+
+typedef enum gdn_path {
+    GDN_PATH_AUTO = 0,   /* chosen from the shapes: DECODE when N <= 2*B, else CHUNK when eligible, else SEQ */
+    GDN_PATH_DECODE = 1, /* state streamed once per call; tiles sized for many short sequences */
+    GDN_PATH_SEQ = 2,    /* token-sequential recurrence with the state resident in registers */
+    GDN_PATH_CHUNK = 3   /* chunked WY form (chunk 64); needs a workspace and positive decays */
+} gdn_path;
+
+typedef struct gdn_scan_desc {
+    int32_t B, N, HQ, H, K, V;
+    int32_t qkv_dtype;  /* gdn_dtype of qkv and out */
+    int32_t gate_dtype; /* gdn_dtype of a and b: GDN_F32 or qkv_dtype */
+    uint32_t flags;     /* GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID */
+    float scale;        /* output scale; <= 0 selects 1/sqrt(K) */
+    int32_t path;       /* gdn_path */
+} gdn_scan_desc;
+
+/* ------------------------------------------------------------------------------------------------
+ * gdn_prepare_qk_gates -- paged_ssm.rs page, kernel string DELTA_PREPARE; gate math also on the
+ * gated_delta_rate_activation.rs page.  Token-local: no offsets.
+ *   qk_out[0, t, hq, :] = q of (t, hq), normalised when GDN_L2NORM (else copied), as fp32
+ *   qk_out[1, t, hq, :] = k of (t, hq), likewise
+ *   gb_out[0, t, h] = g,  gb_out[1, t, h] = beta   (fp32)
+ * Tensors: qkv [N, C] qkv_dtype (required); a, b [N, H] gate_dtype (NULL = absent); A_log,
+ * dt_bias [H] fp32 (required when a is given and GDN_SOFTPLUS is set); qk_out [2, N, HQ, K] fp32;
+ * gb_out [2, N, H] fp32.  Either output may be NULL to skip it (not both).
+ * ---------------------------------------------------------------------------------------------- */
+gdn_status gdn_prepare_qk_gates(const gdn_scan_desc *desc, const void *qkv, const void *a, const void *b,
+                                const float *A_log, const float *dt_bias, float *qk_out, float *gb_out,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * gdn_scan_varlen -- paged_ssm.rs page, kernel string DELTA (and the chunked variant the host fn
+ * delta() selects).  For each sequence b, value head h, value column v, with s = state_in[b,h,v,:]
+ * (a K-vector; zeros when state_in is NULL), over the sequence's tokens t in order:
+ *     s <- g*s;  r = k^.s;  delta = beta*(v_t - r);  s <- s + delta*k^;  out[t,h,v] = scale*(q^.s)
+ * then state_out[b,h,v,:] = s.  q^, k^, g, beta are either computed in-kernel from qkv, a, b,
+ * A_log, dt_bias and the flags ("fused"), or read from a prior gdn_prepare_qk_gates call when both
+ * qk_prep and gb_prep are given ("prepared"; then a, b, A_log, dt_bias and the flags are unused).
+ * v_t always comes from qkv.  All recurrence arithmetic is fp32.
+ *
+ * Tensors:
+ *   qkv        [N, C]        qkv_dtype   required
+ *   qk_prep    [2, N, HQ, K] fp32        NULL = fused (must be NULL together with gb_prep)
+ *   gb_prep    [2, N, H]     fp32
+ *   a, b       [N, H]        gate_dtype  NULL = absent (fused mode)
+ *   A_log, dt_bias [H]       fp32        required in fused mode when a is given with GDN_SOFTPLUS
+ *   state_in   [B, H, V, K]  fp32        NULL = zero state
+ *   out        [N, H, V]     qkv_dtype   required unless N == 0
+ *   state_out  [B, H, V, K]  fp32        NULL = final state not produced; may alias state_in
+ *   offsets    [B+1]         int32       required
+ *   workspace  device scratch of ws_bytes bytes, needed only by GDN_PATH_CHUNK (query the size
+ *              with gdn_scan_workspace_bytes); may be NULL otherwise
+ *   dev_status [1] int32 (NULL ok); path_used: HOST int32 receiving the gdn_path that ran (NULL ok)
+ * GDN_PATH_CHUNK requires fused mode with a decay input and GDN_SOFTPLUS (so every decay is
+ * finite and positive), GDN_L2NORM, and K, V multiples of 16; otherwise GDN_ERR_UNSUPPORTED.
+ * ---------------------------------------------------------------------------------------------- */
+gdn_status gdn_scan_varlen(const gdn_scan_desc *desc, const void *qkv, const float *qk_prep, const float *gb_prep,
+                           const void *a, const void *b, const float *A_log, const float *dt_bias,
+                           const float *state_in, void *out, float *state_out, const int32_t *offsets,
+                           void *workspace, size_t ws_bytes, int32_t *dev_status, int32_t *path_used,
+                           hipStream_t stream);
+
+/* Workspace bytes gdn_scan_varlen needs for `desc` (with its path resolved as AUTO would);
+ * 0 when the resolved path needs none.  Returns the same argument errors as gdn_scan_varlen. */
+gdn_status gdn_scan_workspace_bytes(const gdn_scan_desc *desc, size_t *bytes);
+
+/* Static description of a status code; never NULL. */
+const char *gdn_status_string(gdn_status status);
+
+/* GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

@@ -1,0 +1,12 @@
+"""Cached seeded workloads shared by the GPU test modules (one draw per process)."""
+import functools
+
+import workloads
+
+
+@functools.lru_cache(maxsize=None)
+def get(name: str) -> workloads.Workload:
+    return workloads.NAMED[name]()
+
+
+ALL = ("tiny_fp32", "decode", "prefill", "long", "edge_fp16")

@@ -1,0 +1,139 @@
+"""The C-ABI library on the host (CPU only): it loads, exports every symbol include/gdn.h declares,
+and rejects bad arguments with the documented status codes before launching anything.
+
+Only argument sets that fail host validation are passed here, so no call reaches the HIP runtime;
+device pointers are stand-in addresses that are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gpu_util import ensure_built
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def abi():
+    ensure_built()
+    from gated_delta_rule_varlen_amd import _abi
+
+    _abi.lib()
+    return _abi
+
+
+def test_header_declarations_are_all_exported(abi):
+    header = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    declared = set(re.findall(r"^\s*(?:gdn_status|const char \*|int)\s*(gdn_\w+)\s*\(", header, re.M))
+    assert declared == set(abi.EXPORTS)
+    for name in declared:
+        assert hasattr(abi.lib(), name), name
+
+
+def test_version_and_status_strings(abi):
+    assert abi.lib().gdn_abi_version() == 1
+    for code in range(0, -10, -1):
+        assert abi.status_string(code) and abi.status_string(code) != "unknown status"
+    assert abi.status_string(-99) == "unknown status"
+
+
+P = 0x10000  # a 16-byte-aligned stand-in device address (never dereferenced here)
+
+
+def conv(abi, desc, x=P, w=P, bias=None, sin=None, y=P, sout=None, off=P):
+    return abi.lib().gdn_conv1d_varlen(ctypes.byref(desc), x, w, bias, sin, y, sout, off, None, None)
+
+
+@pytest.mark.parametrize(
+    "fields,kw,want",
+    [
+        (dict(B=0), {}, "ERR_SHAPE"),
+        (dict(N=-1), {}, "ERR_SHAPE"),
+        (dict(C=0), {}, "ERR_SHAPE"),
+        (dict(W=0), {}, "ERR_SHAPE"),
+        (dict(D=0), {}, "ERR_SHAPE"),
+        (dict(W=9), {}, "ERR_UNSUPPORTED"),
+        (dict(x_dtype=7), {}, "ERR_DTYPE"),
+        (dict(x_dtype=0, state_dtype=1), {}, "ERR_DTYPE"),
+        (dict(flags=2), {}, "ERR_UNSUPPORTED"),
+        (dict(D=2**30), {}, "ERR_OVERFLOW"),
+        ({}, dict(w=None), "ERR_NULL"),
+        ({}, dict(off=None), "ERR_NULL"),
+        ({}, dict(x=None), "ERR_NULL"),
+        ({}, dict(y=None), "ERR_NULL"),
+        ({}, dict(x=P + 8), "ERR_ALIGN"),
+        ({}, dict(sin=P + 4), "ERR_ALIGN"),
+    ],
+)
+def test_conv_host_validation(abi, fields, kw, want):
+    base = dict(B=2, N=64, C=192, W=4, D=1, x_dtype=0, state_dtype=0, flags=0)
+    base.update(fields)
+    assert conv(abi, abi.ConvDesc(**base), **kw) == getattr(abi, want)
+
+
+def scan_desc(abi, **fields):
+    base = dict(B=2, N=64, HQ=2, H=2, K=32, V=32, qkv_dtype=0, gate_dtype=0, flags=7, scale=0.0, path=0)
+    base.update(fields)
+    return abi.ScanDesc(**base)
+
+
+def scan(abi, d, qkv=P, qk=None, gb=None, a=None, b=None, alog=None, dtb=None, sin=None, out=P, sout=None, off=P,
+         ws=None, ws_bytes=0):
+    return abi.lib().gdn_scan_varlen(ctypes.byref(d), qkv, qk, gb, a, b, alog, dtb, sin, out, sout, off, ws,
+                                     ws_bytes, None, None, None)
+
+
+@pytest.mark.parametrize(
+    "fields,kw,want",
+    [
+        (dict(B=0), {}, "ERR_SHAPE"),
+        (dict(HQ=3, H=4), {}, "ERR_SHAPE"),  # H % HQ != 0
+        (dict(K=512), {}, "ERR_SHAPE"),  # the pages' limit: K <= 256
+        (dict(K=48), {}, "ERR_UNSUPPORTED"),  # valid, not instantiated
+        (dict(V=0), {}, "ERR_SHAPE"),
+        (dict(qkv_dtype=5), {}, "ERR_DTYPE"),
+        (dict(qkv_dtype=1, gate_dtype=2), {}, "ERR_DTYPE"),
+        (dict(flags=8), {}, "ERR_UNSUPPORTED"),
+        (dict(path=9), {}, "ERR_UNSUPPORTED"),
+        (dict(path=3), {}, "ERR_UNSUPPORTED"),  # chunked path not eligible here
+        (dict(qkv_dtype=1, gate_dtype=1, V=33, H=2), {}, "ERR_ALIGN"),  # token row not a multiple of 16 bytes
+        (dict(HQ=2**22, H=2**22, K=256, V=1), {}, "ERR_OVERFLOW"),
+        ({}, dict(qkv=None), "ERR_NULL"),
+        ({}, dict(out=None), "ERR_NULL"),
+        ({}, dict(off=None), "ERR_NULL"),
+        ({}, dict(qk=P), "ERR_NULL"),  # prepared inputs come in pairs
+        ({}, dict(a=P), "ERR_NULL"),  # softplus needs A_log and dt_bias
+        ({}, dict(out=P + 2), "ERR_ALIGN"),
+        ({}, dict(sin=P + 8), "ERR_ALIGN"),
+    ],
+)
+def test_scan_host_validation(abi, fields, kw, want):
+    assert scan(abi, scan_desc(abi, **fields), **kw) == getattr(abi, want)
+
+
+def test_prepare_host_validation(abi):
+    L = abi.lib()
+    d = scan_desc(abi)
+    assert L.gdn_prepare_qk_gates(ctypes.byref(d), P, None, None, None, None, None, None, None) == abi.ERR_NULL
+    assert L.gdn_prepare_qk_gates(ctypes.byref(d), P, P, None, None, None, P, P, None) == abi.ERR_NULL
+    assert L.gdn_prepare_qk_gates(ctypes.byref(d), P, None, None, None, None, P + 4, P, None) == abi.ERR_ALIGN
+    bad = scan_desc(abi, K=100)
+    assert L.gdn_prepare_qk_gates(ctypes.byref(bad), P, None, None, None, None, P, P, None) == abi.ERR_UNSUPPORTED
+
+
+def test_workspace_query(abi):
+    n = ctypes.c_size_t(123)
+    d = scan_desc(abi, path=2)
+    assert abi.lib().gdn_scan_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == abi.OK and n.value == 0
+    assert abi.lib().gdn_scan_workspace_bytes(ctypes.byref(d), None) == abi.ERR_NULL
+    assert abi.lib().gdn_scan_workspace_bytes(None, ctypes.byref(n)) == abi.ERR_NULL
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from gated_delta_rule_varlen_amd import _abi
+
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "libgdn.so"))
+    with pytest.raises(ImportError):
+        _abi.lib()

@@ -1,0 +1,149 @@
+"""GPU parity of gdn_scan_varlen against the oracle, through the C ABI.
+
+Every path (DECODE, SEQ) runs in both input modes (fused: norms and gates in-kernel; prepared:
+from gdn_prepare_qk_gates) on the five workloads at full size, in the launch configuration the
+benchmark uses; the oracle computes sampled heads and columns of the same launch.  Outputs use
+the dtype tolerance, the final fp32 state 1e-4 for fp32 I/O and 2e-2 otherwise."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import cases
+import oracle
+import workloads
+from gpu_util import (TOL, assert_close, bits, dev, dev_i32, ensure_built, f64, head_subproblem, require_gpu,
+                      sentinel)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    ensure_built()
+    return require_gpu()
+
+
+def gpu_scan(torch, w, path, prepared, offsets=None, state=None, inplace=False, dev_status=None, use_state=True):
+    import gated_delta_rule_varlen_amd as gdn
+
+    qkv = dev(w.qkv, w.io)
+    a, b = dev(w.a, w.gate_dtype), dev(w.b, w.gate_dtype)
+    A_log, dtb = dev(w.A_log, "f32"), dev(w.dt_bias, "f32")
+    qk = gb = None
+    if prepared:
+        qk, gb = gdn.prepare_qk_gates(qkv, HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=a, b=b, A_log=A_log, dt_bias=dtb,
+                                      l2norm=w.l2norm, softplus=w.softplus, sigmoid=w.sigmoid)
+    st_in = dev(w.state if state is None else state, "f32") if use_state else None
+    out = sentinel((w.N, w.H, w.V), w.io)
+    st_out = st_in if (inplace and st_in is not None) else sentinel((w.B, w.H, w.V, w.K), "f32")
+    out, st_out, used = gdn.scan_varlen(qkv, dev_i32(w.offsets if offsets is None else offsets), HQ=w.HQ, H=w.H,
+                                        K=w.K, V=w.V, a=a, b=b, A_log=A_log, dt_bias=dtb, state_in=st_in,
+                                        qk_prep=qk, gb_prep=gb, l2norm=w.l2norm, softplus=w.softplus,
+                                        sigmoid=w.sigmoid, scale=w.scale, path=path, out=out, state_out=st_out,
+                                        dev_status=dev_status)
+    torch.cuda.synchronize()
+    return out, st_out, used
+
+
+# (workload, heads sampled (None = all), columns sampled per head (None = all))
+SAMPLES = {
+    "tiny_fp32": (None, None),
+    "decode": ([0, 1, 17, 31], None),
+    "prefill": ([0, 13, 31], None),
+    "long": ([0, 9], [0, 1, 37, 64, 100, 127]),
+    "edge_fp16": (None, None),
+}
+PARITY = [(n, p, m) for n in cases.ALL for p in ("decode", "seq") for m in ("fused", "prepared")
+          if not (n == "long" and p == "decode")]
+
+
+def check_against_oracle(w, name, out, st):
+    heads, cols = SAMPLES[name]
+    heads = range(w.H) if heads is None else heads
+    og, sg = f64(out), f64(st)
+    state_tol = 1e-4 if w.io == "f32" else 2e-2
+    ref_o, ref_s, got_o, got_s = [], [], [], []
+    for h in heads:
+        sub, vsel = head_subproblem(w, h, cols)
+        o_ref, s_ref = oracle.scan(sub.pop("qkv"), w.offsets, **sub)
+        ref_o.append(o_ref[:, 0])
+        ref_s.append(s_ref[:, 0])
+        got_o.append(og[:, h][:, vsel])
+        got_s.append(sg[:, h][:, vsel])
+    assert_close(np.stack(got_o), np.stack(ref_o), TOL[w.io], f"{name} out")
+    assert_close(np.stack(got_s), np.stack(ref_s), state_tol, f"{name} final state")
+
+
+@pytest.mark.parametrize("name,path,mode", PARITY)
+def test_scan_matches_oracle(torch, name, path, mode):
+    w = cases.get(name)
+    print(f"[scan parity] {name} path={path} mode={mode} B={w.B} N={w.N} H={w.H} K={w.K} V={w.V}", flush=True)
+    out, st, used = gpu_scan(torch, w, path, mode == "prepared")
+    assert used == path
+    assert np.all(np.isfinite(f64(out))), "an output element was left unwritten"
+    check_against_oracle(w, name, out, st)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "decode", "edge_fp16"])
+def test_auto_path_choice(torch, name):
+    w = cases.get(name)
+    _, _, used = gpu_scan(torch, w, "auto", False)
+    assert used == ("decode" if w.N <= 2 * w.B else "seq")
+
+
+@pytest.mark.parametrize("name,path", [("tiny_fp32", "seq"), ("edge_fp16", "seq"), ("decode", "decode")])
+def test_in_place_state_and_determinism(torch, name, path):
+    w = cases.get(name)
+    o1, s1, _ = gpu_scan(torch, w, path, False)
+    o2, s2, _ = gpu_scan(torch, w, path, False)
+    assert np.array_equal(bits(o1), bits(o2)) and np.array_equal(bits(s1), bits(s2)), "not deterministic"
+    o3, s3, _ = gpu_scan(torch, w, path, False, inplace=True)
+    assert np.array_equal(bits(o1), bits(o3)) and np.array_equal(bits(s1), bits(s3)), "in-place update differs"
+
+
+def test_zero_length_sequences_copy_state_bit_exactly(torch):
+    w = cases.get("edge_fp16")
+    empty = np.flatnonzero(w.lengths == 0)
+    assert len(empty) >= 3
+    for path in ("seq", "decode"):
+        _, st, _ = gpu_scan(torch, w, path, False)
+        assert np.array_equal(bits(st)[empty], w.state[empty].view(np.int32))
+
+
+def test_null_initial_state_is_zero_state(torch):
+    w = cases.get("tiny_fp32")
+    wz = dataclasses.replace(w, state=np.zeros((w.B, w.H, w.V, w.K), np.float32))
+    o1, s1, _ = gpu_scan(torch, wz, "seq", False)
+    o2, s2, _ = gpu_scan(torch, wz, "seq", False, use_state=False)
+    assert np.array_equal(bits(o1), bits(o2)) and np.array_equal(bits(s1), bits(s2))
+
+
+@pytest.mark.parametrize("name,path", [("tiny_fp32", "seq"), ("edge_fp16", "decode"), ("edge_fp16", "seq")])
+def test_malformed_offsets_write_nothing(torch, name, path):
+    w = cases.get(name)
+    status = torch.full((1,), 777, dtype=torch.int32, device="cuda")
+    gpu_scan(torch, w, path, False, dev_status=status)
+    assert int(status.item()) == 0
+    for case, bad in workloads.malformed_offsets(w.offsets):
+        print(f"[scan malformed] {name} {path} {case}", flush=True)
+        out, st, _ = gpu_scan(torch, w, path, False, offsets=bad, dev_status=status)
+        assert int(status.item()) == -9, case
+        assert np.all(bits(out) == bits(sentinel(tuple(out.shape), w.io))), case
+        assert np.all(bits(st) == bits(sentinel(tuple(st.shape), "f32"))), case
+
+
+def test_ragged_multi_tile_small_case(torch):
+    # several column tiles per head, a ragged column tail (V not a multiple of the tile), GQA 4,
+    # a long and a zero-length sequence: the oracle computes everything
+    w = workloads.make(name="ragged", seed=11, lengths=[0, 130, 1, 0, 77], HQ=2, H=8, K=64, V=42, io="bf16",
+                       conv_state_dtype="f32")
+    for path in ("seq", "decode"):
+        for prepared in (False, True):
+            out, st, used = gpu_scan(torch, w, path, prepared)
+            assert used == path
+            o_ref, s_ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io,
+                                       gate_dtype=w.gate_dtype, a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias,
+                                       state_in=w.state)
+            assert_close(f64(out), o_ref, TOL[w.io], f"ragged {path} {prepared} out")
+            assert_close(f64(st), s_ref, 2e-2, f"ragged {path} {prepared} state")
