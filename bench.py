@@ -168,6 +168,25 @@ def cpu_baseline(w, budget_s: float = 12.0):
                       f"{t_total:.1f} s"}
 
 
+def copy_calibration(torch, steps: int, warmup: int):
+    """A plain device-to-device copy of 1 GiB: known bytes per launch (1 GiB read + 1 GiB written)."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    nbytes = 2 * 4 * n
+    return {"copy_bytes_per_launch": nbytes, "avg_launch_us": round(us, 2), "gb_per_s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +196,8 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "seq", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="skip the secondary prefill measurement")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="time a plain 1 GiB device-to-device copy (reference for HBM counters and achievable bandwidth)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -189,6 +210,9 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        print(json.dumps(copy_calibration(torch, args.steps, args.warmup)), flush=True)
+        return
     w = workloads.NAMED[args.workload]()
     p = Path(w, torch, args.path)
     ms, scan_ms, used, _ = time_path(p, args.steps, args.warmup)

@@ -204,8 +204,9 @@ gdn_status gdn_scan_varlen(const gdn_scan_desc* d, const void* qkv, const float*
     s.flags = d->flags;
     s.scale = (d->scale > 0.0f && std::isfinite(d->scale)) ? d->scale : 1.0f / std::sqrt((float)d->K);
     s.path = path;
-    const hipError_t e = path == GDN_PATH_CHUNK ? gdn::launch_scan_chunked(s, stream)
-                                                : gdn::launch_scan_recurrent(s, stream);
+    const hipError_t e = path == GDN_PATH_CHUNK  ? gdn::launch_scan_chunked(s, stream)
+                         : path == GDN_PATH_SEQ ? gdn::launch_scan_seq(s, stream)
+                                                : gdn::launch_scan_decode(s, stream);
     const gdn_status rs = from_hip(e);
     if (rs == GDN_OK && path_used != nullptr) *path_used = path;
     return rs;

@@ -76,6 +76,13 @@ __device__ __forceinline__ void store_row(typename T::storage* p, const float (&
     }
 }
 
+// Element i of a 16-byte row vector, as raw storage.
+template <typename T>
+__device__ __forceinline__ typename T::storage raw_elem(const u32x4& raw, int i) {
+    if constexpr (std::is_same<T, F32>::value) return __uint_as_float(raw[i]);
+    else return (uint16_t)((raw[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+}
+
 template <int VEC>
 __device__ __forceinline__ void activate(float (&acc)[VEC], int silu) {
     if (silu) {
@@ -104,10 +111,24 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     float wr[VEC][W];
     {
         const TS* wp = static_cast<const TS*>(p.w) + (size_t)c0 * W;
+        if constexpr (VEC > 1) {
+            // the thread's VEC*W weights are contiguous and 16-byte aligned: W vector loads
+            union {
+                u32x4 v[W];
+                TS e[VEC * W];
+            } u;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i)
+            for (int k = 0; k < W; ++k) u.v[k] = reinterpret_cast<const u32x4*>(wp)[k];
 #pragma unroll
-            for (int j = 0; j < W; ++j) wr[i][j] = to_f32<T>(wp[i * W + j]);
+            for (int i = 0; i < VEC; ++i)
+#pragma unroll
+                for (int j = 0; j < W; ++j) wr[i][j] = to_f32<T>(u.e[i * W + j]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+#pragma unroll
+                for (int j = 0; j < W; ++j) wr[i][j] = to_f32<T>(wp[i * W + j]);
+        }
     }
     float bias[VEC];
     if (p.bias != nullptr) {
@@ -115,6 +136,82 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) bias[i] = 0.0f;
+    }
+
+    if constexpr (VEC > 1 && W > 1) {
+      if (item < p.B && D == 1) {
+        // ---- head, dilation 1: the thread's window block (VEC channels x L entries, contiguous) is
+        // moved with 16-byte vector accesses and held in registers; L = W-1 is a compile-time size.
+        constexpr int L1 = W - 1;
+        constexpr int NE = VEC * L1;                           // window elements of this thread
+        constexpr int NCH = NE * (int)sizeof(SS) / 16;         // 16-byte chunks
+        static_assert(NE * sizeof(SS) % 16 == 0, "window block is whole 16-byte chunks");
+        const int b = item;
+        const int start = p.offsets[b];
+        const int len = p.offsets[b + 1] - start;
+        const size_t wrow = ((size_t)b * C + c0) * (size_t)L1;  // window of channel c0 + i at wrow + i*L1
+        union {
+            u32x4 v[NCH];
+            SS e[NE];
+        } win;
+        if (p.state_in != nullptr) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const SS*>(p.state_in) + wrow);
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) win.v[k] = src[k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) win.v[k] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int l = 0; l < L1; ++l) {
+            if (l >= len) break;
+            float acc[VEC];
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[i] = bias[i];
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                const int m = l + j - L1;  // tap j of local token l (dilation 1)
+                float xv[VEC];
+                if (m >= 0) {
+                    load_row<T, VEC>(x + (size_t)(start + m) * C + c0, xv);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) xv[i] = to_f32<S>(win.e[i * L1 + L1 + m]);
+                }
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[i] = fmaf(wr[i][j], xv[i], acc[i]);
+            }
+            activate<VEC>(acc, p.silu);
+            store_row<T, VEC>(y + (size_t)(start + l) * C + c0, acc);
+        }
+        if (p.state_out != nullptr) {
+            // new window entry j = old entry len + j while that exists, else token len - L1 + j
+            union {
+                u32x4 v[NCH];
+                SS e[NE];
+            } nw;
+#pragma unroll
+            for (int j = 0; j < L1; ++j) {
+                const int src = len + j;
+                u32x4 xr = u32x4{0u, 0u, 0u, 0u};
+                if (src >= L1) xr = *reinterpret_cast<const u32x4*>(x + (size_t)(start + src - L1) * C + c0);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    SS v;
+                    if constexpr (std::is_same<S, T>::value) v = raw_elem<T>(xr, i);
+                    else v = to_f32<T>(raw_elem<T>(xr, i));  // exact widening into an fp32 window
+#pragma unroll
+                    for (int k = 0; k < L1; ++k)
+                        if (src == k) v = win.e[i * L1 + k];
+                    nw.e[i * L1 + j] = v;
+                }
+            }
+            u32x4* dst = reinterpret_cast<u32x4*>(static_cast<SS*>(p.state_out) + wrow);
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) dst[k] = nw.v[k];
+        }
+        return;
+      }
     }
 
     if (item < p.B) {

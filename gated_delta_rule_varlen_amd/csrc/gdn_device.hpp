@@ -141,4 +141,18 @@ __device__ __forceinline__ int find_sequence(const int32_t* __restrict__ offsets
     return lo;
 }
 
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
+
+// Blocks are dispatched round-robin over the 8 XCDs of the chip (block i runs on XCD i % 8).  This
+// maps the i-th block an XCD receives to a logical block so that groups of `gs` consecutive logical
+// blocks (blocks that read the same q/k rows) stay on one XCD and share its L2, while consecutive
+// groups go to different XCDs (which spreads one sequence's work over the whole chip).  Blocks past
+// the last whole round of 8 * gs keep their index.
+__device__ __forceinline__ int xcd_remap(int phys, int n, int gs) {
+    const int round = 8 * gs;
+    if (phys >= (n / round) * round) return phys;
+    const int x = phys & 7, j = phys >> 3;
+    return (8 * (j / gs) + x) * gs + (j % gs);
+}
+
 }  // namespace gdn

@@ -60,7 +60,8 @@ struct ScanLaunch {
     float scale;  // already resolved (> 0)
     int path;     // resolved: GDN_PATH_DECODE, GDN_PATH_SEQ or GDN_PATH_CHUNK
 };
-hipError_t launch_scan_recurrent(const ScanLaunch& a, hipStream_t stream);  // DECODE and SEQ
+hipError_t launch_scan_decode(const ScanLaunch& a, hipStream_t stream);  // DECODE
+hipError_t launch_scan_seq(const ScanLaunch& a, hipStream_t stream);     // SEQ
 hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream);    // CHUNK
 size_t chunked_workspace_bytes(int B, int N, int HQ, int H, int K, int V);
 

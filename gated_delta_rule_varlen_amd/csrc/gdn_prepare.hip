@@ -32,8 +32,6 @@ struct PrepArgs {
     int n_row_blocks;   // blocks that normalise rows; the rest compute gates
 };
 
-__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
-
 // Gate and rate of token t, value head h (fused into the scan as well; see gdn_scan.hip).
 __device__ __forceinline__ void gate_rate(const PrepArgs& p, long long i, int h, float& g, float& beta) {
     g = 1.0f;

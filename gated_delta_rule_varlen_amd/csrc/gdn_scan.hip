@@ -1,4 +1,6 @@
-// gdn_scan.hip -- gated delta-rule recurrence, token-sequential form (gfx950, wave64).
+// gdn_scan.hip -- gated delta-rule recurrence, DECODE path: token-sequential form with the state
+// streamed once per call (gfx950, wave64).  Correct for any sequence lengths; tiled for many short
+// sequences (the prefill path with LDS-staged token chunks is gdn_seq.hip).
 //
 // Operation: paged_ssm.rs page, kernel string DELTA (see gdn.h).  Every value column (b, h, v) is an
 // independent recurrence over a K-vector s.  Work mapping:
@@ -7,7 +9,8 @@
 //     4*(j + LPC*i) + e (i < K/(4*LPC), e < 4), so every 16-byte state access of a group is one
 //     contiguous 16*LPC-byte segment and the state of a block streams with perfectly coalesced
 //     loads and stores;
-//   * a lane group carries CPL columns of the same head, a wave 64/LPC groups, a block NW waves;
+//   * a lane group carries CPL columns of the same head, a wave 64/LPC groups, a block NW waves
+//     (one column tile per wave);
 //     blocks are laid out (sequence, head, column tile) and re-mapped so that the blocks of one
 //     head land on one XCD (they read the same q/k rows through that XCD's L2);
 //   * per token the two state dot products k.s and q.s of the OLD state are computed together, then
@@ -49,16 +52,6 @@ struct ScanArgs {
     int n_vtiles;   // column tiles per (sequence, head)
     int n_blocks;   // grid size
 };
-
-__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
-
-// Blocks are dispatched round-robin over the 8 XCDs; this makes logical blocks [i*n/8, (i+1)*n/8)
-// run on XCD i, so neighbouring logical blocks (same head) share an L2.
-__device__ __forceinline__ int xcd_remap(int phys, int n) {
-    const int per = n >> 3;
-    if (phys >= per * 8) return phys;
-    return (phys & 7) * per + (phys >> 3);
-}
 
 template <bool NT>
 __device__ __forceinline__ f32x4 ld_state(const float* p) {
@@ -124,27 +117,28 @@ __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int 
     for (int c = 0; c < CPL; ++c) o.v[c] = (vbase + c < p.V) ? to_f32<T>(vp[c]) : 0.0f;
 }
 
-template <typename T, int K, int LPC, int CPL, bool PREP, bool NT>
-__global__ __launch_bounds__(64) void scan_kernel(ScanArgs p) {
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT>
+__global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
     constexpr int EPL = K / LPC;  // state elements per lane per column
     static_assert(EPL % 4 == 0, "whole 16-byte chunks per lane");
     constexpr int GPW = 64 / LPC;  // lane groups per wave
-    constexpr int WC = GPW * CPL;  // columns per wave (= per block)
+    constexpr int WC = GPW * CPL;  // columns per wave; a block covers NW * WC
     using TS = typename T::storage;
 
     const bool malformed = offsets_malformed(p.offsets, p.B, p.N);
     report_status(p.dev_status, malformed);
     if (malformed) return;
 
-    const int blk = xcd_remap((int)blockIdx.x, p.n_blocks);
+    const int blk = xcd_remap((int)blockIdx.x, p.n_blocks, p.G * p.n_vtiles);
     const int vt = blk % p.n_vtiles;
     const int bh = blk / p.n_vtiles;
     const int h = bh % p.H;
     const int b = bh / p.H;
     const int kh = h / p.G;
-    const int lane = (int)threadIdx.x;
+    const int wave = (int)threadIdx.x / 64;
+    const int lane = (int)threadIdx.x % 64;
     const int grp = lane / LPC, gl = lane % LPC;
-    const int vbase = vt * WC + grp * CPL;
+    const int vbase = (vt * NW + wave) * WC + grp * CPL;
     const size_t col0 = ((size_t)b * p.H + h) * p.V;
 
     float s[CPL][EPL];
@@ -226,7 +220,7 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs p) {
             const float dk = beta * (cur.v[c] - r) * rk;  // delta * rk: coefficient of the raw k
             const float o = oscale * fmaf(g, pq[c], dk * qk);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) s[c][e] = fmaf(g, s[c][e], dk * cur.k[e]);
+            for (int e = 0; e < EPL; ++e) s[c][e] = fmaf(dk, cur.k[e], g * s[c][e]);
             if (gl == c) mine = o;
         }
         if (gl < CPL && vbase + gl < p.V) outp[((size_t)t * p.H + h) * p.V + vbase + gl] = from_f32<T>(mine);
@@ -246,61 +240,56 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs p) {
     }
 }
 
-template <typename T, int K, int LPC, int CPL, bool PREP, bool NT>
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT>
 hipError_t launch_tile(ScanArgs p, hipStream_t stream) {
-    constexpr int WC = (64 / LPC) * CPL;
-    p.n_vtiles = (p.V + WC - 1) / WC;
+    constexpr int BC = (64 / LPC) * CPL * NW;  // columns per block
+    p.n_vtiles = (p.V + BC - 1) / BC;
     const long long blocks = (long long)p.B * p.H * p.n_vtiles;
     if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
     p.n_blocks = (int)blocks;
-    hipLaunchKernelGGL((scan_kernel<T, K, LPC, CPL, PREP, NT>), dim3((unsigned)blocks), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((scan_kernel<T, K, LPC, CPL, NW, PREP, NT>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
-// Tile choice.  DECODE: 4 columns per lane group (many sequences; streaming).  SEQ: the widest
-// tile that still gives at least two waves per SIMD (2048 waves), down to one column per group.
+// DECODE tile: 16-lane groups (8 for K = 32), GDN_DECODE_CPL columns per group (half that at
+// K = 256), GDN_DECODE_NW waves per block.  The state is streamed once, with non-temporal accesses.
+#ifndef GDN_DECODE_CPL
+#define GDN_DECODE_CPL 8
+#endif
+#ifndef GDN_DECODE_NW
+#define GDN_DECODE_NW 4
+#endif
 template <typename T, int K, bool PREP>
-hipError_t launch_k(const ScanArgs& p, int path, hipStream_t stream) {
+hipError_t launch_k(const ScanArgs& p, hipStream_t stream) {
     constexpr int LPC = K >= 64 ? 16 : 8;
-    if (path == GDN_PATH_DECODE) {
-        if constexpr (K >= 256) return launch_tile<T, K, LPC, 2, PREP, true>(p, stream);
-        else return launch_tile<T, K, LPC, 4, PREP, true>(p, stream);
-    }
-    const long long cols = (long long)p.B * p.H * p.V;
-    constexpr int GPW = 64 / LPC;
-    if constexpr (K <= 128) {
-        if (cols / (GPW * 2) >= 2048) return launch_tile<T, K, LPC, 2, PREP, false>(p, stream);
-    }
-    if constexpr (K >= 128) {
-        if (cols / GPW < 2048) return launch_tile<T, K, 32, 1, PREP, false>(p, stream);
-    }
-    return launch_tile<T, K, LPC, 1, PREP, false>(p, stream);
+    constexpr int CPL = K >= 256 ? (GDN_DECODE_CPL > 1 ? GDN_DECODE_CPL / 2 : 1) : GDN_DECODE_CPL;
+    return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true>(p, stream);
 }
 
 template <typename T, bool PREP>
-hipError_t launch_t(const ScanArgs& p, int path, hipStream_t stream) {
+hipError_t launch_t(const ScanArgs& p, hipStream_t stream) {
     switch (p.K) {
-        case 32: return launch_k<T, 32, PREP>(p, path, stream);
-        case 64: return launch_k<T, 64, PREP>(p, path, stream);
-        case 128: return launch_k<T, 128, PREP>(p, path, stream);
-        case 256: return launch_k<T, 256, PREP>(p, path, stream);
+        case 32: return launch_k<T, 32, PREP>(p, stream);
+        case 64: return launch_k<T, 64, PREP>(p, stream);
+        case 128: return launch_k<T, 128, PREP>(p, stream);
+        case 256: return launch_k<T, 256, PREP>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <bool PREP>
-hipError_t launch_p(const ScanArgs& p, int dtype, int path, hipStream_t stream) {
+hipError_t launch_p(const ScanArgs& p, int dtype, hipStream_t stream) {
     switch (dtype) {
-        case GDN_F32: return launch_t<F32, PREP>(p, path, stream);
-        case GDN_BF16: return launch_t<BF16, PREP>(p, path, stream);
-        case GDN_F16: return launch_t<F16, PREP>(p, path, stream);
+        case GDN_F32: return launch_t<F32, PREP>(p, stream);
+        case GDN_BF16: return launch_t<BF16, PREP>(p, stream);
+        case GDN_F16: return launch_t<F16, PREP>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_scan_recurrent(const ScanLaunch& a, hipStream_t stream) {
+hipError_t launch_scan_decode(const ScanLaunch& a, hipStream_t stream) {
     ScanArgs p;
     p.qkv = a.qkv;
     p.qk_prep = a.qk_prep;
@@ -327,8 +316,8 @@ hipError_t launch_scan_recurrent(const ScanLaunch& a, hipStream_t stream) {
     p.scale = a.scale;
     p.n_vtiles = 0;
     p.n_blocks = 0;
-    if (a.qk_prep != nullptr) return launch_p<true>(p, a.qkv_dtype, a.path, stream);
-    return launch_p<false>(p, a.qkv_dtype, a.path, stream);
+    if (a.qk_prep != nullptr) return launch_p<true>(p, a.qkv_dtype, stream);
+    return launch_p<false>(p, a.qkv_dtype, stream);
 }
 
 }  // namespace gdn
