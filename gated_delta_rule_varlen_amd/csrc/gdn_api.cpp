@@ -42,19 +42,21 @@ gdn_status check_scan_desc(const gdn_scan_desc* d) {
     return GDN_OK;
 }
 
-// The chunked path needs every decay strictly positive and finite (it works with log-decays) and
-// normalised keys; it computes gates and norms itself, so it runs on the fused inputs only.
+// The chunked path sums log-decays, so it needs every decay finite and positive (a decay input with
+// the softplus gate), and it relies on normalised keys for a well-conditioned (I + A); it computes
+// the gates and norms itself, so it runs on fused inputs only.  Built for bf16/fp16 I/O with
+// K = V = 64 or 128.
 bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay) {
-    (void)d;
-    (void)prepared;
-    (void)has_decay;
-    return false;  // the chunked kernels are not part of this build yet
+    return !prepared && has_decay && (d->flags & GDN_SOFTPLUS) && (d->flags & GDN_L2NORM) &&
+           gdn::chunked_shape_supported(d->K, d->V, d->qkv_dtype);
 }
 
+// AUTO: DECODE for at most two tokens per sequence on average; CHUNK when eligible, the average
+// sequence fills at least one chunk of 64 tokens and the workspace suffices; SEQ otherwise.
 int resolve_path(const gdn_scan_desc* d, bool prepared, bool has_decay, size_t ws_bytes) {
     if (d->path != GDN_PATH_AUTO) return d->path;
     if ((long long)d->N <= 2ll * d->B) return GDN_PATH_DECODE;
-    if (chunk_eligible(d, prepared, has_decay) &&
+    if (chunk_eligible(d, prepared, has_decay) && (long long)d->N >= 64ll * d->B &&
         ws_bytes >= gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
         return GDN_PATH_CHUNK;
     return GDN_PATH_SEQ;

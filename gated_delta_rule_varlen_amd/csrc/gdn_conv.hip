@@ -22,6 +22,8 @@
 namespace gdn {
 namespace {
 
+constexpr int kConvTile = 16;  // tokens per body block
+
 struct ConvArgs {
     const void* x;
     const void* w;
@@ -83,11 +85,14 @@ __device__ __forceinline__ typename T::storage raw_elem(const u32x4& raw, int i)
     else return (uint16_t)((raw[i >> 1] >> (16 * (i & 1))) & 0xffffu);
 }
 
+// SiLU z / (1 + e^-z) with the hardware exp2 and reciprocal (each within a couple of ulp of fp32):
+// the IEEE-exact expf and division cost ~35 VALU instructions per element and made the conv
+// arithmetic-bound.  z -> -inf gives e^-z = inf, rcp(inf) = 0 and an output of -0 (the limit).
 template <int VEC>
 __device__ __forceinline__ void activate(float (&acc)[VEC], int silu) {
     if (silu) {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[i] = acc[i] / (1.0f + expf(-acc[i]));
+        for (int i = 0; i < VEC; ++i) acc[i] = acc[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-acc[i]));
     }
 }
 
@@ -267,6 +272,45 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     }
 
     // ---- body: tokens [t0, t1) with local index >= L ----------------------------------------------
+    if constexpr (VEC > 1 && W > 1) {
+        if (D == 1) {
+            // dilation 1: all TILE + L rows of the tile are loaded up front (independent 16-byte loads
+            // in flight together), then every token reads its W taps from registers
+            constexpr int L1 = W - 1;
+            const int t0 = (item - p.B) * kConvTile;
+            const int t1 = min(t0 + kConvTile, p.N);
+            u32x4 rows[kConvTile + L1];
+#pragma unroll
+            for (int r = 0; r < kConvTile + L1; ++r) {
+                const int t = t0 - L1 + r;
+                rows[r] = (t >= 0 && t < t1) ? *reinterpret_cast<const u32x4*>(x + (size_t)t * C + c0) : u32x4{0u, 0u, 0u, 0u};
+            }
+            int b = find_sequence(p.offsets, p.B, t0);
+            int next = p.offsets[b + 1];
+#pragma unroll
+            for (int i = 0; i < kConvTile; ++i) {
+                const int t = t0 + i;
+                if (t >= t1) break;
+                while (next <= t) {
+                    ++b;
+                    next = p.offsets[b + 1];
+                }
+                if (t - p.offsets[b] < L1) continue;  // reaches into the window: computed by the head block
+                float acc[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] = bias[e];
+#pragma unroll
+                for (int j = 0; j < W; ++j) {
+                    const u32x4 raw = rows[i + j];  // token t - (W-1-j)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[e] = fmaf(wr[e][j], to_f32<T>(raw_elem<T>(raw, e)), acc[e]);
+                }
+                activate<VEC>(acc, p.silu);
+                store_row<T, VEC>(y + (size_t)t * C + c0, acc);
+            }
+            return;
+        }
+    }
     const int t0 = (item - p.B) * p.tile;
     const int t1 = min(t0 + p.tile, p.N);
     int b = find_sequence(p.offsets, p.B, t0);
@@ -323,7 +367,7 @@ hipError_t launch_vec(const ConvLaunch& a, hipStream_t stream) {
     p.n_cvec = a.C / VEC;
     const int threads = p.n_cvec >= 256 ? 256 : ((p.n_cvec + 63) / 64) * 64;
     p.n_cblk = (p.n_cvec + threads - 1) / threads;
-    p.tile = 16;
+    p.tile = kConvTile;
     const long long n_tiles = ((long long)a.N + p.tile - 1) / p.tile;
     const long long blocks = ((long long)a.B + n_tiles) * p.n_cblk;
     if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;

@@ -64,6 +64,7 @@ hipError_t launch_scan_decode(const ScanLaunch& a, hipStream_t stream);  // DECO
 hipError_t launch_scan_seq(const ScanLaunch& a, hipStream_t stream);     // SEQ
 hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream);    // CHUNK
 size_t chunked_workspace_bytes(int B, int N, int HQ, int H, int K, int V);
+bool chunked_shape_supported(int K, int V, int qkv_dtype);
 
 // Limits of the launch grids (checked by the entry points before launching).
 constexpr long long kMaxBlocks = (1ll << 31) - 1;

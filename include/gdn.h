@@ -116,7 +116,7 @@ gdn_status gdn_conv1d_varlen(const gdn_conv_desc *desc, const void *x, const voi
 #define GDN_SIGMOID 4u
 
 typedef enum gdn_path {
-    GDN_PATH_AUTO = 0,   /* chosen from the shapes: DECODE when N <= 2*B, else CHUNK when eligible, else SEQ */
+    GDN_PATH_AUTO = 0,   /* DECODE when N <= 2*B; else CHUNK when eligible, N >= 64*B and ws_bytes suffices; else SEQ */
     GDN_PATH_DECODE = 1, /* state streamed once per call; tiles sized for many short sequences */
     GDN_PATH_SEQ = 2,    /* token-sequential recurrence with the state resident in registers */
     GDN_PATH_CHUNK = 3   /* chunked WY form (chunk 64); needs a workspace and positive decays */
@@ -169,7 +169,9 @@ gdn_status gdn_prepare_qk_gates(const gdn_scan_desc *desc, const void *qkv, cons
  *              with gdn_scan_workspace_bytes); may be NULL otherwise
  *   dev_status [1] int32 (NULL ok); path_used: HOST int32 receiving the gdn_path that ran (NULL ok)
  * GDN_PATH_CHUNK requires fused mode with a decay input and GDN_SOFTPLUS (so every decay is
- * finite and positive), GDN_L2NORM, and K, V multiples of 16; otherwise GDN_ERR_UNSUPPORTED.
+ * finite and positive), GDN_L2NORM, bf16 or fp16 qkv, and K = V = 64 or K = V = 128; otherwise
+ * GDN_ERR_UNSUPPORTED.  Its intra-chunk contractions run on bf16 matrix cores with fp32
+ * accumulation (the state itself stays fp32).
  * ---------------------------------------------------------------------------------------------- */
 gdn_status gdn_scan_varlen(const gdn_scan_desc *desc, const void *qkv, const float *qk_prep, const float *gb_prep,
                            const void *a, const void *b, const float *A_log, const float *dt_bias,

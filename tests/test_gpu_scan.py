@@ -24,7 +24,8 @@ def torch():
     return require_gpu()
 
 
-def gpu_scan(torch, w, path, prepared, offsets=None, state=None, inplace=False, dev_status=None, use_state=True):
+def gpu_scan(torch, w, path, prepared, offsets=None, state=None, inplace=False, dev_status=None, use_state=True,
+             workspace=None):
     import gated_delta_rule_varlen_amd as gdn
 
     qkv = dev(w.qkv, w.io)
@@ -41,7 +42,7 @@ def gpu_scan(torch, w, path, prepared, offsets=None, state=None, inplace=False, 
                                         K=w.K, V=w.V, a=a, b=b, A_log=A_log, dt_bias=dtb, state_in=st_in,
                                         qk_prep=qk, gb_prep=gb, l2norm=w.l2norm, softplus=w.softplus,
                                         sigmoid=w.sigmoid, scale=w.scale, path=path, out=out, state_out=st_out,
-                                        dev_status=dev_status)
+                                        dev_status=dev_status, workspace=workspace)
     torch.cuda.synchronize()
     return out, st_out, used
 
@@ -56,6 +57,8 @@ SAMPLES = {
 }
 PARITY = [(n, p, m) for n in cases.ALL for p in ("decode", "seq") for m in ("fused", "prepared")
           if not (n == "long" and p == "decode")]
+# the chunked path runs on fused bf16/fp16 inputs with the softplus gate and L2 norm
+PARITY += [("decode", "chunk", "fused"), ("prefill", "chunk", "fused"), ("long", "chunk", "fused")]
 
 
 def check_against_oracle(w, name, out, st):
@@ -85,14 +88,16 @@ def test_scan_matches_oracle(torch, name, path, mode):
     check_against_oracle(w, name, out, st)
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "decode", "edge_fp16"])
-def test_auto_path_choice(torch, name):
+@pytest.mark.parametrize("name,want", [("tiny_fp32", "seq"), ("decode", "decode"), ("edge_fp16", "seq"),
+                                       ("prefill", "chunk")])
+def test_auto_path_choice(torch, name, want):
     w = cases.get(name)
     _, _, used = gpu_scan(torch, w, "auto", False)
-    assert used == ("decode" if w.N <= 2 * w.B else "seq")
+    assert used == want
 
 
-@pytest.mark.parametrize("name,path", [("tiny_fp32", "seq"), ("edge_fp16", "seq"), ("decode", "decode")])
+@pytest.mark.parametrize("name,path", [("tiny_fp32", "seq"), ("edge_fp16", "seq"), ("decode", "decode"),
+                                       ("prefill", "chunk")])
 def test_in_place_state_and_determinism(torch, name, path):
     w = cases.get(name)
     o1, s1, _ = gpu_scan(torch, w, path, False)
@@ -119,9 +124,10 @@ def test_null_initial_state_is_zero_state(torch):
     assert np.array_equal(bits(o1), bits(o2)) and np.array_equal(bits(s1), bits(s2))
 
 
-@pytest.mark.parametrize("name,path", [("tiny_fp32", "seq"), ("edge_fp16", "decode"), ("edge_fp16", "seq")])
+@pytest.mark.parametrize("name,path", [("tiny_fp32", "seq"), ("edge_fp16", "decode"), ("edge_fp16", "seq"),
+                                       ("chunk_ragged", "chunk")])
 def test_malformed_offsets_write_nothing(torch, name, path):
-    w = cases.get(name)
+    w = chunk_ragged(128) if name == "chunk_ragged" else cases.get(name)
     status = torch.full((1,), 777, dtype=torch.int32, device="cuda")
     gpu_scan(torch, w, path, False, dev_status=status)
     assert int(status.item()) == 0
@@ -147,3 +153,52 @@ def test_ragged_multi_tile_small_case(torch):
                                        state_in=w.state)
             assert_close(f64(out), o_ref, TOL[w.io], f"ragged {path} {prepared} out")
             assert_close(f64(st), s_ref, 2e-2, f"ragged {path} {prepared} state")
+
+
+def chunk_ragged(K, seed=12):
+    """Several chunks per sequence with ragged tails, a one-token and two zero-length sequences,
+    GQA 2, bf16: every shape corner of the chunked path."""
+    return workloads.make(name=f"chunk_ragged_k{K}", seed=seed, lengths=[130, 0, 64, 1, 0, 200, 63], HQ=2, H=4, K=K,
+                          V=K, io="bf16", conv_state_dtype="f32")
+
+
+@pytest.mark.parametrize("K", [64, 128])
+def test_chunk_ragged_against_oracle_and_seq(torch, K):
+    w = chunk_ragged(K)
+    print(f"[chunk ragged] K={K} N={w.N}", flush=True)
+    out_c, st_c, used = gpu_scan(torch, w, "chunk", False)
+    assert used == "chunk"
+    out_s, st_s, _ = gpu_scan(torch, w, "seq", False)
+    o_ref, s_ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io, gate_dtype=w.gate_dtype,
+                               a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias, state_in=w.state)
+    e1 = assert_close(f64(out_c), o_ref, TOL[w.io], "chunk out")
+    e2 = assert_close(f64(st_c), s_ref, 2e-2, "chunk state")
+    # the chunked form agrees with the sequential form on the same launch inputs
+    e3 = assert_close(f64(out_c), f64(out_s), TOL[w.io], "chunk vs seq out")
+    e4 = assert_close(f64(st_c), f64(st_s), 2e-2, "chunk vs seq state")
+    print(f"  errors: out {e1:.2e} state {e2:.2e} vs-seq out {e3:.2e} state {e4:.2e}", flush=True)
+    empty = np.flatnonzero(w.lengths == 0)
+    assert np.array_equal(bits(st_c)[empty], w.state[empty].view(np.int32))
+
+
+def test_chunk_matches_seq_at_full_prefill_size(torch):
+    w = cases.get("prefill")
+    out_c, st_c, _ = gpu_scan(torch, w, "chunk", False)
+    out_s, st_s, _ = gpu_scan(torch, w, "seq", False)
+    e1 = assert_close(f64(out_c), f64(out_s), TOL[w.io], "chunk vs seq out")
+    e2 = assert_close(f64(st_c), f64(st_s), 2e-2, "chunk vs seq state")
+    print(f"  prefill chunk vs seq: out {e1:.2e} state {e2:.2e}", flush=True)
+
+
+def test_chunk_rejects_ineligible_inputs(torch):
+    import gated_delta_rule_varlen_amd as gdn
+
+    for name in ("tiny_fp32", "edge_fp16"):  # fp32 I/O; no L2 norm / raw log-decay
+        w = cases.get(name)
+        with pytest.raises(gdn.GdnError) as ei:
+            gpu_scan(torch, w, "chunk", False)
+        assert ei.value.status == -6
+    w = cases.get("prefill")
+    with pytest.raises(gdn.GdnError) as ei:  # prepared inputs carry g, not log g
+        gpu_scan(torch, w, "chunk", True)
+    assert ei.value.status == -6
