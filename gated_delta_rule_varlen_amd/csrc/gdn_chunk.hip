@@ -38,11 +38,23 @@ namespace gdn {
 namespace {
 
 constexpr int CH = 64;  // tokens per chunk
+// LDS rows holding MFMA fragments are padded by 16 bytes: a fragment read has the 16 lanes of a
+// group on 16 consecutive rows, and unpadded 128- or 256-byte rows would put them all on the same
+// four banks (a 16-way conflict); the pad shifts each row by four banks.
+constexpr int PAD = 8;  // bf16 elements
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Scheduling hint for the current region: NR LDS reads first, then NM matrix products.  Issuing all
+// reads of a phase up front lets their latencies overlap instead of stalling before every product.
+template <int NR, int NM>
+__device__ __forceinline__ void order_reads_then_mfma() {
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
 }
 __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -193,19 +205,20 @@ template <typename T, int K, int V>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
     using TS = typename T::storage;
     static_assert(K % 32 == 0 && V % 32 == 0 && K <= 128 && V <= 128, "chunk tile shapes");
-    __shared__ __align__(16) uint16_t xt[K][CH];    // X^T = (diag(b e^G) Khat)^T
+    __shared__ __align__(16) uint16_t xt[K][CH + PAD];  // X^T = (diag(b e^G) Khat)^T
     __shared__ __align__(16) float am[CH][CH + 4];  // A (fp32); later T in bf16
     __shared__ __align__(16) union {
         struct {
-            uint16_t kn[CH][K];  // Khat rows (bf16)
-            uint16_t qn[CH][K];  // Qhat rows (bf16)
+            uint16_t kn[CH][K + PAD];  // Khat rows (bf16)
+            uint16_t qn[CH][K + PAD];  // Qhat rows (bf16)
         } kq;                    // live until A and P are formed
         float tm[CH][CH + 4];    // T (fp32), until it is rounded to bf16
-        uint16_t yt[V][CH];      // Y^T = (diag(b) V)^T, after that
+        uint16_t yt[V][CH + PAD];  // Y^T = (diag(b) V)^T, after that
     } u1;
     __shared__ __align__(16) float scr[4][16][17];
     __shared__ float s_gam[CH], s_beta[CH];
-    uint16_t(*tb)[CH] = reinterpret_cast<uint16_t(*)[CH]>(&am[0][0]);  // T (bf16), once A is dead
+    uint16_t(*tb)[CH + PAD] = reinterpret_cast<uint16_t(*)[CH + PAD]>(&am[0][0]);  // T (bf16), once A is dead
+    static_assert(sizeof(uint16_t) * CH * (CH + PAD) <= sizeof(float) * CH * (CH + 4), "T (bf16) fits in A's space");
 
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws + p.L.hdr);
     if (hdr[0] != GDN_OK) return;
@@ -318,9 +331,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
         if (jt <= wv) {
 #pragma unroll
             for (int kk = 0; kk < K; kk += 32) {
-                const bf16x8 kj = frag(&u1.kq.kn[16 * jt][kk], K, lane);
-                a = mma_bf16(frag(&u1.kq.kn[16 * wv][kk], K, lane), kj, a);
-                pt = mma_bf16(kj, frag(&u1.kq.qn[16 * wv][kk], K, lane), pt);
+                const bf16x8 kj = frag(&u1.kq.kn[16 * jt][kk], K + PAD, lane);
+                a = mma_bf16(frag(&u1.kq.kn[16 * wv][kk], K + PAD, lane), kj, a);
+                pt = mma_bf16(kj, frag(&u1.kq.qn[16 * wv][kk], K + PAD, lane), pt);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -398,7 +411,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
         const int kt = tile >> 2, it = tile & 3;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int jj = 0; jj < CH; jj += 32) acc = mma_bf16(frag(&xt[16 * kt][jj], CH, lane), frag(&tb[16 * it][jj], CH, lane), acc);
+        for (int jj = 0; jj < CH; jj += 32) acc = mma_bf16(frag(&xt[16 * kt][jj], CH + PAD, lane), frag(&tb[16 * it][jj], CH + PAD, lane), acc);
         const int i = 16 * it + (lane & 15), k = 16 * kt + 4 * (lane >> 4);
         *reinterpret_cast<u32x2*>(wout + (size_t)i * K + k) = pack4(acc[0], acc[1], acc[2], acc[3]);
     }
@@ -408,35 +421,46 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
         const int it = tile / (V / 16), vt = tile % (V / 16);
         f32x4 acc = zero4();
 #pragma unroll
-        for (int jj = 0; jj < CH; jj += 32) acc = mma_bf16(frag(&tb[16 * it][jj], CH, lane), frag(&u1.yt[16 * vt][jj], CH, lane), acc);
+        for (int jj = 0; jj < CH; jj += 32) acc = mma_bf16(frag(&tb[16 * it][jj], CH + PAD, lane), frag(&u1.yt[16 * vt][jj], CH + PAD, lane), acc);
         const int v = 16 * vt + (lane & 15), i = 16 * it + 4 * (lane >> 4);
         *reinterpret_cast<u32x2*>(upt + (size_t)v * CH + i) = pack4(acc[0], acc[1], acc[2], acc[3]);
     }
 }
 
-// Operands of one chunk as one lane of the state kernel reads them.  Two of these alternate
-// (ping-pong): while one chunk is processed the next chunk's loads are in flight, and nothing is
-// derived from a fetched value until it is used, so no wait is forced early.
-template <int K>
-struct ChunkFrags {
+// Operands of one chunk as one lane reads them.  Two of each alternate (ping-pong): while one chunk
+// is processed the next chunk's loads are in flight, and nothing is derived from a fetched value
+// until it is used, so no wait is forced early.  State waves use StateFrags, output waves OutFrags.
+template <int K, int NCT>
+struct StateFrags {
     bf16x8 w[K / 32];          // W rows of this wave's token tile
-    u32x2 up;                  // U'^T[v][4 tokens]
+    u32x2 up[NCT];             // U'^T[v][4 tokens] per column tile
     bf16x8 kd[K / 64][2];      // Kd^T rows of this wave's k tiles
+    float gC;                  // G_C
+};
+template <int K>
+struct OutFrags {
     bf16x8 q[K / 32];          // raw q rows of this wave's token tile (bf16)
     bf16x8 pm[2];              // P rows of this wave's token tile
-    float gC, gi, rq;          // G_C, G_i and 1/|q_i| of this lane's output token
+    float gi, rq;              // G_i and 1/|q_i| of this lane's output token
 };
 
-// ---- state + output --------------------------------------------------------------------------------
-// One block per (sequence, head, 16-column tile); wave w owns token tile w (16 tokens of a chunk)
-// for W S^T and the output, and state columns k in [16 KTW w, 16 KTW (w+1)) for the update.
-template <typename T, int K, int V>
-__global__ __launch_bounds__(256) void chunk_state_kernel(ChunkArgs p) {
+// ---- state + output ---------------------------------------------------------------------------------
+// One block of 8 waves per (sequence, head, VT-column tile; VT = 16 NCT).  Loads of the chunk's
+// W, Kd, q and P are shared by the block's NCT 16-column tiles.
+//   Waves 0-3 ("state") carry the serial chain for chunk c: the entering state -> LDS (bf16),
+//   U = U' - W S^T for token tile w, and S^T <- e^{G_C} S^T + Kd^T U for k tiles of wave w.  The state
+//   is held transposed (accumulator lane: 4 consecutive k of one value column), which makes its LDS
+//   copy and its HBM load/store contiguous.
+//   Waves 4-7 ("output") compute chunk c-1's output O^T[v][i] = rq_i e^{G_i} (S q_i) + (U^T P^T)[v][i]
+//   for token tile w from the double-buffered S and U^T, off the serial chain.
+template <typename T, int K, int V, int NCT>
+__global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
     using TS = typename T::storage;
-    constexpr int VT = 16;
-    constexpr int KTW = K / 64;  // 16-wide k tiles per wave
-    __shared__ __align__(16) uint16_t sb[2][VT][K];   // S entering the chunk (bf16), B operand of W S^T
-    __shared__ __align__(16) uint16_t ut[2][VT][CH];  // U^T (bf16), A operand of U^T Kd and U^T P^T
+    constexpr int VT = 16 * NCT;
+    constexpr int KTW = K / 64;  // 16-wide k tiles per state wave
+    static_assert(V % VT == 0, "column tiles");
+    __shared__ __align__(16) uint16_t sb[2][VT][K + PAD];   // S entering the chunk (bf16)
+    __shared__ __align__(16) uint16_t ut[2][VT][CH + PAD];  // U^T (bf16)
 
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws + p.L.hdr);
     if (hdr[0] != GDN_OK) return;
@@ -447,21 +471,13 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(ChunkArgs p) {
     const int bh = blk / NVT;
     const int h = bh % p.H, b = bh / p.H;
     const int kh = h / p.G;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const bool is_state = tid < 256;
+    const int wv = (tid >> 6) & 3;  // token / k tile of this wave within its group
     const int v0 = vt * VT;
-    const size_t col0 = ((size_t)b * p.H + h) * V + v0;  // first state row of the tile
+    const size_t col0 = ((size_t)b * p.H + h) * V + v0;  // first state row of the block
     const TS* qkv = static_cast<const TS*>(p.qkv);
     TS* outp = static_cast<TS*>(p.out);
-
-    // state tile in accumulator layout: acc[t][r] = S[v0 + 4(l/16) + r][16 (KTW w + t) + l%16]
-    f32x4 acc[KTW];
-#pragma unroll
-    for (int t = 0; t < KTW; ++t) {
-        const int k = 16 * (KTW * wv + t) + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            acc[t][r] = p.state_in ? p.state_in[(col0 + 4 * (lane >> 4) + r) * K + k] : 0.0f;
-    }
     const int c0 = cstart[b], c1 = cstart[b + 1];
     const int seq_start = p.offsets[b], seq_end = p.offsets[b + 1];
     const uint16_t* wbase = reinterpret_cast<const uint16_t*>(p.ws + p.L.w);
@@ -471,18 +487,36 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(ChunkArgs p) {
     const float* gamb = reinterpret_cast<const float*>(p.ws + p.L.gam);
     const float* rqb = reinterpret_cast<const float*>(p.ws + p.L.rq);
 
-    auto fetch = [&](int c, ChunkFrags<K>& f) {
+    // transposed state tiles (state waves): acc[t][ct][r] = S[v0 + 16 ct + l%16][16 (KTW w + t) + 4(l/16) + r]
+    f32x4 acc[KTW][NCT];
+    if (is_state) {
+#pragma unroll
+        for (int t = 0; t < KTW; ++t)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const size_t off = (col0 + 16 * ct + (lane & 15)) * K + 16 * (KTW * wv + t) + 4 * (lane >> 4);
+                acc[t][ct] = p.state_in ? *reinterpret_cast<const f32x4*>(p.state_in + off) : zero4();
+            }
+    }
+
+    auto fetch_s = [&](int c, StateFrags<K, NCT>& f) {
         const size_t chh = (size_t)c * p.H + h;
         const uint16_t* wrow = wbase + (chh * CH + 16 * wv) * K;
 #pragma unroll
         for (int kk = 0; kk < K / 32; ++kk) f.w[kk] = frag(wrow + 32 * kk, K, lane);
-        f.up = *reinterpret_cast<const u32x2*>(uptb + (chh * V + v0 + (lane & 15)) * CH + 16 * wv + 4 * (lane >> 4));
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+            f.up[ct] = *reinterpret_cast<const u32x2*>(uptb + (chh * V + v0 + 16 * ct + (lane & 15)) * CH + 16 * wv + 4 * (lane >> 4));
 #pragma unroll
         for (int t = 0; t < KTW; ++t)
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) f.kd[t][jj] = frag(kdtb + (chh * K + 16 * (KTW * wv + t)) * CH + 32 * jj, CH, lane);
+        f.gC = gamb[chh * CH + CH - 1];
+    };
+    auto fetch_o = [&](int c, OutFrags<K>& f) {
+        const size_t chh = (size_t)c * p.H + h;
         // q rows of this lane's output token; past the sequence end the row index is clamped to the
-        // sequence's last token (always a valid row): those columns of the output tile are never stored
+        // sequence's last token (a valid row): those columns of the tile are never stored
         const int tq = min(seq_start + (c - c0) * CH + 16 * wv + (lane & 15), seq_end - 1);
 #pragma unroll
         for (int kk = 0; kk < K / 32; ++kk) {
@@ -497,83 +531,148 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(ChunkArgs p) {
         }
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) f.pm[jj] = frag(pmb + (chh * CH + 16 * wv) * CH + 32 * jj, CH, lane);
-        const int io = 16 * wv + (lane & 15);  // this lane's output token within the chunk
-        f.gC = gamb[chh * CH + CH - 1];
+        const int io = 16 * wv + (lane & 15);
         f.gi = gamb[chh * CH + io];
         f.rq = rqb[chh * CH + io];
     };
 
-    auto process = [&](int c, const ChunkFrags<K>& f) {
-        const int buf = (c - c0) & 1;
-        // S entering the chunk -> LDS (bf16)
+    // state waves, before the first barrier: S entering the chunk -> LDS (one 8-byte store per tile)
+    auto s_store = [&](int buf) {
 #pragma unroll
-        for (int t = 0; t < KTW; ++t) {
-            const int k = 16 * (KTW * wv + t) + (lane & 15);
+        for (int t = 0; t < KTW; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sb[buf][4 * (lane >> 4) + r][k] = bf(acc[t][r]);
+            for (int ct = 0; ct < NCT; ++ct)
+                *reinterpret_cast<u32x2*>(&sb[buf][16 * ct + (lane & 15)][16 * (KTW * wv + t) + 4 * (lane >> 4)]) =
+                    pack4(acc[t][ct][0], acc[t][ct][1], acc[t][ct][2], acc[t][ct][3]);
+    };
+    // state waves, between the barriers: U = U' - W S^T for token tile wv.  All LDS fragments are read
+    // before the first product so that the NCT accumulation chains run back to back.
+    auto s_u = [&](int buf, const StateFrags<K, NCT>& f) {
+        bf16x8 sf[K / 32][NCT];
+#pragma unroll
+        for (int kk = 0; kk < K / 32; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) sf[kk][ct] = frag(&sb[buf][16 * ct][32 * kk], K + PAD, lane);
+        f32x4 pw[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) pw[ct] = mma_bf16(f.w[0], sf[0][ct], zero4());
+#pragma unroll
+        for (int kk = 1; kk < K / 32; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) pw[ct] = mma_bf16(f.w[kk], sf[kk][ct], pw[ct]);
+        order_reads_then_mfma<K / 32 * NCT, K / 32 * NCT>();
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const float u0 = bf16_bits_to_f32(f.up[ct].x & 0xffffu) - pw[ct][0];
+            const float u1 = bf16_bits_to_f32(f.up[ct].x >> 16) - pw[ct][1];
+            const float u2 = bf16_bits_to_f32(f.up[ct].y & 0xffffu) - pw[ct][2];
+            const float u3 = bf16_bits_to_f32(f.up[ct].y >> 16) - pw[ct][3];
+            *reinterpret_cast<u32x2*>(&ut[buf][16 * ct + (lane & 15)][16 * wv + 4 * (lane >> 4)]) = pack4(u0, u1, u2, u3);
         }
-        __syncthreads();
-        // U = U' - W S^T for token tile wv (lane: tokens 16wv + 4(l/16) + r, column l%16)
-        {
-            f32x4 pw = zero4();
-#pragma unroll
-            for (int kk = 0; kk < K / 32; ++kk) pw = mma_bf16(f.w[kk], frag(&sb[buf][0][32 * kk], K, lane), pw);
-            const float u0 = bf16_bits_to_f32(f.up.x & 0xffffu) - pw[0];
-            const float u1 = bf16_bits_to_f32(f.up.x >> 16) - pw[1];
-            const float u2 = bf16_bits_to_f32(f.up.y & 0xffffu) - pw[2];
-            const float u3 = bf16_bits_to_f32(f.up.y >> 16) - pw[3];
-            *reinterpret_cast<u32x2*>(&ut[buf][lane & 15][16 * wv + 4 * (lane >> 4)]) = pack4(u0, u1, u2, u3);
-        }
-        __syncthreads();
-        // S <- e^{G_C} S + U^T Kd
+    };
+    // state waves, after the second barrier: S^T <- e^{G_C} S^T + Kd^T U
+    auto s_update = [&](int buf, const StateFrags<K, NCT>& f) {
         const float gC = expf(f.gC);
+        bf16x8 uf[NCT][2];
 #pragma unroll
-        for (int t = 0; t < KTW; ++t) {
-            f32x4 a = acc[t] * gC;
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) a = mma_bf16(frag(&ut[buf][0][32 * jj], CH, lane), f.kd[t][jj], a);
-            acc[t] = a;
+            for (int jj = 0; jj < 2; ++jj) uf[ct][jj] = frag(&ut[buf][16 * ct][32 * jj], CH + PAD, lane);
+#pragma unroll
+        for (int t = 0; t < KTW; ++t)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = mma_bf16(f.kd[t][0], uf[ct][0], acc[t][ct] * gC);
+#pragma unroll
+        for (int t = 0; t < KTW; ++t)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = mma_bf16(f.kd[t][1], uf[ct][1], acc[t][ct]);
+        order_reads_then_mfma<2 * NCT, 2 * KTW * NCT>();
+    };
+    // output waves: chunk c's output tiles (token tile wv, all column tiles) from sb[buf], ut[buf]
+    auto o_tile = [&](int c, int buf, const OutFrags<K>& f) {
+        const int t = seq_start + (c - c0) * CH + 16 * wv + (lane & 15);
+        const float cs = f.rq * expf(f.gi);
+        bf16x8 sf[NCT][K / 32], uf[NCT][2];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+            for (int kk = 0; kk < K / 32; ++kk) sf[ct][kk] = frag(&sb[buf][16 * ct][32 * kk], K + PAD, lane);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) uf[ct][jj] = frag(&ut[buf][16 * ct][32 * jj], CH + PAD, lane);
         }
-        // output tile: O^T[v][i] = rq_i e^{G_i} (S q_i) + (U^T P^T)[v][i]; lane: v = 4(l/16)+r, i = 16wv + l%16
-        {
-            f32x4 a1 = zero4(), a2 = zero4();
+        f32x4 a1[NCT], a2[NCT];
 #pragma unroll
-            for (int kk = 0; kk < K / 32; ++kk) a1 = mma_bf16(frag(&sb[buf][0][32 * kk], K, lane), f.q[kk], a1);
+        for (int ct = 0; ct < NCT; ++ct) {
+            a1[ct] = mma_bf16(sf[ct][0], f.q[0], zero4());
+            a2[ct] = mma_bf16(uf[ct][0], f.pm[0], zero4());
+        }
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) a2 = mma_bf16(frag(&ut[buf][0][32 * jj], CH, lane), f.pm[jj], a2);
-            const int t = seq_start + (c - c0) * CH + 16 * wv + (lane & 15);
-            if (t < seq_end) {
-                const float cs = f.rq * expf(f.gi);
+        for (int ct = 0; ct < NCT; ++ct) a2[ct] = mma_bf16(uf[ct][1], f.pm[1], a2[ct]);
+#pragma unroll
+        for (int kk = 1; kk < K / 32; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) a1[ct] = mma_bf16(sf[ct][kk], f.q[kk], a1[ct]);
+        order_reads_then_mfma<(K / 32 + 2) * NCT, (K / 32 + 2) * NCT>();
+        if (t < seq_end) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
                 float o[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = p.scale * fmaf(cs, a1[r], a2[r]);
-                TS* dst = outp + ((size_t)t * p.H + h) * V + v0 + 4 * (lane >> 4);
+                for (int r = 0; r < 4; ++r) o[r] = p.scale * fmaf(cs, a1[ct][r], a2[ct][r]);
+                TS* dst = outp + ((size_t)t * p.H + h) * V + v0 + 16 * ct + 4 * (lane >> 4);
                 *reinterpret_cast<u32x2*>(dst) = u32x2{(uint32_t)from_f32<T>(o[0]) | ((uint32_t)from_f32<T>(o[1]) << 16),
                                                        (uint32_t)from_f32<T>(o[2]) | ((uint32_t)from_f32<T>(o[3]) << 16)};
             }
         }
     };
 
-    // Every fetch is unconditional (the chunk index is clamped to the sequence's last chunk), so the
-    // loads in flight are the same on every path and the wait before a use covers only that use.
-    ChunkFrags<K> fa, fb;
+    // Iteration c (c0 <= c <= c1): state waves process chunk c (when c < c1), output waves chunk c-1
+    // (when c > c0).  Every fetch is unconditional (chunk indices clamped into [c0, c1)), so the loads
+    // in flight are the same on every path and each wait covers only the data about to be used.
     if (c0 < c1) {
-        fetch(c0, fa);
-        for (int c = c0; c < c1; c += 2) {
-            fetch(min(c + 1, c1 - 1), fb);
-            process(c, fa);
-            if (c + 1 >= c1) break;
-            fetch(min(c + 2, c1 - 1), fa);
-            process(c + 1, fb);
+        if (is_state) {
+            StateFrags<K, NCT> fa, fb;
+            fetch_s(c0, fa);
+            for (int c = c0; c <= c1; c += 2) {
+                fetch_s(min(c + 1, c1 - 1), fb);
+                if (c < c1) s_store((c - c0) & 1);
+                __syncthreads();
+                if (c < c1) s_u((c - c0) & 1, fa);
+                __syncthreads();
+                if (c < c1) s_update((c - c0) & 1, fa);
+                if (c + 1 > c1) break;
+                fetch_s(min(c + 2, c1 - 1), fa);
+                if (c + 1 < c1) s_store((c + 1 - c0) & 1);
+                __syncthreads();
+                if (c + 1 < c1) s_u((c + 1 - c0) & 1, fb);
+                __syncthreads();
+                if (c + 1 < c1) s_update((c + 1 - c0) & 1, fb);
+            }
+        } else {
+            // chunk j's operands live in fa (j - c0 even) or fb (odd): fetched in iteration j, used in
+            // iteration j + 1
+            OutFrags<K> fa, fb;
+            for (int c = c0; c <= c1; c += 2) {
+                fetch_o(min(c, c1 - 1), fa);
+                __syncthreads();
+                if (c > c0) o_tile(c - 1, (c - 1 - c0) & 1, fb);
+                __syncthreads();
+                if (c + 1 > c1) break;
+                fetch_o(min(c + 1, c1 - 1), fb);
+                __syncthreads();
+                o_tile(c, (c - c0) & 1, fa);
+                __syncthreads();
+            }
         }
     }
-    if (p.state_out != nullptr) {
+    if (is_state && p.state_out != nullptr) {
 #pragma unroll
-        for (int t = 0; t < KTW; ++t) {
-            const int k = 16 * (KTW * wv + t) + (lane & 15);
+        for (int t = 0; t < KTW; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p.state_out[(col0 + 4 * (lane >> 4) + r) * K + k] = acc[t][r];
-        }
+            for (int ct = 0; ct < NCT; ++ct) {
+                const size_t off = (col0 + 16 * ct + (lane & 15)) * K + 16 * (KTW * wv + t) + 4 * (lane >> 4);
+                *reinterpret_cast<f32x4*>(p.state_out + off) = acc[t][ct];
+            }
     }
 }
 
@@ -581,13 +680,20 @@ template <typename T, int K, int V>
 hipError_t launch_kv(ChunkArgs p, hipStream_t stream) {
     const long long nch = ((long long)p.N + CH - 1) / CH + p.B;
     const long long par_blocks = nch * p.H;
-    const long long seq_blocks = (long long)p.B * p.H * (V / 16);
+    // Column tile of the state kernel: 64 columns share one load of the chunk's operands, 16 columns
+    // give four times the blocks.  Wide tiles win once they still fill every compute unit.
+    const long long wide_blocks = (long long)p.B * p.H * (V / 64);
+    const bool wide = wide_blocks >= 256;
+    const long long seq_blocks = wide ? wide_blocks : (long long)p.B * p.H * (V / 16);
     if (par_blocks > kMaxBlocks || seq_blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(1024), 0, stream, p);
     p.n_blocks = (int)par_blocks;
     hipLaunchKernelGGL((chunk_prep_kernel<T, K, V>), dim3((unsigned)par_blocks), dim3(256), 0, stream, p);
     p.n_blocks = (int)seq_blocks;
-    hipLaunchKernelGGL((chunk_state_kernel<T, K, V>), dim3((unsigned)seq_blocks), dim3(256), 0, stream, p);
+    if (wide)
+        hipLaunchKernelGGL((chunk_state_kernel<T, K, V, 4>), dim3((unsigned)seq_blocks), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((chunk_state_kernel<T, K, V, 1>), dim3((unsigned)seq_blocks), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -155,17 +155,19 @@ def test_ragged_multi_tile_small_case(torch):
             assert_close(f64(st), s_ref, 2e-2, f"ragged {path} {prepared} state")
 
 
-def chunk_ragged(K, seed=12):
+def chunk_ragged(K, H=4, io="bf16", seed=12):
     """Several chunks per sequence with ragged tails, a one-token and two zero-length sequences,
-    GQA 2, bf16: every shape corner of the chunked path."""
-    return workloads.make(name=f"chunk_ragged_k{K}", seed=seed, lengths=[130, 0, 64, 1, 0, 200, 63], HQ=2, H=4, K=K,
-                          V=K, io="bf16", conv_state_dtype="f32")
+    GQA 2: every shape corner of the chunked path.  With H*V/64 >= 256/7 value-column blocks the
+    state kernel takes its 64-column tile, else its 16-column tile."""
+    return workloads.make(name=f"chunk_ragged_k{K}_h{H}_{io}", seed=seed, lengths=[130, 0, 64, 1, 0, 200, 63],
+                          HQ=H // 2, H=H, K=K, V=K, io=io, conv_state_dtype="f32")
 
 
-@pytest.mark.parametrize("K", [64, 128])
-def test_chunk_ragged_against_oracle_and_seq(torch, K):
-    w = chunk_ragged(K)
-    print(f"[chunk ragged] K={K} N={w.N}", flush=True)
+@pytest.mark.parametrize("K,H,io", [(64, 4, "bf16"), (128, 4, "bf16"), (128, 4, "f16"), (64, 64, "bf16"),
+                                    (128, 32, "f16")])
+def test_chunk_ragged_against_oracle_and_seq(torch, K, H, io):
+    w = chunk_ragged(K, H, io)
+    print(f"[chunk ragged] K={K} H={H} {io} N={w.N}", flush=True)
     out_c, st_c, used = gpu_scan(torch, w, "chunk", False)
     assert used == "chunk"
     out_s, st_s, _ = gpu_scan(torch, w, "seq", False)
