@@ -16,19 +16,21 @@
 // Kernels (all on the caller's stream; bf16 MFMA operands, fp32 accumulation, fp32 state):
 //   index  one block: checks the offsets (nothing is written anywhere when they are malformed),
 //          builds the table of each sequence's first chunk.
-//   prep   one block per (chunk, head), parallel: gates, G, the normalised keys, A by MFMA
-//          (K K^T), T by blocked inversion (16x16 diagonal blocks by substitution, off-diagonal
-//          blocks by fp32 MFMA), W^T = X^T T^T and U' = T Y by MFMA.  Writes W, U'^T,
-//          Kd^T = (diag(e^{G_C - G}) K)^T, G and the key norms to the workspace.
-//   state  one block per (sequence, head, 16-column tile), sequential over the sequence's chunks:
-//          U = U' - W S^T, S <- e^{G_C} S + U^T Kd.  The fp32 state stays in MFMA accumulators.
-//          Writes U^T and the chunk-entry state S (bf16) to the workspace; the final state out.
-//   out    one block per (chunk, head), parallel: O^T = diag-scaled S Q^T + U^T (M o Q K^T)^T.
+//   prep   one block per (chunk, head), parallel: gates, G, the normalised q and k, A and the masked
+//          Q K^T by MFMA, T by blocked inversion (16x16 diagonal blocks by substitution, off-diagonal
+//          blocks by fp32 MFMA), W^T = X^T T^T and U' = T Y by MFMA.  Writes W, Kd^T =
+//          (diag(e^{G_C - G}) K)^T, Qhat, P = M o (Qhat Khat^T), U' and G to the workspace.
+//   state  one block per (sequence, head, column tile), sequential over the sequence's chunks:
+//          U = U' - W S^T, S <- e^{G_C} S + U^T Kd, with the fp32 state in MFMA accumulators; the
+//          output of the previous chunk from the same LDS copies of S and U on separate waves.
 //
-// Every MFMA operand is staged "inner-dimension contiguous" so each lane's 8-element fragment is one
-// 16-byte access (operand lane layouts of v_mfma_f32_16x16x32_bf16 / 16x16x4f32: lane l holds row
-// l%16, inner elements 8*(l/16)..+7 (resp. l/16); accumulator lane l holds rows 4*(l/16)..+3 of
-// column l%16).
+// Every MFMA operand the state kernel reads from the workspace is stored in fragment order: the
+// 16 x 32 bf16 block one instruction consumes is 64 consecutive 16-byte pieces, lane l's piece at
+// 16 l (operand lane layout of v_mfma_f32_16x16x32_bf16: lane l holds row l%16, inner elements
+// 8*(l/16)..+7; accumulator lane l holds rows 4*(l/16)..+3 of column l%16).  A wave then loads a
+// fragment as one contiguous 1 KB access: a row-major fragment touches sixteen 128-byte lines per
+// instruction, and on gfx950 that pattern moves about a third of the bytes per clock per compute unit
+// that a contiguous one does.
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -69,15 +71,21 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Workspace layout (byte offsets), identical on host and device.
+// Fragment tiles.  An A tile is one 16 x 32 bf16 operand block in lane order (lane l: row l%16,
+// inner elements 8(l/16)..+7; 512 elements).  A D tile is one 16 x 16 block in accumulator order
+// (lane l: rows 4(l/16)..+3 of column l%16; 256 elements).
+constexpr int AT = 512;
+constexpr int DT = 256;
+
+// Workspace layout (byte offsets), identical on host and device.  Per (chunk, head) "chh":
 struct WsLayout {
     size_t hdr;      // int32: [0] status, [1] total chunks; cstart[B+1] at +64
-    size_t w;        // W      [chunk-head][CH][K]  bf16
-    size_t upt;      // U'^T   [chunk-head][V][CH]  bf16
-    size_t kdt;      // Kd^T   [chunk-head][K][CH]  bf16, Kd = diag(e^{G_C - G}) Khat
-    size_t pm;       // P      [chunk-head][CH][CH] bf16, P = M o (Qhat Khat^T)
-    size_t gam;      // G      [chunk-head][CH]     f32
-    size_t rq;       // 1/|q|  [chunk-head][CH]     f32
+    size_t w;        // W     (CH x K, rows = tokens):      A tiles [4][K/32]
+    size_t kdt;      // Kd^T  (K x CH, rows = keys):        A tiles [K/16][2], Kd = diag(e^{G_C - G}) Khat
+    size_t qf;       // Qhat  (CH x K, rows = tokens):      A tiles [4][K/32]
+    size_t pm;       // P     (CH x CH, rows = tokens i):   A tiles [4][2], P = M o (Qhat Khat^T)
+    size_t upt;      // U'    (CH x V):                     D tiles [4][V/16]
+    size_t gam;      // G     [CH] f32
     size_t total;
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -90,18 +98,27 @@ __host__ __device__ inline WsLayout ws_layout(int B, int N, int H, int K, int V)
     o = align256(o + 64 + 4 * ((size_t)B + 1));
     L.w = o;
     o = align256(o + nh * CH * K * 2);
-    L.upt = o;
-    o = align256(o + nh * V * CH * 2);
     L.kdt = o;
     o = align256(o + nh * K * CH * 2);
+    L.qf = o;
+    o = align256(o + nh * CH * K * 2);
     L.pm = o;
     o = align256(o + nh * CH * CH * 2);
+    L.upt = o;
+    o = align256(o + nh * CH * V * 2);
     L.gam = o;
-    o = align256(o + nh * CH * 4);
-    L.rq = o;
     o = align256(o + nh * CH * 4);
     L.total = o;
     return L;
+}
+
+// Half of an A tile's lane piece from an accumulator: an accumulator lane holding rows 4(l/16)..+3
+// of column l%16 of the 16 x 16 block at inner offset 16*half of a 32-wide A tile writes elements
+// [4(l/16) + 16 half, +4) of row l%16, which is lane piece (l%16) + 16*(2 half + (l/16)/2) at
+// element 4*((l/16)%2).  Returns the element offset inside the tile.
+__device__ __forceinline__ int a_tile_half_offset(int lane, int half) {
+    const int g = lane >> 4;
+    return ((lane & 15) + 16 * (2 * half + (g >> 1))) * 8 + 4 * (g & 1);
 }
 
 struct ChunkArgs {
@@ -201,22 +218,26 @@ __device__ __forceinline__ u32x4 pack8(const float* x, float s) {
 }
 
 // ---- prep ----------------------------------------------------------------------------------------
+// Token rows are read whole: LPT = K/8 lanes per row, 8 elements (16 bytes) each, so one wave
+// instruction covers 64/LPT complete rows.  Column operands (8 consecutive tokens of one key or
+// value index) are gathered from the row-major LDS copies with 2-byte reads.
 template <typename T, int K, int V>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
     using TS = typename T::storage;
-    static_assert(K % 32 == 0 && V % 32 == 0 && K <= 128 && V <= 128, "chunk tile shapes");
-    __shared__ __align__(16) uint16_t xt[K][CH + PAD];  // X^T = (diag(b e^G) Khat)^T
-    __shared__ __align__(16) float am[CH][CH + 4];  // A (fp32); later T in bf16
+    static_assert(K == V && (K == 64 || K == 128), "chunk tile shapes");
+    constexpr int LPT = K / 8;     // lanes per token row
+    constexpr int TPI = 64 / LPT;  // token rows per wave instruction
+    constexpr int NI = 16 / TPI;   // instructions per wave for its 16 rows
+    constexpr int KT4 = K / 64;    // 16-wide key (value) tiles per wave
+    __shared__ __align__(16) uint16_t kn[CH][K + PAD];  // Khat rows
+    __shared__ __align__(16) uint16_t qn[CH][K + PAD];  // Qhat rows
+    __shared__ __align__(16) float am[CH][CH + 4];      // A (fp32); later T in bf16
     __shared__ __align__(16) union {
-        struct {
-            uint16_t kn[CH][K + PAD];  // Khat rows (bf16)
-            uint16_t qn[CH][K + PAD];  // Qhat rows (bf16)
-        } kq;                    // live until A and P are formed
-        float tm[CH][CH + 4];    // T (fp32), until it is rounded to bf16
-        uint16_t yt[V][CH + PAD];  // Y^T = (diag(b) V)^T, after that
+        uint16_t vn[CH][V + PAD];  // Y = diag(b) V rows, until its fragments are in registers
+        float tm[CH][CH + 4];      // T (fp32), until it is rounded to bf16
     } u1;
     __shared__ __align__(16) float scr[4][16][17];
-    __shared__ float s_gam[CH], s_beta[CH];
+    __shared__ float s_gam[CH], s_beta[CH], s_xs[CH], s_ks[CH];
     uint16_t(*tb)[CH + PAD] = reinterpret_cast<uint16_t(*)[CH + PAD]>(&am[0][0]);  // T (bf16), once A is dead
     static_assert(sizeof(uint16_t) * CH * (CH + PAD) <= sizeof(float) * CH * (CH + 4), "T (bf16) fits in A's space");
 
@@ -233,24 +254,33 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
     const int kh = h / p.G;
     const size_t chh = (size_t)cid * p.H + h;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int pc = lane % LPT, tsub = lane / LPT;
     const TS* qkv = static_cast<const TS*>(p.qkv);
+    uint16_t* const wsb = reinterpret_cast<uint16_t*>(p.ws);
+    uint16_t* const w_out = wsb + p.L.w / 2 + chh * CH * K;
+    uint16_t* const kd_out = wsb + p.L.kdt / 2 + chh * K * CH;
+    uint16_t* const q_out = wsb + p.L.qf / 2 + chh * CH * K;
+    uint16_t* const p_out = wsb + p.L.pm / 2 + chh * CH * CH;
+    uint16_t* const u_out = wsb + p.L.upt / 2 + chh * CH * V;
 
-    // raw v rows, fetched now and staged once T is done (4 threads per token)
-    constexpr int KPT = K / 4, VPT = V / 4;
-    const int ti = tid >> 2, part = tid & 3;
-    float vv[VPT];
+    // this wave's 16 token rows (row 16 wv + TPI u + tsub), elements 8 pc .. 8 pc + 7
+    float kr[NI][8], qr[NI][8], vr[NI][8];
 #pragma unroll
-    for (int e = 0; e < VPT; e += 8) {
-        float t8[8];
-        if (ti < n) load8<T>(qkv + (size_t)(t0 + ti) * p.C + (size_t)2 * p.HQ * K + (size_t)h * V + part * VPT + e, t8);
-        else
+    for (int u = 0; u < NI; ++u) {
+        const int ti = 16 * wv + TPI * u + tsub;
+        if (ti < n) {
+            const TS* row = qkv + (size_t)(t0 + ti) * p.C;
+            load8<T>(row + (size_t)(p.HQ + kh) * K + 8 * pc, kr[u]);
+            load8<T>(row + (size_t)kh * K + 8 * pc, qr[u]);
+            load8<T>(row + (size_t)2 * p.HQ * K + (size_t)h * V + 8 * pc, vr[u]);
+        } else {
 #pragma unroll
-            for (int z = 0; z < 8; ++z) t8[z] = 0.0f;
-#pragma unroll
-        for (int z = 0; z < 8; ++z) vv[e + z] = t8[z];
+            for (int z = 0; z < 8; ++z) kr[u][z] = qr[u][z] = vr[u][z] = 0.0f;
+        }
     }
 
-    // gates and the cumulative log-decay (wave 0, one token per lane)
+    // gates and the cumulative log-decay (wave 0, one token per lane); padding tokens have b = 0
+    // and no decay
     if (wv == 0) {
         float ell = 0.0f, beta = 0.0f;
         if (lane < n) {
@@ -269,71 +299,75 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
             const float y = __shfl_up(gam, d);
             if (lane >= d) gam += y;
         }
+        const float gC = __shfl(gam, CH - 1);
         s_gam[lane] = gam;
         s_beta[lane] = beta;
+        s_xs[lane] = beta * expf(gam);
+        s_ks[lane] = expf(gC - gam);
         reinterpret_cast<float*>(p.ws + p.L.gam)[chh * CH + lane] = gam;
     }
-    // q and k rows: norms by a 4-lane reduction
-    float kv[KPT], qv[KPT];
-    float rq, rk;
-    {
+    __syncthreads();  // gates ready
+
+    // normalised rows -> LDS
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+        const int ti = 16 * wv + TPI * u + tsub;
         float sk = 0.0f, sq = 0.0f;
 #pragma unroll
-        for (int e = 0; e < KPT; e += 8) {
-            float tk[8], tq[8];
-            if (ti < n) {
-                const TS* row = qkv + (size_t)(t0 + ti) * p.C;
-                load8<T>(row + (size_t)(p.HQ + kh) * K + part * KPT + e, tk);
-                load8<T>(row + (size_t)kh * K + part * KPT + e, tq);
-            } else {
-#pragma unroll
-                for (int z = 0; z < 8; ++z) tk[z] = tq[z] = 0.0f;
-            }
-#pragma unroll
-            for (int z = 0; z < 8; ++z) {
-                kv[e + z] = tk[z];
-                qv[e + z] = tq[z];
-                sk = fmaf(tk[z], tk[z], sk);
-                sq = fmaf(tq[z], tq[z], sq);
-            }
+        for (int z = 0; z < 8; ++z) {
+            sk = fmaf(kr[u][z], kr[u][z], sk);
+            sq = fmaf(qr[u][z], qr[u][z], sq);
         }
-        sk = group_sum<4>(sk);
-        sq = group_sum<4>(sq);
-        rk = rsqrtf(sk + 1e-12f);
-        rq = rsqrtf(sq + 1e-12f);
-        if (part == 0) reinterpret_cast<float*>(p.ws + p.L.rq)[chh * CH + ti] = rq;
+        sk = group_sum<LPT>(sk);
+        sq = group_sum<LPT>(sq);
+        *reinterpret_cast<u32x4*>(&kn[ti][8 * pc]) = pack8(kr[u], rsqrtf(sk + 1e-12f));
+        *reinterpret_cast<u32x4*>(&qn[ti][8 * pc]) = pack8(qr[u], rsqrtf(sq + 1e-12f));
+        *reinterpret_cast<u32x4*>(&u1.vn[ti][8 * pc]) = pack8(vr[u], s_beta[ti]);
     }
-    __syncthreads();  // s_gam, s_beta ready
-    {
-        const float gi = s_gam[ti], gC = s_gam[CH - 1], bi = s_beta[ti];
-        const float xs = bi * expf(gi), ks = expf(gC - gi);
-        uint16_t* kdt = reinterpret_cast<uint16_t*>(p.ws + p.L.kdt) + chh * K * CH;
+    __syncthreads();  // kn, qn, vn ready
+
+    // Qhat tiles (token tile wv) straight from its rows
 #pragma unroll
-        for (int e = 0; e < KPT; e += 8) {
-            *reinterpret_cast<u32x4*>(&u1.kq.kn[ti][part * KPT + e]) = pack8(&kv[e], rk);
-            *reinterpret_cast<u32x4*>(&u1.kq.qn[ti][part * KPT + e]) = pack8(&qv[e], rq);
-        }
+    for (int kk = 0; kk < K / 32; ++kk)
+        *reinterpret_cast<u32x4*>(q_out + (size_t)(wv * (K / 32) + kk) * AT + 8 * lane) =
+            *reinterpret_cast<const u32x4*>(&qn[16 * wv + (lane & 15)][32 * kk + 8 * (lane >> 4)]);
+
+    // Column fragments of key tiles kt = wv + 4m: Kd^T (stored) and X^T = (diag(b e^G) Khat)^T (kept
+    // for W), and of value tiles vt = wv + 4m: Y (kept for U').  Lane l: index 16 kt + l%16, tokens
+    // 32 c + 8(l/16) + e.
+    bf16x8 xf[KT4][2], yf[KT4][2];
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const int k = part * KPT + e;
-            const float khat = kv[e] * rk;
-            xt[k][ti] = bf(xs * khat);
-            kdt[(size_t)k * CH + ti] = bf(ks * khat);
+    for (int m = 0; m < KT4; ++m) {
+        const int kt = wv + 4 * m, col = 16 * kt + (lane & 15);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int tb0 = 32 * c + 8 * (lane >> 4);
+            float kx[8], kdv[8];
+            bf16x8 y;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kv = bf16_bits_to_f32(kn[tb0 + e][col]);
+                kx[e] = s_xs[tb0 + e] * kv;
+                kdv[e] = s_ks[tb0 + e] * kv;
+                y[e] = __builtin_bit_cast(__bf16, u1.vn[tb0 + e][col]);
+            }
+            *reinterpret_cast<u32x4*>(kd_out + (size_t)(kt * 2 + c) * AT + 8 * lane) = pack8(kdv, 1.0f);
+            const u32x4 xp = pack8(kx, 1.0f);
+            xf[m][c] = __builtin_bit_cast(bf16x8, xp);
+            yf[m][c] = y;
         }
     }
-    __syncthreads();  // kn, qn, xt ready
 
     // Row block wv: A_ij = b_i e^{G_i - G_j} (khat_i . khat_j) for j < i, and
     // P_ij = e^{G_i - G_j} (qhat_i . khat_j) for j <= i (computed transposed: 4 consecutive j per lane)
-    uint16_t* pout = reinterpret_cast<uint16_t*>(p.ws + p.L.pm) + chh * CH * CH;
     for (int jt = 0; jt < 4; ++jt) {
         f32x4 a = zero4(), pt = zero4();
         if (jt <= wv) {
 #pragma unroll
             for (int kk = 0; kk < K; kk += 32) {
-                const bf16x8 kj = frag(&u1.kq.kn[16 * jt][kk], K + PAD, lane);
-                a = mma_bf16(frag(&u1.kq.kn[16 * wv][kk], K + PAD, lane), kj, a);
-                pt = mma_bf16(kj, frag(&u1.kq.qn[16 * wv][kk], K + PAD, lane), pt);
+                const bf16x8 kj = frag(&kn[16 * jt][kk], K + PAD, lane);
+                a = mma_bf16(frag(&kn[16 * wv][kk], K + PAD, lane), kj, a);
+                pt = mma_bf16(kj, frag(&qn[16 * wv][kk], K + PAD, lane), pt);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -345,9 +379,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
         float pv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) pv[r] = (j + r <= i) ? expf(s_gam[i] - s_gam[j + r]) * pt[r] : 0.0f;
-        *reinterpret_cast<u32x2*>(pout + (size_t)i * CH + j) = pack4(pv[0], pv[1], pv[2], pv[3]);
+        *reinterpret_cast<u32x2*>(p_out + (size_t)(wv * 2 + (jt >> 1)) * AT + a_tile_half_offset(lane, jt & 1)) =
+            pack4(pv[0], pv[1], pv[2], pv[3]);
     }
-    __syncthreads();  // A ready; kn and qn dead (tm may be written)
+    __syncthreads();  // A ready; kn, qn, vn dead (tm may be written)
 
     // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution (wave w, lanes 0..15 own the
     // columns of block w); T is zero above the diagonal.
@@ -397,33 +432,30 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
         const int i = idx / CH, j = idx % CH;
         tb[i][j] = bf(u1.tm[i][j]);
     }
-    __syncthreads();  // tm dead: Y^T may be staged in its place
-    {
-        const float bi = s_beta[ti];
-#pragma unroll
-        for (int e = 0; e < VPT; ++e) u1.yt[part * VPT + e][ti] = bf(bi * vv[e]);
-    }
     __syncthreads();
 
-    // W^T = X^T T^T  ->  lane writes W[i][k..k+3]
-    uint16_t* wout = reinterpret_cast<uint16_t*>(p.ws + p.L.w) + chh * CH * K;
-    for (int tile = wv; tile < (K / 16) * 4; tile += 4) {
-        const int kt = tile >> 2, it = tile & 3;
-        f32x4 acc = zero4();
+    // W^T = X^T T^T for key tiles kt = wv + 4m: lane holds W[i][k..k+3], half of a W tile piece
 #pragma unroll
-        for (int jj = 0; jj < CH; jj += 32) acc = mma_bf16(frag(&xt[16 * kt][jj], CH + PAD, lane), frag(&tb[16 * it][jj], CH + PAD, lane), acc);
-        const int i = 16 * it + (lane & 15), k = 16 * kt + 4 * (lane >> 4);
-        *reinterpret_cast<u32x2*>(wout + (size_t)i * K + k) = pack4(acc[0], acc[1], acc[2], acc[3]);
+    for (int m = 0; m < KT4; ++m) {
+        const int kt = wv + 4 * m;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            f32x4 acc = mma_bf16(xf[m][0], frag(&tb[16 * it][0], CH + PAD, lane), zero4());
+            acc = mma_bf16(xf[m][1], frag(&tb[16 * it][32], CH + PAD, lane), acc);
+            *reinterpret_cast<u32x2*>(w_out + (size_t)(it * (K / 32) + (kt >> 1)) * AT + a_tile_half_offset(lane, kt & 1)) =
+                pack4(acc[0], acc[1], acc[2], acc[3]);
+        }
     }
-    // U' = T Y  ->  lane writes U'^T[v][i..i+3]
-    uint16_t* upt = reinterpret_cast<uint16_t*>(p.ws + p.L.upt) + chh * V * CH;
-    for (int tile = wv; tile < 4 * (V / 16); tile += 4) {
-        const int it = tile / (V / 16), vt = tile % (V / 16);
-        f32x4 acc = zero4();
+    // U' = T Y for value tiles vt = wv + 4m: accumulator order is the D tile order
 #pragma unroll
-        for (int jj = 0; jj < CH; jj += 32) acc = mma_bf16(frag(&tb[16 * it][jj], CH + PAD, lane), frag(&u1.yt[16 * vt][jj], CH + PAD, lane), acc);
-        const int v = 16 * vt + (lane & 15), i = 16 * it + 4 * (lane >> 4);
-        *reinterpret_cast<u32x2*>(upt + (size_t)v * CH + i) = pack4(acc[0], acc[1], acc[2], acc[3]);
+    for (int m = 0; m < KT4; ++m) {
+        const int vt = wv + 4 * m;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            f32x4 acc = mma_bf16(frag(&tb[16 * it][0], CH + PAD, lane), yf[m][0], zero4());
+            acc = mma_bf16(frag(&tb[16 * it][32], CH + PAD, lane), yf[m][1], acc);
+            *reinterpret_cast<u32x2*>(u_out + (size_t)(it * (V / 16) + vt) * DT + 4 * lane) = pack4(acc[0], acc[1], acc[2], acc[3]);
+        }
     }
 }
 
@@ -432,35 +464,37 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
 // until it is used, so no wait is forced early.  State waves use StateFrags, output waves OutFrags.
 template <int K, int NCT>
 struct StateFrags {
-    bf16x8 w[K / 32];          // W rows of this wave's token tile
-    u32x2 up[NCT];             // U'^T[v][4 tokens] per column tile
-    bf16x8 kd[K / 64][2];      // Kd^T rows of this wave's k tiles
+    bf16x8 w[K / 32];          // W tiles of this wave's token tile
+    u32x2 up[NCT];             // U' D-tile pieces, one per column tile
+    bf16x8 kd[K / 64][2];      // Kd^T tiles of this wave's key tiles
     float gC;                  // G_C
 };
 template <int K>
 struct OutFrags {
-    bf16x8 q[K / 32];          // raw q rows of this wave's token tile (bf16)
-    bf16x8 pm[2];              // P rows of this wave's token tile
-    float gi, rq;              // G_i and 1/|q_i| of this lane's output token
+    bf16x8 q[K / 32];          // Qhat tiles of this wave's token tile
+    bf16x8 pm[2];              // P tiles of this wave's token tile
+    float gi;                  // G_i of this lane's output token
 };
 
 // ---- state + output ---------------------------------------------------------------------------------
 // One block of 8 waves per (sequence, head, VT-column tile; VT = 16 NCT).  Loads of the chunk's
-// W, Kd, q and P are shared by the block's NCT 16-column tiles.
+// W, Kd, Qhat and P are shared by the block's NCT 16-column tiles.
 //   Waves 0-3 ("state") carry the serial chain for chunk c: the entering state -> LDS (bf16),
-//   U = U' - W S^T for token tile w, and S^T <- e^{G_C} S^T + Kd^T U for k tiles of wave w.  The state
-//   is held transposed (accumulator lane: 4 consecutive k of one value column), which makes its LDS
-//   copy and its HBM load/store contiguous.
-//   Waves 4-7 ("output") compute chunk c-1's output O^T[v][i] = rq_i e^{G_i} (S q_i) + (U^T P^T)[v][i]
-//   for token tile w from the double-buffered S and U^T, off the serial chain.
+//   U = U' - W S^T for token tile w, and S^T <- e^{G_C} S^T + Kd^T U for key tiles of wave w.  The
+//   state is held transposed (accumulator lane: 4 consecutive keys of one value column), which makes
+//   its LDS copy and its HBM load/store contiguous.
+//   Waves 4-7 ("output") compute chunk c-1's output O^T[v][i] = e^{G_i} (S qhat_i) + (U^T P^T)[v][i]
+//   for token tile w from the double-buffered S and U^T, off the serial chain, and write it as whole
+//   token rows through a per-wave LDS tile.
 template <typename T, int K, int V, int NCT>
 __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
     using TS = typename T::storage;
     constexpr int VT = 16 * NCT;
-    constexpr int KTW = K / 64;  // 16-wide k tiles per state wave
+    constexpr int KTW = K / 64;  // 16-wide key tiles per state wave
     static_assert(V % VT == 0, "column tiles");
     __shared__ __align__(16) uint16_t sb[2][VT][K + PAD];   // S entering the chunk (bf16)
     __shared__ __align__(16) uint16_t ut[2][VT][CH + PAD];  // U^T (bf16)
+    __shared__ __align__(16) uint16_t ot[4][16][VT + 8];    // output rows, one tile per output wave
 
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws + p.L.hdr);
     if (hdr[0] != GDN_OK) return;
@@ -470,22 +504,21 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
     const int vt = blk % NVT;
     const int bh = blk / NVT;
     const int h = bh % p.H, b = bh / p.H;
-    const int kh = h / p.G;
     const int tid = threadIdx.x, lane = tid & 63;
     const bool is_state = tid < 256;
-    const int wv = (tid >> 6) & 3;  // token / k tile of this wave within its group
+    const int wv = (tid >> 6) & 3;  // token / key tile of this wave within its group
     const int v0 = vt * VT;
     const size_t col0 = ((size_t)b * p.H + h) * V + v0;  // first state row of the block
-    const TS* qkv = static_cast<const TS*>(p.qkv);
     TS* outp = static_cast<TS*>(p.out);
     const int c0 = cstart[b], c1 = cstart[b + 1];
     const int seq_start = p.offsets[b], seq_end = p.offsets[b + 1];
-    const uint16_t* wbase = reinterpret_cast<const uint16_t*>(p.ws + p.L.w);
-    const uint16_t* uptb = reinterpret_cast<const uint16_t*>(p.ws + p.L.upt);
-    const uint16_t* kdtb = reinterpret_cast<const uint16_t*>(p.ws + p.L.kdt);
-    const uint16_t* pmb = reinterpret_cast<const uint16_t*>(p.ws + p.L.pm);
+    const uint16_t* const wsb = reinterpret_cast<const uint16_t*>(p.ws);
+    const uint16_t* const wbase = wsb + p.L.w / 2;
+    const uint16_t* const kdbase = wsb + p.L.kdt / 2;
+    const uint16_t* const qbase = wsb + p.L.qf / 2;
+    const uint16_t* const pbase = wsb + p.L.pm / 2;
+    const uint16_t* const ubase = wsb + p.L.upt / 2;
     const float* gamb = reinterpret_cast<const float*>(p.ws + p.L.gam);
-    const float* rqb = reinterpret_cast<const float*>(p.ws + p.L.rq);
 
     // transposed state tiles (state waves): acc[t][ct][r] = S[v0 + 16 ct + l%16][16 (KTW w + t) + 4(l/16) + r]
     f32x4 acc[KTW][NCT];
@@ -499,41 +532,29 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
             }
     }
 
+    auto afrag = [&](const uint16_t* tile) { return *reinterpret_cast<const bf16x8*>(tile + 8 * lane); };
     auto fetch_s = [&](int c, StateFrags<K, NCT>& f) {
         const size_t chh = (size_t)c * p.H + h;
-        const uint16_t* wrow = wbase + (chh * CH + 16 * wv) * K;
+        const uint16_t* wt = wbase + (chh * 4 + wv) * (K / 32) * AT;
 #pragma unroll
-        for (int kk = 0; kk < K / 32; ++kk) f.w[kk] = frag(wrow + 32 * kk, K, lane);
+        for (int kk = 0; kk < K / 32; ++kk) f.w[kk] = afrag(wt + kk * AT);
+        const uint16_t* ud = ubase + ((chh * 4 + wv) * (V / 16) + vt * NCT) * DT + 4 * lane;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-            f.up[ct] = *reinterpret_cast<const u32x2*>(uptb + (chh * V + v0 + 16 * ct + (lane & 15)) * CH + 16 * wv + 4 * (lane >> 4));
+        for (int ct = 0; ct < NCT; ++ct) f.up[ct] = *reinterpret_cast<const u32x2*>(ud + ct * DT);
 #pragma unroll
         for (int t = 0; t < KTW; ++t)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) f.kd[t][jj] = frag(kdtb + (chh * K + 16 * (KTW * wv + t)) * CH + 32 * jj, CH, lane);
+            for (int jj = 0; jj < 2; ++jj) f.kd[t][jj] = afrag(kdbase + ((chh * (K / 16) + KTW * wv + t) * 2 + jj) * AT);
         f.gC = gamb[chh * CH + CH - 1];
     };
     auto fetch_o = [&](int c, OutFrags<K>& f) {
         const size_t chh = (size_t)c * p.H + h;
-        // q rows of this lane's output token; past the sequence end the row index is clamped to the
-        // sequence's last token (a valid row): those columns of the tile are never stored
-        const int tq = min(seq_start + (c - c0) * CH + 16 * wv + (lane & 15), seq_end - 1);
+        const uint16_t* qt = qbase + (chh * 4 + wv) * (K / 32) * AT;
 #pragma unroll
-        for (int kk = 0; kk < K / 32; ++kk) {
-            if constexpr (std::is_same<T, BF16>::value) {
-                f.q[kk] = *reinterpret_cast<const bf16x8*>(qkv + (size_t)tq * p.C + (size_t)kh * K + 32 * kk + 8 * (lane >> 4));
-            } else {
-                float t8[8];
-                load8<T>(qkv + (size_t)tq * p.C + (size_t)kh * K + 32 * kk + 8 * (lane >> 4), t8);
+        for (int kk = 0; kk < K / 32; ++kk) f.q[kk] = afrag(qt + kk * AT);
 #pragma unroll
-                for (int z = 0; z < 8; ++z) f.q[kk][z] = (__bf16)t8[z];
-            }
-        }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) f.pm[jj] = frag(pmb + (chh * CH + 16 * wv) * CH + 32 * jj, CH, lane);
-        const int io = 16 * wv + (lane & 15);
-        f.gi = gamb[chh * CH + io];
-        f.rq = rqb[chh * CH + io];
+        for (int jj = 0; jj < 2; ++jj) f.pm[jj] = afrag(pbase + ((chh * 4 + wv) * 2 + jj) * AT);
+        f.gi = gamb[chh * CH + 16 * wv + (lane & 15)];
     };
 
     // state waves, before the first barrier: S entering the chunk -> LDS (one 8-byte store per tile)
@@ -589,9 +610,10 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
         order_reads_then_mfma<2 * NCT, 2 * KTW * NCT>();
     };
     // output waves: chunk c's output tiles (token tile wv, all column tiles) from sb[buf], ut[buf]
+    constexpr int LPR = VT / 8;         // lanes per output row (16 bytes each)
+    constexpr int RPI = 64 / LPR;       // rows per store instruction
     auto o_tile = [&](int c, int buf, const OutFrags<K>& f) {
-        const int t = seq_start + (c - c0) * CH + 16 * wv + (lane & 15);
-        const float cs = f.rq * expf(f.gi);
+        const float cs = expf(f.gi);
         bf16x8 sf[NCT][K / 32], uf[NCT][2];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
@@ -613,16 +635,28 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) a1[ct] = mma_bf16(sf[ct][kk], f.q[kk], a1[ct]);
         order_reads_then_mfma<(K / 32 + 2) * NCT, (K / 32 + 2) * NCT>();
-        if (t < seq_end) {
+        // lane: token 16 wv + l%16, columns 16 ct + 4(l/16) .. +3
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                float o[4];
+        for (int ct = 0; ct < NCT; ++ct) {
+            float o[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = p.scale * fmaf(cs, a1[ct][r], a2[ct][r]);
-                TS* dst = outp + ((size_t)t * p.H + h) * V + v0 + 16 * ct + 4 * (lane >> 4);
-                *reinterpret_cast<u32x2*>(dst) = u32x2{(uint32_t)from_f32<T>(o[0]) | ((uint32_t)from_f32<T>(o[1]) << 16),
-                                                       (uint32_t)from_f32<T>(o[2]) | ((uint32_t)from_f32<T>(o[3]) << 16)};
-            }
+            for (int r = 0; r < 4; ++r) o[r] = p.scale * fmaf(cs, a1[ct][r], a2[ct][r]);
+            *reinterpret_cast<u32x2*>(&ot[wv][lane & 15][16 * ct + 4 * (lane >> 4)]) =
+                u32x2{(uint32_t)from_f32<T>(o[0]) | ((uint32_t)from_f32<T>(o[1]) << 16),
+                      (uint32_t)from_f32<T>(o[2]) | ((uint32_t)from_f32<T>(o[3]) << 16)};
+        }
+        // the tile is this wave's alone: LDS keeps one wave's accesses in order, the fence keeps the
+        // compiler from moving the reads above the writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int tbase = seq_start + (c - c0) * CH + 16 * wv;
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += RPI) {
+            const int row = r0 + lane / LPR;
+            if (row < 16 && tbase + row < seq_end)
+                *reinterpret_cast<u32x4*>(outp + ((size_t)(tbase + row) * p.H + h) * V + v0 + 8 * (lane % LPR)) =
+                    *reinterpret_cast<const u32x4*>(&ot[wv][row][8 * (lane % LPR)]);
         }
     };
 
