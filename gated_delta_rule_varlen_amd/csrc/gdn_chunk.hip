@@ -212,6 +212,16 @@ __device__ __forceinline__ void load8(const typename T::storage* p, float (&v)[8
     }
 }
 
+// Eight 16-bit values packed in 16 bytes -> fp32.
+template <typename T>
+__device__ __forceinline__ void unpack8(u32x4 raw, float (&v)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = to_f32<T>((uint16_t)(raw[e] & 0xffffu));
+        v[2 * e + 1] = to_f32<T>((uint16_t)(raw[e] >> 16));
+    }
+}
+
 __device__ __forceinline__ u32x4 pack8(const float* x, float s) {
     return u32x4{(uint32_t)bf(x[0] * s) | ((uint32_t)bf(x[1] * s) << 16), (uint32_t)bf(x[2] * s) | ((uint32_t)bf(x[3] * s) << 16),
                  (uint32_t)bf(x[4] * s) | ((uint32_t)bf(x[5] * s) << 16), (uint32_t)bf(x[6] * s) | ((uint32_t)bf(x[7] * s) << 16)};
@@ -221,25 +231,39 @@ __device__ __forceinline__ u32x4 pack8(const float* x, float s) {
 // Token rows are read whole: LPT = K/8 lanes per row, 8 elements (16 bytes) each, so one wave
 // instruction covers 64/LPT complete rows.  Column operands (8 consecutive tokens of one key or
 // value index) are gathered from the row-major LDS copies with 2-byte reads.
+// LDS is shared by lifetime (52 KB at K = 128, so three blocks fit on a compute unit):
+//   region 0: Khat rows, until A and P are formed; then T (fp32)
+//   region 1: Qhat rows, until A and P are formed; then the inversion scratch
+//   region 2: Y rows, until their fragments are in registers; then A (fp32); then T (bf16)
 template <typename T, int K, int V>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
+__global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
     using TS = typename T::storage;
     static_assert(K == V && (K == 64 || K == 128), "chunk tile shapes");
     constexpr int LPT = K / 8;     // lanes per token row
     constexpr int TPI = 64 / LPT;  // token rows per wave instruction
     constexpr int NI = 16 / TPI;   // instructions per wave for its 16 rows
     constexpr int KT4 = K / 64;    // 16-wide key (value) tiles per wave
-    __shared__ __align__(16) uint16_t kn[CH][K + PAD];  // Khat rows
-    __shared__ __align__(16) uint16_t qn[CH][K + PAD];  // Qhat rows
-    __shared__ __align__(16) float am[CH][CH + 4];      // A (fp32); later T in bf16
     __shared__ __align__(16) union {
-        uint16_t vn[CH][V + PAD];  // Y = diag(b) V rows, until its fragments are in registers
-        float tm[CH][CH + 4];      // T (fp32), until it is rounded to bf16
-    } u1;
-    __shared__ __align__(16) float scr[4][16][17];
+        uint16_t kn[CH][K + PAD];  // Khat rows
+        float tm[CH][CH + 4];      // T (fp32)
+    } r0;
+    __shared__ __align__(16) union {
+        uint16_t qn[CH][K + PAD];  // Qhat rows
+        float scr[4][16][17];      // off-diagonal inversion scratch
+    } r1;
+    __shared__ __align__(16) union {
+        uint16_t vn[CH][V + PAD];  // Y = diag(b) V rows
+        float am[CH][CH + 4];      // A (fp32)
+        uint16_t tb[CH][CH + PAD];  // T (bf16)
+    } r2;
     __shared__ float s_gam[CH], s_beta[CH], s_xs[CH], s_ks[CH];
-    uint16_t(*tb)[CH + PAD] = reinterpret_cast<uint16_t(*)[CH + PAD]>(&am[0][0]);  // T (bf16), once A is dead
-    static_assert(sizeof(uint16_t) * CH * (CH + PAD) <= sizeof(float) * CH * (CH + 4), "T (bf16) fits in A's space");
+    auto& kn = r0.kn;
+    auto& tm = r0.tm;
+    auto& qn = r1.qn;
+    auto& scr = r1.scr;
+    auto& vn = r2.vn;
+    auto& am = r2.am;
+    auto& tb = r2.tb;
 
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws + p.L.hdr);
     if (hdr[0] != GDN_OK) return;
@@ -263,19 +287,19 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
     uint16_t* const p_out = wsb + p.L.pm / 2 + chh * CH * CH;
     uint16_t* const u_out = wsb + p.L.upt / 2 + chh * CH * V;
 
-    // this wave's 16 token rows (row 16 wv + TPI u + tsub), elements 8 pc .. 8 pc + 7
-    float kr[NI][8], qr[NI][8], vr[NI][8];
+    // this wave's 16 token rows (row 16 wv + TPI u + tsub), elements 8 pc .. 8 pc + 7, kept packed
+    // (16-bit inputs) until the gates are known
+    u32x4 kr[NI], qr[NI], vr[NI];
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
         const int ti = 16 * wv + TPI * u + tsub;
         if (ti < n) {
             const TS* row = qkv + (size_t)(t0 + ti) * p.C;
-            load8<T>(row + (size_t)(p.HQ + kh) * K + 8 * pc, kr[u]);
-            load8<T>(row + (size_t)kh * K + 8 * pc, qr[u]);
-            load8<T>(row + (size_t)2 * p.HQ * K + (size_t)h * V + 8 * pc, vr[u]);
+            kr[u] = *reinterpret_cast<const u32x4*>(row + (size_t)(p.HQ + kh) * K + 8 * pc);
+            qr[u] = *reinterpret_cast<const u32x4*>(row + (size_t)kh * K + 8 * pc);
+            vr[u] = *reinterpret_cast<const u32x4*>(row + (size_t)2 * p.HQ * K + (size_t)h * V + 8 * pc);
         } else {
-#pragma unroll
-            for (int z = 0; z < 8; ++z) kr[u][z] = qr[u][z] = vr[u][z] = 0.0f;
+            kr[u] = qr[u] = vr[u] = u32x4{0u, 0u, 0u, 0u};
         }
     }
 
@@ -312,17 +336,21 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
         const int ti = 16 * wv + TPI * u + tsub;
+        float kf[8], qf[8], vf[8];
+        unpack8<T>(kr[u], kf);
+        unpack8<T>(qr[u], qf);
+        unpack8<T>(vr[u], vf);
         float sk = 0.0f, sq = 0.0f;
 #pragma unroll
         for (int z = 0; z < 8; ++z) {
-            sk = fmaf(kr[u][z], kr[u][z], sk);
-            sq = fmaf(qr[u][z], qr[u][z], sq);
+            sk = fmaf(kf[z], kf[z], sk);
+            sq = fmaf(qf[z], qf[z], sq);
         }
         sk = group_sum<LPT>(sk);
         sq = group_sum<LPT>(sq);
-        *reinterpret_cast<u32x4*>(&kn[ti][8 * pc]) = pack8(kr[u], rsqrtf(sk + 1e-12f));
-        *reinterpret_cast<u32x4*>(&qn[ti][8 * pc]) = pack8(qr[u], rsqrtf(sq + 1e-12f));
-        *reinterpret_cast<u32x4*>(&u1.vn[ti][8 * pc]) = pack8(vr[u], s_beta[ti]);
+        *reinterpret_cast<u32x4*>(&kn[ti][8 * pc]) = pack8(kf, rsqrtf(sk + 1e-12f));
+        *reinterpret_cast<u32x4*>(&qn[ti][8 * pc]) = pack8(qf, rsqrtf(sq + 1e-12f));
+        *reinterpret_cast<u32x4*>(&vn[ti][8 * pc]) = pack8(vf, s_beta[ti]);
     }
     __syncthreads();  // kn, qn, vn ready
 
@@ -349,7 +377,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
                 const float kv = bf16_bits_to_f32(kn[tb0 + e][col]);
                 kx[e] = s_xs[tb0 + e] * kv;
                 kdv[e] = s_ks[tb0 + e] * kv;
-                y[e] = __builtin_bit_cast(__bf16, u1.vn[tb0 + e][col]);
+                y[e] = __builtin_bit_cast(__bf16, vn[tb0 + e][col]);
             }
             *reinterpret_cast<u32x4*>(kd_out + (size_t)(kt * 2 + c) * AT + 8 * lane) = pack8(kdv, 1.0f);
             const u32x4 xp = pack8(kx, 1.0f);
@@ -357,6 +385,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
             yf[m][c] = y;
         }
     }
+
+    __syncthreads();  // Y gathered: A may overwrite it
 
     // Row block wv: A_ij = b_i e^{G_i - G_j} (khat_i . khat_j) for j < i, and
     // P_ij = e^{G_i - G_j} (qhat_i . khat_j) for j <= i (computed transposed: 4 consecutive j per lane)
@@ -382,11 +412,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
         *reinterpret_cast<u32x2*>(p_out + (size_t)(wv * 2 + (jt >> 1)) * AT + a_tile_half_offset(lane, jt & 1)) =
             pack4(pv[0], pv[1], pv[2], pv[3]);
     }
-    __syncthreads();  // A ready; kn, qn, vn dead (tm may be written)
+    __syncthreads();  // A ready; Khat and Qhat rows dead (T and the scratch may be written)
 
     // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution (wave w, lanes 0..15 own the
     // columns of block w); T is zero above the diagonal.
-    for (int idx = tid; idx < CH * CH; idx += 256) u1.tm[idx / CH][idx % CH] = 0.0f;
+    for (int idx = tid; idx < CH * CH; idx += 256) tm[idx / CH][idx % CH] = 0.0f;
     __syncthreads();
     if (lane < 16) {
         const int c = lane, o = 16 * wv;
@@ -399,7 +429,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
             x[i] = v;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) u1.tm[o + i][o + c] = x[i];
+        for (int i = 0; i < 16; ++i) tm[o + i][o + c] = x[i];
     }
     __syncthreads();
     // Off-diagonal blocks, one block diagonal at a time: T_ij = -T_ii sum_{j<=m<i} A_im T_mj.
@@ -412,7 +442,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
 #pragma unroll
                 for (int kk = 0; kk < 16; kk += 4)
                     y = mma_f32(am[16 * bi + (lane & 15)][16 * m + kk + (lane >> 4)],
-                                u1.tm[16 * m + kk + (lane >> 4)][16 * bj + (lane & 15)], y);
+                                tm[16 * m + kk + (lane >> 4)][16 * bj + (lane & 15)], y);
 #pragma unroll
             for (int r = 0; r < 4; ++r) scr[wv][4 * (lane >> 4) + r][lane & 15] = y[r];
         }
@@ -421,16 +451,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs p) {
             f32x4 z = zero4();
 #pragma unroll
             for (int kk = 0; kk < 16; kk += 4)
-                z = mma_f32(u1.tm[16 * bi + (lane & 15)][16 * bi + kk + (lane >> 4)], scr[wv][kk + (lane >> 4)][lane & 15], z);
+                z = mma_f32(tm[16 * bi + (lane & 15)][16 * bi + kk + (lane >> 4)], scr[wv][kk + (lane >> 4)][lane & 15], z);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) u1.tm[16 * bi + 4 * (lane >> 4) + r][16 * bj + (lane & 15)] = -z[r];
+            for (int r = 0; r < 4; ++r) tm[16 * bi + 4 * (lane >> 4) + r][16 * bj + (lane & 15)] = -z[r];
         }
         __syncthreads();
     }
     // T to bf16 (overwrites A, which is dead)
     for (int idx = tid; idx < CH * CH; idx += 256) {
         const int i = idx / CH, j = idx % CH;
-        tb[i][j] = bf(u1.tm[i][j]);
+        tb[i][j] = bf(tm[i][j]);
     }
     __syncthreads();
 
