@@ -4,7 +4,8 @@ A step is one pass of the whole path over one batch of seeded synthetic input, w
 in HBM: the varlen causal conv1d (its window updated in place) followed by the gated delta-rule
 recurrence (state updated in place).  The default workload is the decode step (B=256 sequences x 1
 token, HQ=16, H=32, K=V=128, bf16, fp32 state), where the recurrence runs in one fused launch.
-The prefill workload (B=8, lengths ~ U[512, 4096]) is measured too and reported in "also".
+The prefill workload (B=8, lengths ~ U[512, 4096]) and the long single sequence (N=65536, H=16) are
+measured too and reported in "also", with the arithmetic roofline of the path they take.
 
 Prints ONE JSON line.  The dominant kernel (the recurrence) is timed with HIP events on the stream
 it is launched on; its algorithmic bytes per launch are the fp32 state read and written plus the
@@ -127,12 +128,44 @@ def time_path(p: "Path", steps: int, warmup: int):
     return total_ms / steps, scan_ms, used, wall
 
 
-def roofline(w, scan_ms: float, workload: str):
+def roofline(w, scan_ms: float, workload: str, kernel: str = "scan_kernel"):
     achieved = scan_bytes(w) / (scan_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(workload),
-            "kernel": "scan_kernel", "algorithmic_bytes_per_launch": scan_bytes(w),
+            "kernel": kernel, "algorithmic_bytes_per_launch": scan_bytes(w),
             "avg_launch_us": round(scan_ms * 1e3, 2)}
+
+
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, published
+VALU_FP32_PEAK_TFS = 78.6    # 256 CUs x 64 fp32 FMA lanes per clock x 2 flops x 2.4 GHz, non-packed FMA
+
+
+def compute_roofline(w, scan_ms: float, used: str):
+    """Arithmetic side of one recurrence launch.  The chunked form's dense contractions per token and
+    value head are 2C(3K + 2V) + 6KV flops (C = 64 tokens per chunk), on bf16 matrix cores; the
+    token-sequential form does 7KV fp32 flops per token and value head on the vector ALUs (packed
+    fp32 is not used, so the peak is the non-packed one)."""
+    if used == "chunk":
+        flops = (2 * 64 * (3 * w.K + 2 * w.V) + 6 * w.K * w.V) * w.H * w.N
+        bound, peak = "mfma", MFMA_BF16_PEAK_TFS
+    else:
+        flops = 7 * w.K * w.V * w.H * w.N
+        bound, peak = "alu", VALU_FP32_PEAK_TFS
+    tfs = flops / (scan_ms * 1e-3) / 1e12
+    return {"bound": bound, "achieved": round(tfs, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4),
+            "flops_per_launch": flops}
+
+
+def secondary(torch, wl, steps: int, warmup: int):
+    """One more workload, measured the same way (chunked path when eligible)."""
+    pp = Path(wl, torch, "auto")
+    pms, pscan_ms, pused, _ = time_path(pp, steps, warmup)
+    rec = {"workload": wl.name, "N": wl.N, "path": pused, "tokens_per_s": round(wl.N / (pms * 1e-3), 1),
+           "ms_per_step": round(pms, 4), "scan_ms": round(pscan_ms, 4),
+           "roofline": roofline(wl, pscan_ms, "none", "gdn_scan_varlen call (all its kernels)"), "compute_roofline": compute_roofline(wl, pscan_ms, pused)}
+    del pp
+    torch.cuda.empty_cache()
+    return rec
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
@@ -144,7 +177,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
     seqs = 0
     t_total = 0.0
     reps = 0
-    while t_total < budget_s and reps < 64:
+    while t_total < budget_s and reps < 1024:
         for b in range(w.B):
             s, e = int(w.offsets[b]), int(w.offsets[b + 1])
             off = np.array([0, e - s], np.int32)
@@ -234,18 +267,13 @@ def main():
                    "conv_W": w.W, "conv_D": w.D, "path": used, "parallelism": "single GPU"},
         "roofline": roofline(w, scan_ms, args.workload),
     }
+    if used != "decode":
+        line["compute_roofline"] = compute_roofline(w, scan_ms, used)
     if not args.no_also and args.workload == "decode":
         del p
         torch.cuda.empty_cache()
-        wp = workloads.varlen_prefill()
-        pp = Path(wp, torch, "auto")
-        pms, pscan_ms, pused, _ = time_path(pp, max(3, args.steps // 10), 2)
-        line["also"] = {"prefill": {"workload": wp.name, "N": wp.N, "path": pused,
-                                    "tokens_per_s": round(wp.N / (pms * 1e-3), 1), "ms_per_step": round(pms, 4),
-                                    "scan_ms": round(pscan_ms, 4),
-                                    "scan_tflops_fp32": round(7 * wp.K * wp.V * wp.H * wp.N / (pscan_ms * 1e-3) / 1e12, 2),
-                                    "roofline": roofline(wp, pscan_ms, "prefill")}}
-        del pp
+        line["also"] = {"prefill": secondary(torch, workloads.varlen_prefill(), max(3, args.steps // 10), 2),
+                        "long": secondary(torch, workloads.long_single(), 3, 1)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
