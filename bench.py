@@ -3,13 +3,16 @@
 A step is one pass of the whole path over one batch of seeded synthetic input, with inputs resident
 in HBM: the varlen causal conv1d (its window updated in place) followed by the gated delta-rule
 recurrence (state updated in place).  The default workload is the decode step (B=256 sequences x 1
-token, HQ=16, H=32, K=V=128, bf16, fp32 state), where the recurrence runs in one fused launch.
+token, HQ=16, H=32, K=V=128, bf16, fp32 state): gdn_conv1d_varlen then gdn_scan_varlen on its DECODE
+path (--fused-step runs the single-launch gdn_decode_step instead; "also" compares the two forms at
+several batch sizes).
 The prefill workload (B=8, lengths ~ U[512, 4096]) and the long single sequence (N=65536, H=16) are
 measured too and reported in "also", with the arithmetic roofline of the path they take.
 
-Prints ONE JSON line.  The dominant kernel (the recurrence) is timed with HIP events on the stream
-it is launched on; its algorithmic bytes per launch are the fp32 state read and written plus the
-token streams it must read (q, k, v, a, b) and write (out).
+Prints ONE JSON line.  The dominant kernel (the fused step, or the recurrence in the two-call form)
+is timed with HIP events on the stream it is launched on; its algorithmic bytes per launch are the
+fp32 state read and written, the token streams it must read (q, k, v, a, b) and write (out), and
+for the fused step also the carried conv window read and written and the conv weights.
 """
 from __future__ import annotations
 
@@ -28,6 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 SCAN_SOURCES = ["gated_delta_rule_varlen_amd/csrc/gdn_scan.hip", "gated_delta_rule_varlen_amd/csrc/gdn_device.hpp"]
+STEP_SOURCES = ["gated_delta_rule_varlen_amd/csrc/gdn_decode.hip", "gated_delta_rule_varlen_amd/csrc/gdn_device.hpp"]
 
 
 def sizeof(dt: str) -> int:
@@ -42,21 +46,30 @@ def scan_bytes(w) -> int:
     return state + tokens
 
 
-def src_digest() -> str:
+def step_bytes(w) -> int:
+    """Algorithmic HBM bytes of one fused decode step (gdn_decode_step): the recurrence's bytes with
+    the raw token rows in place of the conv output, plus the carried window read and written and the
+    conv weights and bias read once."""
+    window = 2 * w.B * w.C * w.L * sizeof(w.conv_state_dtype)
+    params = w.C * w.W * sizeof(w.io) + (w.C * sizeof(w.io) if w.conv_bias is not None else 0)
+    return scan_bytes(w) + window + params
+
+
+def src_digest(sources=SCAN_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in SCAN_SOURCES:
+    for p in sources:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(record: str, sources=SCAN_SOURCES):
     """HBM bytes per launch from committed rocprofv3 counter runs, only while the kernel source is
     unchanged since they were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{record}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("src_digest") != src_digest():
+    if rec.get("src_digest") != src_digest(sources):
         return None
     return rec.get("bytes_per_launch")
 
@@ -64,10 +77,10 @@ def measured_traffic(workload: str):
 class Path:
     """Device-resident inputs of one workload and one step of the hot path."""
 
-    def __init__(self, w, torch, path: str):
+    def __init__(self, w, torch, path: str, fused_step: bool = False):
         import gated_delta_rule_varlen_amd as gdn
 
-        self.gdn, self.torch, self.w, self.path = gdn, torch, w, path
+        self.gdn, self.torch, self.w, self.path, self.fused_step = gdn, torch, w, path, fused_step
         dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
         def dev(a, d):
@@ -94,6 +107,18 @@ class Path:
 
     def step(self, ev=None):
         w, gdn = self.w, self.gdn
+        if self.fused_step:
+            # conv and recurrence in one launch; window and state updated in place
+            if ev is not None:
+                ev[0].record()
+            gdn.decode_step(self.x, self.conv_w, self.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, bias=self.conv_b,
+                            conv_state_in=self.conv_state, conv_state_out=self.conv_state, dilation=w.D,
+                            silu=w.silu, a=self.a, b=self.b, A_log=self.A_log, dt_bias=self.dt_bias,
+                            state_in=self.state, state_out=self.state, l2norm=w.l2norm, softplus=w.softplus,
+                            sigmoid=w.sigmoid, out=self.out)
+            if ev is not None:
+                ev[1].record()
+            return "decode_step"
         gdn.conv1d_varlen(self.x, self.conv_w, self.offsets, bias=self.conv_b, state_in=self.conv_state,
                           dilation=w.D, silu=w.silu, y=self.y, state_out=self.conv_state)
         if ev is not None:
@@ -128,11 +153,13 @@ def time_path(p: "Path", steps: int, warmup: int):
     return total_ms / steps, scan_ms, used, wall
 
 
-def roofline(w, scan_ms: float, workload: str, kernel: str = "scan_kernel"):
-    achieved = scan_bytes(w) / (scan_ms * 1e-3) / 1e9
+def roofline(w, scan_ms: float, workload: str, kernel: str = "scan_kernel", fused_step: bool = False):
+    nbytes = step_bytes(w) if fused_step else scan_bytes(w)
+    traffic = measured_traffic(f"{workload}_step", STEP_SOURCES) if fused_step else measured_traffic(workload)
+    achieved = nbytes / (scan_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(workload),
-            "kernel": kernel, "algorithmic_bytes_per_launch": scan_bytes(w),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": kernel, "algorithmic_bytes_per_launch": nbytes,
             "avg_launch_us": round(scan_ms * 1e3, 2)}
 
 
@@ -166,6 +193,25 @@ def secondary(torch, wl, steps: int, warmup: int):
     del pp
     torch.cuda.empty_cache()
     return rec
+
+
+def fused_comparison(torch, batches=(1, 8, 256), steps: int = 100):
+    """Whole decode steps (HQ=16, H=32, K=V=128, bf16) as one gdn_decode_step launch and as two
+    launches, at several batch sizes: microseconds per step, launch cost included (best of 3)."""
+    import workloads
+
+    res = {}
+    for B in batches:
+        w = workloads.make(name=f"decode_b{B}", seed=102, lengths=[1] * B, HQ=16, H=32, K=128, V=128, W=4, D=1,
+                           io="bf16", conv_state_dtype="f32", conv_state_std=1.0, state_std=0.1)
+        rec = {}
+        for fused in (False, True):
+            p = Path(w, torch, "decode", fused_step=fused)
+            rec["fused_us" if fused else "two_call_us"] = round(min(time_path(p, steps, 10)[0] for _ in range(3)) * 1e3, 2)
+            del p
+        res[f"B{B}"] = rec
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
@@ -229,6 +275,9 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "seq", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="skip the secondary prefill measurement")
+    ap.add_argument("--fused-step", action="store_true",
+                    help="decode: run the step as one gdn_decode_step launch instead of gdn_conv1d_varlen + "
+                         "gdn_scan_varlen (faster for small batches, slower at B=256)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device-to-device copy (reference for HBM counters and achievable bandwidth)")
     args = ap.parse_args()
@@ -247,7 +296,10 @@ def main():
         print(json.dumps(copy_calibration(torch, args.steps, args.warmup)), flush=True)
         return
     w = workloads.NAMED[args.workload]()
-    p = Path(w, torch, args.path)
+    # a decode step (at most one token per sequence) can run as one fused launch
+    fused = (args.fused_step and args.workload == "decode" and args.path in ("auto", "decode")
+             and int(np.max(np.diff(w.offsets))) <= 1)
+    p = Path(w, torch, args.path, fused_step=fused)
     ms, scan_ms, used, _ = time_path(p, args.steps, args.warmup)
     tokens_per_s = w.N / (ms * 1e-3)
     line = {
@@ -265,15 +317,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "HQ": w.HQ, "H": w.H, "K": w.K, "V": w.V,
                    "conv_W": w.W, "conv_D": w.D, "path": used, "parallelism": "single GPU"},
-        "roofline": roofline(w, scan_ms, args.workload),
+        "roofline": roofline(w, scan_ms, args.workload, "decode_kernel (conv + recurrence)" if fused else "scan_kernel",
+                             fused_step=fused),
     }
-    if used != "decode":
+    if used not in ("decode", "decode_step"):
         line["compute_roofline"] = compute_roofline(w, scan_ms, used)
     if not args.no_also and args.workload == "decode":
         del p
         torch.cuda.empty_cache()
         line["also"] = {"prefill": secondary(torch, workloads.varlen_prefill(), max(3, args.steps // 10), 2),
-                        "long": secondary(torch, workloads.long_single(), 3, 1)}
+                        "long": secondary(torch, workloads.long_single(), 3, 1),
+                        "decode_step_fused_vs_two_call": fused_comparison(torch)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

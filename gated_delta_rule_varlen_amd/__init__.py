@@ -15,7 +15,8 @@ import torch
 from . import _abi
 from ._abi import GdnError, PATH_NAMES, lib  # noqa: F401
 
-__all__ = ["conv1d_varlen", "prepare_qk_gates", "scan_varlen", "scan_workspace_bytes", "GdnError", "lib"]
+__all__ = ["conv1d_varlen", "prepare_qk_gates", "scan_varlen", "scan_workspace_bytes", "decode_step", "GdnError",
+           "lib"]
 
 _DTYPE = {torch.float32: _abi.F32, torch.bfloat16: _abi.BF16, torch.float16: _abi.F16}
 _TORCH = {v: k for k, v in _DTYPE.items()}
@@ -135,3 +136,38 @@ def scan_varlen(qkv: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K:
                                _ptr(dev_status, "dev_status"), ctypes.byref(used), _stream(qkv.device))
     _check(st, "gdn_scan_varlen")
     return out, state_out, PATH_NAMES.get(used.value, str(used.value))
+
+
+def decode_step(x: torch.Tensor, weight: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K: int, V: int,
+                bias=None, conv_state_in=None, conv_state_out=None, dilation: int = 1, silu: bool = True,
+                conv_state_dtype=None, a=None, b=None, A_log=None, dt_bias=None, state_in=None, state_out=None,
+                l2norm=True, softplus=True, sigmoid=True, scale: float = 0.0, out=None, write_state: bool = True,
+                dev_status=None):
+    """A decode step in one launch (gdn_decode_step): conv1d_varlen over x followed by scan_varlen over
+    its output on the DECODE path, for at most one token per sequence.  Pass conv_state_out=conv_state_in
+    and state_out=state_in for in-place updates.  Returns (out [N, H, V], state_out, conv_state_out)."""
+    if weight.dim() == 3:
+        weight = weight.reshape(weight.shape[0], weight.shape[2])
+    N, C = x.shape
+    W = weight.shape[1]
+    B = offsets.numel() - 1
+    L = (W - 1) * dilation
+    if conv_state_dtype is None:
+        src = conv_state_in if conv_state_in is not None else conv_state_out
+        conv_state_dtype = src.dtype if src is not None else x.dtype
+    if out is None:
+        out = torch.empty((N, H, V), dtype=x.dtype, device=x.device)
+    if state_out is None and write_state:
+        state_out = torch.empty((B, H, V, K), dtype=torch.float32, device=x.device)
+    if conv_state_out is None and write_state and L > 0:
+        conv_state_out = torch.empty((B, C, L), dtype=conv_state_dtype, device=x.device)
+    cd = _abi.ConvDesc(B, N, C, W, dilation, _code(x, "x"), _DTYPE[conv_state_dtype], _abi.CONV_SILU if silu else 0)
+    sd = _scan_desc(x, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, "decode")
+    st = lib().gdn_decode_step(ctypes.byref(cd), ctypes.byref(sd), _ptr(x, "x"), _ptr(weight, "weight"),
+                               _ptr(bias, "bias"), _ptr(conv_state_in, "conv_state_in"),
+                               _ptr(conv_state_out, "conv_state_out"), _ptr(a, "a"), _ptr(b, "b"),
+                               _ptr(A_log, "A_log"), _ptr(dt_bias, "dt_bias"), _ptr(state_in, "state_in"),
+                               _ptr(out, "out"), _ptr(state_out, "state_out"), _ptr(offsets, "offsets"),
+                               _ptr(dev_status, "dev_status"), _stream(x.device))
+    _check(st, "gdn_decode_step")
+    return out, state_out, conv_state_out

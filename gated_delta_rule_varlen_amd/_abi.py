@@ -27,6 +27,7 @@ EXPORTS = (
     "gdn_prepare_qk_gates",
     "gdn_scan_varlen",
     "gdn_scan_workspace_bytes",
+    "gdn_decode_step",
     "gdn_status_string",
     "gdn_abi_version",
 )
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_prepare_qk_gates.restype = st
         L.gdn_scan_varlen.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 12 + [ctypes.c_size_t, vp, i32p, vp]
         L.gdn_scan_varlen.restype = st
+        L.gdn_decode_step.argtypes = [ctypes.POINTER(ConvDesc), ctypes.POINTER(ScanDesc)] + [vp] * 15
+        L.gdn_decode_step.restype = st
         L.gdn_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(ctypes.c_size_t)]
         L.gdn_scan_workspace_bytes.restype = st
         L.gdn_status_string.argtypes = [ctypes.c_int]

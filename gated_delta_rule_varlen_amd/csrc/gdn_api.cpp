@@ -214,4 +214,63 @@ gdn_status gdn_scan_varlen(const gdn_scan_desc* d, const void* qkv, const float*
     return rs;
 }
 
+gdn_status gdn_decode_step(const gdn_conv_desc* cd, const gdn_scan_desc* sd, const void* x, const void* conv_w,
+                           const void* conv_bias, const void* conv_state_in, void* conv_state_out, const void* a,
+                           const void* b, const float* A_log, const float* dt_bias, const float* state_in, void* out,
+                           float* state_out, const int32_t* offsets, int32_t* dev_status, hipStream_t stream) {
+    if (cd == nullptr || conv_w == nullptr || offsets == nullptr) return GDN_ERR_NULL;
+    const gdn_status st = check_scan_desc(sd);
+    if (st != GDN_OK) return st;
+    // the conv descriptor as gdn_conv1d_varlen checks it, and agreement with the scan descriptor
+    if (cd->B < 1 || cd->N < 0 || cd->C < 1 || cd->W < 1 || cd->D < 1) return GDN_ERR_SHAPE;
+    if (!dtype_ok(cd->x_dtype)) return GDN_ERR_DTYPE;
+    if (cd->state_dtype != cd->x_dtype && cd->state_dtype != GDN_F32) return GDN_ERR_DTYPE;
+    if (cd->flags & ~(uint32_t)GDN_CONV_SILU) return GDN_ERR_UNSUPPORTED;
+    if (cd->W > 8 || (long long)(cd->W - 1) * cd->D > INT_MAX) return GDN_ERR_UNSUPPORTED;
+    if (cd->B != sd->B || cd->N != sd->N || (long long)cd->C != 2ll * sd->HQ * sd->K + (long long)sd->H * sd->V)
+        return GDN_ERR_SHAPE;
+    if (cd->x_dtype != sd->qkv_dtype) return GDN_ERR_DTYPE;
+    // a decode step: at most one token per sequence (so N <= B; the device checks each length),
+    // the recurrence on its DECODE path with fused inputs
+    if (sd->N > sd->B) return GDN_ERR_UNSUPPORTED;
+    if (sd->path != GDN_PATH_AUTO && sd->path != GDN_PATH_DECODE) return GDN_ERR_UNSUPPORTED;
+    if (!gdn::decode_step_supported(sd->K, sd->V, sd->H / sd->HQ, cd->W, cd->D)) return GDN_ERR_UNSUPPORTED;
+    if (sd->N > 0 && (x == nullptr || out == nullptr)) return GDN_ERR_NULL;
+    if (a != nullptr && (sd->flags & GDN_SOFTPLUS) && (A_log == nullptr || dt_bias == nullptr)) return GDN_ERR_NULL;
+    if (misaligned(x) || misaligned(conv_w) || misaligned(conv_bias) || misaligned(conv_state_in) ||
+        misaligned(conv_state_out) || misaligned(state_in) || misaligned(out) || misaligned(state_out))
+        return GDN_ERR_ALIGN;
+    const bool has_window = cd->W > 1;
+    gdn::DecodeStepLaunch l;
+    l.x = x;
+    l.conv_w = conv_w;
+    l.conv_bias = conv_bias;
+    l.conv_state_in = has_window ? conv_state_in : nullptr;
+    l.conv_state_out = has_window ? conv_state_out : nullptr;
+    l.a = a;
+    l.b = b;
+    l.A_log = A_log;
+    l.dt_bias = dt_bias;
+    l.state_in = state_in;
+    l.out = out;
+    l.state_out = state_out;
+    l.offsets = offsets;
+    l.dev_status = dev_status;
+    l.B = sd->B;
+    l.N = sd->N;
+    l.HQ = sd->HQ;
+    l.H = sd->H;
+    l.K = sd->K;
+    l.V = sd->V;
+    l.W = cd->W;
+    l.D = cd->D;
+    l.qkv_dtype = sd->qkv_dtype;
+    l.state_dtype = cd->state_dtype;
+    l.gate_dtype = sd->gate_dtype;
+    l.flags = sd->flags;
+    l.silu = (cd->flags & GDN_CONV_SILU) != 0;
+    l.scale = (sd->scale > 0.0f && std::isfinite(sd->scale)) ? sd->scale : 1.0f / std::sqrt((float)sd->K);
+    return from_hip(gdn::launch_decode_step(l, stream));
+}
+
 }  // extern "C"

@@ -64,6 +64,30 @@ hipError_t launch_scan_decode(const ScanLaunch& a, hipStream_t stream);  // DECO
 hipError_t launch_scan_seq(const ScanLaunch& a, hipStream_t stream);     // SEQ
 hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream);    // CHUNK
 size_t chunked_workspace_bytes(int B, int N, int HQ, int H, int K, int V);
+
+struct DecodeStepLaunch {
+    const void* x;
+    const void* conv_w;
+    const void* conv_bias;
+    const void* conv_state_in;
+    void* conv_state_out;
+    const void* a;
+    const void* b;
+    const float* A_log;
+    const float* dt_bias;
+    const float* state_in;
+    void* out;
+    float* state_out;
+    const int32_t* offsets;
+    int32_t* dev_status;
+    int B, N, HQ, H, K, V, W, D;
+    int qkv_dtype, state_dtype, gate_dtype;
+    uint32_t flags;
+    bool silu;
+    float scale;  // already resolved (> 0)
+};
+hipError_t launch_decode_step(const DecodeStepLaunch& a, hipStream_t stream);
+bool decode_step_supported(int K, int V, int G, int W, int D);
 bool chunked_shape_supported(int K, int V, int qkv_dtype);
 
 // Limits of the launch grids (checked by the entry points before launching).

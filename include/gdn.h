@@ -6,6 +6,8 @@
  *                         (W-1)*D window per (sequence, channel)
  *   gdn_prepare_qk_gates  per-token q/k L2 normalisation plus the decay and update-rate gates
  *   gdn_scan_varlen       the gated delta-rule recurrence with a per-(sequence, head) state
+ * and one fusion of them for decode steps (at most one token per sequence):
+ *   gdn_decode_step       gdn_conv1d_varlen then gdn_scan_varlen in a single launch
  *
  * Sources (docs.rs source pages): "onnxruntime-ep-mlx 0.31.1 src/ops/paged_ssm.rs" -- kernel strings
  * CONV, DELTA_PREPARE and DELTA, host functions conv(), delta() and the claim predicates; and
@@ -40,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -178,6 +180,30 @@ gdn_status gdn_scan_varlen(const gdn_scan_desc *desc, const void *qkv, const flo
                            const float *state_in, void *out, float *state_out, const int32_t *offsets,
                            void *workspace, size_t ws_bytes, int32_t *dev_status, int32_t *path_used,
                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * gdn_decode_step -- a decode step in one launch: exactly gdn_conv1d_varlen(conv, x -> y) followed
+ * by gdn_scan_varlen(scan, y, fused mode, DECODE path), with bit-identical outputs, new window and
+ * final state, for calls where every sequence holds at most one token.  y is not materialised.
+ * (paged_ssm.rs page, kernel strings CONV and DELTA; the gated_delta_rate_activation.rs page names
+ * launches per decode step as this layer's cost.)
+ *
+ * Tensors are those of the two calls it replaces, with the same layouts, dtypes and NULL rules:
+ *   x [N, C], conv_w [C, W], conv_bias [C] (NULL = none), conv_state_in / conv_state_out
+ *   [B, C, L] (window; NULL in = zeros, NULL out = not produced, may alias), a, b [N, H],
+ *   A_log, dt_bias [H], state_in / state_out [B, H, V, K] fp32 (may alias), out [N, H, V].
+ * The descriptors must agree: conv->B == scan->B, conv->N == scan->N,
+ * conv->C == 2*HQ*K + H*V, conv->x_dtype == scan->qkv_dtype (GDN_ERR_SHAPE / GDN_ERR_DTYPE);
+ * scan->path is GDN_PATH_AUTO or GDN_PATH_DECODE.  Built for K in {32, 64, 128, 256},
+ * V % 4 == 0, (W-1)*D <= 4 and (2K + (H/HQ)*V) * 4 <= 65536 bytes; N > B is rejected
+ * (GDN_ERR_UNSUPPORTED).  On the device, malformed offsets give *dev_status = GDN_ERR_OFFSETS
+ * and a sequence with more than one token gives GDN_ERR_UNSUPPORTED; in both cases nothing is
+ * written.
+ * ---------------------------------------------------------------------------------------------- */
+gdn_status gdn_decode_step(const gdn_conv_desc *conv, const gdn_scan_desc *scan, const void *x, const void *conv_w,
+                           const void *conv_bias, const void *conv_state_in, void *conv_state_out, const void *a,
+                           const void *b, const float *A_log, const float *dt_bias, const float *state_in, void *out,
+                           float *state_out, const int32_t *offsets, int32_t *dev_status, hipStream_t stream);
 
 /* Workspace bytes gdn_scan_varlen needs for `desc` (with its path resolved as AUTO would);
  * 0 when the resolved path needs none.  Returns the same argument errors as gdn_scan_varlen. */

@@ -32,7 +32,7 @@ def test_header_declarations_are_all_exported(abi):
 
 
 def test_version_and_status_strings(abi):
-    assert abi.lib().gdn_abi_version() == 1
+    assert abi.lib().gdn_abi_version() == 2
     for code in range(0, -10, -1):
         assert abi.status_string(code) and abi.status_string(code) != "unknown status"
     assert abi.status_string(-99) == "unknown status"
@@ -110,6 +110,52 @@ def scan(abi, d, qkv=P, qk=None, gb=None, a=None, b=None, alog=None, dtb=None, s
 )
 def test_scan_host_validation(abi, fields, kw, want):
     assert scan(abi, scan_desc(abi, **fields), **kw) == getattr(abi, want)
+
+
+def decode_step(abi, cfields=None, sfields=None, x=P, w=P, out=P, off=P, a=None, alog=None, dtb=None, sin=None,
+                sout=None, csin=None, csout=None):
+    cbase = dict(B=4, N=4, C=192, W=4, D=1, x_dtype=0, state_dtype=0, flags=1)
+    cbase.update(cfields or {})
+    sbase = dict(B=4, N=4, HQ=2, H=2, K=32, V=32, qkv_dtype=0, gate_dtype=0, flags=7, scale=0.0, path=0)
+    sbase.update(sfields or {})
+    cd, sd = abi.ConvDesc(**cbase), abi.ScanDesc(**sbase)
+    return abi.lib().gdn_decode_step(ctypes.byref(cd), ctypes.byref(sd), x, w, None, csin, csout, a, None, alog, dtb,
+                                     sin, out, sout, off, None, None)
+
+
+@pytest.mark.parametrize(
+    "cf,sf,kw,want",
+    [
+        (dict(C=200), {}, {}, "ERR_SHAPE"),  # conv width != 2*HQ*K + H*V
+        (dict(B=3), {}, {}, "ERR_SHAPE"),  # descriptors disagree
+        (dict(N=3), {}, {}, "ERR_SHAPE"),
+        (dict(x_dtype=1, state_dtype=1), {}, {}, "ERR_DTYPE"),  # conv and scan dtypes differ
+        (dict(N=5), dict(N=5), {}, "ERR_UNSUPPORTED"),  # more tokens than sequences: not a decode step
+        ({}, dict(path=2), {}, "ERR_UNSUPPORTED"),  # SEQ requested
+        (dict(W=6), {}, {}, "ERR_UNSUPPORTED"),  # (W-1)*D > 4
+        (dict(W=3, D=3), {}, {}, "ERR_UNSUPPORTED"),
+        (dict(W=9), {}, {}, "ERR_UNSUPPORTED"),
+        (dict(flags=4), {}, {}, "ERR_UNSUPPORTED"),
+        (dict(C=4 * 32 + 2 * 30), dict(V=30), {}, "ERR_UNSUPPORTED"),  # V % 4 != 0
+        ({}, dict(K=48), {}, "ERR_UNSUPPORTED"),
+        ({}, dict(HQ=3), {}, "ERR_SHAPE"),
+        ({}, {}, dict(w=None), "ERR_NULL"),
+        ({}, {}, dict(off=None), "ERR_NULL"),
+        ({}, {}, dict(x=None), "ERR_NULL"),
+        ({}, {}, dict(out=None), "ERR_NULL"),
+        ({}, {}, dict(a=P), "ERR_NULL"),  # softplus needs A_log and dt_bias
+        ({}, {}, dict(x=P + 2), "ERR_ALIGN"),
+        ({}, {}, dict(csin=P + 4), "ERR_ALIGN"),
+        ({}, {}, dict(sout=P + 8), "ERR_ALIGN"),
+    ],
+)
+def test_decode_step_host_validation(abi, cf, sf, kw, want):
+    assert decode_step(abi, cf, sf, **kw) == getattr(abi, want)
+
+
+def test_decode_step_rejects_missing_descriptor(abi):
+    sd = scan_desc(abi)
+    assert abi.lib().gdn_decode_step(None, ctypes.byref(sd), *([P] * 2), *([None] * 13)) == abi.ERR_NULL
 
 
 def test_prepare_host_validation(abi):
