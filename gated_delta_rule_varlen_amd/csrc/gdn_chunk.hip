@@ -389,7 +389,10 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
     __syncthreads();  // Y gathered: A may overwrite it
 
     // Row block wv: A_ij = b_i e^{G_i - G_j} (khat_i . khat_j) for j < i, and
-    // P_ij = e^{G_i - G_j} (qhat_i . khat_j) for j <= i (computed transposed: 4 consecutive j per lane)
+    // P_ij = e^{G_i - G_j} (qhat_i . khat_j) for j <= i (computed transposed: 4 consecutive j per lane).
+    // The tile loop stays rolled: the X and Y fragments are live across it, and unrolled it needs
+    // more registers than three blocks per compute unit leave.
+#pragma unroll 1
     for (int jt = 0; jt < 4; ++jt) {
         f32x4 a = zero4(), pt = zero4();
         if (jt <= wv) {
