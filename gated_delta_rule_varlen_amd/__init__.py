@@ -75,8 +75,9 @@ def conv1d_varlen(x: torch.Tensor, weight: torch.Tensor, offsets: torch.Tensor, 
     return y, state_out
 
 
-def _scan_desc(qkv, B, HQ, H, K, V, gate, l2norm, softplus, sigmoid, scale, path):
+def _scan_desc(qkv, B, HQ, H, K, V, gate, l2norm, softplus, sigmoid, scale, path, retrieve=True):
     flags = (_abi.L2NORM if l2norm else 0) | (_abi.SOFTPLUS if softplus else 0) | (_abi.SIGMOID if sigmoid else 0)
+    flags |= 0 if retrieve else _abi.NO_RETRIEVE
     qd = _code(qkv, "qkv")
     gd = _code(gate, "gate inputs") if gate is not None else qd
     return _abi.ScanDesc(B, qkv.shape[0], HQ, H, K, V, qd, gd, flags, float(scale), _abi.PATH_CODES[path])
@@ -112,8 +113,9 @@ def scan_workspace_bytes(qkv: torch.Tensor, B: int, *, HQ, H, K, V, l2norm=True,
 def scan_varlen(qkv: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K: int, V: int, a=None, b=None,
                 A_log=None, dt_bias=None, state_in=None, qk_prep=None, gb_prep=None, l2norm=True, softplus=True,
                 sigmoid=True, scale: float = 0.0, path: str = "auto", out=None, state_out=None,
-                write_state: bool = True, workspace=None, dev_status=None):
-    """Gated delta-rule recurrence over offset-packed sequences (gdn_scan_varlen).
+                write_state: bool = True, workspace=None, dev_status=None, retrieve: bool = True):
+    """Gated delta-rule recurrence over offset-packed sequences (gdn_scan_varlen).  retrieve=False
+    selects the linear/gated update rules (no retrieval term).
     Returns (out [N, H, V], state_out [B, H, V, K] fp32 or None, path name that ran)."""
     N = qkv.shape[0]
     B = offsets.numel() - 1
@@ -121,7 +123,7 @@ def scan_varlen(qkv: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K:
         out = torch.empty((N, H, V), dtype=qkv.dtype, device=qkv.device)
     if state_out is None and write_state:
         state_out = torch.empty((B, H, V, K), dtype=torch.float32, device=qkv.device)
-    d = _scan_desc(qkv, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, path)
+    d = _scan_desc(qkv, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, path, retrieve)
     if workspace is None and path in ("auto", "chunk"):
         n = ctypes.c_size_t(0)
         _check(lib().gdn_scan_workspace_bytes(ctypes.byref(d), ctypes.byref(n)), "gdn_scan_workspace_bytes")
@@ -142,7 +144,7 @@ def decode_step(x: torch.Tensor, weight: torch.Tensor, offsets: torch.Tensor, *,
                 bias=None, conv_state_in=None, conv_state_out=None, dilation: int = 1, silu: bool = True,
                 conv_state_dtype=None, a=None, b=None, A_log=None, dt_bias=None, state_in=None, state_out=None,
                 l2norm=True, softplus=True, sigmoid=True, scale: float = 0.0, out=None, write_state: bool = True,
-                dev_status=None):
+                dev_status=None, retrieve: bool = True):
     """A decode step in one launch (gdn_decode_step): conv1d_varlen over x followed by scan_varlen over
     its output on the DECODE path, for at most one token per sequence.  Pass conv_state_out=conv_state_in
     and state_out=state_in for in-place updates.  Returns (out [N, H, V], state_out, conv_state_out)."""
@@ -162,7 +164,8 @@ def decode_step(x: torch.Tensor, weight: torch.Tensor, offsets: torch.Tensor, *,
     if conv_state_out is None and write_state and L > 0:
         conv_state_out = torch.empty((B, C, L), dtype=conv_state_dtype, device=x.device)
     cd = _abi.ConvDesc(B, N, C, W, dilation, _code(x, "x"), _DTYPE[conv_state_dtype], _abi.CONV_SILU if silu else 0)
-    sd = _scan_desc(x, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, "decode")
+    sd = _scan_desc(x, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, "decode",
+                    retrieve)
     st = lib().gdn_decode_step(ctypes.byref(cd), ctypes.byref(sd), _ptr(x, "x"), _ptr(weight, "weight"),
                                _ptr(bias, "bias"), _ptr(conv_state_in, "conv_state_in"),
                                _ptr(conv_state_out, "conv_state_out"), _ptr(a, "a"), _ptr(b, "b"),

@@ -32,7 +32,7 @@ gdn_status check_scan_desc(const gdn_scan_desc* d) {
     if (d->H % d->HQ != 0 || d->K > 256) return GDN_ERR_SHAPE;
     if (!dtype_ok(d->qkv_dtype)) return GDN_ERR_DTYPE;
     if (d->gate_dtype != GDN_F32 && d->gate_dtype != d->qkv_dtype) return GDN_ERR_DTYPE;
-    if (d->flags & ~(uint32_t)(GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID)) return GDN_ERR_UNSUPPORTED;
+    if (d->flags & ~(uint32_t)(GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID | GDN_NO_RETRIEVE)) return GDN_ERR_UNSUPPORTED;
     const long long C = 2ll * d->HQ * d->K + (long long)d->H * d->V;
     if (C > INT_MAX) return GDN_ERR_OVERFLOW;
     if ((long long)d->B * d->H > INT_MAX) return GDN_ERR_OVERFLOW;
@@ -44,11 +44,12 @@ gdn_status check_scan_desc(const gdn_scan_desc* d) {
 
 // The chunked path sums log-decays, so it needs every decay finite and positive (a decay input with
 // the softplus gate), and it relies on normalised keys for a well-conditioned (I + A); it computes
-// the gates and norms itself, so it runs on fused inputs only.  Built for bf16/fp16 I/O with
+// the gates and norms itself, so it runs on fused inputs only; its algebra is that of the rules
+// with the retrieval term.  Built for bf16/fp16 I/O with
 // K = V = 64 or 128.
 bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay) {
     return !prepared && has_decay && (d->flags & GDN_SOFTPLUS) && (d->flags & GDN_L2NORM) &&
-           gdn::chunked_shape_supported(d->K, d->V, d->qkv_dtype);
+           !(d->flags & GDN_NO_RETRIEVE) && gdn::chunked_shape_supported(d->K, d->V, d->qkv_dtype);
 }
 
 // AUTO: DECODE for at most two tokens per sequence on average; CHUNK when eligible, the average

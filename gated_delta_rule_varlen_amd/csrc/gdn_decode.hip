@@ -216,6 +216,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(DecodeArgs p) {
     }
     const float oscale = p.scale * rq;
     const bool softplus = (p.flags & GDN_SOFTPLUS) != 0;
+    const float rmul = (p.flags & GDN_NO_RETRIEVE) ? 0.0f : 1.0f;  // the retrieval term's weight
 
     auto run_tile = [&](int tl, const f32x4 (&st)[CPL][EPL / 4]) {
         const int gc0 = tl * WC + grp * CPL;
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(DecodeArgs p) {
             }
             pk = group_sum<LPC>(pk);
             pq = group_sum<LPC>(pq);
-            const float r = g * rk * pk;
+            const float r = rmul * (g * rk * pk);
             const float dk = beta * (yv[gc0 + c] - r) * rk;
             const float o = oscale * fmaf(g, pq, dk * qk);
             if (so != nullptr) {

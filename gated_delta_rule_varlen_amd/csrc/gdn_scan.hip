@@ -157,6 +157,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
     const bool l2 = (p.flags & GDN_L2NORM) != 0;
     const bool softplus = (p.flags & GDN_SOFTPLUS) != 0;
     const bool sigmoid = (p.flags & GDN_SIGMOID) != 0;
+    const float rmul = (p.flags & GDN_NO_RETRIEVE) ? 0.0f : 1.0f;  // the retrieval term's weight
     const float a_mul = (!PREP && p.a && softplus) ? -expf(p.A_log[h]) : 0.0f;
     const float a_bias = (!PREP && p.a && softplus) ? p.dt_bias[h] : 0.0f;
     TS* outp = static_cast<TS*>(p.out);
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                     }
                 pk = group_sum<LPC>(pk);
                 pq = group_sum<LPC>(pq);
-                const float r = g * rk * pk;
+                const float r = rmul * (g * rk * pk);
                 const float dk = beta * (tok.v[c] - r) * rk;
                 const float o = oscale * fmaf(g, pq, dk * qk);
                 float* sp = p.state_out + (col0 + vbase + c) * K;
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
         float mine = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            const float r = g * rk * pk[c];
+            const float r = rmul * (g * rk * pk[c]);
             const float dk = beta * (cur.v[c] - r) * rk;  // delta * rk: coefficient of the raw k
             const float o = oscale * fmaf(g, pq[c], dk * qk);
 #pragma unroll

@@ -124,6 +124,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     const bool l2 = (p.flags & GDN_L2NORM) != 0;
     const bool softplus = (p.flags & GDN_SOFTPLUS) != 0;
     const bool sigmoid = (p.flags & GDN_SIGMOID) != 0;
+    const float rmul = (p.flags & GDN_NO_RETRIEVE) ? 0.0f : 1.0f;  // the retrieval term's weight
     const float a_mul = (!PREP && p.a && softplus) ? -expf(p.A_log[h]) : 0.0f;
     const float a_bias = (!PREP && p.a && softplus) ? p.dt_bias[h] : 0.0f;
     const TS* qkv = static_cast<const TS*>(p.qkv);
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
                 float mine = 0.0f;
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) {
-                    const float d = beta * (sv[buf][i][cw + cc] - g * pk[cc]);
+                    const float d = beta * (sv[buf][i][cw + cc] - rmul * (g * pk[cc]));
                     const float o = p.scale * fmaf(g, pq[cc], d * qk);
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) s[cc][e] = fmaf(d, k[e], g * s[cc][e]);

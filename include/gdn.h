@@ -107,6 +107,10 @@ gdn_status gdn_conv1d_varlen(const gdn_conv_desc *desc, const void *x, const voi
  *   GDN_SOFTPLUS  decay g = exp(-exp(A_log[h]) * softplus(a + dt_bias[h])); without it a is a raw
  *                 log-decay and g = exp(a).  softplus(x) = max(x,0) + log1p(exp(-|x|)).
  *   GDN_SIGMOID   update rate beta = 1/(1+exp(-b)); without it beta = b.
+ *   GDN_NO_RETRIEVE  the write is delta = beta*v_t, without the retrieval term k^.s: the "linear"
+ *                 (no decay input) and "gated" update rules of the pages' update_rule attribute,
+ *                 where the DELTA kernel string is compiled with RETRIEVE = 0.  Without this flag
+ *                 the rule is "delta" (no decay input) or "gated_delta".
  * A NULL decay input a means g = 1; a NULL rate input b means beta = 1.  Gate arithmetic is fp32
  * (gate inputs are widened to fp32 first).  scale <= 0 selects 1/sqrt(K).
  * Constraints: B >= 1, N >= 0, HQ >= 1, H >= 1, H % HQ == 0, 1 <= K <= 256 (the pages' limit),
@@ -116,6 +120,7 @@ gdn_status gdn_conv1d_varlen(const gdn_conv_desc *desc, const void *x, const voi
 #define GDN_L2NORM 1u
 #define GDN_SOFTPLUS 2u
 #define GDN_SIGMOID 4u
+#define GDN_NO_RETRIEVE 8u
 
 typedef enum gdn_path {
     GDN_PATH_AUTO = 0,   /* DECODE when N <= 2*B; else CHUNK when eligible, N >= 64*B and ws_bytes suffices; else SEQ */
@@ -128,7 +133,7 @@ typedef struct gdn_scan_desc {
     int32_t B, N, HQ, H, K, V;
     int32_t qkv_dtype;  /* gdn_dtype of qkv and out */
     int32_t gate_dtype; /* gdn_dtype of a and b: GDN_F32 or qkv_dtype */
-    uint32_t flags;     /* GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID */
+    uint32_t flags;     /* GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID | GDN_NO_RETRIEVE */
     float scale;        /* output scale; <= 0 selects 1/sqrt(K) */
     int32_t path;       /* gdn_path */
 } gdn_scan_desc;
@@ -152,6 +157,7 @@ gdn_status gdn_prepare_qk_gates(const gdn_scan_desc *desc, const void *qkv, cons
  * delta() selects).  For each sequence b, value head h, value column v, with s = state_in[b,h,v,:]
  * (a K-vector; zeros when state_in is NULL), over the sequence's tokens t in order:
  *     s <- g*s;  r = k^.s;  delta = beta*(v_t - r);  s <- s + delta*k^;  out[t,h,v] = scale*(q^.s)
+ * (r = 0 with GDN_NO_RETRIEVE)
  * then state_out[b,h,v,:] = s.  q^, k^, g, beta are either computed in-kernel from qkv, a, b,
  * A_log, dt_bias and the flags ("fused"), or read from a prior gdn_prepare_qk_gates call when both
  * qk_prep and gb_prep are given ("prepared"; then a, b, A_log, dt_bias and the flags are unused).
@@ -171,7 +177,8 @@ gdn_status gdn_prepare_qk_gates(const gdn_scan_desc *desc, const void *qkv, cons
  *              with gdn_scan_workspace_bytes); may be NULL otherwise
  *   dev_status [1] int32 (NULL ok); path_used: HOST int32 receiving the gdn_path that ran (NULL ok)
  * GDN_PATH_CHUNK requires fused mode with a decay input and GDN_SOFTPLUS (so every decay is
- * finite and positive), GDN_L2NORM, bf16 or fp16 qkv, and K = V = 64 or K = V = 128; otherwise
+ * finite and positive), GDN_L2NORM, the retrieval term (no GDN_NO_RETRIEVE), bf16 or fp16 qkv, and
+ * K = V = 64 or K = V = 128; otherwise
  * GDN_ERR_UNSUPPORTED.  Its intra-chunk contractions run on bf16 matrix cores with fp32
  * accumulation (the state itself stays fp32).
  * ---------------------------------------------------------------------------------------------- */

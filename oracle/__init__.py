@@ -51,7 +51,7 @@ def lib():
             L.gdn_oracle_conv.restype = i32
             L.gdn_oracle_prepare.argtypes = [i32] * 10 + [vp] * 7
             L.gdn_oracle_prepare.restype = None
-            L.gdn_oracle_scan.argtypes = [i32] * 11 + [ctypes.c_double] + [vp] * 9
+            L.gdn_oracle_scan.argtypes = [i32] * 12 + [ctypes.c_double] + [vp] * 9
             L.gdn_oracle_scan.restype = i32
             L.gdn_oracle_threads.argtypes = []
             L.gdn_oracle_threads.restype = i32
@@ -132,9 +132,10 @@ def prepare(qkv, *, HQ, H, K, V, qkv_dtype, gate_dtype=None, a=None, b=None, A_l
 
 
 def scan(qkv, offsets, *, HQ, H, K, V, qkv_dtype, gate_dtype=None, a=None, b=None, A_log=None,
-         dt_bias=None, state_in=None, l2norm=True, softplus=True, sigmoid=True, scale=0.0):
-    """Gated delta-rule recurrence.  Returns (out [N,H,V] f64, state_out [B,H,V,K] f64) or None
-    when the offsets are malformed."""
+         dt_bias=None, state_in=None, l2norm=True, softplus=True, sigmoid=True, scale=0.0, retrieve=True):
+    """Gated delta-rule recurrence.  retrieve=False drops the retrieval term (the linear and gated
+    update rules).  Returns (out [N,H,V] f64, state_out [B,H,V,K] f64) or None when the offsets are
+    malformed."""
     qd = DTYPE_CODES[qkv_dtype]
     gd = DTYPE_CODES[gate_dtype or qkv_dtype]
     qkv = _raw(qkv, qd)
@@ -150,7 +151,8 @@ def scan(qkv, offsets, *, HQ, H, K, V, qkv_dtype, gate_dtype=None, a=None, b=Non
     out = np.zeros((N, H, V), np.float64)
     st = np.zeros((B, H, V, K), np.float64)
     rc = lib().gdn_oracle_scan(B, N, HQ, H, K, V, qd, gd, int(bool(l2norm)), int(bool(softplus)),
-                               int(bool(sigmoid)), float(scale), _ptr(qkv), _ptr(a), _ptr(b), _ptr(A_log),
+                               int(bool(sigmoid)), int(bool(retrieve)), float(scale), _ptr(qkv), _ptr(a), _ptr(b),
+                               _ptr(A_log),
                                _ptr(dt_bias), _ptr(state_in), _ptr(off), _ptr(out), _ptr(st))
     if rc == 1:
         return None

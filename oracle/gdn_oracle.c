@@ -212,12 +212,15 @@ void gdn_oracle_prepare(int N, int HQ, int H, int K, int V, int qkv_dtype, int g
  *     s <- s + delta * k^
  *     out[t,h,v] = scale * (q^ . s)
  * with q^, k^, g, beta as produced by gdn_oracle_prepare.  The final s is state_out[b,h,v,:].
+ * retrieve == 0 drops the retrieval term (delta = beta * v_t): the "linear" and "gated" update rules
+ * of the pages' update_rule attribute, which the DELTA kernel string compiles with RETRIEVE = 0
+ * (the rule's decay side is the presence of the decay input, as for the other rules).
  * scale <= 0 selects 1/sqrt(K) (host fn delta(): a zero scale attribute means 1/sqrt(K)).
  * Layouts: qkv [N, 2*HQ*K + H*V]; out [N,H,V]; state [B,H,V,K] float32 in, fp64 out.
  * Returns 0 on success, 1 when the offsets are malformed (then nothing is written), 2 when out of
  * memory.  Parallel over independent (b, h) pairs with OpenMP when built with it. */
 int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, int gate_dtype,
-                    int l2norm, int softplus, int sigmoid, double scale, const void *qkv,
+                    int l2norm, int softplus, int sigmoid, int retrieve, double scale, const void *qkv,
                     const void *a, const void *b, const float *A_log, const float *dt_bias,
                     const float *state_in, const int32_t *offsets, double *out, double *state_out) {
     if (!gdn_oracle_offsets_valid(offsets, B, N)) return 1;
@@ -257,7 +260,8 @@ int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, in
                 const double vt = dec(qkv, qkv_dtype, (size_t)t * C + (size_t)2 * HQ * K + (size_t)h * V + v);
                 for (int i = 0; i < K; ++i) s[i] *= g;
                 double r = 0.0;
-                for (int i = 0; i < K; ++i) r += kk[i] * s[i];
+                if (retrieve)
+                    for (int i = 0; i < K; ++i) r += kk[i] * s[i];
                 const double delta = beta * (vt - r);
                 for (int i = 0; i < K; ++i) s[i] += delta * kk[i];
                 double o = 0.0;

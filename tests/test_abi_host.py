@@ -94,8 +94,10 @@ def scan(abi, d, qkv=P, qk=None, gb=None, a=None, b=None, alog=None, dtb=None, s
         (dict(V=0), {}, "ERR_SHAPE"),
         (dict(qkv_dtype=5), {}, "ERR_DTYPE"),
         (dict(qkv_dtype=1, gate_dtype=2), {}, "ERR_DTYPE"),
-        (dict(flags=8), {}, "ERR_UNSUPPORTED"),
+        (dict(flags=16), {}, "ERR_UNSUPPORTED"),
         (dict(path=9), {}, "ERR_UNSUPPORTED"),
+        # the chunked form needs the retrieval term: shape and dtype eligible, GDN_NO_RETRIEVE set
+        (dict(qkv_dtype=1, gate_dtype=1, K=64, V=64, flags=7 | 8, path=3), dict(a=P, alog=P, dtb=P), "ERR_UNSUPPORTED"),
         (dict(path=3), {}, "ERR_UNSUPPORTED"),  # chunked path not eligible here
         (dict(qkv_dtype=1, gate_dtype=1, V=33, H=2), {}, "ERR_ALIGN"),  # token row not a multiple of 16 bytes
         (dict(HQ=2**22, H=2**22, K=256, V=1), {}, "ERR_OVERFLOW"),
