@@ -49,9 +49,11 @@ def lib():
             L.gdn_oracle_decode.restype = ctypes.c_double
             L.gdn_oracle_conv.argtypes = [i32] * 8 + [vp] * 7
             L.gdn_oracle_conv.restype = i32
+            L.gdn_oracle_conv_capture.argtypes = [i32] * 5 + [vp] * 4
+            L.gdn_oracle_conv_capture.restype = i32
             L.gdn_oracle_prepare.argtypes = [i32] * 10 + [vp] * 7
             L.gdn_oracle_prepare.restype = None
-            L.gdn_oracle_scan.argtypes = [i32] * 12 + [ctypes.c_double] + [vp] * 9
+            L.gdn_oracle_scan.argtypes = [i32] * 12 + [ctypes.c_double] + [vp] * 11 + [i32, vp]
             L.gdn_oracle_scan.restype = i32
             L.gdn_oracle_threads.argtypes = []
             L.gdn_oracle_threads.restype = i32
@@ -131,11 +133,26 @@ def prepare(qkv, *, HQ, H, K, V, qkv_dtype, gate_dtype=None, a=None, b=None, A_l
     return qk, gb
 
 
+def conv_capture(x, offsets, counts, *, cap, x_dtype):
+    """Recorded conv inputs for speculative decoding: updates [B, cap, C] f64 (see the C source),
+    or None when the offsets are malformed."""
+    xd = DTYPE_CODES[x_dtype]
+    x = _raw(x, xd)
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    cnt = np.ascontiguousarray(counts, dtype=np.int32)
+    N, C = x.shape
+    B = off.size - 1
+    upd = np.zeros((B, cap, C), np.float64)
+    rc = lib().gdn_oracle_conv_capture(B, N, C, cap, xd, _ptr(x), _ptr(off), _ptr(cnt), _ptr(upd))
+    return None if rc == 1 else upd
+
+
 def scan(qkv, offsets, *, HQ, H, K, V, qkv_dtype, gate_dtype=None, a=None, b=None, A_log=None,
-         dt_bias=None, state_in=None, l2norm=True, softplus=True, sigmoid=True, scale=0.0, retrieve=True):
+         dt_bias=None, state_in=None, l2norm=True, softplus=True, sigmoid=True, scale=0.0, retrieve=True,
+         counts=None, active=None, cap=0):
     """Gated delta-rule recurrence.  retrieve=False drops the retrieval term (the linear and gated
-    update rules).  Returns (out [N,H,V] f64, state_out [B,H,V,K] f64) or None when the offsets are
-    malformed."""
+    update rules).  Returns (out [N,H,V] f64, state_out [B,H,V,K] f64), plus the capture capsule
+    [B, cap*(H + HQ*K + H*V)] f64 when counts is given; None when the offsets are malformed."""
     qd = DTYPE_CODES[qkv_dtype]
     gd = DTYPE_CODES[gate_dtype or qkv_dtype]
     qkv = _raw(qkv, qd)
@@ -150,15 +167,20 @@ def scan(qkv, offsets, *, HQ, H, K, V, qkv_dtype, gate_dtype=None, a=None, b=Non
     assert qkv.shape[1] == 2 * HQ * K + H * V
     out = np.zeros((N, H, V), np.float64)
     st = np.zeros((B, H, V, K), np.float64)
+    capsule = cnt = act = None
+    if counts is not None:
+        cnt = np.ascontiguousarray(counts, dtype=np.int32)
+        act = None if active is None else np.ascontiguousarray(active, dtype=np.int32)
+        capsule = np.zeros((B, cap * (H + HQ * K + H * V)), np.float64)
     rc = lib().gdn_oracle_scan(B, N, HQ, H, K, V, qd, gd, int(bool(l2norm)), int(bool(softplus)),
                                int(bool(sigmoid)), int(bool(retrieve)), float(scale), _ptr(qkv), _ptr(a), _ptr(b),
-                               _ptr(A_log),
-                               _ptr(dt_bias), _ptr(state_in), _ptr(off), _ptr(out), _ptr(st))
+                               _ptr(A_log), _ptr(dt_bias), _ptr(state_in), _ptr(off), _ptr(out), _ptr(st),
+                               _ptr(cnt), _ptr(act), int(cap), _ptr(capsule))
     if rc == 1:
         return None
     if rc != 0:
         raise MemoryError("oracle scan could not allocate its buffers")
-    return out, st
+    return (out, st) if counts is None else (out, st, capsule)
 
 
 def threads() -> int:

@@ -201,6 +201,25 @@ void gdn_oracle_prepare(int N, int HQ, int H, int K, int V, int qkv_dtype, int g
     }
 }
 
+/* [conv capture]: the raw inputs of the first tokens of each sequence, for speculative decoding
+ * (paged_ssm.rs page, CONV_CAPTURE_INIT / CONV_CAPTURE_STEP): with captured = max(0, min(counts[b],
+ * cap, len_b)), updates[b,i,c] = x[start_b + i, c] for i < captured and 0 for captured <= i < cap.
+ * updates is [B, cap, C] decoded to fp64.  Returns 0, or 1 when the offsets are malformed. */
+int gdn_oracle_conv_capture(int B, int N, int C, int cap, int x_dtype, const void *x, const int32_t *offsets,
+                            const int32_t *counts, double *updates) {
+    if (!gdn_oracle_offsets_valid(offsets, B, N)) return 1;
+    for (int b = 0; b < B; ++b) {
+        const int start = offsets[b], len = offsets[b + 1] - start;
+        int captured = counts[b] < cap ? counts[b] : cap;
+        if (captured > len) captured = len;
+        if (captured < 0) captured = 0;
+        for (int i = 0; i < cap; ++i)
+            for (int c = 0; c < C; ++c)
+                updates[((size_t)b * cap + i) * C + c] = i < captured ? dec(x, x_dtype, (size_t)(start + i) * C + c) : 0.0;
+    }
+    return 0;
+}
+
 /* ---- the gated delta-rule recurrence ------------------------------------------------------------ */
 
 /* [delta]: for each sequence b, value head h (key head kh = h / (H/HQ)) and value column v, the
@@ -212,6 +231,12 @@ void gdn_oracle_prepare(int N, int HQ, int H, int K, int V, int qkv_dtype, int g
  *     s <- s + delta * k^
  *     out[t,h,v] = scale * (q^ . s)
  * with q^, k^, g, beta as produced by gdn_oracle_prepare.  The final s is state_out[b,h,v,:].
+ * Capture (paged_ssm.rs page, DELTA_CAPTURE_INIT / DELTA_CAPTURE_STEP), when capsule is not NULL:
+ * per sequence b the first captured = (active && !active[0]) ? 0 : max(0, min(counts[b], cap, len_b))
+ * steps are recorded in capsule[b] = [cap*H g | cap*HQ*K k^ | cap*H*V delta] (slot i: g of (i, h) at
+ * i*H + h; k^ of (i, kh) at cap*H + (i*HQ + kh)*K; delta of (i, h, v) at cap*(H + HQ*K) +
+ * (i*H + h)*V + v); slots from captured on are 0.  delta is the written value beta*(v_t - r), so
+ * S_i = g_i S_{i-1} + delta_i k^_i^T replays the recurrence.
  * retrieve == 0 drops the retrieval term (delta = beta * v_t): the "linear" and "gated" update rules
  * of the pages' update_rule attribute, which the DELTA kernel string compiles with RETRIEVE = 0
  * (the rule's decay side is the presence of the decay input, as for the other rules).
@@ -222,7 +247,8 @@ void gdn_oracle_prepare(int N, int HQ, int H, int K, int V, int qkv_dtype, int g
 int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, int gate_dtype,
                     int l2norm, int softplus, int sigmoid, int retrieve, double scale, const void *qkv,
                     const void *a, const void *b, const float *A_log, const float *dt_bias,
-                    const float *state_in, const int32_t *offsets, double *out, double *state_out) {
+                    const float *state_in, const int32_t *offsets, double *out, double *state_out,
+                    const int32_t *counts, const int32_t *active, int cap, double *capsule) {
     if (!gdn_oracle_offsets_valid(offsets, B, N)) return 1;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)K);
     const size_t C = (size_t)2 * HQ * K + (size_t)H * V;
@@ -244,6 +270,20 @@ int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, in
         const int bb = (int)(bh / H), h = (int)(bh % H);
         const int kh = h / G;
         const int start = offsets[bb], end = offsets[bb + 1];
+        int captured = 0;
+        double *cb = NULL;
+        if (capsule) {
+            captured = counts[bb] < cap ? counts[bb] : cap;
+            if (captured > end - start) captured = end - start;
+            if (captured < 0 || (active && active[0] == 0)) captured = 0;
+            cb = capsule + (size_t)bb * cap * ((size_t)H + (size_t)HQ * K + (size_t)H * V);
+            for (int i = 0; i < cap; ++i) {  /* every slot of (b, h), then filled below */
+                cb[(size_t)i * H + h] = 0.0;
+                if (h == kh * G)
+                    for (int j = 0; j < K; ++j) cb[(size_t)cap * H + ((size_t)i * HQ + kh) * K + j] = 0.0;
+                for (int v = 0; v < V; ++v) cb[(size_t)cap * (H + (size_t)HQ * K) + ((size_t)i * H + h) * V + v] = 0.0;
+            }
+        }
         double *s = (double *)malloc(sizeof(double) * (size_t)K);
         if (!s) {
             failed = 1;
@@ -263,6 +303,13 @@ int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, in
                 if (retrieve)
                     for (int i = 0; i < K; ++i) r += kk[i] * s[i];
                 const double delta = beta * (vt - r);
+                const int slot = t - start;
+                if (cb && slot < captured) {
+                    if (v == 0) cb[(size_t)slot * H + h] = g;
+                    if (v == 0 && h == kh * G)
+                        for (int j = 0; j < K; ++j) cb[(size_t)cap * H + ((size_t)slot * HQ + kh) * K + j] = kk[j];
+                    cb[(size_t)cap * (H + (size_t)HQ * K) + ((size_t)slot * H + h) * V + v] = delta;
+                }
                 for (int i = 0; i < K; ++i) s[i] += delta * kk[i];
                 double o = 0.0;
                 for (int i = 0; i < K; ++i) o += qh[i] * s[i];
