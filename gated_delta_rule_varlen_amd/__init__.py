@@ -15,8 +15,8 @@ import torch
 from . import _abi
 from ._abi import GdnError, PATH_NAMES, lib  # noqa: F401
 
-__all__ = ["conv1d_varlen", "prepare_qk_gates", "scan_varlen", "scan_workspace_bytes", "decode_step", "GdnError",
-           "lib"]
+__all__ = ["conv1d_varlen", "conv1d_varlen_capture", "prepare_qk_gates", "scan_varlen", "scan_varlen_capture",
+           "scan_workspace_bytes", "decode_step", "GdnError", "lib"]
 
 _DTYPE = {torch.float32: _abi.F32, torch.bfloat16: _abi.BF16, torch.float16: _abi.F16}
 _TORCH = {v: k for k, v in _DTYPE.items()}
@@ -73,6 +73,35 @@ def conv1d_varlen(x: torch.Tensor, weight: torch.Tensor, offsets: torch.Tensor, 
                                  _ptr(offsets, "offsets"), _ptr(dev_status, "dev_status"), _stream(x.device))
     _check(st, "gdn_conv1d_varlen")
     return y, state_out
+
+
+def conv1d_varlen_capture(x: torch.Tensor, weight: torch.Tensor, offsets: torch.Tensor, *, cap: int,
+                          counts: torch.Tensor, updates=None, bias=None, state_in=None, dilation: int = 1,
+                          silu: bool = False, state_dtype=None, y=None, state_out=None, write_state: bool = True,
+                          dev_status=None):
+    """conv1d_varlen that also records the first min(counts[b], cap, len) input rows of each sequence
+    (gdn_conv1d_varlen_capture).  counts int32 [B].  Returns (y, state_out, updates [B, cap, C])."""
+    if weight.dim() == 3:
+        weight = weight.reshape(weight.shape[0], weight.shape[2])
+    N, C = x.shape
+    W = weight.shape[1]
+    B = offsets.numel() - 1
+    L = (W - 1) * dilation
+    if state_dtype is None:
+        state_dtype = state_in.dtype if state_in is not None else (state_out.dtype if state_out is not None else x.dtype)
+    if y is None:
+        y = torch.empty_like(x)
+    if state_out is None and write_state and L > 0:
+        state_out = torch.empty((B, C, L), dtype=state_dtype, device=x.device)
+    if updates is None:
+        updates = torch.empty((B, cap, C), dtype=x.dtype, device=x.device)
+    d = _abi.ConvDesc(B, N, C, W, dilation, _code(x, "x"), _DTYPE[state_dtype], _abi.CONV_SILU if silu else 0)
+    st = lib().gdn_conv1d_varlen_capture(ctypes.byref(d), _ptr(x, "x"), _ptr(weight, "weight"), _ptr(bias, "bias"),
+                                         _ptr(state_in, "state_in"), _ptr(y, "y"), _ptr(state_out, "state_out"),
+                                         _ptr(offsets, "offsets"), int(cap), _ptr(counts, "counts"),
+                                         _ptr(updates, "updates"), _ptr(dev_status, "dev_status"), _stream(x.device))
+    _check(st, "gdn_conv1d_varlen_capture")
+    return y, state_out, updates
 
 
 def _scan_desc(qkv, B, HQ, H, K, V, gate, l2norm, softplus, sigmoid, scale, path, retrieve=True):
@@ -138,6 +167,39 @@ def scan_varlen(qkv: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K:
                                _ptr(dev_status, "dev_status"), ctypes.byref(used), _stream(qkv.device))
     _check(st, "gdn_scan_varlen")
     return out, state_out, PATH_NAMES.get(used.value, str(used.value))
+
+
+def capsule_width(cap: int, *, HQ: int, H: int, K: int, V: int) -> int:
+    """Row width of the fp32 capture capsule: cap * (H + HQ*K + H*V)."""
+    return cap * (H + HQ * K + H * V)
+
+
+def scan_varlen_capture(qkv: torch.Tensor, offsets: torch.Tensor, *, cap: int, counts: torch.Tensor, HQ: int, H: int,
+                        K: int, V: int, active=None, capsule=None, a=None, b=None, A_log=None, dt_bias=None,
+                        state_in=None, qk_prep=None, gb_prep=None, l2norm=True, softplus=True, sigmoid=True,
+                        scale: float = 0.0, path: str = "auto", out=None, state_out=None, write_state: bool = True,
+                        dev_status=None, retrieve: bool = True):
+    """scan_varlen that also records g, k^ and delta of the first min(counts[b], cap, len) tokens of
+    each sequence (gdn_scan_varlen_capture); active int32 [1] or None.
+    Returns (out, state_out, capsule [B, cap*(H + HQ*K + H*V)] fp32, path name that ran)."""
+    N = qkv.shape[0]
+    B = offsets.numel() - 1
+    if out is None:
+        out = torch.empty((N, H, V), dtype=qkv.dtype, device=qkv.device)
+    if state_out is None and write_state:
+        state_out = torch.empty((B, H, V, K), dtype=torch.float32, device=qkv.device)
+    if capsule is None:
+        capsule = torch.empty((B, capsule_width(cap, HQ=HQ, H=H, K=K, V=V)), dtype=torch.float32, device=qkv.device)
+    d = _scan_desc(qkv, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, path, retrieve)
+    used = ctypes.c_int32(-1)
+    st = lib().gdn_scan_varlen_capture(ctypes.byref(d), _ptr(qkv, "qkv"), _ptr(qk_prep, "qk_prep"),
+                                       _ptr(gb_prep, "gb_prep"), _ptr(a, "a"), _ptr(b, "b"), _ptr(A_log, "A_log"),
+                                       _ptr(dt_bias, "dt_bias"), _ptr(state_in, "state_in"), _ptr(out, "out"),
+                                       _ptr(state_out, "state_out"), _ptr(offsets, "offsets"), int(cap),
+                                       _ptr(counts, "counts"), _ptr(active, "active"), _ptr(capsule, "capsule"), None,
+                                       0, _ptr(dev_status, "dev_status"), ctypes.byref(used), _stream(qkv.device))
+    _check(st, "gdn_scan_varlen_capture")
+    return out, state_out, capsule, PATH_NAMES.get(used.value, str(used.value))
 
 
 def decode_step(x: torch.Tensor, weight: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K: int, V: int,

@@ -24,8 +24,10 @@ PATH_CODES = {v: k for k, v in PATH_NAMES.items()}
 # Every symbol include/gdn.h declares.
 EXPORTS = (
     "gdn_conv1d_varlen",
+    "gdn_conv1d_varlen_capture",
     "gdn_prepare_qk_gates",
     "gdn_scan_varlen",
+    "gdn_scan_varlen_capture",
     "gdn_scan_workspace_bytes",
     "gdn_decode_step",
     "gdn_status_string",
@@ -81,10 +83,15 @@ def lib() -> ctypes.CDLL:
         vp, i32p, st = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int
         L.gdn_conv1d_varlen.argtypes = [ctypes.POINTER(ConvDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_conv1d_varlen.restype = st
+        L.gdn_conv1d_varlen_capture.argtypes = [ctypes.POINTER(ConvDesc)] + [vp] * 7 + [ctypes.c_int32, vp, vp, vp, vp]
+        L.gdn_conv1d_varlen_capture.restype = st
         L.gdn_prepare_qk_gates.argtypes = [ctypes.POINTER(ScanDesc), vp, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_prepare_qk_gates.restype = st
         L.gdn_scan_varlen.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 12 + [ctypes.c_size_t, vp, i32p, vp]
         L.gdn_scan_varlen.restype = st
+        L.gdn_scan_varlen_capture.argtypes = ([ctypes.POINTER(ScanDesc)] + [vp] * 11 + [ctypes.c_int32, vp, vp, vp, vp,
+                                              ctypes.c_size_t, vp, i32p, vp])
+        L.gdn_scan_varlen_capture.restype = st
         L.gdn_decode_step.argtypes = [ctypes.POINTER(ConvDesc), ctypes.POINTER(ScanDesc)] + [vp] * 15
         L.gdn_decode_step.restype = st
         L.gdn_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(ctypes.c_size_t)]

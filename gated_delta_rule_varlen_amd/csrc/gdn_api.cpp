@@ -45,19 +45,19 @@ gdn_status check_scan_desc(const gdn_scan_desc* d) {
 // The chunked path sums log-decays, so it needs every decay finite and positive (a decay input with
 // the softplus gate), and it relies on normalised keys for a well-conditioned (I + A); it computes
 // the gates and norms itself, so it runs on fused inputs only; its algebra is that of the rules
-// with the retrieval term.  Built for bf16/fp16 I/O with
-// K = V = 64 or 128.
-bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay) {
-    return !prepared && has_decay && (d->flags & GDN_SOFTPLUS) && (d->flags & GDN_L2NORM) &&
+// with the retrieval term.  Built for bf16/fp16 I/O with K = V = 64 or 128.  Capture is recorded
+// by the token-sequential paths only.
+bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay, bool capture) {
+    return !prepared && has_decay && !capture && (d->flags & GDN_SOFTPLUS) && (d->flags & GDN_L2NORM) &&
            !(d->flags & GDN_NO_RETRIEVE) && gdn::chunked_shape_supported(d->K, d->V, d->qkv_dtype);
 }
 
 // AUTO: DECODE for at most two tokens per sequence on average; CHUNK when eligible, the average
 // sequence fills at least one chunk of 64 tokens and the workspace suffices; SEQ otherwise.
-int resolve_path(const gdn_scan_desc* d, bool prepared, bool has_decay, size_t ws_bytes) {
+int resolve_path(const gdn_scan_desc* d, bool prepared, bool has_decay, bool capture, size_t ws_bytes) {
     if (d->path != GDN_PATH_AUTO) return d->path;
     if ((long long)d->N <= 2ll * d->B) return GDN_PATH_DECODE;
-    if (chunk_eligible(d, prepared, has_decay) && (long long)d->N >= 64ll * d->B &&
+    if (chunk_eligible(d, prepared, has_decay, capture) && (long long)d->N >= 64ll * d->B &&
         ws_bytes >= gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
         return GDN_PATH_CHUNK;
     return GDN_PATH_SEQ;
@@ -85,9 +85,14 @@ const char* gdn_status_string(gdn_status s) {
     return "unknown status";
 }
 
-gdn_status gdn_conv1d_varlen(const gdn_conv_desc* d, const void* x, const void* w, const void* bias,
-                             const void* state_in, void* y, void* state_out, const int32_t* offsets,
-                             int32_t* dev_status, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_conv1d_varlen with an optional capture (cap == 0: none; the capture arguments were checked).
+gdn_status conv_call(const gdn_conv_desc* d, const void* x, const void* w, const void* bias, const void* state_in,
+                     void* y, void* state_out, const int32_t* offsets, int cap, const int32_t* counts,
+                     void* updates, int32_t* dev_status, hipStream_t stream) {
     if (d == nullptr || w == nullptr || offsets == nullptr) return GDN_ERR_NULL;
     if (d->B < 1 || d->N < 0 || d->C < 1 || d->W < 1 || d->D < 1) return GDN_ERR_SHAPE;
     if (d->N > 0 && (x == nullptr || y == nullptr)) return GDN_ERR_NULL;
@@ -117,7 +122,31 @@ gdn_status gdn_conv1d_varlen(const gdn_conv_desc* d, const void* x, const void* 
     a.x_dtype = d->x_dtype;
     a.state_dtype = d->state_dtype;
     a.silu = (d->flags & GDN_CONV_SILU) != 0;
+    a.cap = cap;
+    a.counts = counts;
+    a.updates = updates;
     return from_hip(gdn::launch_conv(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_conv1d_varlen(const gdn_conv_desc* d, const void* x, const void* w, const void* bias,
+                             const void* state_in, void* y, void* state_out, const int32_t* offsets,
+                             int32_t* dev_status, hipStream_t stream) {
+    return conv_call(d, x, w, bias, state_in, y, state_out, offsets, 0, nullptr, nullptr, dev_status, stream);
+}
+
+gdn_status gdn_conv1d_varlen_capture(const gdn_conv_desc* d, const void* x, const void* w, const void* bias,
+                                     const void* state_in, void* y, void* state_out, const int32_t* offsets,
+                                     int32_t cap, const int32_t* counts, void* updates, int32_t* dev_status,
+                                     hipStream_t stream) {
+    if (d == nullptr || counts == nullptr || updates == nullptr) return GDN_ERR_NULL;
+    if (cap < 1) return GDN_ERR_SHAPE;
+    if ((long long)cap * d->C > INT_MAX) return GDN_ERR_OVERFLOW;
+    if (misaligned(updates)) return GDN_ERR_ALIGN;
+    return conv_call(d, x, w, bias, state_in, y, state_out, offsets, cap, counts, updates, dev_status, stream);
 }
 
 gdn_status gdn_prepare_qk_gates(const gdn_scan_desc* d, const void* qkv, const void* a, const void* b,
@@ -153,17 +182,23 @@ gdn_status gdn_scan_workspace_bytes(const gdn_scan_desc* d, size_t* bytes) {
     if (bytes == nullptr) return GDN_ERR_NULL;
     const gdn_status st = check_scan_desc(d);
     if (st != GDN_OK) return st;
-    // Resolved as AUTO would with an unlimited workspace, assuming fused inputs with a decay input.
-    const int path = resolve_path(d, false, true, SIZE_MAX);
+    // Resolved as AUTO would with an unlimited workspace, assuming fused inputs with a decay input
+    // and no capture.
+    const int path = resolve_path(d, false, true, false, SIZE_MAX);
     *bytes = path == GDN_PATH_CHUNK ? gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V) : 0;
     return GDN_OK;
 }
 
-gdn_status gdn_scan_varlen(const gdn_scan_desc* d, const void* qkv, const float* qk_prep, const float* gb_prep,
-                           const void* a, const void* b, const float* A_log, const float* dt_bias,
-                           const float* state_in, void* out, float* state_out, const int32_t* offsets,
-                           void* workspace, size_t ws_bytes, int32_t* dev_status, int32_t* path_used,
-                           hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_scan_varlen with an optional capture (cap == 0: none; the capture arguments were checked).
+gdn_status scan_call(const gdn_scan_desc* d, const void* qkv, const float* qk_prep, const float* gb_prep,
+                     const void* a, const void* b, const float* A_log, const float* dt_bias, const float* state_in,
+                     void* out, float* state_out, const int32_t* offsets, int cap, const int32_t* counts,
+                     const int32_t* active, float* capsule, void* workspace, size_t ws_bytes, int32_t* dev_status,
+                     int32_t* path_used, hipStream_t stream) {
     const gdn_status st = check_scan_desc(d);
     if (st != GDN_OK) return st;
     if (offsets == nullptr) return GDN_ERR_NULL;
@@ -175,9 +210,10 @@ gdn_status gdn_scan_varlen(const gdn_scan_desc* d, const void* qkv, const float*
     if (misaligned(qkv) || misaligned(qk_prep) || misaligned(gb_prep) || misaligned(state_in) || misaligned(out) ||
         misaligned(state_out) || misaligned(workspace))
         return GDN_ERR_ALIGN;
-    const int path = resolve_path(d, prepared, a != nullptr, workspace ? ws_bytes : 0);
+    const bool capture = cap > 0;
+    const int path = resolve_path(d, prepared, a != nullptr, capture, workspace ? ws_bytes : 0);
     if (path == GDN_PATH_CHUNK) {
-        if (!chunk_eligible(d, prepared, a != nullptr)) return GDN_ERR_UNSUPPORTED;
+        if (!chunk_eligible(d, prepared, a != nullptr, capture)) return GDN_ERR_UNSUPPORTED;
         if (workspace == nullptr || ws_bytes < gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
             return GDN_ERR_WORKSPACE;
     }
@@ -207,12 +243,48 @@ gdn_status gdn_scan_varlen(const gdn_scan_desc* d, const void* qkv, const float*
     s.flags = d->flags;
     s.scale = (d->scale > 0.0f && std::isfinite(d->scale)) ? d->scale : 1.0f / std::sqrt((float)d->K);
     s.path = path;
+    s.cap = cap;
+    s.counts = counts;
+    s.active = active;
+    s.capsule = capsule;
     const hipError_t e = path == GDN_PATH_CHUNK  ? gdn::launch_scan_chunked(s, stream)
                          : path == GDN_PATH_SEQ ? gdn::launch_scan_seq(s, stream)
                                                 : gdn::launch_scan_decode(s, stream);
     const gdn_status rs = from_hip(e);
     if (rs == GDN_OK && path_used != nullptr) *path_used = path;
     return rs;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_scan_varlen(const gdn_scan_desc* d, const void* qkv, const float* qk_prep, const float* gb_prep,
+                           const void* a, const void* b, const float* A_log, const float* dt_bias,
+                           const float* state_in, void* out, float* state_out, const int32_t* offsets,
+                           void* workspace, size_t ws_bytes, int32_t* dev_status, int32_t* path_used,
+                           hipStream_t stream) {
+    return scan_call(d, qkv, qk_prep, gb_prep, a, b, A_log, dt_bias, state_in, out, state_out, offsets, 0, nullptr,
+                     nullptr, nullptr, workspace, ws_bytes, dev_status, path_used, stream);
+}
+
+gdn_status gdn_scan_varlen_capture(const gdn_scan_desc* d, const void* qkv, const float* qk_prep,
+                                   const float* gb_prep, const void* a, const void* b, const float* A_log,
+                                   const float* dt_bias, const float* state_in, void* out, float* state_out,
+                                   const int32_t* offsets, int32_t cap, const int32_t* counts, const int32_t* active,
+                                   float* capsule, void* workspace, size_t ws_bytes, int32_t* dev_status,
+                                   int32_t* path_used, hipStream_t stream) {
+    const gdn_status st = check_scan_desc(d);
+    if (st != GDN_OK) return st;
+    if (counts == nullptr || capsule == nullptr) return GDN_ERR_NULL;
+    if (cap < 1) return GDN_ERR_SHAPE;
+    // the capsule row width must be an int32, as the pages' capsule geometry requires
+    if ((long long)cap * ((long long)d->H + (long long)d->HQ * d->K + (long long)d->H * d->V) > INT_MAX)
+        return GDN_ERR_OVERFLOW;
+    if (misaligned(capsule)) return GDN_ERR_ALIGN;
+    if (d->path == GDN_PATH_CHUNK) return GDN_ERR_UNSUPPORTED;
+    return scan_call(d, qkv, qk_prep, gb_prep, a, b, A_log, dt_bias, state_in, out, state_out, offsets, cap, counts,
+                     active, capsule, workspace, ws_bytes, dev_status, path_used, stream);
 }
 
 gdn_status gdn_decode_step(const gdn_conv_desc* cd, const gdn_scan_desc* sd, const void* x, const void* conv_w,

@@ -11,7 +11,10 @@
 //     through registers, so each token row is loaded once;
 //   * "head" blocks own one sequence: they compute its first min(L, len) tokens -- the only ones
 //     whose taps reach into the carried window -- and then write the new window.  The window is
-//     read and written by the same thread in that order, so state_out may alias state_in.
+//     read and written by the same thread in that order, so state_out may alias state_in;
+//   * with capture (speculative decoding: paged_ssm.rs page, CONV_CAPTURE_INIT / _STEP) the head
+//     blocks also copy the sequence's first captured token rows into its update slots and zero the
+//     slots after them.
 //
 // Every block checks the whole offsets array first and writes nothing when it is malformed.
 #include <type_traits>
@@ -38,6 +41,9 @@ struct ConvArgs {
     int n_cvec;  // C / VEC
     int n_cblk;  // channel blocks per item
     int tile;    // tokens per body block
+    int cap;                // capture slots per sequence (0 = no capture)
+    const int32_t* counts;  // [B] tokens to capture
+    void* updates;          // [B, cap, C] x dtype
 };
 
 template <typename T, int VEC>
@@ -83,6 +89,25 @@ template <typename T>
 __device__ __forceinline__ typename T::storage raw_elem(const u32x4& raw, int i) {
     if constexpr (std::is_same<T, F32>::value) return __uint_as_float(raw[i]);
     else return (uint16_t)((raw[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+}
+
+// Capture of sequence b by the thread owning channels c0 .. c0+VEC-1: slot i < captured holds the
+// raw row x[start + i] (bit copy), the remaining slots zeros.
+template <typename T, int VEC>
+__device__ __forceinline__ void capture_rows(const ConvArgs& p, int b, int start, int len, int c0) {
+    using TS = typename T::storage;
+    const int n = captured_tokens(p.counts, nullptr, p.cap, b, len);
+    const TS* x = static_cast<const TS*>(p.x);
+    TS* u = static_cast<TS*>(p.updates) + (size_t)b * p.cap * p.C + c0;
+    for (int i = 0; i < p.cap; ++i) {
+        if constexpr (VEC > 1) {
+            const u32x4 v = i < n ? *reinterpret_cast<const u32x4*>(x + (size_t)(start + i) * p.C + c0)
+                                  : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(u + (size_t)i * p.C) = v;
+        } else {
+            u[(size_t)i * p.C] = i < n ? x[(size_t)(start + i) * p.C + c0] : (TS)0;
+        }
+    }
 }
 
 // SiLU z / (1 + e^-z) with the hardware exp2 and reciprocal (each within a couple of ulp of fp32):
@@ -215,6 +240,7 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
 #pragma unroll
             for (int k = 0; k < NCH; ++k) dst[k] = nw.v[k];
         }
+        if (p.cap > 0) capture_rows<T, VEC>(p, b, start, len, c0);
         return;
       }
     }
@@ -268,6 +294,7 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
                 }
             }
         }
+        if (p.cap > 0) capture_rows<T, VEC>(p, b, start, len, c0);
         return;
     }
 
@@ -364,6 +391,9 @@ hipError_t launch_vec(const ConvLaunch& a, hipStream_t stream) {
     p.D = a.D;
     p.L = (a.W - 1) * a.D;
     p.silu = a.silu ? 1 : 0;
+    p.cap = a.cap;
+    p.counts = a.counts;
+    p.updates = a.updates;
     p.n_cvec = a.C / VEC;
     const int threads = p.n_cvec >= 256 ? 256 : ((p.n_cvec + 63) / 64) * 64;
     p.n_cblk = (p.n_cvec + threads - 1) / threads;

@@ -141,6 +141,35 @@ __device__ __forceinline__ int find_sequence(const int32_t* __restrict__ offsets
     return lo;
 }
 
+// Tokens of a sequence of length len recorded by a capture of cap slots: min(counts[b], cap, len),
+// at least 0, and 0 when the device flag active is given and reads 0.
+__device__ __forceinline__ int captured_tokens(const int32_t* counts, const int32_t* active, int cap, int b,
+                                               int len) {
+    if (active != nullptr && active[0] == 0) return 0;
+    int n = counts[b];
+    n = n < cap ? n : cap;
+    n = n < len ? n : len;
+    return n > 0 ? n : 0;
+}
+
+// The capture record of one sequence (paged_ssm.rs page, DELTA_CAPTURE_INIT / _STEP): the row
+// [cap*H decays | cap*HQ*K normalised keys | cap*H*V written values delta] of the fp32 capsule
+// [B, cap*(H + HQ*K + H*V)].  Slot i holds token start + i.
+struct CaptureRow {
+    float* base;
+    int cap, H, HQ, K, V;
+    __device__ __forceinline__ float* g(int i, int h) const { return base + (size_t)i * H + h; }
+    __device__ __forceinline__ float* k(int i, int kh) const {
+        return base + (size_t)cap * H + ((size_t)i * HQ + kh) * K;
+    }
+    __device__ __forceinline__ float* d(int i, int h) const {
+        return base + (size_t)cap * ((size_t)H + (size_t)HQ * K) + ((size_t)i * H + h) * V;
+    }
+};
+__device__ __forceinline__ CaptureRow capture_row(float* capsule, int b, int cap, int H, int HQ, int K, int V) {
+    return CaptureRow{capsule + (size_t)b * cap * ((size_t)H + (size_t)HQ * K + (size_t)H * V), cap, H, HQ, K, V};
+}
+
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
 
 // Blocks are dispatched round-robin over the 8 XCDs of the chip (block i runs on XCD i % 8).  This

@@ -22,6 +22,10 @@ struct ConvLaunch {
     int B, N, C, W, D;
     int x_dtype, state_dtype;
     bool silu;
+    // capture (cap > 0): the first captured tokens' rows of x into updates [B, cap, C] x_dtype
+    int cap;
+    const int32_t* counts;
+    void* updates;
 };
 hipError_t launch_conv(const ConvLaunch& a, hipStream_t stream);
 
@@ -59,6 +63,12 @@ struct ScanLaunch {
     uint32_t flags;
     float scale;  // already resolved (> 0)
     int path;     // resolved: GDN_PATH_DECODE, GDN_PATH_SEQ or GDN_PATH_CHUNK
+    // capture (cap > 0): g, k^ and delta of the first captured tokens into capsule
+    // [B, cap*(H + HQ*K + H*V)] fp32; active (device, NULL = always) switches it off when 0
+    int cap;
+    const int32_t* counts;
+    const int32_t* active;
+    float* capsule;
 };
 hipError_t launch_scan_decode(const ScanLaunch& a, hipStream_t stream);  // DECODE
 hipError_t launch_scan_seq(const ScanLaunch& a, hipStream_t stream);     // SEQ

@@ -25,7 +25,11 @@
 //   * a block whose sequence has exactly one token (the decode step) streams its columns instead:
 //     token operands first, then the state columns of a group with all their loads in flight, each
 //     column reduced, updated, written back and its output taken in turn, so reads and writes of
-//     the state interleave.  Same arithmetic in the same order, so the results are bit-identical.
+//     the state interleave.  Same arithmetic in the same order, so the results are bit-identical;
+//   * with capture (speculative decoding: paged_ssm.rs page, DELTA_CAPTURE_INIT / _STEP) the first
+//     captured tokens of a sequence also record g (one lane of the head's first block), k^ (the
+//     first lane group of that block, for the first value head of each key head) and delta (the
+//     lane that writes the column's output); the slots after them are zeroed by the same lanes.
 //
 // DECODE instances stream the state with non-temporal loads/stores (read once, written once).
 #include <type_traits>
@@ -63,6 +67,10 @@ struct ScanArgs {
     float scale;
     int n_vtiles;   // column tiles per (sequence, head)
     int n_blocks;   // grid size
+    int cap;                // capture slots per sequence (0 = no capture)
+    const int32_t* counts;  // [B]
+    const int32_t* active;  // [1] or NULL
+    float* capsule;         // [B, cap*(H + HQ*K + H*V)]
 };
 
 template <bool NT>
@@ -162,6 +170,41 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
     const float a_bias = (!PREP && p.a && softplus) ? p.dt_bias[h] : 0.0f;
     TS* outp = static_cast<TS*>(p.out);
 
+    int captured = 0;  // tokens recorded (0 without capture)
+    CaptureRow crow{};
+    if (p.cap > 0) {
+        captured = captured_tokens(p.counts, p.active, p.cap, b, end - start);
+        crow = capture_row(p.capsule, b, p.cap, p.H, p.HQ, K, p.V);
+    }
+    const bool cap_g = vt == 0 && wave == 0 && lane == 0;
+    const bool cap_k = vt == 0 && wave == 0 && grp == 0 && h == kh * p.G;
+    const bool cap_d = gl < CPL && vbase + gl < p.V;
+    // record slot i: g, the lane's share of k^ = kv * rk, and delta of column vbase + gl
+    auto capture = [&](int i, float g, const float (&kv)[EPL], float rk, float dmine) {
+        if (cap_g) *crow.g(i, h) = g;
+        if (cap_k) {
+            float* kd = crow.k(i, kh);
+#pragma unroll
+            for (int m = 0; m < EPL / 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kd[4 * (gl + LPC * m) + e] = kv[4 * m + e] * rk;
+        }
+        if (cap_d) crow.d(i, h)[vbase + gl] = dmine;
+    };
+    auto capture_zeros = [&]() {
+        for (int i = captured; i < p.cap; ++i) {
+            if (cap_g) *crow.g(i, h) = 0.0f;
+            if (cap_k) {
+                float* kd = crow.k(i, kh);
+#pragma unroll
+                for (int m = 0; m < EPL / 4; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) kd[4 * (gl + LPC * m) + e] = 0.0f;
+            }
+            if (cap_d) crow.d(i, h)[vbase + gl] = 0.0f;
+        }
+    };
+
     if constexpr (GDN_DECODE_STREAM > 0) {
         // One token, a whole column tile and a carried state (block-uniform conditions): stream the
         // columns with GDN_DECODE_STREAM columns of loads ahead, storing each column as soon as it is
@@ -207,7 +250,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                 }
             }
             const float oscale = p.scale * rq;
-            float mine = 0.0f;
+            float mine = 0.0f, dmine = 0.0f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 if (c + PD < CPL) load_col(c + PD, ring[(c + PD) % (PD + 1)]);
@@ -223,7 +266,8 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                 pk = group_sum<LPC>(pk);
                 pq = group_sum<LPC>(pq);
                 const float r = rmul * (g * rk * pk);
-                const float dk = beta * (tok.v[c] - r) * rk;
+                const float delta = beta * (tok.v[c] - r);
+                const float dk = delta * rk;
                 const float o = oscale * fmaf(g, pq, dk * qk);
                 float* sp = p.state_out + (col0 + vbase + c) * K;
 #pragma unroll
@@ -233,9 +277,16 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                     for (int e = 0; e < 4; ++e) nv[e] = fmaf(dk, tok.k[4 * i + e], g * sc[i][e]);
                     st_state<NT>(sp + 4 * (gl + LPC * i), nv);
                 }
-                if (gl == c) mine = o;
+                if (gl == c) {
+                    mine = o;
+                    dmine = delta;
+                }
             }
             if (gl < CPL) outp[((size_t)start * p.H + h) * p.V + vbase + gl] = from_f32<T>(mine);
+            if (p.cap > 0) {
+                if (captured > 0) capture(0, g, tok.k, rk, dmine);
+                capture_zeros();
+            }
             return;
         }
     }
@@ -304,17 +355,22 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
             }
         }
         const float oscale = p.scale * rq;
-        float mine = 0.0f;
+        float mine = 0.0f, dmine = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const float r = rmul * (g * rk * pk[c]);
-            const float dk = beta * (cur.v[c] - r) * rk;  // delta * rk: coefficient of the raw k
+            const float delta = beta * (cur.v[c] - r);
+            const float dk = delta * rk;  // coefficient of the raw k
             const float o = oscale * fmaf(g, pq[c], dk * qk);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) s[c][e] = fmaf(dk, cur.k[e], g * s[c][e]);
-            if (gl == c) mine = o;
+            if (gl == c) {
+                mine = o;
+                dmine = delta;
+            }
         }
         if (gl < CPL && vbase + gl < p.V) outp[((size_t)t * p.H + h) * p.V + vbase + gl] = from_f32<T>(mine);
+        if (t - start < captured) capture(t - start, g, cur.k, rk, dmine);
         cur = nxt;
     }
 
@@ -329,6 +385,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                              f32x4{s[c][4 * i], s[c][4 * i + 1], s[c][4 * i + 2], s[c][4 * i + 3]});
         }
     }
+    if (p.cap > 0) capture_zeros();
 }
 
 template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT>
@@ -407,6 +464,10 @@ hipError_t launch_scan_decode(const ScanLaunch& a, hipStream_t stream) {
     p.scale = a.scale;
     p.n_vtiles = 0;
     p.n_blocks = 0;
+    p.cap = a.cap;
+    p.counts = a.counts;
+    p.active = a.active;
+    p.capsule = a.capsule;
     if (a.qk_prep != nullptr) return launch_p<true>(p, a.qkv_dtype, stream);
     return launch_p<false>(p, a.qkv_dtype, stream);
 }

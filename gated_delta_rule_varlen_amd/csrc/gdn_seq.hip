@@ -17,7 +17,11 @@
 //     one 4-step DPP reduction pair and EPL multiply-adds for the update
 //         r = g (k^.s),  delta = beta (v - r),  out = scale (g (q^.s) + delta (q^.k^)),
 //         s <- g s + delta k^;
-//   * outputs of a chunk are collected in LDS and written back as 16-byte vectors.
+//   * outputs of a chunk are collected in LDS and written back as 16-byte vectors;
+//   * with capture (speculative decoding: paged_ssm.rs page, DELTA_CAPTURE_INIT / _STEP) the first
+//     captured tokens of a sequence also record g and k^ (copied out of the LDS stage by the head's
+//     first block; k^ only for the first value head of each key head) and delta (by the lane that
+//     produces the column's output); the slots after them are zeroed.
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -46,6 +50,10 @@ struct SeqArgs {
     int n_vtiles;
     int n_blocks;
     int vec_ok;  // V is a multiple of the 16-byte vector width: v columns and outputs move as vectors
+    int cap;                // capture slots per sequence (0 = no capture)
+    const int32_t* counts;  // [B]
+    const int32_t* active;  // [1] or NULL
+    float* capsule;         // [B, cap*(H + HQ*K + H*V)]
 };
 
 template <typename T, int K, int LPC, int CPL, int NW, bool PREP>
@@ -129,6 +137,14 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     const float a_bias = (!PREP && p.a && softplus) ? p.dt_bias[h] : 0.0f;
     const TS* qkv = static_cast<const TS*>(p.qkv);
     TS* outp = static_cast<TS*>(p.out);
+
+    int captured = 0;  // tokens recorded (0 without capture)
+    CaptureRow crow{};
+    if (p.cap > 0) {
+        captured = captured_tokens(p.counts, p.active, p.cap, b, end - start);
+        crow = capture_row(p.capsule, b, p.cap, p.H, p.HQ, K, p.V);
+    }
+    const bool cap_d = gl < CPL && v0 + cw + gl < p.V;  // this lane records delta of its output column
 
     // ---- staging: global -> registers (fetch) and registers -> LDS (commit) ------------------------
     auto fetch = [&](int t0, int n, Fetch<PASSES, VPASSES>& f) {
@@ -280,6 +296,14 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
             const bool more = c + 1 < nchunks;
             if (more) fetch(t0 + TC, min(TC, end - t0 - TC), f);
 
+            if (t0 - start < captured && vt == 0) {
+                // g and k^ of the chunk's recorded tokens, straight from the LDS stage
+                const int nc = min(n, captured - (t0 - start));
+                for (int idx = tid; idx < nc; idx += NT) *crow.g(t0 - start + idx, h) = sg[buf][idx];
+                if (h == kh * p.G)
+                    for (int idx = tid; idx < nc * K; idx += NT)
+                        crow.k(t0 - start + idx / K, kh)[idx % K] = sk[buf][idx / K][idx % K];
+            }
             for (int i = 0; i < n; ++i) {
                 float q[EPL], k[EPL];
 #pragma unroll
@@ -309,16 +333,20 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
                     pk[cc] = group_sum<LPC>(pk[cc]);
                     pq[cc] = group_sum<LPC>(pq[cc]);
                 }
-                float mine = 0.0f;
+                float mine = 0.0f, dmine = 0.0f;
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) {
                     const float d = beta * (sv[buf][i][cw + cc] - rmul * (g * pk[cc]));
                     const float o = p.scale * fmaf(g, pq[cc], d * qk);
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) s[cc][e] = fmaf(d, k[e], g * s[cc][e]);
-                    if (gl == cc) mine = o;
+                    if (gl == cc) {
+                        mine = o;
+                        dmine = d;
+                    }
                 }
                 if (gl < CPL) so[i][cw + gl] = mine;
+                if (cap_d && t0 + i - start < captured) crow.d(t0 + i - start, h)[v0 + cw + gl] = dmine;
             }
             __syncthreads();  // outputs of the chunk are complete in LDS
             for (int idx = tid; idx < n * VPT; idx += NT) {
@@ -353,6 +381,20 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
             for (int i = 0; i < EPL / 4; ++i)
                 *reinterpret_cast<f32x4*>(sp + 4 * (gl + LPC * i)) =
                     f32x4{s[c][4 * i], s[c][4 * i + 1], s[c][4 * i + 2], s[c][4 * i + 3]};
+        }
+    }
+
+    if (p.cap > 0) {
+        // zeros in the slots after the recorded tokens: g and k^ by the head's first block, delta
+        // for the block's own columns
+        for (int i = captured; i < p.cap; ++i) {
+            if (vt == 0) {
+                if (tid == 0) *crow.g(i, h) = 0.0f;
+                if (h == kh * p.G)
+                    for (int j = tid; j < K; j += NT) crow.k(i, kh)[j] = 0.0f;
+            }
+            for (int j = tid; j < BC; j += NT)
+                if (v0 + j < p.V) crow.d(i, h)[v0 + j] = 0.0f;
         }
     }
 }
@@ -436,6 +478,10 @@ hipError_t launch_scan_seq(const ScanLaunch& a, hipStream_t stream) {
     p.n_vtiles = 0;
     p.n_blocks = 0;
     p.vec_ok = 0;
+    p.cap = a.cap;
+    p.counts = a.counts;
+    p.active = a.active;
+    p.capsule = a.capsule;
     if (a.qk_prep != nullptr) return launch_p<true>(p, a.qkv_dtype, stream);
     return launch_p<false>(p, a.qkv_dtype, stream);
 }

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -96,6 +96,24 @@ typedef struct gdn_conv_desc {
 gdn_status gdn_conv1d_varlen(const gdn_conv_desc *desc, const void *x, const void *w, const void *bias,
                              const void *state_in, void *y, void *state_out, const int32_t *offsets,
                              int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * gdn_conv1d_varlen_capture -- gdn_conv1d_varlen that also records, for speculative decoding, the
+ * inputs of the first tokens of each sequence (paged_ssm.rs page, CONV_CAPTURE_INIT /
+ * CONV_CAPTURE_STEP, the conv node's state_update_capacity attribute and capture_count input):
+ *     captured_b = max(0, min(counts[b], cap, len_b))
+ *     updates[b, i, :] = x[start_b + i, :]   for i < captured_b   (bit copy)
+ *     updates[b, i, :] = 0                  for captured_b <= i < cap
+ * Everything else is exactly gdn_conv1d_varlen (same outputs, bit for bit).
+ *   cap        slots per sequence, >= 1 (GDN_ERR_SHAPE otherwise); cap*C must fit an int32
+ *   counts     [B]          int32 device, required
+ *   updates    [B, cap, C]  x_dtype device, required, 16-byte aligned
+ * Malformed offsets write nothing here either (the device status word reports them).
+ * ---------------------------------------------------------------------------------------------- */
+gdn_status gdn_conv1d_varlen_capture(const gdn_conv_desc *desc, const void *x, const void *w, const void *bias,
+                                     const void *state_in, void *y, void *state_out, const int32_t *offsets,
+                                     int32_t cap, const int32_t *counts, void *updates, int32_t *dev_status,
+                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------------
  * Recurrence descriptor shared by gdn_prepare_qk_gates and gdn_scan_varlen.
@@ -187,6 +205,35 @@ gdn_status gdn_scan_varlen(const gdn_scan_desc *desc, const void *qkv, const flo
                            const float *state_in, void *out, float *state_out, const int32_t *offsets,
                            void *workspace, size_t ws_bytes, int32_t *dev_status, int32_t *path_used,
                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * gdn_scan_varlen_capture -- gdn_scan_varlen that also records, for speculative decoding, the
+ * rank-one updates of the first tokens of each sequence (paged_ssm.rs page, DELTA_CAPTURE_INIT /
+ * DELTA_CAPTURE_STEP, the recurrence node's state_update_capacity attribute, capture_count and
+ * state_update_active inputs and compact capsule output).  With
+ *     captured_b = (active != NULL && active[0] == 0) ? 0 : max(0, min(counts[b], cap, len_b))
+ * the fp32 capsule row of sequence b is [cap*H g | cap*HQ*K k^ | cap*H*V delta]:
+ *     capsule[b, i*H + h]                          = g of token start_b + i, head h
+ *     capsule[b, cap*H + (i*HQ + kh)*K + j]        = k^[j] of that token, key head kh
+ *     capsule[b, cap*(H + HQ*K) + (i*H + h)*V + v] = delta = beta*(v_t - r) of column (h, v)
+ * for i < captured_b, and 0 in every slot i >= captured_b.  Replaying
+ *     S_i = g_i * S_{i-1} + delta_i k^_i^T   (S_0 = state_in, rows v, columns over K)
+ * for i < captured_b gives the state after those tokens, which is how a speculative decoder rolls
+ * the state forward to the accepted prefix.  Outputs and final state are those of gdn_scan_varlen.
+ *   cap        slots per sequence, >= 1 (GDN_ERR_SHAPE); cap*(H + HQ*K + H*V) must fit an int32
+ *              (GDN_ERR_OVERFLOW)
+ *   counts     [B] int32 device, required
+ *   active     [1] int32 device, NULL = always active
+ *   capsule    [B, cap*(H + HQ*K + H*V)] fp32 device, required, 16-byte aligned
+ * Recorded by the DECODE and SEQ paths; AUTO never selects CHUNK for a capture and an explicit
+ * GDN_PATH_CHUNK is GDN_ERR_UNSUPPORTED.  Malformed offsets write nothing.
+ * ---------------------------------------------------------------------------------------------- */
+gdn_status gdn_scan_varlen_capture(const gdn_scan_desc *desc, const void *qkv, const float *qk_prep,
+                                   const float *gb_prep, const void *a, const void *b, const float *A_log,
+                                   const float *dt_bias, const float *state_in, void *out, float *state_out,
+                                   const int32_t *offsets, int32_t cap, const int32_t *counts, const int32_t *active,
+                                   float *capsule, void *workspace, size_t ws_bytes, int32_t *dev_status,
+                                   int32_t *path_used, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------------
  * gdn_decode_step -- a decode step in one launch: exactly gdn_conv1d_varlen(conv, x -> y) followed

@@ -32,7 +32,7 @@ def test_header_declarations_are_all_exported(abi):
 
 
 def test_version_and_status_strings(abi):
-    assert abi.lib().gdn_abi_version() == 2
+    assert abi.lib().gdn_abi_version() == 3
     for code in range(0, -10, -1):
         assert abi.status_string(code) and abi.status_string(code) != "unknown status"
     assert abi.status_string(-99) == "unknown status"
@@ -185,3 +185,51 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "libgdn.so"))
     with pytest.raises(ImportError):
         _abi.lib()
+
+
+def conv_capture(abi, desc, cap=4, counts=P, updates=P, **kw):
+    x, w, y, off = kw.get("x", P), kw.get("w", P), kw.get("y", P), kw.get("off", P)
+    return abi.lib().gdn_conv1d_varlen_capture(ctypes.byref(desc), x, w, None, None, y, None, off, cap, counts,
+                                               updates, None, None)
+
+
+@pytest.mark.parametrize(
+    "fields,kw,want",
+    [
+        ({}, dict(cap=0), "ERR_SHAPE"),
+        ({}, dict(cap=-3), "ERR_SHAPE"),
+        ({}, dict(counts=None), "ERR_NULL"),
+        ({}, dict(updates=None), "ERR_NULL"),
+        ({}, dict(updates=P + 2), "ERR_ALIGN"),
+        ({}, dict(cap=2**24), "ERR_OVERFLOW"),  # cap * C beyond int32
+        (dict(W=9), {}, "ERR_UNSUPPORTED"),  # the conv's own checks still apply
+        ({}, dict(x=None), "ERR_NULL"),
+    ],
+)
+def test_conv_capture_host_validation(abi, fields, kw, want):
+    base = dict(B=2, N=64, C=192, W=4, D=1, x_dtype=0, state_dtype=0, flags=0)
+    base.update(fields)
+    assert conv_capture(abi, abi.ConvDesc(**base), **kw) == getattr(abi, want)
+
+
+def scan_capture(abi, d, cap=4, counts=P, active=None, capsule=P, qkv=P, out=P, off=P):
+    return abi.lib().gdn_scan_varlen_capture(ctypes.byref(d), qkv, None, None, None, None, None, None, None, out,
+                                             None, off, cap, counts, active, capsule, None, 0, None, None, None)
+
+
+@pytest.mark.parametrize(
+    "fields,kw,want",
+    [
+        ({}, dict(cap=0), "ERR_SHAPE"),
+        ({}, dict(counts=None), "ERR_NULL"),
+        ({}, dict(capsule=None), "ERR_NULL"),
+        ({}, dict(capsule=P + 4), "ERR_ALIGN"),
+        ({}, dict(cap=2**24), "ERR_OVERFLOW"),  # the capsule row width must be an int32
+        (dict(path=3), {}, "ERR_UNSUPPORTED"),  # capture is not recorded by the chunked form
+        (dict(K=48), {}, "ERR_UNSUPPORTED"),  # the recurrence's own checks still apply
+        ({}, dict(off=None), "ERR_NULL"),
+        ({}, dict(out=None), "ERR_NULL"),
+    ],
+)
+def test_scan_capture_host_validation(abi, fields, kw, want):
+    assert scan_capture(abi, scan_desc(abi, **fields), **kw) == getattr(abi, want)
