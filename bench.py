@@ -7,7 +7,9 @@ token, HQ=16, H=32, K=V=128, bf16, fp32 state): gdn_conv1d_varlen then gdn_scan_
 path (--fused-step runs the single-launch gdn_decode_step instead; "also" compares the two forms at
 several batch sizes).
 The prefill workload (B=8, lengths ~ U[512, 4096]) and the long single sequence (N=65536, H=16) are
-measured too and reported in "also", with the arithmetic roofline of the path they take.
+measured too and reported in "also", with the arithmetic roofline of the path they take, and so is a
+speculative verification step (B=256 x 5 tokens) with and without the capture of 4 tokens per
+sequence.
 
 Prints ONE JSON line.  The dominant kernel (the fused step, or the recurrence in the two-call form)
 is timed with HIP events on the stream it is launched on; its algorithmic bytes per launch are the
@@ -46,6 +48,12 @@ def scan_bytes(w) -> int:
     return state + tokens
 
 
+def capsule_bytes(w, cap: int) -> int:
+    """Bytes of the fp32 capture capsule the recurrence writes: cap slots of (H decays, HQ*K keys,
+    H*V written values) per sequence."""
+    return w.B * cap * (w.H + w.HQ * w.K + w.H * w.V) * 4
+
+
 def step_bytes(w) -> int:
     """Algorithmic HBM bytes of one fused decode step (gdn_decode_step): the recurrence's bytes with
     the raw token rows in place of the conv output, plus the carried window read and written and the
@@ -77,10 +85,10 @@ def measured_traffic(record: str, sources=SCAN_SOURCES):
 class Path:
     """Device-resident inputs of one workload and one step of the hot path."""
 
-    def __init__(self, w, torch, path: str, fused_step: bool = False):
+    def __init__(self, w, torch, path: str, fused_step: bool = False, cap: int = 0):
         import gated_delta_rule_varlen_amd as gdn
 
-        self.gdn, self.torch, self.w, self.path, self.fused_step = gdn, torch, w, path, fused_step
+        self.gdn, self.torch, self.w, self.path, self.fused_step, self.cap = gdn, torch, w, path, fused_step, cap
         dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
         def dev(a, d):
@@ -104,6 +112,12 @@ class Path:
             self.state = torch.zeros((w.B, w.H, w.V, w.K), dtype=torch.float32, device="cuda")
         self.y = torch.empty_like(self.x)
         self.out = torch.empty((w.N, w.H, w.V), dtype=self.x.dtype, device="cuda")
+        if cap > 0:
+            # speculative decoding: record every token up to the capacity
+            self.counts = torch.full((w.B,), cap, dtype=torch.int32, device="cuda")
+            self.updates = torch.empty((w.B, cap, w.C), dtype=self.x.dtype, device="cuda")
+            self.capsule = torch.empty((w.B, capsule_bytes(w, cap) // (4 * w.B)), dtype=torch.float32,
+                                       device="cuda")
 
     def step(self, ev=None):
         w, gdn = self.w, self.gdn
@@ -119,6 +133,20 @@ class Path:
             if ev is not None:
                 ev[1].record()
             return "decode_step"
+        scan_kw = dict(HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=self.a, b=self.b, A_log=self.A_log, dt_bias=self.dt_bias,
+                       state_in=self.state, l2norm=w.l2norm, softplus=w.softplus, sigmoid=w.sigmoid, path=self.path,
+                       out=self.out, state_out=self.state)
+        if self.cap > 0:
+            gdn.conv1d_varlen_capture(self.x, self.conv_w, self.offsets, cap=self.cap, counts=self.counts,
+                                      updates=self.updates, bias=self.conv_b, state_in=self.conv_state,
+                                      dilation=w.D, silu=w.silu, y=self.y, state_out=self.conv_state)
+            if ev is not None:
+                ev[0].record()
+            _, _, _, used = gdn.scan_varlen_capture(self.y, self.offsets, cap=self.cap, counts=self.counts,
+                                                    capsule=self.capsule, **scan_kw)
+            if ev is not None:
+                ev[1].record()
+            return used
         gdn.conv1d_varlen(self.x, self.conv_w, self.offsets, bias=self.conv_b, state_in=self.conv_state,
                           dilation=w.D, silu=w.silu, y=self.y, state_out=self.conv_state)
         if ev is not None:
@@ -214,6 +242,30 @@ def fused_comparison(torch, batches=(1, 8, 256), steps: int = 100):
     return res
 
 
+def verify_comparison(torch, steps: int = 50, cap: int = 4):
+    """The speculative verification step (B=256 x 5 tokens, HQ=16, H=32, K=V=128, bf16) on the DECODE
+    and SEQ paths, without and with capture of cap tokens per sequence: microseconds per whole step
+    (best of 3) and the recurrence launch against HBM (its algorithmic bytes include the capsule)."""
+    import workloads
+
+    w = workloads.spec_verify()
+    res = {"workload": w.name, "cap": cap}
+    for path in ("decode", "seq"):
+        for c in (0, cap):
+            p = Path(w, torch, path, cap=c)
+            best = min((time_path(p, steps, 5) for _ in range(3)), key=lambda r: r[0])
+            ms, scan_ms, used, _ = best
+            nbytes = scan_bytes(w) + (capsule_bytes(w, c) if c else 0)
+            gbs = nbytes / (scan_ms * 1e-3) / 1e9
+            res[f"{path}_{'capture' if c else 'plain'}"] = {
+                "path": used, "step_us": round(ms * 1e3, 2), "tokens_per_s": round(w.N / (ms * 1e-3), 1),
+                "scan_us": round(scan_ms * 1e3, 2), "scan_bytes": nbytes, "scan_gbs": round(gbs, 1),
+                "scan_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+            del p
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle (conv + scan, fp64, OpenMP) on a bounded sample of the same workload:
     whole sequences, taken in order until about budget_s seconds of CPU work."""
@@ -271,7 +323,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "long", "edge_fp16", "tiny_fp32"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "long", "edge_fp16", "tiny_fp32", "verify"])
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "seq", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="skip the secondary prefill measurement")
@@ -327,7 +380,8 @@ def main():
         torch.cuda.empty_cache()
         line["also"] = {"prefill": secondary(torch, workloads.varlen_prefill(), max(3, args.steps // 10), 2),
                         "long": secondary(torch, workloads.long_single(), 3, 1),
-                        "decode_step_fused_vs_two_call": fused_comparison(torch)}
+                        "decode_step_fused_vs_two_call": fused_comparison(torch),
+                        "speculative_verify_capture": verify_comparison(torch)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

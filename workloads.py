@@ -203,12 +203,20 @@ def edge_fp16(seed: int = 105) -> Workload:
                 decay_range=(-1.0, 0.0), beta_range=(0.0, 1.0), unit_k_scan=True)
 
 
+def spec_verify(seed: int = 106) -> Workload:
+    """A speculative-decoding verification step: B=256 sequences x 5 tokens (the last accepted token
+    and 4 drafts), HQ=16, H=32, K=V=128, bf16, fp32 state and conv window."""
+    return make(name="verify_b256_t5_h32_k128", seed=seed, lengths=[5] * 256, HQ=16, H=32, K=128, V=128, W=4,
+                D=1, io="bf16", conv_state_dtype="f32", conv_state_std=1.0, state_std=0.1)
+
+
 NAMED = {
     "tiny_fp32": tiny_fp32,
     "decode": decode_step,
     "prefill": varlen_prefill,
     "long": long_single,
     "edge_fp16": edge_fp16,
+    "verify": spec_verify,
 }
 
 # Offsets patterns that every entry point must reject by writing nothing.
