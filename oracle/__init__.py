@@ -53,7 +53,7 @@ def lib():
             L.gdn_oracle_conv_capture.restype = i32
             L.gdn_oracle_prepare.argtypes = [i32] * 10 + [vp] * 7
             L.gdn_oracle_prepare.restype = None
-            L.gdn_oracle_scan.argtypes = [i32] * 12 + [ctypes.c_double] + [vp] * 11 + [i32, vp]
+            L.gdn_oracle_scan.argtypes = [i32] * 13 + [ctypes.c_double] + [vp] * 11 + [i32, vp]
             L.gdn_oracle_scan.restype = i32
             L.gdn_oracle_threads.argtypes = []
             L.gdn_oracle_threads.restype = i32
@@ -149,9 +149,9 @@ def conv_capture(x, offsets, counts, *, cap, x_dtype):
 
 def scan(qkv, offsets, *, HQ, H, K, V, qkv_dtype, gate_dtype=None, a=None, b=None, A_log=None,
          dt_bias=None, state_in=None, l2norm=True, softplus=True, sigmoid=True, scale=0.0, retrieve=True,
-         counts=None, active=None, cap=0):
+         gate_per_key=False, counts=None, active=None, cap=0):
     """Gated delta-rule recurrence.  retrieve=False drops the retrieval term (the linear and gated
-    update rules).  Returns (out [N,H,V] f64, state_out [B,H,V,K] f64), plus the capture capsule
+    update rules); gate_per_key=True takes a [N,H,K] decay input, one decay per key channel.  Returns (out [N,H,V] f64, state_out [B,H,V,K] f64), plus the capture capsule
     [B, cap*(H + HQ*K + H*V)] f64 when counts is given; None when the offsets are malformed."""
     qd = DTYPE_CODES[qkv_dtype]
     gd = DTYPE_CODES[gate_dtype or qkv_dtype]
@@ -173,11 +173,14 @@ def scan(qkv, offsets, *, HQ, H, K, V, qkv_dtype, gate_dtype=None, a=None, b=Non
         act = None if active is None else np.ascontiguousarray(active, dtype=np.int32)
         capsule = np.zeros((B, cap * (H + HQ * K + H * V)), np.float64)
     rc = lib().gdn_oracle_scan(B, N, HQ, H, K, V, qd, gd, int(bool(l2norm)), int(bool(softplus)),
-                               int(bool(sigmoid)), int(bool(retrieve)), float(scale), _ptr(qkv), _ptr(a), _ptr(b),
+                               int(bool(sigmoid)), int(bool(retrieve)), int(bool(gate_per_key)), float(scale),
+                               _ptr(qkv), _ptr(a), _ptr(b),
                                _ptr(A_log), _ptr(dt_bias), _ptr(state_in), _ptr(off), _ptr(out), _ptr(st),
                                _ptr(cnt), _ptr(act), int(cap), _ptr(capsule))
     if rc == 1:
         return None
+    if rc == 3:
+        raise ValueError("a per-key-channel gate is not combined with a capture")
     if rc != 0:
         raise MemoryError("oracle scan could not allocate its buffers")
     return (out, st) if counts is None else (out, st, capsule)

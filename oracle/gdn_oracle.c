@@ -12,6 +12,7 @@
  *   [prep]    same page -- kernel string DELTA_PREPARE
  *   [delta]   same page -- kernel string DELTA and host fn delta()
  *   [rates]   mlx-c-rust, compile/gated_delta_rate_activation.rs -- the rate-activation graph builder
+ *   [thunk]   rlx-cpu 0.2.14, thunk/types.rs -- Thunk::GatedDeltaNet (its gate_per_channel field)
  *
  * Readings taken where the pages are silent (each is listed in the design notes):
  *   - offsets are valid iff offsets[0]==0, offsets[B]==N and offsets never decrease; an invalid
@@ -240,18 +241,26 @@ int gdn_oracle_conv_capture(int B, int N, int C, int cap, int x_dtype, const voi
  * retrieve == 0 drops the retrieval term (delta = beta * v_t): the "linear" and "gated" update rules
  * of the pages' update_rule attribute, which the DELTA kernel string compiles with RETRIEVE = 0
  * (the rule's decay side is the presence of the decay input, as for the other rules).
+ * gate_per_key != 0 gives every key channel its own decay (the rlx-cpu thunk/types.rs page,
+ * Thunk::GatedDeltaNet with gate_per_channel: g shaped like the keys): a is [N,H,K] and the first step
+ * becomes s[i] <- g_i * s[i] with g_i = decay_gate(a[t,h,i]) (A_log and dt_bias stay per head);
+ * in matrix form S <- S diag(g) (I - beta k^ k^T) + beta v k^T.  Not combined with a capture.
  * scale <= 0 selects 1/sqrt(K) (host fn delta(): a zero scale attribute means 1/sqrt(K)).
  * Layouts: qkv [N, 2*HQ*K + H*V]; out [N,H,V]; state [B,H,V,K] float32 in, fp64 out.
  * Returns 0 on success, 1 when the offsets are malformed (then nothing is written), 2 when out of
- * memory.  Parallel over independent (b, h) pairs with OpenMP when built with it. */
+ * memory, 3 for a per-key gate with a capture.  Parallel over independent (b, h) pairs with OpenMP
+ * when built with it. */
 int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, int gate_dtype,
-                    int l2norm, int softplus, int sigmoid, int retrieve, double scale, const void *qkv,
+                    int l2norm, int softplus, int sigmoid, int retrieve, int gate_per_key, double scale,
+                    const void *qkv,
                     const void *a, const void *b, const float *A_log, const float *dt_bias,
                     const float *state_in, const int32_t *offsets, double *out, double *state_out,
                     const int32_t *counts, const int32_t *active, int cap, double *capsule) {
     if (!gdn_oracle_offsets_valid(offsets, B, N)) return 1;
+    if (gate_per_key && a && capsule) return 3;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)K);
     const size_t C = (size_t)2 * HQ * K + (size_t)H * V;
+    const void *a_head = gate_per_key ? NULL : a; /* per-head decay input, evaluated by prepare */
     const int G = H / HQ;
     double *qk = (double *)malloc(sizeof(double) * ((size_t)2 * N * HQ * K + 1));
     double *gb = (double *)malloc(sizeof(double) * ((size_t)2 * N * H + 1));
@@ -260,7 +269,7 @@ int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, in
         free(gb);
         return 2;
     }
-    gdn_oracle_prepare(N, HQ, H, K, V, qkv_dtype, gate_dtype, l2norm, softplus, sigmoid, qkv, a, b,
+    gdn_oracle_prepare(N, HQ, H, K, V, qkv_dtype, gate_dtype, l2norm, softplus, sigmoid, qkv, a_head, b,
                        A_log, dt_bias, qk, gb);
     int failed = 0;
 #ifdef _OPENMP
@@ -298,7 +307,13 @@ int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, in
                 const double g = gb[(size_t)t * H + h];
                 const double beta = gb[((size_t)N + t) * H + h];
                 const double vt = dec(qkv, qkv_dtype, (size_t)t * C + (size_t)2 * HQ * K + (size_t)h * V + v);
-                for (int i = 0; i < K; ++i) s[i] *= g;
+                if (gate_per_key && a) {
+                    for (int i = 0; i < K; ++i)
+                        s[i] *= decay_gate(dec(a, gate_dtype, ((size_t)t * H + h) * K + i), softplus,
+                                           softplus ? (double)A_log[h] : 0.0, softplus ? (double)dt_bias[h] : 0.0);
+                } else {
+                    for (int i = 0; i < K; ++i) s[i] *= g;
+                }
                 double r = 0.0;
                 if (retrieve)
                     for (int i = 0; i < K; ++i) r += kk[i] * s[i];
