@@ -9,7 +9,7 @@ several batch sizes).
 The prefill workload (B=8, lengths ~ U[512, 4096]) and the long single sequence (N=65536, H=16) are
 measured too and reported in "also", with the arithmetic roofline of the path they take, and so is a
 speculative verification step (B=256 x 5 tokens) with and without the capture of 4 tokens per
-sequence.
+sequence, and both steps with one decay per key channel instead of one per head.
 
 Prints ONE JSON line.  The dominant kernel (the fused step, or the recurrence in the two-call form)
 is timed with HIP events on the stream it is launched on; its algorithmic bytes per launch are the
@@ -85,10 +85,11 @@ def measured_traffic(record: str, sources=SCAN_SOURCES):
 class Path:
     """Device-resident inputs of one workload and one step of the hot path."""
 
-    def __init__(self, w, torch, path: str, fused_step: bool = False, cap: int = 0):
+    def __init__(self, w, torch, path: str, fused_step: bool = False, cap: int = 0, gate_per_key: bool = False):
         import gated_delta_rule_varlen_amd as gdn
 
         self.gdn, self.torch, self.w, self.path, self.fused_step, self.cap = gdn, torch, w, path, fused_step, cap
+        self.gate_per_key = gate_per_key
         dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
         def dev(a, d):
@@ -106,6 +107,11 @@ class Path:
             self.conv_state = torch.zeros((w.B, w.C, w.L), dtype=dt[w.conv_state_dtype], device="cuda")
         self.offsets = torch.from_numpy(w.offsets).cuda()
         self.a, self.b = dev(w.a, w.gate_dtype), dev(w.b, w.gate_dtype)
+        if gate_per_key:
+            # one decay input per key channel, drawn like the per-head ones
+            rng = np.random.default_rng(7)
+            a_pk = rng.standard_normal((w.N, w.H, w.K), dtype=np.float32)
+            self.a = torch.from_numpy(a_pk).cuda().to(self.b.dtype if self.b is not None else torch.float32)
         self.A_log, self.dt_bias = dev(w.A_log, "f32"), dev(w.dt_bias, "f32")
         self.state = dev(w.state, "f32")
         if self.state is None:
@@ -136,6 +142,8 @@ class Path:
         scan_kw = dict(HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=self.a, b=self.b, A_log=self.A_log, dt_bias=self.dt_bias,
                        state_in=self.state, l2norm=w.l2norm, softplus=w.softplus, sigmoid=w.sigmoid, path=self.path,
                        out=self.out, state_out=self.state)
+        if self.gate_per_key:
+            scan_kw["gate_per_key"] = True
         if self.cap > 0:
             gdn.conv1d_varlen_capture(self.x, self.conv_w, self.offsets, cap=self.cap, counts=self.counts,
                                       updates=self.updates, bias=self.conv_b, state_in=self.conv_state,
@@ -151,10 +159,7 @@ class Path:
                           dilation=w.D, silu=w.silu, y=self.y, state_out=self.conv_state)
         if ev is not None:
             ev[0].record()
-        _, _, used = gdn.scan_varlen(self.y, self.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=self.a, b=self.b,
-                                     A_log=self.A_log, dt_bias=self.dt_bias, state_in=self.state,
-                                     l2norm=w.l2norm, softplus=w.softplus, sigmoid=w.sigmoid, path=self.path,
-                                     out=self.out, state_out=self.state)
+        _, _, used = gdn.scan_varlen(self.y, self.offsets, **scan_kw)
         if ev is not None:
             ev[1].record()
         return used
@@ -261,6 +266,27 @@ def verify_comparison(torch, steps: int = 50, cap: int = 4):
                 "path": used, "step_us": round(ms * 1e3, 2), "tokens_per_s": round(w.N / (ms * 1e-3), 1),
                 "scan_us": round(scan_ms * 1e3, 2), "scan_bytes": nbytes, "scan_gbs": round(gbs, 1),
                 "scan_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+            del p
+    torch.cuda.empty_cache()
+    return res
+
+
+def per_key_comparison(torch, steps: int = 50):
+    """The decode step (B=256) and the verification step (B=256 x 5 tokens) with one decay per head
+    and with one decay per key channel ([N, H, K] decay input): microseconds per whole step (best of
+    3) and the recurrence launch against HBM (the per-key form also reads the [N, H, K] decays)."""
+    import workloads
+
+    res = {}
+    for w in (workloads.decode_step(), workloads.spec_verify()):
+        for pk in (False, True):
+            p = Path(w, torch, "auto", gate_per_key=pk)
+            ms, scan_ms, used, _ = min((time_path(p, steps, 5) for _ in range(3)), key=lambda r: r[0])
+            nbytes = scan_bytes(w) + (w.N * w.H * (w.K - 1) * sizeof(w.gate_dtype) if pk else 0)
+            gbs = nbytes / (scan_ms * 1e-3) / 1e9
+            res[f"{w.name}_{'per_key' if pk else 'per_head'}"] = {
+                "path": used, "step_us": round(ms * 1e3, 2), "scan_us": round(scan_ms * 1e3, 2),
+                "scan_gbs": round(gbs, 1), "scan_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
             del p
     torch.cuda.empty_cache()
     return res
@@ -381,7 +407,8 @@ def main():
         line["also"] = {"prefill": secondary(torch, workloads.varlen_prefill(), max(3, args.steps // 10), 2),
                         "long": secondary(torch, workloads.long_single(), 3, 1),
                         "decode_step_fused_vs_two_call": fused_comparison(torch),
-                        "speculative_verify_capture": verify_comparison(torch)}
+                        "speculative_verify_capture": verify_comparison(torch),
+                        "per_key_decay": per_key_comparison(torch)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

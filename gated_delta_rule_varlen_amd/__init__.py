@@ -104,9 +104,10 @@ def conv1d_varlen_capture(x: torch.Tensor, weight: torch.Tensor, offsets: torch.
     return y, state_out, updates
 
 
-def _scan_desc(qkv, B, HQ, H, K, V, gate, l2norm, softplus, sigmoid, scale, path, retrieve=True):
+def _scan_desc(qkv, B, HQ, H, K, V, gate, l2norm, softplus, sigmoid, scale, path, retrieve=True,
+               gate_per_key=False):
     flags = (_abi.L2NORM if l2norm else 0) | (_abi.SOFTPLUS if softplus else 0) | (_abi.SIGMOID if sigmoid else 0)
-    flags |= 0 if retrieve else _abi.NO_RETRIEVE
+    flags |= (0 if retrieve else _abi.NO_RETRIEVE) | (_abi.GATE_PER_KEY if gate_per_key else 0)
     qd = _code(qkv, "qkv")
     gd = _code(gate, "gate inputs") if gate is not None else qd
     return _abi.ScanDesc(B, qkv.shape[0], HQ, H, K, V, qd, gd, flags, float(scale), _abi.PATH_CODES[path])
@@ -142,9 +143,11 @@ def scan_workspace_bytes(qkv: torch.Tensor, B: int, *, HQ, H, K, V, l2norm=True,
 def scan_varlen(qkv: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K: int, V: int, a=None, b=None,
                 A_log=None, dt_bias=None, state_in=None, qk_prep=None, gb_prep=None, l2norm=True, softplus=True,
                 sigmoid=True, scale: float = 0.0, path: str = "auto", out=None, state_out=None,
-                write_state: bool = True, workspace=None, dev_status=None, retrieve: bool = True):
+                write_state: bool = True, workspace=None, dev_status=None, retrieve: bool = True,
+                gate_per_key: bool = False):
     """Gated delta-rule recurrence over offset-packed sequences (gdn_scan_varlen).  retrieve=False
-    selects the linear/gated update rules (no retrieval term).
+    selects the linear/gated update rules (no retrieval term); gate_per_key=True takes a [N, H, K]
+    decay input, one decay per key channel.
     Returns (out [N, H, V], state_out [B, H, V, K] fp32 or None, path name that ran)."""
     N = qkv.shape[0]
     B = offsets.numel() - 1
@@ -152,7 +155,8 @@ def scan_varlen(qkv: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K:
         out = torch.empty((N, H, V), dtype=qkv.dtype, device=qkv.device)
     if state_out is None and write_state:
         state_out = torch.empty((B, H, V, K), dtype=torch.float32, device=qkv.device)
-    d = _scan_desc(qkv, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, path, retrieve)
+    d = _scan_desc(qkv, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, path, retrieve,
+                   gate_per_key)
     if workspace is None and path in ("auto", "chunk"):
         n = ctypes.c_size_t(0)
         _check(lib().gdn_scan_workspace_bytes(ctypes.byref(d), ctypes.byref(n)), "gdn_scan_workspace_bytes")

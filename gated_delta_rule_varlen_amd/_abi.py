@@ -15,7 +15,7 @@ ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_OFFSETS = -6, -7, -8, -9
 F32, BF16, F16 = 0, 1, 2
 # flags
 CONV_SILU = 1
-L2NORM, SOFTPLUS, SIGMOID, NO_RETRIEVE = 1, 2, 4, 8
+L2NORM, SOFTPLUS, SIGMOID, NO_RETRIEVE, GATE_PER_KEY = 1, 2, 4, 8, 16
 # gdn_path
 PATH_AUTO, PATH_DECODE, PATH_SEQ, PATH_CHUNK = 0, 1, 2, 3
 PATH_NAMES = {PATH_AUTO: "auto", PATH_DECODE: "decode", PATH_SEQ: "seq", PATH_CHUNK: "chunk"}

@@ -32,7 +32,8 @@ gdn_status check_scan_desc(const gdn_scan_desc* d) {
     if (d->H % d->HQ != 0 || d->K > 256) return GDN_ERR_SHAPE;
     if (!dtype_ok(d->qkv_dtype)) return GDN_ERR_DTYPE;
     if (d->gate_dtype != GDN_F32 && d->gate_dtype != d->qkv_dtype) return GDN_ERR_DTYPE;
-    if (d->flags & ~(uint32_t)(GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID | GDN_NO_RETRIEVE)) return GDN_ERR_UNSUPPORTED;
+    if (d->flags & ~(uint32_t)(GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID | GDN_NO_RETRIEVE | GDN_GATE_PER_KEY))
+        return GDN_ERR_UNSUPPORTED;
     const long long C = 2ll * d->HQ * d->K + (long long)d->H * d->V;
     if (C > INT_MAX) return GDN_ERR_OVERFLOW;
     if ((long long)d->B * d->H > INT_MAX) return GDN_ERR_OVERFLOW;
@@ -45,11 +46,12 @@ gdn_status check_scan_desc(const gdn_scan_desc* d) {
 // The chunked path sums log-decays, so it needs every decay finite and positive (a decay input with
 // the softplus gate), and it relies on normalised keys for a well-conditioned (I + A); it computes
 // the gates and norms itself, so it runs on fused inputs only; its algebra is that of the rules
-// with the retrieval term.  Built for bf16/fp16 I/O with K = V = 64 or 128.  Capture is recorded
-// by the token-sequential paths only.
+// with the retrieval term and one decay per head.  Built for bf16/fp16 I/O with K = V = 64 or 128.
+// Capture is recorded by the token-sequential paths only.
 bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay, bool capture) {
     return !prepared && has_decay && !capture && (d->flags & GDN_SOFTPLUS) && (d->flags & GDN_L2NORM) &&
-           !(d->flags & GDN_NO_RETRIEVE) && gdn::chunked_shape_supported(d->K, d->V, d->qkv_dtype);
+           !(d->flags & (GDN_NO_RETRIEVE | GDN_GATE_PER_KEY)) &&
+           gdn::chunked_shape_supported(d->K, d->V, d->qkv_dtype);
 }
 
 // AUTO: DECODE for at most two tokens per sequence on average; CHUNK when eligible, the average
@@ -154,6 +156,7 @@ gdn_status gdn_prepare_qk_gates(const gdn_scan_desc* d, const void* qkv, const v
                                 hipStream_t stream) {
     const gdn_status st = check_scan_desc(d);
     if (st != GDN_OK) return st;
+    if (d->flags & GDN_GATE_PER_KEY) return GDN_ERR_UNSUPPORTED;  // its gate plane is one decay per head
     if (qk_out == nullptr && gb_out == nullptr) return GDN_ERR_NULL;
     if (d->N > 0 && qkv == nullptr && qk_out != nullptr) return GDN_ERR_NULL;
     if (a != nullptr && (d->flags & GDN_SOFTPLUS) && (A_log == nullptr || dt_bias == nullptr)) return GDN_ERR_NULL;
@@ -207,6 +210,11 @@ gdn_status scan_call(const gdn_scan_desc* d, const void* qkv, const float* qk_pr
     const bool prepared = qk_prep != nullptr;
     if (!prepared && a != nullptr && (d->flags & GDN_SOFTPLUS) && (A_log == nullptr || dt_bias == nullptr))
         return GDN_ERR_NULL;
+    if (d->flags & GDN_GATE_PER_KEY) {
+        // decays per key channel are evaluated in-kernel from raw inputs; nothing records them
+        if (prepared || cap > 0) return GDN_ERR_UNSUPPORTED;
+        if (misaligned(a)) return GDN_ERR_ALIGN;
+    }
     if (misaligned(qkv) || misaligned(qk_prep) || misaligned(gb_prep) || misaligned(state_in) || misaligned(out) ||
         misaligned(state_out) || misaligned(workspace))
         return GDN_ERR_ALIGN;
@@ -307,6 +315,7 @@ gdn_status gdn_decode_step(const gdn_conv_desc* cd, const gdn_scan_desc* sd, con
     // the recurrence on its DECODE path with fused inputs
     if (sd->N > sd->B) return GDN_ERR_UNSUPPORTED;
     if (sd->path != GDN_PATH_AUTO && sd->path != GDN_PATH_DECODE) return GDN_ERR_UNSUPPORTED;
+    if (sd->flags & GDN_GATE_PER_KEY) return GDN_ERR_UNSUPPORTED;
     if (!gdn::decode_step_supported(sd->K, sd->V, sd->H / sd->HQ, cd->W, cd->D)) return GDN_ERR_UNSUPPORTED;
     if (sd->N > 0 && (x == nullptr || out == nullptr)) return GDN_ERR_NULL;
     if (a != nullptr && (sd->flags & GDN_SOFTPLUS) && (A_log == nullptr || dt_bias == nullptr)) return GDN_ERR_NULL;

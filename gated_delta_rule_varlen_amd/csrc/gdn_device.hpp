@@ -141,6 +141,13 @@ __device__ __forceinline__ int find_sequence(const int32_t* __restrict__ offsets
     return lo;
 }
 
+// Four consecutive gate inputs (element type T, the qkv type, or fp32), widened to fp32.
+template <typename T>
+__device__ __forceinline__ f32x4 load4_gate(const void* p, int gate_dtype, size_t i) {
+    if (gate_dtype == GDN_F32) return load4<F32>(static_cast<const float*>(p) + i);
+    return load4<T>(static_cast<const typename T::storage*>(p) + i);
+}
+
 // Tokens of a sequence of length len recorded by a capture of cap slots: min(counts[b], cap, len),
 // at least 0, and 0 when the device flag active is given and reads 0.
 __device__ __forceinline__ int captured_tokens(const int32_t* counts, const int32_t* active, int cap, int b,

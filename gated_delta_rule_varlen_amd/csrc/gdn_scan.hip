@@ -26,6 +26,10 @@
 //     token operands first, then the state columns of a group with all their loads in flight, each
 //     column reduced, updated, written back and its output taken in turn, so reads and writes of
 //     the state interleave.  Same arithmetic in the same order, so the results are bit-identical;
+//   * with a per-key-channel decay (GDN_GATE_PER_KEY; "PK" instances) thread i of the block
+//     evaluates the decay of key channel i once per token into LDS (every wave of a block serves
+//     the same head), and each lane decays its state slice before the two dot products
+//     (s' = g o s), so r and the readout use the decayed state directly;
 //   * with capture (speculative decoding: paged_ssm.rs page, DELTA_CAPTURE_INIT / _STEP) the first
 //     captured tokens of a sequence also record g (one lane of the head's first block), k^ (the
 //     first lane group of that block, for the first value head of each key head) and delta (the
@@ -85,18 +89,19 @@ __device__ __forceinline__ void st_state(float* p, f32x4 v) {
 }
 
 // Operands of one token as seen by one lane.
-template <int EPL, int CPL>
+template <int EPL, int CPL, bool PK>
 struct TokenOps {
     float q[EPL];
     float k[EPL];
     float v[CPL];
-    float ga;  // prepared: g; fused: raw decay input (0 when absent)
-    float gb;  // prepared: beta; fused: raw rate input (0 when absent)
+    float ga;               // prepared: g; fused: raw decay input (0 when absent; unused with PK)
+    float gb;               // prepared: beta; fused: raw rate input (0 when absent)
+    float gkr;              // PK: raw decay input of key channel threadIdx.x (threads below K)
 };
 
-template <typename T, int K, int LPC, int CPL, bool PREP>
+template <typename T, int K, int LPC, int CPL, bool PREP, bool PK>
 __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int kh, int gl, int vbase,
-                                           TokenOps<K / LPC, CPL>& o) {
+                                           TokenOps<K / LPC, CPL, PK>& o) {
     constexpr int EPL = K / LPC;
     using TS = typename T::storage;
     if constexpr (PREP) {
@@ -129,7 +134,12 @@ __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int 
             }
         }
         const size_t gi = (size_t)t * p.H + h;
-        o.ga = p.a ? load_any(p.a, p.gate_dtype, gi) : 0.0f;
+        if constexpr (PK) {
+            o.ga = 0.0f;
+            o.gkr = (int)threadIdx.x < K ? load_any(p.a, p.gate_dtype, gi * K + threadIdx.x) : 0.0f;
+        } else {
+            o.ga = p.a ? load_any(p.a, p.gate_dtype, gi) : 0.0f;
+        }
         o.gb = p.b ? load_any(p.b, p.gate_dtype, gi) : 0.0f;
     }
     const TS* vp = static_cast<const TS*>(p.qkv) + (size_t)t * p.C + (size_t)2 * p.HQ * K + (size_t)h * p.V + vbase;
@@ -137,13 +147,17 @@ __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int 
     for (int c = 0; c < CPL; ++c) o.v[c] = (vbase + c < p.V) ? to_f32<T>(vp[c]) : 0.0f;
 }
 
-template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT>
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK>
 __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
+    static_assert(!(PK && PREP), "the per-key decay is evaluated in-kernel from raw inputs");
     constexpr int EPL = K / LPC;  // state elements per lane per column
     static_assert(EPL % 4 == 0, "whole 16-byte chunks per lane");
     constexpr int GPW = 64 / LPC;  // lane groups per wave
     constexpr int WC = GPW * CPL;  // columns per wave; a block covers NW * WC
     using TS = typename T::storage;
+
+    static_assert(!PK || 64 * NW >= K, "one thread per key channel stages the decays");
+    __shared__ __align__(16) float gks[PK ? K : 1];  // PK: the token's decay per key channel
 
     const bool malformed = offsets_malformed(p.offsets, p.B, p.N);
     report_status(p.dev_status, malformed);
@@ -212,8 +226,8 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
         constexpr int PD = GDN_DECODE_STREAM < CPL ? GDN_DECODE_STREAM : CPL;
         const bool full_tile = (vt * NW + NW) * WC <= p.V;
         if (end - start == 1 && full_tile && p.state_in != nullptr && p.state_out != nullptr) {
-            TokenOps<EPL, CPL> tok;
-            load_token<T, K, LPC, CPL, PREP>(p, start, h, kh, gl, vbase, tok);
+            TokenOps<EPL, CPL, PK> tok;
+            load_token<T, K, LPC, CPL, PREP, PK>(p, start, h, kh, gl, vbase, tok);
             f32x4 ring[PD + 1][EPL / 4];
             auto load_col = [&](int c, f32x4 (&dst)[EPL / 4]) {
                 const float* sp = p.state_in + (col0 + vbase + c) * K;
@@ -228,9 +242,21 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                 beta = tok.gb;
             } else {
                 g = 1.0f;
-                if (p.a) g = softplus ? expf(a_mul * softplus_f(tok.ga + a_bias)) : expf(tok.ga);
+                if (!PK && p.a) g = softplus ? expf(a_mul * softplus_f(tok.ga + a_bias)) : expf(tok.ga);
                 beta = 1.0f;
                 if (p.b) beta = sigmoid ? 1.0f / (1.0f + expf(-tok.gb)) : tok.gb;
+            }
+            float gk[PK ? EPL : 1];  // PK: the lane's channel decays (the state is decayed before the dots)
+            if constexpr (PK) {
+                if ((int)threadIdx.x < K)
+                    gks[threadIdx.x] = softplus ? expf(a_mul * softplus_f(tok.gkr + a_bias)) : expf(tok.gkr);
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < EPL / 4; ++i) {
+                    const f32x4 gv = *reinterpret_cast<const f32x4*>(&gks[4 * (gl + LPC * i)]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gk[4 * i + e] = gv[e];
+                }
             }
             float qk = 0.0f, nq = 0.0f, nk = 0.0f;
 #pragma unroll
@@ -254,7 +280,13 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 if (c + PD < CPL) load_col(c + PD, ring[(c + PD) % (PD + 1)]);
-                const f32x4(&sc)[EPL / 4] = ring[c % (PD + 1)];
+                f32x4(&sc)[EPL / 4] = ring[c % (PD + 1)];
+                if constexpr (PK) {
+#pragma unroll
+                    for (int i = 0; i < EPL / 4; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sc[i][e] *= gk[4 * i + e];
+                }
                 float pk = 0.0f, pq = 0.0f;
 #pragma unroll
                 for (int i = 0; i < EPL / 4; ++i)
@@ -274,7 +306,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                 for (int i = 0; i < EPL / 4; ++i) {
                     f32x4 nv;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) nv[e] = fmaf(dk, tok.k[4 * i + e], g * sc[i][e]);
+                    for (int e = 0; e < 4; ++e) nv[e] = fmaf(dk, tok.k[4 * i + e], PK ? sc[i][e] : g * sc[i][e]);
                     st_state<NT>(sp + 4 * (gl + LPC * i), nv);
                 }
                 if (gl == c) {
@@ -304,11 +336,11 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
         }
     }
 
-    TokenOps<EPL, CPL> cur;
-    if (start < end) load_token<T, K, LPC, CPL, PREP>(p, start, h, kh, gl, vbase, cur);
+    TokenOps<EPL, CPL, PK> cur;
+    if (start < end) load_token<T, K, LPC, CPL, PREP, PK>(p, start, h, kh, gl, vbase, cur);
     for (int t = start; t < end; ++t) {
-        TokenOps<EPL, CPL> nxt;
-        if (t + 1 < end) load_token<T, K, LPC, CPL, PREP>(p, t + 1, h, kh, gl, vbase, nxt);
+        TokenOps<EPL, CPL, PK> nxt;
+        if (t + 1 < end) load_token<T, K, LPC, CPL, PREP, PK>(p, t + 1, h, kh, gl, vbase, nxt);
 
         float g, beta;
         if constexpr (PREP) {
@@ -316,9 +348,25 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
             beta = cur.gb;
         } else {
             g = 1.0f;
-            if (p.a) g = softplus ? expf(a_mul * softplus_f(cur.ga + a_bias)) : expf(cur.ga);
+            if (!PK && p.a) g = softplus ? expf(a_mul * softplus_f(cur.ga + a_bias)) : expf(cur.ga);
             beta = 1.0f;
             if (p.b) beta = sigmoid ? 1.0f / (1.0f + expf(-cur.gb)) : cur.gb;
+        }
+        if constexpr (PK) {
+            // decay the lane's state slice channel by channel (decays staged once per block); g
+            // stays 1 below.  The loop is block-uniform, so every thread reaches both barriers.
+            __syncthreads();  // the previous token's decays have been read
+            if ((int)threadIdx.x < K)
+                gks[threadIdx.x] = softplus ? expf(a_mul * softplus_f(cur.gkr + a_bias)) : expf(cur.gkr);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < EPL / 4; ++i) {
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(&gks[4 * (gl + LPC * i)]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) s[c][4 * i + e] *= gv[e];
+            }
         }
 
         float pk[CPL], pq[CPL];
@@ -363,7 +411,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
             const float dk = delta * rk;  // coefficient of the raw k
             const float o = oscale * fmaf(g, pq[c], dk * qk);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) s[c][e] = fmaf(dk, cur.k[e], g * s[c][e]);
+            for (int e = 0; e < EPL; ++e) s[c][e] = fmaf(dk, cur.k[e], PK ? s[c][e] : g * s[c][e]);
             if (gl == c) {
                 mine = o;
                 dmine = delta;
@@ -388,14 +436,15 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
     if (p.cap > 0) capture_zeros();
 }
 
-template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT>
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK>
 hipError_t launch_tile(ScanArgs p, hipStream_t stream) {
     constexpr int BC = (64 / LPC) * CPL * NW;  // columns per block
     p.n_vtiles = (p.V + BC - 1) / BC;
     const long long blocks = (long long)p.B * p.H * p.n_vtiles;
     if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
     p.n_blocks = (int)blocks;
-    hipLaunchKernelGGL((scan_kernel<T, K, LPC, CPL, NW, PREP, NT>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((scan_kernel<T, K, LPC, CPL, NW, PREP, NT, PK>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream,
+                       p);
     return hipGetLastError();
 }
 
@@ -407,30 +456,30 @@ hipError_t launch_tile(ScanArgs p, hipStream_t stream) {
 #ifndef GDN_DECODE_NW
 #define GDN_DECODE_NW 4
 #endif
-template <typename T, int K, bool PREP>
+template <typename T, int K, bool PREP, bool PK>
 hipError_t launch_k(const ScanArgs& p, hipStream_t stream) {
     constexpr int LPC = K >= 64 ? 16 : 8;
     constexpr int CPL = K >= 256 ? (GDN_DECODE_CPL > 1 ? GDN_DECODE_CPL / 2 : 1) : GDN_DECODE_CPL;
-    return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true>(p, stream);
+    return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, PK>(p, stream);
 }
 
-template <typename T, bool PREP>
+template <typename T, bool PREP, bool PK>
 hipError_t launch_t(const ScanArgs& p, hipStream_t stream) {
     switch (p.K) {
-        case 32: return launch_k<T, 32, PREP>(p, stream);
-        case 64: return launch_k<T, 64, PREP>(p, stream);
-        case 128: return launch_k<T, 128, PREP>(p, stream);
-        case 256: return launch_k<T, 256, PREP>(p, stream);
+        case 32: return launch_k<T, 32, PREP, PK>(p, stream);
+        case 64: return launch_k<T, 64, PREP, PK>(p, stream);
+        case 128: return launch_k<T, 128, PREP, PK>(p, stream);
+        case 256: return launch_k<T, 256, PREP, PK>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool PREP>
+template <bool PREP, bool PK>
 hipError_t launch_p(const ScanArgs& p, int dtype, hipStream_t stream) {
     switch (dtype) {
-        case GDN_F32: return launch_t<F32, PREP>(p, stream);
-        case GDN_BF16: return launch_t<BF16, PREP>(p, stream);
-        case GDN_F16: return launch_t<F16, PREP>(p, stream);
+        case GDN_F32: return launch_t<F32, PREP, PK>(p, stream);
+        case GDN_BF16: return launch_t<BF16, PREP, PK>(p, stream);
+        case GDN_F16: return launch_t<F16, PREP, PK>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -468,8 +517,9 @@ hipError_t launch_scan_decode(const ScanLaunch& a, hipStream_t stream) {
     p.counts = a.counts;
     p.active = a.active;
     p.capsule = a.capsule;
-    if (a.qk_prep != nullptr) return launch_p<true>(p, a.qkv_dtype, stream);
-    return launch_p<false>(p, a.qkv_dtype, stream);
+    if (a.qk_prep != nullptr) return launch_p<true, false>(p, a.qkv_dtype, stream);
+    if ((a.flags & GDN_GATE_PER_KEY) && a.a != nullptr) return launch_p<false, true>(p, a.qkv_dtype, stream);
+    return launch_p<false, false>(p, a.qkv_dtype, stream);
 }
 
 }  // namespace gdn

@@ -18,6 +18,9 @@
 //         r = g (k^.s),  delta = beta (v - r),  out = scale (g (q^.s) + delta (q^.k^)),
 //         s <- g s + delta k^;
 //   * outputs of a chunk are collected in LDS and written back as 16-byte vectors;
+//   * with a per-key-channel decay (GDN_GATE_PER_KEY; "PK" instances) the staging also evaluates
+//     the decay of every (token, key channel) once per block into LDS, and the recurrence decays
+//     each state slice channel by channel before the dot products;
 //   * with capture (speculative decoding: paged_ssm.rs page, DELTA_CAPTURE_INIT / _STEP) the first
 //     captured tokens of a sequence also record g and k^ (copied out of the LDS stage by the head's
 //     first block; k^ only for the first value head of each key head) and delta (by the lane that
@@ -56,14 +59,15 @@ struct SeqArgs {
     float* capsule;         // [B, cap*(H + HQ*K + H*V)]
 };
 
-template <typename T, int K, int LPC, int CPL, int NW, bool PREP>
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool PK>
 struct Cfg {
     using TS = typename T::storage;
     static constexpr int NT = 64 * NW;                                  // threads per block
     static constexpr int EPL = K / LPC;                                 // state elements per lane
     static constexpr int WC = (64 / LPC) * CPL;                         // columns per wave
     static constexpr int BC = NW * WC;                                  // columns per block
-    static constexpr int TC = 2048 / K;                                 // tokens per chunk
+    // tokens per chunk; halved with per-key decays, whose LDS stage would otherwise cost a block per CU
+    static constexpr int TC = (PK ? 1024 : 2048) / K;
     static constexpr int SVEC = PREP ? 4 : 16 / (int)sizeof(TS);        // q/k elements per 16-byte load
     static constexpr int RL = K / SVEC;                                 // lanes per token for q/k staging
     static constexpr int TPP = NT / RL;                                 // tokens per staging pass
@@ -75,17 +79,19 @@ struct Cfg {
 };
 
 // Raw operands of one chunk as fetched by one thread (kept in registers across a chunk of work).
-template <int PASSES, int VPASSES>
+template <int PASSES, int VPASSES, int GKN>
 struct Fetch {
     u32x4 q[PASSES];
     u32x4 k[PASSES];
     u32x4 v[VPASSES];
     float ga, gb;
+    float gk[GKN];  // per-key decay inputs of the thread's q/k elements (PK only)
 };
 
-template <typename T, int K, int LPC, int CPL, int NW, bool PREP>
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool PK>
 __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
-    using C_ = Cfg<T, K, LPC, CPL, NW, PREP>;
+    static_assert(!(PK && PREP), "the per-key decay is evaluated in-kernel from raw inputs");
+    using C_ = Cfg<T, K, LPC, CPL, NW, PREP, PK>;
     using TS = typename C_::TS;
     constexpr int EPL = C_::EPL, WC = C_::WC, BC = C_::BC, TC = C_::TC;
     constexpr int SVEC = C_::SVEC, RL = C_::RL, TPP = C_::TPP, PASSES = C_::PASSES;
@@ -96,6 +102,8 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     __shared__ __align__(16) float sv[2][TC][BC];
     __shared__ float sg[2][TC], sb[2][TC], sqk[2][TC];
     __shared__ __align__(16) float so[TC][BC];
+    __shared__ __align__(16) float sgk[PK ? 2 : 1][PK ? TC : 1][PK ? K : 1];
+    constexpr int GKN = PK ? PASSES * SVEC : 1;
 
     const bool malformed = offsets_malformed(p.offsets, p.B, p.N);
     report_status(p.dev_status, malformed);
@@ -147,11 +155,24 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     const bool cap_d = gl < CPL && v0 + cw + gl < p.V;  // this lane records delta of its output column
 
     // ---- staging: global -> registers (fetch) and registers -> LDS (commit) ------------------------
-    auto fetch = [&](int t0, int n, Fetch<PASSES, VPASSES>& f) {
+    auto fetch = [&](int t0, int n, Fetch<PASSES, VPASSES, GKN>& f) {
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             const int ti = ps * TPP + tid / RL, rl = tid % RL;
             f.q[ps] = f.k[ps] = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (PK) {
+#pragma unroll
+                for (int e = 0; e < SVEC; ++e) f.gk[ps * SVEC + e] = 0.0f;
+                if (ti < n && ti < TC) {
+                    const size_t gi = ((size_t)(t0 + ti) * p.H + h) * K + rl * SVEC;
+#pragma unroll
+                    for (int e = 0; e < SVEC; e += 4) {
+                        const f32x4 av = load4_gate<T>(p.a, p.gate_dtype, gi + e);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) f.gk[ps * SVEC + e + j] = av[j];
+                    }
+                }
+            }
             if (ti < n) {
                 const size_t t = (size_t)(t0 + ti);
                 if constexpr (PREP) {
@@ -171,7 +192,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
                 f.ga = p.gb_prep[gi];
                 f.gb = p.gb_prep[(size_t)p.N * p.H + gi];
             } else {
-                if (p.a) f.ga = load_any(p.a, p.gate_dtype, gi);
+                if (!PK && p.a) f.ga = load_any(p.a, p.gate_dtype, gi);
                 if (p.b) f.gb = load_any(p.b, p.gate_dtype, gi);
             }
         }
@@ -200,7 +221,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
         }
     };
 
-    auto commit = [&](const Fetch<PASSES, VPASSES>& f, int buf) {
+    auto commit = [&](const Fetch<PASSES, VPASSES, GKN>& f, int buf) {
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             const int ti = ps * TPP + tid / RL, rl = tid % RL;
@@ -248,6 +269,14 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
                     *reinterpret_cast<f32x4*>(dk + e) = f32x4{kf[e] * rk, kf[e + 1] * rk, kf[e + 2] * rk, kf[e + 3] * rk};
                 }
                 if (rl == 0) sqk[buf][ti] = qk * rq * rk;
+                if constexpr (PK) {
+                    float* dg = &sgk[buf][ti][rl * SVEC];
+#pragma unroll
+                    for (int e = 0; e < SVEC; ++e) {
+                        const float x = f.gk[ps * SVEC + e];
+                        dg[e] = softplus ? expf(a_mul * softplus_f(x + a_bias)) : expf(x);
+                    }
+                }
             }
         }
         if (tid < TC) {
@@ -257,7 +286,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
                 beta = f.gb;
             } else {
                 g = 1.0f;
-                if (p.a) g = softplus ? expf(a_mul * softplus_f(f.ga + a_bias)) : expf(f.ga);
+                if (!PK && p.a) g = softplus ? expf(a_mul * softplus_f(f.ga + a_bias)) : expf(f.ga);
                 beta = 1.0f;
                 if (p.b) beta = sigmoid ? 1.0f / (1.0f + expf(-f.gb)) : f.gb;
             }
@@ -285,7 +314,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     };
 
     if (nchunks > 0) {
-        Fetch<PASSES, VPASSES> f;
+        Fetch<PASSES, VPASSES, GKN> f;
         fetch(start, min(TC, end - start), f);
         commit(f, 0);
         __syncthreads();
@@ -317,6 +346,17 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
                     }
                 }
                 const float g = sg[buf][i], beta = sb[buf][i], qk = sqk[buf][i];
+                if constexpr (PK) {
+                    // channel-wise decay of the lane's state slice (g is 1 for PK)
+#pragma unroll
+                    for (int m = 0; m < EPL / 4; ++m) {
+                        const f32x4 gv = *reinterpret_cast<const f32x4*>(&sgk[buf][i][4 * (gl + LPC * m)]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+#pragma unroll
+                            for (int cc = 0; cc < CPL; ++cc) s[cc][4 * m + e] *= gv[e];
+                    }
+                }
                 float pk[CPL], pq[CPL];
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) {
@@ -339,7 +379,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
                     const float d = beta * (sv[buf][i][cw + cc] - rmul * (g * pk[cc]));
                     const float o = p.scale * fmaf(g, pq[cc], d * qk);
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) s[cc][e] = fmaf(d, k[e], g * s[cc][e]);
+                    for (int e = 0; e < EPL; ++e) s[cc][e] = fmaf(d, k[e], PK ? s[cc][e] : g * s[cc][e]);
                     if (gl == cc) {
                         mine = o;
                         dmine = d;
@@ -399,51 +439,51 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     }
 }
 
-template <typename T, int K, int LPC, int CPL, bool PREP>
+template <typename T, int K, int LPC, int CPL, bool PREP, bool PK>
 hipError_t launch_tile(SeqArgs p, hipStream_t stream) {
     constexpr int NW = 4;
-    using C_ = Cfg<T, K, LPC, CPL, NW, PREP>;
+    using C_ = Cfg<T, K, LPC, CPL, NW, PREP, PK>;
     p.n_vtiles = (p.V + C_::BC - 1) / C_::BC;
     const long long blocks = (long long)p.B * p.H * p.n_vtiles;
     if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
     p.n_blocks = (int)blocks;
     p.vec_ok = (p.V % C_::VVEC) == 0;
-    hipLaunchKernelGGL((seq_kernel<T, K, LPC, CPL, NW, PREP>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((seq_kernel<T, K, LPC, CPL, NW, PREP, PK>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
 // Tile choice: two columns per lane group when that still gives 4 blocks per CU, else one; for
 // K >= 128 and very few columns, 32-lane groups halve the columns per block once more.
-template <typename T, int K, bool PREP>
+template <typename T, int K, bool PREP, bool PK>
 hipError_t launch_k(const SeqArgs& p, hipStream_t stream) {
     constexpr int LPC = K >= 64 ? 16 : 8;
     constexpr int BC2 = 4 * (64 / LPC) * 2;
     const long long bh = (long long)p.B * p.H;
-    if (bh * ((p.V + BC2 - 1) / BC2) >= 1024) return launch_tile<T, K, LPC, 2, PREP>(p, stream);
+    if (bh * ((p.V + BC2 - 1) / BC2) >= 1024) return launch_tile<T, K, LPC, 2, PREP, PK>(p, stream);
     if constexpr (K >= 128) {
         constexpr int BC1 = 4 * (64 / LPC);
-        if (bh * ((p.V + BC1 - 1) / BC1) < 1024) return launch_tile<T, K, 32, 1, PREP>(p, stream);
+        if (bh * ((p.V + BC1 - 1) / BC1) < 1024) return launch_tile<T, K, 32, 1, PREP, PK>(p, stream);
     }
-    return launch_tile<T, K, LPC, 1, PREP>(p, stream);
+    return launch_tile<T, K, LPC, 1, PREP, PK>(p, stream);
 }
 
-template <typename T, bool PREP>
+template <typename T, bool PREP, bool PK>
 hipError_t launch_t(const SeqArgs& p, hipStream_t stream) {
     switch (p.K) {
-        case 32: return launch_k<T, 32, PREP>(p, stream);
-        case 64: return launch_k<T, 64, PREP>(p, stream);
-        case 128: return launch_k<T, 128, PREP>(p, stream);
-        case 256: return launch_k<T, 256, PREP>(p, stream);
+        case 32: return launch_k<T, 32, PREP, PK>(p, stream);
+        case 64: return launch_k<T, 64, PREP, PK>(p, stream);
+        case 128: return launch_k<T, 128, PREP, PK>(p, stream);
+        case 256: return launch_k<T, 256, PREP, PK>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool PREP>
+template <bool PREP, bool PK>
 hipError_t launch_p(const SeqArgs& p, int dtype, hipStream_t stream) {
     switch (dtype) {
-        case GDN_F32: return launch_t<F32, PREP>(p, stream);
-        case GDN_BF16: return launch_t<BF16, PREP>(p, stream);
-        case GDN_F16: return launch_t<F16, PREP>(p, stream);
+        case GDN_F32: return launch_t<F32, PREP, PK>(p, stream);
+        case GDN_BF16: return launch_t<BF16, PREP, PK>(p, stream);
+        case GDN_F16: return launch_t<F16, PREP, PK>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -482,8 +522,9 @@ hipError_t launch_scan_seq(const ScanLaunch& a, hipStream_t stream) {
     p.counts = a.counts;
     p.active = a.active;
     p.capsule = a.capsule;
-    if (a.qk_prep != nullptr) return launch_p<true>(p, a.qkv_dtype, stream);
-    return launch_p<false>(p, a.qkv_dtype, stream);
+    if (a.qk_prep != nullptr) return launch_p<true, false>(p, a.qkv_dtype, stream);
+    if ((a.flags & GDN_GATE_PER_KEY) && a.a != nullptr) return launch_p<false, true>(p, a.qkv_dtype, stream);
+    return launch_p<false, false>(p, a.qkv_dtype, stream);
 }
 
 }  // namespace gdn

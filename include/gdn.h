@@ -129,6 +129,12 @@ gdn_status gdn_conv1d_varlen_capture(const gdn_conv_desc *desc, const void *x, c
  *                 (no decay input) and "gated" update rules of the pages' update_rule attribute,
  *                 where the DELTA kernel string is compiled with RETRIEVE = 0.  Without this flag
  *                 the rule is "delta" (no decay input) or "gated_delta".
+ *   GDN_GATE_PER_KEY  one decay per key channel: a is [N, H, K] and the decay step becomes
+ *                 s[i] <- g[i]*s[i] with g[i] the gate of a[t,h,i] (A_log and dt_bias stay per
+ *                 head): S <- S diag(g) before the retrieval.  The gate_per_channel form of the
+ *                 GatedDeltaNet thunk (rlx-cpu thunk/types.rs page).  Fused inputs on the DECODE and
+ *                 SEQ paths only: prepare, prepared scans, CHUNK, capture and gdn_decode_step reject
+ *                 it (GDN_ERR_UNSUPPORTED); a must then be 16-byte aligned.
  * A NULL decay input a means g = 1; a NULL rate input b means beta = 1.  Gate arithmetic is fp32
  * (gate inputs are widened to fp32 first).  scale <= 0 selects 1/sqrt(K).
  * Constraints: B >= 1, N >= 0, HQ >= 1, H >= 1, H % HQ == 0, 1 <= K <= 256 (the pages' limit),
@@ -139,6 +145,7 @@ gdn_status gdn_conv1d_varlen_capture(const gdn_conv_desc *desc, const void *x, c
 #define GDN_SOFTPLUS 2u
 #define GDN_SIGMOID 4u
 #define GDN_NO_RETRIEVE 8u
+#define GDN_GATE_PER_KEY 16u
 
 typedef enum gdn_path {
     GDN_PATH_AUTO = 0,   /* DECODE when N <= 2*B; else CHUNK when eligible, N >= 64*B and ws_bytes suffices; else SEQ */
@@ -151,7 +158,7 @@ typedef struct gdn_scan_desc {
     int32_t B, N, HQ, H, K, V;
     int32_t qkv_dtype;  /* gdn_dtype of qkv and out */
     int32_t gate_dtype; /* gdn_dtype of a and b: GDN_F32 or qkv_dtype */
-    uint32_t flags;     /* GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID | GDN_NO_RETRIEVE */
+    uint32_t flags;     /* GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID | GDN_NO_RETRIEVE | GDN_GATE_PER_KEY */
     float scale;        /* output scale; <= 0 selects 1/sqrt(K) */
     int32_t path;       /* gdn_path */
 } gdn_scan_desc;
@@ -185,7 +192,8 @@ gdn_status gdn_prepare_qk_gates(const gdn_scan_desc *desc, const void *qkv, cons
  *   qkv        [N, C]        qkv_dtype   required
  *   qk_prep    [2, N, HQ, K] fp32        NULL = fused (must be NULL together with gb_prep)
  *   gb_prep    [2, N, H]     fp32
- *   a, b       [N, H]        gate_dtype  NULL = absent (fused mode)
+ *   a          [N, H]        gate_dtype  NULL = absent (fused mode); [N, H, K] with GDN_GATE_PER_KEY
+ *   b          [N, H]        gate_dtype  NULL = absent (fused mode)
  *   A_log, dt_bias [H]       fp32        required in fused mode when a is given with GDN_SOFTPLUS
  *   state_in   [B, H, V, K]  fp32        NULL = zero state
  *   out        [N, H, V]     qkv_dtype   required unless N == 0

@@ -94,7 +94,7 @@ def scan(abi, d, qkv=P, qk=None, gb=None, a=None, b=None, alog=None, dtb=None, s
         (dict(V=0), {}, "ERR_SHAPE"),
         (dict(qkv_dtype=5), {}, "ERR_DTYPE"),
         (dict(qkv_dtype=1, gate_dtype=2), {}, "ERR_DTYPE"),
-        (dict(flags=16), {}, "ERR_UNSUPPORTED"),
+        (dict(flags=32), {}, "ERR_UNSUPPORTED"),
         (dict(path=9), {}, "ERR_UNSUPPORTED"),
         # the chunked form needs the retrieval term: shape and dtype eligible, GDN_NO_RETRIEVE set
         (dict(qkv_dtype=1, gate_dtype=1, K=64, V=64, flags=7 | 8, path=3), dict(a=P, alog=P, dtb=P), "ERR_UNSUPPORTED"),
@@ -233,3 +233,20 @@ def scan_capture(abi, d, cap=4, counts=P, active=None, capsule=P, qkv=P, out=P, 
 )
 def test_scan_capture_host_validation(abi, fields, kw, want):
     assert scan_capture(abi, scan_desc(abi, **fields), **kw) == getattr(abi, want)
+
+
+def test_per_key_gate_host_validation(abi):
+    """GDN_GATE_PER_KEY runs on fused inputs through the token-sequential paths only."""
+    L = abi.lib()
+    pk = 7 | 16
+    d = scan_desc(abi, flags=pk)
+    assert L.gdn_prepare_qk_gates(ctypes.byref(d), P, P, None, P, P, P, P, None) == abi.ERR_UNSUPPORTED
+    assert scan(abi, d, qk=P, gb=P) == abi.ERR_UNSUPPORTED  # prepared inputs carry one decay per head
+    assert scan(abi, d, a=P + 4, alog=P, dtb=P) == abi.ERR_ALIGN  # the [N, H, K] decays load as vectors
+    chunk = scan_desc(abi, flags=pk, qkv_dtype=1, gate_dtype=1, K=64, V=64, path=3)
+    assert scan(abi, chunk, a=P, alog=P, dtb=P) == abi.ERR_UNSUPPORTED
+    assert scan_capture(abi, scan_desc(abi, flags=pk, path=2)) == abi.ERR_UNSUPPORTED
+    assert decode_step(abi, None, dict(flags=pk)) == abi.ERR_UNSUPPORTED
+    n = ctypes.c_size_t(1)
+    big = scan_desc(abi, flags=pk, qkv_dtype=1, gate_dtype=1, K=64, V=64, N=64 * 2)
+    assert L.gdn_scan_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == abi.OK and n.value == 0
