@@ -9,7 +9,8 @@ several batch sizes).
 The prefill workload (B=8, lengths ~ U[512, 4096]) and the long single sequence (N=65536, H=16) are
 measured too and reported in "also", with the arithmetic roofline of the path they take, and so is a
 speculative verification step (B=256 x 5 tokens) with and without the capture of 4 tokens per
-sequence, and both steps with one decay per key channel instead of one per head.
+sequence, both steps with one decay per key channel instead of one per head, and the recurrence
+reading separate padded q/k/v buffers instead of the packed row.
 
 Prints ONE JSON line.  The dominant kernel (the fused step, or the recurrence in the two-call form)
 is timed with HIP events on the stream it is launched on; its algorithmic bytes per launch are the
@@ -292,6 +293,51 @@ def per_key_comparison(torch, steps: int = 50):
     return res
 
 
+def strided_comparison(torch, steps: int = 20):
+    """The recurrence on the decode (DECODE) and prefill (CHUNK) workloads reading the packed
+    [q | k | v] row and reading three separate buffers with padded rows (row strides HQ*K + 64,
+    HQ*K + 64, H*V + 64): microseconds per launch (HIP events, best of 3)."""
+    import gated_delta_rule_varlen_amd as gdn
+    import workloads
+
+    res = {}
+    for w in (workloads.decode_step(), workloads.varlen_prefill()):
+        p = Path(w, torch, "auto")
+        HQK, HV = w.HQ * w.K, w.H * w.V
+        x = p.x
+        sep = []
+        for lo, width in ((0, HQK), (HQK, HQK), (2 * HQK, HV)):
+            buf = torch.empty((w.N, width + 64), dtype=x.dtype, device="cuda")
+            buf[:, :width] = x[:, lo:lo + width]
+            sep.append(buf[:, :width])
+        kw = dict(HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=p.a, b=p.b, A_log=p.A_log, dt_bias=p.dt_bias, state_in=p.state,
+                  l2norm=w.l2norm, softplus=w.softplus, sigmoid=w.sigmoid, out=p.out, state_out=p.state)
+        ws_n = gdn.scan_workspace_bytes(x, w.B, HQ=w.HQ, H=w.H, K=w.K, V=w.V)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+        runs = {"packed": lambda: gdn.scan_varlen(x, p.offsets, workspace=ws, **kw)[2],
+                "strided": lambda: gdn.scan_varlen_strided(*sep, p.offsets, workspace=ws, **kw)[2]}
+        rec = {}
+        for name, fn in runs.items():
+            best = None
+            for _ in range(3):
+                for _ in range(3):
+                    used = fn()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / steps
+                best = us if best is None else min(best, us)
+            rec[name] = {"path": used, "us": round(best, 2)}
+        res[w.name] = rec
+        del p, sep, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle (conv + scan, fp64, OpenMP) on a bounded sample of the same workload:
     whole sequences, taken in order until about budget_s seconds of CPU work."""
@@ -408,7 +454,8 @@ def main():
                         "long": secondary(torch, workloads.long_single(), 3, 1),
                         "decode_step_fused_vs_two_call": fused_comparison(torch),
                         "speculative_verify_capture": verify_comparison(torch),
-                        "per_key_decay": per_key_comparison(torch)}
+                        "per_key_decay": per_key_comparison(torch),
+                        "strided_qkv": strided_comparison(torch)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

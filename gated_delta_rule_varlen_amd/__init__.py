@@ -15,8 +15,8 @@ import torch
 from . import _abi
 from ._abi import GdnError, PATH_NAMES, lib  # noqa: F401
 
-__all__ = ["conv1d_varlen", "conv1d_varlen_capture", "prepare_qk_gates", "scan_varlen", "scan_varlen_capture",
-           "scan_workspace_bytes", "decode_step", "GdnError", "lib"]
+__all__ = ["conv1d_varlen", "conv1d_varlen_capture", "prepare_qk_gates", "prepare_qk_gates_strided", "scan_varlen",
+           "scan_varlen_capture", "scan_varlen_strided", "scan_workspace_bytes", "decode_step", "GdnError", "lib"]
 
 _DTYPE = {torch.float32: _abi.F32, torch.bfloat16: _abi.BF16, torch.float16: _abi.F16}
 _TORCH = {v: k for k, v in _DTYPE.items()}
@@ -36,6 +36,29 @@ def _ptr(t: Optional[torch.Tensor], what: str):
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _row_view(t: Optional[torch.Tensor], width: int, what: str):
+    """(device pointer, row stride in elements) of a [N, ...] tensor whose rows are contiguous
+    blocks of `width` elements; the row stride itself is free."""
+    if t is None:
+        return None, width
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if t.shape[0] == 0:
+        return ctypes.c_void_p(t.data_ptr()), width
+    # [N, heads, width] with each token's block contiguous merges into a [N, heads*width] view
+    rows = t.reshape(t.shape[0], -1) if t.dim() > 2 and t[0].is_contiguous() else t
+    if rows.dim() != 2 or rows.shape[1] != width or (rows.shape[0] > 1 and rows.stride(1) != 1):
+        raise ValueError(f"{what} must be [N, {width}] (or [N, heads, width]) with contiguous rows")
+    return ctypes.c_void_p(rows.data_ptr()), rows.stride(0) if rows.shape[0] > 1 else width
+
+
+def _streams(q, k, v, HQ, H, K, V):
+    qp, qs = _row_view(q, HQ * K, "q")
+    kp, ks = _row_view(k, HQ * K, "k")
+    vp, vs = _row_view(v, H * V, "v")
+    return _abi.QKVStreams(qp, kp, vp, qs, ks, vs)
 
 
 def _stream(device) -> ctypes.c_void_p:
@@ -130,6 +153,25 @@ def prepare_qk_gates(qkv: torch.Tensor, *, HQ: int, H: int, K: int, V: int, a=No
     return qk_out, gb_out
 
 
+def prepare_qk_gates_strided(q: torch.Tensor, k: torch.Tensor, *, HQ: int, H: int, K: int, V: int, a=None, b=None,
+                             A_log=None, dt_bias=None, l2norm=True, softplus=True, sigmoid=True, qk_out=None,
+                             gb_out=None):
+    """prepare_qk_gates on separate q and k token streams (gdn_prepare_qk_gates_strided): q, k are
+    [N, HQ, K] or [N, HQ*K] with contiguous rows and any row stride."""
+    N = q.shape[0]
+    if qk_out is None:
+        qk_out = torch.empty((2, N, HQ, K), dtype=torch.float32, device=q.device)
+    if gb_out is None:
+        gb_out = torch.empty((2, N, H), dtype=torch.float32, device=q.device)
+    d = _scan_desc(q, 1, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, 0.0, "auto")
+    s = _streams(q, k, None, HQ, H, K, V)
+    st = lib().gdn_prepare_qk_gates_strided(ctypes.byref(d), ctypes.byref(s), _ptr(a, "a"), _ptr(b, "b"),
+                                            _ptr(A_log, "A_log"), _ptr(dt_bias, "dt_bias"), _ptr(qk_out, "qk_out"),
+                                            _ptr(gb_out, "gb_out"), _stream(q.device))
+    _check(st, "gdn_prepare_qk_gates_strided")
+    return qk_out, gb_out
+
+
 def scan_workspace_bytes(qkv: torch.Tensor, B: int, *, HQ, H, K, V, l2norm=True, softplus=True, sigmoid=True,
                          path="auto", gate_dtype=None) -> int:
     d = _scan_desc(qkv, B, HQ, H, K, V, None, l2norm, softplus, sigmoid, 0.0, path)
@@ -170,6 +212,41 @@ def scan_varlen(qkv: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K:
                                _ptr(offsets, "offsets"), _ptr(workspace, "workspace"), ws_bytes,
                                _ptr(dev_status, "dev_status"), ctypes.byref(used), _stream(qkv.device))
     _check(st, "gdn_scan_varlen")
+    return out, state_out, PATH_NAMES.get(used.value, str(used.value))
+
+
+def scan_varlen_strided(q, k, v, offsets: torch.Tensor, *, HQ: int, H: int, K: int, V: int, a=None, b=None,
+                        A_log=None, dt_bias=None, state_in=None, qk_prep=None, gb_prep=None, l2norm=True,
+                        softplus=True, sigmoid=True, scale: float = 0.0, path: str = "auto", out=None, state_out=None,
+                        write_state: bool = True, workspace=None, dev_status=None, retrieve: bool = True,
+                        gate_per_key: bool = False):
+    """scan_varlen on separate token streams (gdn_scan_varlen_strided): q, k [N, HQ, K] (or
+    [N, HQ*K]) and v [N, H, V] (or [N, H*V]), each with contiguous rows and any row stride; q and k
+    may be None with prepared inputs.  Returns (out, state_out, path name that ran)."""
+    N = v.shape[0]
+    B = offsets.numel() - 1
+    if out is None:
+        out = torch.empty((N, H, V), dtype=v.dtype, device=v.device)
+    if state_out is None and write_state:
+        state_out = torch.empty((B, H, V, K), dtype=torch.float32, device=v.device)
+    d = _scan_desc(v, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, path, retrieve,
+                   gate_per_key)
+    d.N = N
+    if workspace is None and path in ("auto", "chunk"):
+        n = ctypes.c_size_t(0)
+        _check(lib().gdn_scan_workspace_bytes(ctypes.byref(d), ctypes.byref(n)), "gdn_scan_workspace_bytes")
+        if n.value:
+            workspace = torch.empty(int(n.value), dtype=torch.uint8, device=v.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    s = _streams(q, k, v, HQ, H, K, V)
+    used = ctypes.c_int32(-1)
+    st = lib().gdn_scan_varlen_strided(ctypes.byref(d), ctypes.byref(s), _ptr(qk_prep, "qk_prep"),
+                                       _ptr(gb_prep, "gb_prep"), _ptr(a, "a"), _ptr(b, "b"), _ptr(A_log, "A_log"),
+                                       _ptr(dt_bias, "dt_bias"), _ptr(state_in, "state_in"), _ptr(out, "out"),
+                                       _ptr(state_out, "state_out"), _ptr(offsets, "offsets"),
+                                       _ptr(workspace, "workspace"), ws_bytes, _ptr(dev_status, "dev_status"),
+                                       ctypes.byref(used), _stream(v.device))
+    _check(st, "gdn_scan_varlen_strided")
     return out, state_out, PATH_NAMES.get(used.value, str(used.value))
 
 

@@ -26,8 +26,10 @@ EXPORTS = (
     "gdn_conv1d_varlen",
     "gdn_conv1d_varlen_capture",
     "gdn_prepare_qk_gates",
+    "gdn_prepare_qk_gates_strided",
     "gdn_scan_varlen",
     "gdn_scan_varlen_capture",
+    "gdn_scan_varlen_strided",
     "gdn_scan_workspace_bytes",
     "gdn_decode_step",
     "gdn_status_string",
@@ -64,6 +66,17 @@ class ScanDesc(ctypes.Structure):
     ]
 
 
+class QKVStreams(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("q_stride", ctypes.c_int64),
+        ("k_stride", ctypes.c_int64),
+        ("v_stride", ctypes.c_int64),
+    ]
+
+
 class GdnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -87,11 +100,16 @@ def lib() -> ctypes.CDLL:
         L.gdn_conv1d_varlen_capture.restype = st
         L.gdn_prepare_qk_gates.argtypes = [ctypes.POINTER(ScanDesc), vp, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_prepare_qk_gates.restype = st
+        L.gdn_prepare_qk_gates_strided.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(QKVStreams)] + [vp] * 7
+        L.gdn_prepare_qk_gates_strided.restype = st
         L.gdn_scan_varlen.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 12 + [ctypes.c_size_t, vp, i32p, vp]
         L.gdn_scan_varlen.restype = st
         L.gdn_scan_varlen_capture.argtypes = ([ctypes.POINTER(ScanDesc)] + [vp] * 11 + [ctypes.c_int32, vp, vp, vp, vp,
                                               ctypes.c_size_t, vp, i32p, vp])
         L.gdn_scan_varlen_capture.restype = st
+        L.gdn_scan_varlen_strided.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(QKVStreams)] + [vp] * 11 +
+                                              [ctypes.c_size_t, vp, i32p, vp])
+        L.gdn_scan_varlen_strided.restype = st
         L.gdn_decode_step.argtypes = [ctypes.POINTER(ConvDesc), ctypes.POINTER(ScanDesc)] + [vp] * 15
         L.gdn_decode_step.restype = st
         L.gdn_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(ctypes.c_size_t)]

@@ -38,8 +38,49 @@ gdn_status check_scan_desc(const gdn_scan_desc* d) {
     if (C > INT_MAX) return GDN_ERR_OVERFLOW;
     if ((long long)d->B * d->H > INT_MAX) return GDN_ERR_OVERFLOW;
     if (d->K != 32 && d->K != 64 && d->K != 128 && d->K != 256) return GDN_ERR_UNSUPPORTED;
-    if ((C * dsize(d->qkv_dtype)) % 16 != 0) return GDN_ERR_ALIGN;  // token rows must start 16-byte aligned
     if (d->path < GDN_PATH_AUTO || d->path > GDN_PATH_CHUNK) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+// The packed [q | k | v] row as three token streams; its rows must start 16-byte aligned.
+gdn_status packed_streams(const gdn_scan_desc* d, const void* qkv, gdn::TokenStreams* x) {
+    const long long C = 2ll * d->HQ * d->K + (long long)d->H * d->V;
+    if ((C * dsize(d->qkv_dtype)) % 16 != 0) return GDN_ERR_ALIGN;
+    if (misaligned(qkv)) return GDN_ERR_ALIGN;
+    const char* base = static_cast<const char*>(qkv);
+    const long long es = dsize(d->qkv_dtype);
+    x->q = qkv;
+    x->k = base ? base + (long long)d->HQ * d->K * es : nullptr;
+    x->v = base ? base + 2ll * d->HQ * d->K * es : nullptr;
+    x->sq = x->sk = x->sv = C;
+    return GDN_OK;
+}
+
+// Separate token streams: each used stream present (when there are tokens), 16-byte aligned, with
+// a row stride of at least its row width whose rows all start 16-byte aligned.
+gdn_status strided_streams(const gdn_scan_desc* d, const gdn_qkv_streams* s, bool need_qk, bool need_v,
+                           gdn::TokenStreams* x) {
+    if (s == nullptr) return GDN_ERR_NULL;
+    const long long es = dsize(d->qkv_dtype);
+    const long long wqk = (long long)d->HQ * d->K, wv = (long long)d->H * d->V;
+    struct {
+        const void* p;
+        long long stride, width;
+        bool used;
+    } st[3] = {{s->q, s->q_stride, wqk, need_qk}, {s->k, s->k_stride, wqk, need_qk}, {s->v, s->v_stride, wv, need_v}};
+    for (const auto& e : st) {
+        if (!e.used) continue;
+        if (d->N > 0 && e.p == nullptr) return GDN_ERR_NULL;
+        if (e.stride < e.width) return GDN_ERR_SHAPE;
+        if (d->N > 0 && e.stride > (LLONG_MAX / 4) / d->N) return GDN_ERR_OVERFLOW;
+        if (misaligned(e.p) || (e.stride * es) % 16 != 0) return GDN_ERR_ALIGN;
+    }
+    x->q = need_qk ? s->q : nullptr;
+    x->k = need_qk ? s->k : nullptr;
+    x->v = need_v ? s->v : nullptr;
+    x->sq = s->q_stride;
+    x->sk = s->k_stride;
+    x->sv = s->v_stride;
     return GDN_OK;
 }
 
@@ -151,19 +192,16 @@ gdn_status gdn_conv1d_varlen_capture(const gdn_conv_desc* d, const void* x, cons
     return conv_call(d, x, w, bias, state_in, y, state_out, offsets, cap, counts, updates, dev_status, stream);
 }
 
-gdn_status gdn_prepare_qk_gates(const gdn_scan_desc* d, const void* qkv, const void* a, const void* b,
-                                const float* A_log, const float* dt_bias, float* qk_out, float* gb_out,
-                                hipStream_t stream) {
-    const gdn_status st = check_scan_desc(d);
-    if (st != GDN_OK) return st;
-    if (d->flags & GDN_GATE_PER_KEY) return GDN_ERR_UNSUPPORTED;  // its gate plane is one decay per head
-    if (qk_out == nullptr && gb_out == nullptr) return GDN_ERR_NULL;
-    if (d->N > 0 && qkv == nullptr && qk_out != nullptr) return GDN_ERR_NULL;
-    if (a != nullptr && (d->flags & GDN_SOFTPLUS) && (A_log == nullptr || dt_bias == nullptr)) return GDN_ERR_NULL;
-    if (misaligned(qkv) || misaligned(qk_out) || misaligned(gb_out)) return GDN_ERR_ALIGN;
+}  // extern "C"
+
+namespace {
+
+// gdn_prepare_qk_gates on token streams x (already checked; q/k unread when qk_out is NULL).
+gdn_status prepare_call(const gdn_scan_desc* d, const gdn::TokenStreams& x, const void* a, const void* b,
+                        const float* A_log, const float* dt_bias, float* qk_out, float* gb_out, hipStream_t stream) {
     if (d->N == 0) return GDN_OK;
     gdn::PrepareLaunch p;
-    p.qkv = qkv;
+    p.x = x;
     p.a = a;
     p.b = b;
     p.A_log = A_log;
@@ -179,6 +217,43 @@ gdn_status gdn_prepare_qk_gates(const gdn_scan_desc* d, const void* qkv, const v
     p.gate_dtype = d->gate_dtype;
     p.flags = d->flags;
     return from_hip(gdn::launch_prepare(p, stream));
+}
+
+// Checks shared by the two prepare entry points (everything but the token streams).
+gdn_status check_prepare(const gdn_scan_desc* d, const void* a, const float* A_log, const float* dt_bias,
+                         const float* qk_out, const float* gb_out) {
+    const gdn_status st = check_scan_desc(d);
+    if (st != GDN_OK) return st;
+    if (d->flags & GDN_GATE_PER_KEY) return GDN_ERR_UNSUPPORTED;  // its gate plane is one decay per head
+    if (qk_out == nullptr && gb_out == nullptr) return GDN_ERR_NULL;
+    if (a != nullptr && (d->flags & GDN_SOFTPLUS) && (A_log == nullptr || dt_bias == nullptr)) return GDN_ERR_NULL;
+    if (misaligned(qk_out) || misaligned(gb_out)) return GDN_ERR_ALIGN;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prepare_qk_gates(const gdn_scan_desc* d, const void* qkv, const void* a, const void* b,
+                                const float* A_log, const float* dt_bias, float* qk_out, float* gb_out,
+                                hipStream_t stream) {
+    gdn_status st = check_prepare(d, a, A_log, dt_bias, qk_out, gb_out);
+    if (st != GDN_OK) return st;
+    if (d->N > 0 && qkv == nullptr && qk_out != nullptr) return GDN_ERR_NULL;
+    gdn::TokenStreams x;
+    if ((st = packed_streams(d, qkv, &x)) != GDN_OK) return st;
+    return prepare_call(d, x, a, b, A_log, dt_bias, qk_out, gb_out, stream);
+}
+
+gdn_status gdn_prepare_qk_gates_strided(const gdn_scan_desc* d, const gdn_qkv_streams* streams, const void* a,
+                                        const void* b, const float* A_log, const float* dt_bias, float* qk_out,
+                                        float* gb_out, hipStream_t stream) {
+    gdn_status st = check_prepare(d, a, A_log, dt_bias, qk_out, gb_out);
+    if (st != GDN_OK) return st;
+    gdn::TokenStreams x;
+    if ((st = strided_streams(d, streams, qk_out != nullptr, false, &x)) != GDN_OK) return st;
+    return prepare_call(d, x, a, b, A_log, dt_bias, qk_out, gb_out, stream);
 }
 
 gdn_status gdn_scan_workspace_bytes(const gdn_scan_desc* d, size_t* bytes) {
@@ -197,15 +272,14 @@ gdn_status gdn_scan_workspace_bytes(const gdn_scan_desc* d, size_t* bytes) {
 namespace {
 
 // gdn_scan_varlen with an optional capture (cap == 0: none; the capture arguments were checked).
-gdn_status scan_call(const gdn_scan_desc* d, const void* qkv, const float* qk_prep, const float* gb_prep,
+// The token streams x were checked by the caller (packed or strided); the rest is checked here.
+gdn_status scan_call(const gdn_scan_desc* d, const gdn::TokenStreams& x, const float* qk_prep, const float* gb_prep,
                      const void* a, const void* b, const float* A_log, const float* dt_bias, const float* state_in,
                      void* out, float* state_out, const int32_t* offsets, int cap, const int32_t* counts,
                      const int32_t* active, float* capsule, void* workspace, size_t ws_bytes, int32_t* dev_status,
                      int32_t* path_used, hipStream_t stream) {
-    const gdn_status st = check_scan_desc(d);
-    if (st != GDN_OK) return st;
     if (offsets == nullptr) return GDN_ERR_NULL;
-    if (d->N > 0 && (qkv == nullptr || out == nullptr)) return GDN_ERR_NULL;
+    if (d->N > 0 && out == nullptr) return GDN_ERR_NULL;
     if ((qk_prep == nullptr) != (gb_prep == nullptr)) return GDN_ERR_NULL;
     const bool prepared = qk_prep != nullptr;
     if (!prepared && a != nullptr && (d->flags & GDN_SOFTPLUS) && (A_log == nullptr || dt_bias == nullptr))
@@ -215,7 +289,7 @@ gdn_status scan_call(const gdn_scan_desc* d, const void* qkv, const float* qk_pr
         if (prepared || cap > 0) return GDN_ERR_UNSUPPORTED;
         if (misaligned(a)) return GDN_ERR_ALIGN;
     }
-    if (misaligned(qkv) || misaligned(qk_prep) || misaligned(gb_prep) || misaligned(state_in) || misaligned(out) ||
+    if (misaligned(qk_prep) || misaligned(gb_prep) || misaligned(state_in) || misaligned(out) ||
         misaligned(state_out) || misaligned(workspace))
         return GDN_ERR_ALIGN;
     const bool capture = cap > 0;
@@ -226,7 +300,7 @@ gdn_status scan_call(const gdn_scan_desc* d, const void* qkv, const float* qk_pr
             return GDN_ERR_WORKSPACE;
     }
     gdn::ScanLaunch s;
-    s.qkv = qkv;
+    s.x = x;
     s.qk_prep = qk_prep;
     s.gb_prep = gb_prep;
     s.a = prepared ? nullptr : a;
@@ -272,7 +346,25 @@ gdn_status gdn_scan_varlen(const gdn_scan_desc* d, const void* qkv, const float*
                            const float* state_in, void* out, float* state_out, const int32_t* offsets,
                            void* workspace, size_t ws_bytes, int32_t* dev_status, int32_t* path_used,
                            hipStream_t stream) {
-    return scan_call(d, qkv, qk_prep, gb_prep, a, b, A_log, dt_bias, state_in, out, state_out, offsets, 0, nullptr,
+    gdn_status st = check_scan_desc(d);
+    if (st != GDN_OK) return st;
+    if (d->N > 0 && qkv == nullptr) return GDN_ERR_NULL;
+    gdn::TokenStreams x;
+    if ((st = packed_streams(d, qkv, &x)) != GDN_OK) return st;
+    return scan_call(d, x, qk_prep, gb_prep, a, b, A_log, dt_bias, state_in, out, state_out, offsets, 0, nullptr,
+                     nullptr, nullptr, workspace, ws_bytes, dev_status, path_used, stream);
+}
+
+gdn_status gdn_scan_varlen_strided(const gdn_scan_desc* d, const gdn_qkv_streams* streams, const float* qk_prep,
+                                   const float* gb_prep, const void* a, const void* b, const float* A_log,
+                                   const float* dt_bias, const float* state_in, void* out, float* state_out,
+                                   const int32_t* offsets, void* workspace, size_t ws_bytes, int32_t* dev_status,
+                                   int32_t* path_used, hipStream_t stream) {
+    gdn_status st = check_scan_desc(d);
+    if (st != GDN_OK) return st;
+    gdn::TokenStreams x;  // prepared inputs replace q and k; v is always read
+    if ((st = strided_streams(d, streams, qk_prep == nullptr, true, &x)) != GDN_OK) return st;
+    return scan_call(d, x, qk_prep, gb_prep, a, b, A_log, dt_bias, state_in, out, state_out, offsets, 0, nullptr,
                      nullptr, nullptr, workspace, ws_bytes, dev_status, path_used, stream);
 }
 
@@ -291,7 +383,11 @@ gdn_status gdn_scan_varlen_capture(const gdn_scan_desc* d, const void* qkv, cons
         return GDN_ERR_OVERFLOW;
     if (misaligned(capsule)) return GDN_ERR_ALIGN;
     if (d->path == GDN_PATH_CHUNK) return GDN_ERR_UNSUPPORTED;
-    return scan_call(d, qkv, qk_prep, gb_prep, a, b, A_log, dt_bias, state_in, out, state_out, offsets, cap, counts,
+    if (d->N > 0 && qkv == nullptr) return GDN_ERR_NULL;
+    gdn::TokenStreams x;
+    gdn_status ps = packed_streams(d, qkv, &x);
+    if (ps != GDN_OK) return ps;
+    return scan_call(d, x, qk_prep, gb_prep, a, b, A_log, dt_bias, state_in, out, state_out, offsets, cap, counts,
                      active, capsule, workspace, ws_bytes, dev_status, path_used, stream);
 }
 
@@ -302,6 +398,8 @@ gdn_status gdn_decode_step(const gdn_conv_desc* cd, const gdn_scan_desc* sd, con
     if (cd == nullptr || conv_w == nullptr || offsets == nullptr) return GDN_ERR_NULL;
     const gdn_status st = check_scan_desc(sd);
     if (st != GDN_OK) return st;
+    // token rows (packed [q | k | v], the conv output) must start 16-byte aligned
+    if (((2ll * sd->HQ * sd->K + (long long)sd->H * sd->V) * dsize(sd->qkv_dtype)) % 16 != 0) return GDN_ERR_ALIGN;
     // the conv descriptor as gdn_conv1d_varlen checks it, and agreement with the scan descriptor
     if (cd->B < 1 || cd->N < 0 || cd->C < 1 || cd->W < 1 || cd->D < 1) return GDN_ERR_SHAPE;
     if (!dtype_ok(cd->x_dtype)) return GDN_ERR_DTYPE;

@@ -122,7 +122,7 @@ __device__ __forceinline__ int a_tile_half_offset(int lane, int half) {
 }
 
 struct ChunkArgs {
-    const void* qkv;
+    TokenStreams x;
     const void* a;
     const void* b;
     const float* A_log;
@@ -134,7 +134,7 @@ struct ChunkArgs {
     int32_t* dev_status;
     char* ws;
     WsLayout L;
-    int B, N, HQ, H, K, V, C, G;
+    int B, N, HQ, H, K, V, G;
     int gate_dtype;
     uint32_t flags;
     float scale;
@@ -279,7 +279,9 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
     const size_t chh = (size_t)cid * p.H + h;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int pc = lane % LPT, tsub = lane / LPT;
-    const TS* qkv = static_cast<const TS*>(p.qkv);
+    const TS* const xq = static_cast<const TS*>(p.x.q);
+    const TS* const xk = static_cast<const TS*>(p.x.k);
+    const TS* const xv = static_cast<const TS*>(p.x.v);
     uint16_t* const wsb = reinterpret_cast<uint16_t*>(p.ws);
     uint16_t* const w_out = wsb + p.L.w / 2 + chh * CH * K;
     uint16_t* const kd_out = wsb + p.L.kdt / 2 + chh * K * CH;
@@ -294,10 +296,10 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
     for (int u = 0; u < NI; ++u) {
         const int ti = 16 * wv + TPI * u + tsub;
         if (ti < n) {
-            const TS* row = qkv + (size_t)(t0 + ti) * p.C;
-            kr[u] = *reinterpret_cast<const u32x4*>(row + (size_t)(p.HQ + kh) * K + 8 * pc);
-            qr[u] = *reinterpret_cast<const u32x4*>(row + (size_t)kh * K + 8 * pc);
-            vr[u] = *reinterpret_cast<const u32x4*>(row + (size_t)2 * p.HQ * K + (size_t)h * V + 8 * pc);
+            const size_t t = (size_t)(t0 + ti);
+            kr[u] = *reinterpret_cast<const u32x4*>(xk + t * p.x.sk + (size_t)kh * K + 8 * pc);
+            qr[u] = *reinterpret_cast<const u32x4*>(xq + t * p.x.sq + (size_t)kh * K + 8 * pc);
+            vr[u] = *reinterpret_cast<const u32x4*>(xv + t * p.x.sv + (size_t)h * V + 8 * pc);
         } else {
             kr[u] = qr[u] = vr[u] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -784,7 +786,7 @@ size_t chunked_workspace_bytes(int B, int N, int HQ, int H, int K, int V) {
 
 hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream) {
     ChunkArgs p;
-    p.qkv = a.qkv;
+    p.x = a.x;
     p.a = a.a;
     p.b = a.b;
     p.A_log = a.A_log;
@@ -802,7 +804,6 @@ hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream) {
     p.H = a.H;
     p.K = a.K;
     p.V = a.V;
-    p.C = 2 * a.HQ * a.K + a.H * a.V;
     p.G = a.H / a.HQ;
     p.gate_dtype = a.gate_dtype;
     p.flags = a.flags;

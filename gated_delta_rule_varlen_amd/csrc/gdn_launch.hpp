@@ -29,8 +29,18 @@ struct ConvLaunch {
 };
 hipError_t launch_conv(const ConvLaunch& a, hipStream_t stream);
 
+// The token streams the recurrence reads: q and k rows (HQ*K elements per token) and v rows (H*V per
+// token), each from its own base with its own row stride in elements.  A packed [q | k | v] row of
+// width C = 2*HQ*K + H*V is the case q = qkv, k = qkv + HQ*K, v = qkv + 2*HQ*K, all strides C.
+struct TokenStreams {
+    const void* q;
+    const void* k;
+    const void* v;
+    long long sq, sk, sv;
+};
+
 struct PrepareLaunch {
-    const void* qkv;
+    TokenStreams x;
     const void* a;
     const void* b;
     const float* A_log;
@@ -44,7 +54,7 @@ struct PrepareLaunch {
 hipError_t launch_prepare(const PrepareLaunch& a, hipStream_t stream);
 
 struct ScanLaunch {
-    const void* qkv;
+    TokenStreams x;
     const float* qk_prep;  // non-NULL selects the prepared variant
     const float* gb_prep;
     const void* a;

@@ -18,14 +18,14 @@ namespace gdn {
 namespace {
 
 struct PrepArgs {
-    const void* qkv;
+    TokenStreams x;
     const void* a;
     const void* b;
     const float* A_log;
     const float* dt_bias;
     float* qk_out;
     float* gb_out;
-    int N, HQ, H, K, C;
+    int N, HQ, H, K;
     int gate_dtype;
     uint32_t flags;
     long long n_rows;   // N * 2 * HQ
@@ -63,7 +63,9 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs p) {
         const long long rr = live ? row : 0;
         const long long t = rr / (2 * p.HQ);
         const int r = (int)(rr % (2 * p.HQ));  // 0..HQ-1: q rows, HQ..2HQ-1: k rows
-        const TS* src = static_cast<const TS*>(p.qkv) + (size_t)t * p.C + (size_t)r * K + lane * VEC;
+        const TS* src = (r < p.HQ ? static_cast<const TS*>(p.x.q) + (size_t)t * p.x.sq + (size_t)r * K
+                                  : static_cast<const TS*>(p.x.k) + (size_t)t * p.x.sk + (size_t)(r - p.HQ) * K) +
+                        lane * VEC;
         float v[VEC];
         {
             const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
@@ -130,7 +132,7 @@ hipError_t launch_t(const PrepArgs& p, hipStream_t stream) {
 
 hipError_t launch_prepare(const PrepareLaunch& a, hipStream_t stream) {
     PrepArgs p;
-    p.qkv = a.qkv;
+    p.x = a.x;
     p.a = a.a;
     p.b = a.b;
     p.A_log = a.A_log;
@@ -141,7 +143,6 @@ hipError_t launch_prepare(const PrepareLaunch& a, hipStream_t stream) {
     p.HQ = a.HQ;
     p.H = a.H;
     p.K = a.K;
-    p.C = 2 * a.HQ * a.K + a.H * a.V;
     p.gate_dtype = a.gate_dtype;
     p.flags = a.flags;
     p.n_rows = (long long)a.N * 2 * a.HQ;

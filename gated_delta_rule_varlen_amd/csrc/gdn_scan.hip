@@ -53,7 +53,7 @@ namespace gdn {
 namespace {
 
 struct ScanArgs {
-    const void* qkv;
+    TokenStreams x;
     const float* qk_prep;
     const float* gb_prep;
     const void* a;
@@ -65,7 +65,7 @@ struct ScanArgs {
     float* state_out;
     const int32_t* offsets;
     int32_t* dev_status;
-    int B, N, HQ, H, K, V, C, G;
+    int B, N, HQ, H, K, V, G;
     int gate_dtype;
     uint32_t flags;
     float scale;
@@ -120,9 +120,8 @@ __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int 
         o.ga = p.gb_prep[(size_t)t * p.H + h];
         o.gb = p.gb_prep[((size_t)p.N + t) * p.H + h];
     } else {
-        const TS* row = static_cast<const TS*>(p.qkv) + (size_t)t * p.C;
-        const TS* qp = row + (size_t)kh * K;
-        const TS* kp = row + (size_t)p.HQ * K + (size_t)kh * K;
+        const TS* qp = static_cast<const TS*>(p.x.q) + (size_t)t * p.x.sq + (size_t)kh * K;
+        const TS* kp = static_cast<const TS*>(p.x.k) + (size_t)t * p.x.sk + (size_t)kh * K;
 #pragma unroll
         for (int i = 0; i < EPL / 4; ++i) {
             const f32x4 qv = load4<T>(qp + 4 * (gl + LPC * i));
@@ -142,7 +141,7 @@ __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int 
         }
         o.gb = p.b ? load_any(p.b, p.gate_dtype, gi) : 0.0f;
     }
-    const TS* vp = static_cast<const TS*>(p.qkv) + (size_t)t * p.C + (size_t)2 * p.HQ * K + (size_t)h * p.V + vbase;
+    const TS* vp = static_cast<const TS*>(p.x.v) + (size_t)t * p.x.sv + (size_t)h * p.V + vbase;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) o.v[c] = (vbase + c < p.V) ? to_f32<T>(vp[c]) : 0.0f;
 }
@@ -488,7 +487,7 @@ hipError_t launch_p(const ScanArgs& p, int dtype, hipStream_t stream) {
 
 hipError_t launch_scan_decode(const ScanLaunch& a, hipStream_t stream) {
     ScanArgs p;
-    p.qkv = a.qkv;
+    p.x = a.x;
     p.qk_prep = a.qk_prep;
     p.gb_prep = a.gb_prep;
     p.a = a.a;
@@ -506,7 +505,6 @@ hipError_t launch_scan_decode(const ScanLaunch& a, hipStream_t stream) {
     p.H = a.H;
     p.K = a.K;
     p.V = a.V;
-    p.C = 2 * a.HQ * a.K + a.H * a.V;
     p.G = a.H / a.HQ;
     p.gate_dtype = a.gate_dtype;
     p.flags = a.flags;

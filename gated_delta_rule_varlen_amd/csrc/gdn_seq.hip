@@ -34,7 +34,7 @@ namespace gdn {
 namespace {
 
 struct SeqArgs {
-    const void* qkv;
+    TokenStreams x;
     const float* qk_prep;
     const float* gb_prep;
     const void* a;
@@ -46,7 +46,7 @@ struct SeqArgs {
     float* state_out;
     const int32_t* offsets;
     int32_t* dev_status;
-    int B, N, HQ, H, K, V, C, G;
+    int B, N, HQ, H, K, V, G;
     int gate_dtype;
     uint32_t flags;
     float scale;
@@ -143,7 +143,9 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     const float rmul = (p.flags & GDN_NO_RETRIEVE) ? 0.0f : 1.0f;  // the retrieval term's weight
     const float a_mul = (!PREP && p.a && softplus) ? -expf(p.A_log[h]) : 0.0f;
     const float a_bias = (!PREP && p.a && softplus) ? p.dt_bias[h] : 0.0f;
-    const TS* qkv = static_cast<const TS*>(p.qkv);
+    const TS* const xq = static_cast<const TS*>(p.x.q);
+    const TS* const xk = static_cast<const TS*>(p.x.k);
+    const TS* const xv = static_cast<const TS*>(p.x.v);
     TS* outp = static_cast<TS*>(p.out);
 
     int captured = 0;  // tokens recorded (0 without capture)
@@ -179,9 +181,8 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
                     f.q[ps] = *reinterpret_cast<const u32x4*>(p.qk_prep + (t * p.HQ + kh) * K + rl * SVEC);
                     f.k[ps] = *reinterpret_cast<const u32x4*>(p.qk_prep + (((size_t)p.N + t) * p.HQ + kh) * K + rl * SVEC);
                 } else {
-                    const TS* row = qkv + t * p.C;
-                    f.q[ps] = *reinterpret_cast<const u32x4*>(row + (size_t)kh * K + rl * SVEC);
-                    f.k[ps] = *reinterpret_cast<const u32x4*>(row + (size_t)(p.HQ + kh) * K + rl * SVEC);
+                    f.q[ps] = *reinterpret_cast<const u32x4*>(xq + t * p.x.sq + (size_t)kh * K + rl * SVEC);
+                    f.k[ps] = *reinterpret_cast<const u32x4*>(xk + t * p.x.sk + (size_t)kh * K + rl * SVEC);
                 }
             }
         }
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
             const int col = v0 + j * VVEC;
             f.v[vp] = u32x4{0u, 0u, 0u, 0u};
             if (idx < TC * VPT && ti < n) {
-                const TS* src = qkv + (size_t)(t0 + ti) * p.C + (size_t)2 * p.HQ * K + (size_t)h * p.V + col;
+                const TS* src = xv + (size_t)(t0 + ti) * p.x.sv + (size_t)h * p.V + col;
                 if (p.vec_ok && col + VVEC <= p.V) {
                     f.v[vp] = *reinterpret_cast<const u32x4*>(src);
                 } else {
@@ -492,7 +493,7 @@ hipError_t launch_p(const SeqArgs& p, int dtype, hipStream_t stream) {
 
 hipError_t launch_scan_seq(const ScanLaunch& a, hipStream_t stream) {
     SeqArgs p;
-    p.qkv = a.qkv;
+    p.x = a.x;
     p.qk_prep = a.qk_prep;
     p.gb_prep = a.gb_prep;
     p.a = a.a;
@@ -510,7 +511,6 @@ hipError_t launch_scan_seq(const ScanLaunch& a, hipStream_t stream) {
     p.H = a.H;
     p.K = a.K;
     p.V = a.V;
-    p.C = 2 * a.HQ * a.K + a.H * a.V;
     p.G = a.H / a.HQ;
     p.gate_dtype = a.gate_dtype;
     p.flags = a.flags;

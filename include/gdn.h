@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -164,6 +164,29 @@ typedef struct gdn_scan_desc {
 } gdn_scan_desc;
 
 /* ------------------------------------------------------------------------------------------------
+ * Separate token streams (the *_strided entry points).  The pages' recurrence node reads one packed
+ * [q | k | v] row per token and lists separate query/key/value inputs as not implemented
+ * (paged_ssm.rs page, delta_claim); these entry points take the three streams apart, each with its
+ * own row stride, so that q, k and v may live in separate buffers or be strided views:
+ *   q row t (key head kh at kh*K):  q + t*q_stride   [HQ*K elements]
+ *   k row t:                        k + t*k_stride   [HQ*K]
+ *   v row t (value head h at h*V):  v + t*v_stride   [H*V]
+ * Element type qkv_dtype; strides in elements, at least the row width (GDN_ERR_SHAPE); every
+ * stream 16-byte aligned with rows starting 16-byte aligned (stride * element size a multiple of
+ * 16; GDN_ERR_ALIGN).  Streams a call does not read may be NULL: q and k of a prepared scan, v of a
+ * prepare.  A packed row of width C is q = qkv, k = qkv + HQ*K, v = qkv + 2*HQ*K, all strides C,
+ * and gives bit-identical results.
+ * ---------------------------------------------------------------------------------------------- */
+typedef struct gdn_qkv_streams {
+    const void *q;
+    const void *k;
+    const void *v;
+    int64_t q_stride;
+    int64_t k_stride;
+    int64_t v_stride;
+} gdn_qkv_streams;
+
+/* ------------------------------------------------------------------------------------------------
  * gdn_prepare_qk_gates -- paged_ssm.rs page, kernel string DELTA_PREPARE; gate math also on the
  * gated_delta_rate_activation.rs page.  Token-local: no offsets.
  *   qk_out[0, t, hq, :] = q of (t, hq), normalised when GDN_L2NORM (else copied), as fp32
@@ -176,6 +199,11 @@ typedef struct gdn_scan_desc {
 gdn_status gdn_prepare_qk_gates(const gdn_scan_desc *desc, const void *qkv, const void *a, const void *b,
                                 const float *A_log, const float *dt_bias, float *qk_out, float *gb_out,
                                 hipStream_t stream);
+
+/* gdn_prepare_qk_gates on separate token streams (v is not read and may be NULL). */
+gdn_status gdn_prepare_qk_gates_strided(const gdn_scan_desc *desc, const gdn_qkv_streams *streams, const void *a,
+                                        const void *b, const float *A_log, const float *dt_bias, float *qk_out,
+                                        float *gb_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------------
  * gdn_scan_varlen -- paged_ssm.rs page, kernel string DELTA (and the chunked variant the host fn
@@ -213,6 +241,14 @@ gdn_status gdn_scan_varlen(const gdn_scan_desc *desc, const void *qkv, const flo
                            const float *state_in, void *out, float *state_out, const int32_t *offsets,
                            void *workspace, size_t ws_bytes, int32_t *dev_status, int32_t *path_used,
                            hipStream_t stream);
+
+/* gdn_scan_varlen on separate token streams: every path, flag and argument as above, with qkv
+ * replaced by the three streams (q and k unread, and may be NULL, with prepared inputs). */
+gdn_status gdn_scan_varlen_strided(const gdn_scan_desc *desc, const gdn_qkv_streams *streams, const float *qk_prep,
+                                   const float *gb_prep, const void *a, const void *b, const float *A_log,
+                                   const float *dt_bias, const float *state_in, void *out, float *state_out,
+                                   const int32_t *offsets, void *workspace, size_t ws_bytes, int32_t *dev_status,
+                                   int32_t *path_used, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------------
  * gdn_scan_varlen_capture -- gdn_scan_varlen that also records, for speculative decoding, the

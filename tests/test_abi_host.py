@@ -32,7 +32,7 @@ def test_header_declarations_are_all_exported(abi):
 
 
 def test_version_and_status_strings(abi):
-    assert abi.lib().gdn_abi_version() == 3
+    assert abi.lib().gdn_abi_version() == 4
     for code in range(0, -10, -1):
         assert abi.status_string(code) and abi.status_string(code) != "unknown status"
     assert abi.status_string(-99) == "unknown status"
@@ -250,3 +250,48 @@ def test_per_key_gate_host_validation(abi):
     n = ctypes.c_size_t(1)
     big = scan_desc(abi, flags=pk, qkv_dtype=1, gate_dtype=1, K=64, V=64, N=64 * 2)
     assert L.gdn_scan_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == abi.OK and n.value == 0
+
+
+def scan_strided(abi, d, q=P, k=P, v=P, qs=None, ks=None, vs=None, qk=None, gb=None, off=P, out=P):
+    w_qk, w_v = d.HQ * d.K, d.H * d.V
+    s = abi.QKVStreams(q, k, v, w_qk if qs is None else qs, w_qk if ks is None else ks, w_v if vs is None else vs)
+    return abi.lib().gdn_scan_varlen_strided(ctypes.byref(d), ctypes.byref(s), qk, gb, None, None, None, None, None,
+                                             out, None, off, None, 0, None, None, None)
+
+
+@pytest.mark.parametrize(
+    "fields,kw,want",
+    [
+        ({}, dict(qs=63), "ERR_SHAPE"),  # q rows overlap (stride below the row width 2*32)
+        ({}, dict(vs=60), "ERR_SHAPE"),
+        ({}, dict(ks=65), "ERR_ALIGN"),  # rows would not start 16-byte aligned
+        ({}, dict(v=P + 4), "ERR_ALIGN"),
+        ({}, dict(q=None), "ERR_NULL"),
+        ({}, dict(v=None), "ERR_NULL"),
+        ({}, dict(qk=P, gb=P, q=None, k=None, qs=1, ks=1, off=None), "ERR_NULL"),  # prepared: q, k unread
+        (dict(qkv_dtype=1, gate_dtype=1, V=33, H=2), dict(vs=72), "ERR_OK"),  # a packed row could not hold these
+        (dict(N=2**30), dict(qs=2**40), "ERR_OVERFLOW"),
+        ({}, dict(off=None), "ERR_NULL"),
+    ],
+)
+def test_scan_strided_host_validation(abi, fields, kw, want):
+    d = scan_desc(abi, **fields)
+    if want == "ERR_OK":
+        # valid streams: the call gets past the stream checks and fails on the missing offsets
+        assert scan_strided(abi, d, off=None, **kw) == abi.ERR_NULL
+        return
+    assert scan_strided(abi, d, **kw) == getattr(abi, want)
+
+
+def test_prepare_strided_host_validation(abi):
+    L = abi.lib()
+    d = scan_desc(abi)
+    good = abi.QKVStreams(P, P, None, 64, 64, 0)  # v is not read by prepare
+    assert L.gdn_prepare_qk_gates_strided(ctypes.byref(d), None, None, None, None, None, P, P, None) == abi.ERR_NULL
+    bad = abi.QKVStreams(P, P, None, 62, 64, 0)
+    assert L.gdn_prepare_qk_gates_strided(ctypes.byref(d), ctypes.byref(bad), None, None, None, None, P, P,
+                                          None) == abi.ERR_SHAPE
+    assert L.gdn_prepare_qk_gates_strided(ctypes.byref(d), ctypes.byref(good), None, None, None, None, None, None,
+                                          None) == abi.ERR_NULL
+    assert L.gdn_prepare_qk_gates_strided(ctypes.byref(d), ctypes.byref(good), None, None, None, None, P + 4, P,
+                                          None) == abi.ERR_ALIGN
