@@ -16,7 +16,9 @@
 //     blocks also copy the sequence's first captured token rows into its update slots and zero the
 //     slots after them.
 //
-// Every block checks the whole offsets array first and writes nothing when it is malformed.
+// Every block checks the whole offsets array first and writes nothing when it is malformed; the
+// offsets are staged in LDS on the way (up to kStagedOffsets entries), so that body blocks map their
+// tokens to sequences without chains of dependent global loads.
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -25,7 +27,8 @@
 namespace gdn {
 namespace {
 
-constexpr int kConvTile = 16;  // tokens per body block
+constexpr int kConvTile = 16;        // tokens per body block
+constexpr int kStagedOffsets = 2048;  // offsets kept in LDS when B + 1 fits
 
 struct ConvArgs {
     const void* x;
@@ -110,6 +113,20 @@ __device__ __forceinline__ void capture_rows(const ConvArgs& p, int b, int start
     }
 }
 
+// The whole-call offsets check of offsets_malformed, storing each entry into s_off on the way when
+// s_off is given.  Ends with a block barrier, after which s_off is complete.
+__device__ __forceinline__ bool check_stage_offsets(const int32_t* __restrict__ offsets, int B, int N, int* s_off) {
+    int bad = 0;
+    for (int i = threadIdx.x; i <= B; i += blockDim.x) {
+        const int o = offsets[i];
+        if (s_off != nullptr) s_off[i] = o;
+        if (i == 0) bad |= (o != 0);
+        else bad |= (offsets[i - 1] > o);
+        if (i == B) bad |= (o != N);
+    }
+    return __syncthreads_or(bad) != 0;
+}
+
 // SiLU z / (1 + e^-z) with the hardware exp2 and reciprocal (each within a couple of ulp of fp32):
 // the IEEE-exact expf and division cost ~35 VALU instructions per element and made the conv
 // arithmetic-bound.  z -> -inf gives e^-z = inf, rcp(inf) = 0 and an output of -0 (the limit).
@@ -126,14 +143,45 @@ template <typename T, typename S, int VEC, int W>
 __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     using TS = typename T::storage;
     using SS = typename S::storage;
-    const bool malformed = offsets_malformed(p.offsets, p.B, p.N);
+    __shared__ int s_off[kStagedOffsets];
+    const bool staged = p.B < kStagedOffsets;
+    const bool malformed = check_stage_offsets(p.offsets, p.B, p.N, staged ? s_off : nullptr);
     report_status(p.dev_status, malformed);
     if (malformed) return;
+    auto off = [&](int i) { return staged ? s_off[i] : p.offsets[i]; };
+    // sequence containing token t (t < N): the last b with off(b) <= t
+    auto find_seq = [&](int t) {
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off(mid) <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    };
 
     const int item = (int)(blockIdx.x / (unsigned)p.n_cblk);
     const int cvec = (int)(blockIdx.x % (unsigned)p.n_cblk) * (int)blockDim.x + (int)threadIdx.x;
     if (cvec >= p.n_cvec) return;
     const int C = p.C, D = p.D, L = p.L;
+
+    // Body blocks: which tokens of the tile have local index >= L (the rest belong to head blocks).
+    // A tile without any -- every tile of a batch of short sequences -- ends here, before any load.
+    unsigned body_mask = 0;
+    if (item >= p.B) {
+        const int t0 = (item - p.B) * p.tile;
+        const int t1 = min(t0 + p.tile, p.N);
+        int b = find_seq(t0);
+        int next = off(b + 1);
+        for (int t = t0; t < t1; ++t) {
+            while (next <= t) {
+                ++b;
+                next = off(b + 1);
+            }
+            if (t - off(b) >= L) body_mask |= 1u << (t - t0);
+        }
+        if (body_mask == 0) return;
+    }
     const int c0 = cvec * VEC;
     const TS* __restrict__ x = static_cast<const TS*>(p.x);
     TS* __restrict__ y = static_cast<TS*>(p.y);
@@ -171,20 +219,36 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     if constexpr (VEC > 1 && W > 1) {
       if (item < p.B && D == 1) {
         // ---- head, dilation 1: the thread's window block (VEC channels x L entries, contiguous) is
-        // moved with 16-byte vector accesses and held in registers; L = W-1 is a compile-time size.
+        // held in registers; L = W-1 is a compile-time size.  In a block whose threads are all live,
+        // the block's whole window range (contiguous in memory) moves between HBM and LDS with
+        // consecutive 16-byte accesses per lane, and each thread takes its block from LDS: a thread's
+        // own block is VEC*L entries wide, so direct per-thread vector accesses would stride lanes
+        // that far apart and cost several memory requests per lane.
         constexpr int L1 = W - 1;
         constexpr int NE = VEC * L1;                           // window elements of this thread
         constexpr int NCH = NE * (int)sizeof(SS) / 16;         // 16-byte chunks
         static_assert(NE * sizeof(SS) % 16 == 0, "window block is whole 16-byte chunks");
+        __shared__ u32x4 s_win[256 * NCH];
+        const int nthr = (int)blockDim.x, tid = (int)threadIdx.x;
+        const bool full_block = ((int)(blockIdx.x % (unsigned)p.n_cblk) + 1) * nthr <= p.n_cvec;  // block-uniform
         const int b = item;
-        const int start = p.offsets[b];
-        const int len = p.offsets[b + 1] - start;
+        const int start = off(b);
+        const int len = off(b + 1) - start;
         const size_t wrow = ((size_t)b * C + c0) * (size_t)L1;  // window of channel c0 + i at wrow + i*L1
+        // the block's window range, in 16-byte chunks, starts where thread 0's block does
+        const size_t wblk = (((size_t)b * C + (size_t)(cvec - tid) * VEC) * (size_t)L1 * sizeof(SS)) / 16;
         union {
             u32x4 v[NCH];
             SS e[NE];
         } win;
-        if (p.state_in != nullptr) {
+        if (p.state_in != nullptr && full_block) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(p.state_in) + wblk;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) s_win[k * nthr + tid] = src[k * nthr + tid];
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) win.v[k] = s_win[tid * NCH + k];
+        } else if (p.state_in != nullptr) {
             const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const SS*>(p.state_in) + wrow);
 #pragma unroll
             for (int k = 0; k < NCH; ++k) win.v[k] = src[k];
@@ -236,9 +300,20 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
                     nw.e[i * L1 + j] = v;
                 }
             }
-            u32x4* dst = reinterpret_cast<u32x4*>(static_cast<SS*>(p.state_out) + wrow);
+            if (full_block) {
+                // a thread reads and writes only its own block of s_win after the load barrier; the
+                // barrier below hands the blocks to the threads that store them
 #pragma unroll
-            for (int k = 0; k < NCH; ++k) dst[k] = nw.v[k];
+                for (int k = 0; k < NCH; ++k) s_win[tid * NCH + k] = nw.v[k];
+                __syncthreads();
+                u32x4* dst = reinterpret_cast<u32x4*>(p.state_out) + wblk;
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) dst[k * nthr + tid] = s_win[k * nthr + tid];
+            } else {
+                u32x4* dst = reinterpret_cast<u32x4*>(static_cast<SS*>(p.state_out) + wrow);
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) dst[k] = nw.v[k];
+            }
         }
         if (p.cap > 0) capture_rows<T, VEC>(p, b, start, len, c0);
         return;
@@ -248,8 +323,8 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     if (item < p.B) {
         // ---- head: the first min(L, len) tokens of sequence b, then the new window ----------------
         const int b = item;
-        const int start = p.offsets[b];
-        const int len = p.offsets[b + 1] - start;
+        const int start = off(b);
+        const int len = off(b + 1) - start;
         const SS* st_in = static_cast<const SS*>(p.state_in);
         SS* st_out = static_cast<SS*>(p.state_out);
         const size_t wrow = ((size_t)b * C + c0) * (size_t)L;  // window of channel c0 + i at wrow + i*L
@@ -312,17 +387,10 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
                 const int t = t0 - L1 + r;
                 rows[r] = (t >= 0 && t < t1) ? *reinterpret_cast<const u32x4*>(x + (size_t)t * C + c0) : u32x4{0u, 0u, 0u, 0u};
             }
-            int b = find_sequence(p.offsets, p.B, t0);
-            int next = p.offsets[b + 1];
 #pragma unroll
             for (int i = 0; i < kConvTile; ++i) {
                 const int t = t0 + i;
-                if (t >= t1) break;
-                while (next <= t) {
-                    ++b;
-                    next = p.offsets[b + 1];
-                }
-                if (t - p.offsets[b] < L1) continue;  // reaches into the window: computed by the head block
+                if (!(body_mask & (1u << i))) continue;
                 float acc[VEC];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) acc[e] = bias[e];
@@ -340,17 +408,10 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     }
     const int t0 = (item - p.B) * p.tile;
     const int t1 = min(t0 + p.tile, p.N);
-    int b = find_sequence(p.offsets, p.B, t0);
-    int next = p.offsets[b + 1];
     float ring[W][VEC];  // ring[j] = x[t - (W-1-j)*D]
     int ring_t = -2;
     for (int t = t0; t < t1; ++t) {
-        while (next <= t) {
-            ++b;
-            next = p.offsets[b + 1];
-        }
-        const int l = t - p.offsets[b];
-        if (l < L) continue;  // reaches into the window: computed by the head block
+        if (!(body_mask & (1u << (t - t0)))) continue;  // reaches into the window: a head block's
         if (D == 1 && ring_t == t - 1) {
 #pragma unroll
             for (int j = 0; j + 1 < W; ++j)
