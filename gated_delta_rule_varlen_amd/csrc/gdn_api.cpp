@@ -95,11 +95,12 @@ bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay, bool 
            gdn::chunked_shape_supported(d->K, d->V, d->qkv_dtype);
 }
 
-// AUTO: DECODE for at most two tokens per sequence on average; CHUNK when eligible, the average
-// sequence fills at least one chunk of 64 tokens and the workspace suffices; SEQ otherwise.
+// AUTO: DECODE for at most kDecodeShortTokens tokens per sequence on average (single tokens and
+// short blocks stream the state once); CHUNK when eligible, the average sequence fills at least one
+// chunk of 64 tokens and the workspace suffices; SEQ otherwise.
 int resolve_path(const gdn_scan_desc* d, bool prepared, bool has_decay, bool capture, size_t ws_bytes) {
     if (d->path != GDN_PATH_AUTO) return d->path;
-    if ((long long)d->N <= 2ll * d->B) return GDN_PATH_DECODE;
+    if ((long long)d->N <= (long long)gdn::kDecodeShortTokens * d->B) return GDN_PATH_DECODE;
     if (chunk_eligible(d, prepared, has_decay, capture) && (long long)d->N >= 64ll * d->B &&
         ws_bytes >= gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
         return GDN_PATH_CHUNK;

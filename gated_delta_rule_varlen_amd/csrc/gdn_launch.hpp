@@ -110,6 +110,10 @@ hipError_t launch_decode_step(const DecodeStepLaunch& a, hipStream_t stream);
 bool decode_step_supported(int K, int V, int G, int W, int D);
 bool chunked_shape_supported(int K, int V, int qkv_dtype);
 
+// Longest sequence the DECODE kernel carries column by column with staged token operands; AUTO
+// takes DECODE while the average sequence is no longer than this.
+constexpr int kDecodeShortTokens = 8;
+
 // Limits of the launch grids (checked by the entry points before launching).
 constexpr long long kMaxBlocks = (1ll << 31) - 1;
 

@@ -26,6 +26,11 @@
 //     token operands first, then the state columns of a group with all their loads in flight, each
 //     column reduced, updated, written back and its output taken in turn, so reads and writes of
 //     the state interleave.  Same arithmetic in the same order, so the results are bit-identical;
+//   * "SHORT" instances serve calls with more tokens than sequences.  A block whose sequence has
+//     2 .. GDN_DECODE_SHORT tokens (a speculative verification step, a short prefill) first stages
+//     the tokens' normalised q and k, gates, q^.k^ and its columns' v in LDS, once per block instead
+//     of once per lane group, then streams its state columns as the single-token form does, each
+//     column carried through all the tokens before it is stored;
 //   * with a per-key-channel decay (GDN_GATE_PER_KEY; "PK" instances) thread i of the block
 //     evaluates the decay of key channel i once per token into LDS (every wave of a block serves
 //     the same head), and each lane decays its state slice before the two dot products
@@ -47,6 +52,10 @@
 // moves the state at 6.2 TB/s, against 5.7 TB/s for load-all / compute / store-all at 8 columns.
 #ifndef GDN_DECODE_STREAM
 #define GDN_DECODE_STREAM 4
+#endif
+// Longest sequence the SHORT instances carry column by column with staged token operands.
+#ifndef GDN_DECODE_SHORT
+#define GDN_DECODE_SHORT kDecodeShortTokens
 #endif
 
 namespace gdn {
@@ -146,9 +155,10 @@ __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int 
     for (int c = 0; c < CPL; ++c) o.v[c] = (vbase + c < p.V) ? to_f32<T>(vp[c]) : 0.0f;
 }
 
-template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK>
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK, bool SHORT>
 __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
     static_assert(!(PK && PREP), "the per-key decay is evaluated in-kernel from raw inputs");
+    static_assert(!(PK && SHORT), "per-key decays take the general loop");
     constexpr int EPL = K / LPC;  // state elements per lane per column
     static_assert(EPL % 4 == 0, "whole 16-byte chunks per lane");
     constexpr int GPW = 64 / LPC;  // lane groups per wave
@@ -218,7 +228,185 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
         }
     };
 
-    if constexpr (GDN_DECODE_STREAM > 0) {
+    if constexpr (SHORT) {
+        // ---- 2 .. TSH tokens, a whole column tile and a carried state (block-uniform conditions) --
+        constexpr int TSH = GDN_DECODE_SHORT;
+        constexpr int BC = NW * WC;        // columns of the block
+        constexpr int EPT = K / 32;        // q/k elements per staging thread (32 threads per token)
+        constexpr int PD = GDN_DECODE_STREAM > 0 ? (GDN_DECODE_STREAM < CPL ? GDN_DECODE_STREAM : CPL) : 1;
+        __shared__ __align__(16) float shq[TSH][K];
+        __shared__ __align__(16) float shk[TSH][K];
+        __shared__ float shv[TSH][BC];
+        __shared__ float shg[TSH], shb[TSH], shqk[TSH];
+        const int ntok = end - start;  // tokens of the sequence
+        const bool full_tile = (vt * NW + NW) * WC <= p.V;
+        if (ntok >= 2 && ntok <= TSH && full_tile && p.state_in != nullptr && p.state_out != nullptr) {
+            const int tid = (int)threadIdx.x;
+            const int vb0 = vt * NW * WC;  // first column of the block
+            // (1) token operands, once per block: 32 threads per token, EPT elements each
+            for (int tb = 0; tb < ntok; tb += 2 * NW) {
+                const int t = tb + tid / 32, j = tid % 32;
+                const bool live = t < ntok;
+                const int tt = start + (live ? t : 0);
+                float qv[EPT], kv[EPT];
+                if constexpr (PREP) {
+                    const float* qp = p.qk_prep + ((size_t)tt * p.HQ + kh) * K + j * EPT;
+                    const float* kp = p.qk_prep + (((size_t)p.N + tt) * p.HQ + kh) * K + j * EPT;
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e) {
+                        qv[e] = qp[e];
+                        kv[e] = kp[e];
+                    }
+                } else {
+                    const TS* qp = static_cast<const TS*>(p.x.q) + (size_t)tt * p.x.sq + (size_t)kh * K + j * EPT;
+                    const TS* kp = static_cast<const TS*>(p.x.k) + (size_t)tt * p.x.sk + (size_t)kh * K + j * EPT;
+                    if constexpr (EPT % 4 == 0) {
+#pragma unroll
+                        for (int e = 0; e < EPT; e += 4) {
+                            const f32x4 a4 = load4<T>(qp + e), b4 = load4<T>(kp + e);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                qv[e + i] = a4[i];
+                                kv[e + i] = b4[i];
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < EPT; ++e) {
+                            qv[e] = to_f32<T>(qp[e]);
+                            kv[e] = to_f32<T>(kp[e]);
+                        }
+                    }
+                }
+                float qk = 0.0f, nq = 0.0f, nk = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) {
+                    qk = fmaf(qv[e], kv[e], qk);
+                    nq = fmaf(qv[e], qv[e], nq);
+                    nk = fmaf(kv[e], kv[e], nk);
+                }
+                qk = group_sum<32>(qk);
+                float rq = 1.0f, rk = 1.0f;
+                if (!PREP && l2) {
+                    rq = rsqrtf(group_sum<32>(nq) + 1e-12f);
+                    rk = rsqrtf(group_sum<32>(nk) + 1e-12f);
+                }
+                if (live) {
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e) {
+                        shq[t][j * EPT + e] = qv[e] * rq;
+                        shk[t][j * EPT + e] = kv[e] * rk;
+                    }
+                    if (j == 0) {
+                        float g, beta;
+                        const size_t gi = (size_t)tt * p.H + h;
+                        if constexpr (PREP) {
+                            g = p.gb_prep[gi];
+                            beta = p.gb_prep[(size_t)p.N * p.H + gi];
+                        } else {
+                            g = 1.0f;
+                            if (p.a) {
+                                const float x = load_any(p.a, p.gate_dtype, gi);
+                                g = softplus ? expf(a_mul * softplus_f(x + a_bias)) : expf(x);
+                            }
+                            beta = 1.0f;
+                            if (p.b) {
+                                const float x = load_any(p.b, p.gate_dtype, gi);
+                                beta = sigmoid ? 1.0f / (1.0f + expf(-x)) : x;
+                            }
+                        }
+                        shg[t] = g;
+                        shb[t] = beta;
+                        shqk[t] = qk * rq * rk;
+                    }
+                }
+            }
+            for (int i = tid; i < ntok * BC; i += 64 * NW) {
+                const int t = i / BC, col = i % BC;
+                shv[t][col] = to_f32<T>(static_cast<const TS*>(p.x.v)[(size_t)(start + t) * p.x.sv + (size_t)h * p.V + vb0 + col]);
+            }
+            __syncthreads();
+
+            // (2) the group's columns, streamed with PD columns of loads ahead; each column goes
+            // through all the tokens, then is stored
+            f32x4 ring[PD + 1][EPL / 4];
+            auto load_col = [&](int c, f32x4 (&dst)[EPL / 4]) {
+                const float* sp = p.state_in + (col0 + vbase + c) * K;
+#pragma unroll
+                for (int i = 0; i < EPL / 4; ++i) dst[i] = ld_state<NT>(sp + 4 * (gl + LPC * i));
+            };
+#pragma unroll
+            for (int c = 0; c < PD; ++c) load_col(c, ring[c]);
+            const int lc = vbase - vb0;  // block-local column of the group's first column
+            float mine[TSH], dmine[TSH];
+#pragma unroll
+            for (int t = 0; t < TSH; ++t) mine[t] = dmine[t] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                if (c + PD < CPL) load_col(c + PD, ring[(c + PD) % (PD + 1)]);
+                f32x4(&sc)[EPL / 4] = ring[c % (PD + 1)];
+#pragma unroll
+                for (int t = 0; t < TSH; ++t) {
+                    if (t >= ntok) break;
+                    f32x4 qf[EPL / 4], kf[EPL / 4];
+#pragma unroll
+                    for (int i = 0; i < EPL / 4; ++i) {
+                        qf[i] = *reinterpret_cast<const f32x4*>(&shq[t][4 * (gl + LPC * i)]);
+                        kf[i] = *reinterpret_cast<const f32x4*>(&shk[t][4 * (gl + LPC * i)]);
+                    }
+                    float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < EPL / 4; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            pk = fmaf(sc[i][e], kf[i][e], pk);
+                            pq = fmaf(sc[i][e], qf[i][e], pq);
+                        }
+                    pk = group_sum<LPC>(pk);
+                    pq = group_sum<LPC>(pq);
+                    const float g = shg[t], beta = shb[t];
+                    const float r = rmul * (g * pk);
+                    const float delta = beta * (shv[t][lc + c] - r);
+                    const float o = p.scale * fmaf(g, pq, delta * shqk[t]);
+#pragma unroll
+                    for (int i = 0; i < EPL / 4; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sc[i][e] = fmaf(delta, kf[i][e], g * sc[i][e]);
+                    if (gl == c) {
+                        mine[t] = o;
+                        dmine[t] = delta;
+                    }
+                }
+                float* sp = p.state_out + (col0 + vbase + c) * K;
+#pragma unroll
+                for (int i = 0; i < EPL / 4; ++i) st_state<NT>(sp + 4 * (gl + LPC * i), sc[i]);
+            }
+#pragma unroll
+            for (int t = 0; t < TSH; ++t) {
+                if (t >= ntok) break;
+                if (gl < CPL) outp[((size_t)(start + t) * p.H + h) * p.V + vbase + gl] = from_f32<T>(mine[t]);
+            }
+            if (p.cap > 0) {
+#pragma unroll
+                for (int t = 0; t < TSH; ++t) {
+                    if (t >= captured) break;
+                    if (cap_g) *crow.g(t, h) = shg[t];
+                    if (cap_k) {
+                        float* kd = crow.k(t, kh);
+#pragma unroll
+                        for (int m = 0; m < EPL / 4; ++m)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) kd[4 * (gl + LPC * m) + e] = shk[t][4 * (gl + LPC * m) + e];
+                    }
+                    if (cap_d) crow.d(t, h)[vbase + gl] = dmine[t];
+                }
+                capture_zeros();
+            }
+            return;
+        }
+    }
+
+    if constexpr (GDN_DECODE_STREAM > 0 && !SHORT) {
         // One token, a whole column tile and a carried state (block-uniform conditions): stream the
         // columns with GDN_DECODE_STREAM columns of loads ahead, storing each column as soon as it is
         // updated, so that each lane keeps few accesses in flight and reads and writes interleave.
@@ -435,15 +623,15 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
     if (p.cap > 0) capture_zeros();
 }
 
-template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK>
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK, bool SHORT>
 hipError_t launch_tile(ScanArgs p, hipStream_t stream) {
     constexpr int BC = (64 / LPC) * CPL * NW;  // columns per block
     p.n_vtiles = (p.V + BC - 1) / BC;
     const long long blocks = (long long)p.B * p.H * p.n_vtiles;
     if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
     p.n_blocks = (int)blocks;
-    hipLaunchKernelGGL((scan_kernel<T, K, LPC, CPL, NW, PREP, NT, PK>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream,
-                       p);
+    hipLaunchKernelGGL((scan_kernel<T, K, LPC, CPL, NW, PREP, NT, PK, SHORT>), dim3((unsigned)blocks), dim3(64 * NW), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -459,7 +647,10 @@ template <typename T, int K, bool PREP, bool PK>
 hipError_t launch_k(const ScanArgs& p, hipStream_t stream) {
     constexpr int LPC = K >= 64 ? 16 : 8;
     constexpr int CPL = K >= 256 ? (GDN_DECODE_CPL > 1 ? GDN_DECODE_CPL / 2 : 1) : GDN_DECODE_CPL;
-    return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, PK>(p, stream);
+    // calls with more tokens than sequences hold short sequences: SHORT instances (per-key decays
+    // take the general loop of the plain instances)
+    if (!PK && p.N > p.B) return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, false, true>(p, stream);
+    return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, PK, false>(p, stream);
 }
 
 template <typename T, bool PREP, bool PK>

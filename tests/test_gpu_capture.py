@@ -259,7 +259,7 @@ def test_speculative_verification_step_replay(torch):
              dt_bias=dev(w.dt_bias, "f32"))
     S0 = dev(w.state, "f32")
     _, _, caps, used = gdn.scan_varlen_capture(y, off, cap=CAP, counts=cnt, HQ=HQ, H=H, K=K, V=V, state_in=S0, **A)
-    assert used == "seq"
+    assert used == "decode"  # at most 8 tokens per sequence on average
     # replay on the device in fp32 (torch: plumbing for the check only)
     g = caps[:, :CAP * H].reshape(B, CAP, H)
     kh = caps[:, CAP * H:CAP * (H + HQ * K)].reshape(B, CAP, HQ, K).repeat_interleave(H // HQ, dim=2)
