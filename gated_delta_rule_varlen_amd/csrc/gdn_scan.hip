@@ -29,8 +29,9 @@
 //   * "SHORT" instances serve calls with more tokens than sequences.  A block whose sequence has
 //     2 .. GDN_DECODE_SHORT tokens (a speculative verification step, a short prefill) first stages
 //     the tokens' normalised q and k, gates, q^.k^ and its columns' v in LDS, once per block instead
-//     of once per lane group, then streams its state columns as the single-token form does, each
-//     column carried through all the tokens before it is stored;
+//     of once per lane group, then carries its whole column tile through the tokens with the state
+//     kept as s = c * s' (c the product of the decays so far, uniform over the block), so that a
+//     token costs the two dot products and one fused multiply-add per state element;
 //   * with a per-key-channel decay (GDN_GATE_PER_KEY; "PK" instances) thread i of the block
 //     evaluates the decay of key channel i once per token into LDS (every wave of a block serves
 //     the same head), and each lane decays its state slice before the two dot products
@@ -233,7 +234,6 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
         constexpr int TSH = GDN_DECODE_SHORT;
         constexpr int BC = NW * WC;        // columns of the block
         constexpr int EPT = K / 32;        // q/k elements per staging thread (32 threads per token)
-        constexpr int PD = GDN_DECODE_STREAM > 0 ? (GDN_DECODE_STREAM < CPL ? GDN_DECODE_STREAM : CPL) : 1;
         __shared__ __align__(16) float shq[TSH][K];
         __shared__ __align__(16) float shk[TSH][K];
         __shared__ float shv[TSH][BC];
@@ -327,64 +327,90 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
             }
             __syncthreads();
 
-            // (2) the group's columns, streamed with PD columns of loads ahead; each column goes
-            // through all the tokens, then is stored
-            f32x4 ring[PD + 1][EPL / 4];
-            auto load_col = [&](int c, f32x4 (&dst)[EPL / 4]) {
-                const float* sp = p.state_in + (col0 + vbase + c) * K;
-#pragma unroll
-                for (int i = 0; i < EPL / 4; ++i) dst[i] = ld_state<NT>(sp + 4 * (gl + LPC * i));
-            };
-#pragma unroll
-            for (int c = 0; c < PD; ++c) load_col(c, ring[c]);
-            const int lc = vbase - vb0;  // block-local column of the group's first column
-            float mine[TSH], dmine[TSH];
-#pragma unroll
-            for (int t = 0; t < TSH; ++t) mine[t] = dmine[t] = 0.0f;
+            // (2) the tile's columns go through the tokens together, the state kept as s = c * s' with
+            // a block-uniform scale c (the product of the decays so far), so that a token's update is
+            // one fused multiply-add per element.  When c would leave [1e-30, 1e30] (including a zero
+            // decay) it is folded into s' first.
+            f32x4 sc[CPL][EPL / 4];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                if (c + PD < CPL) load_col(c + PD, ring[(c + PD) % (PD + 1)]);
-                f32x4(&sc)[EPL / 4] = ring[c % (PD + 1)];
+                const float* sp = p.state_in + (col0 + vbase + c) * K;
 #pragma unroll
-                for (int t = 0; t < TSH; ++t) {
-                    if (t >= ntok) break;
-                    f32x4 qf[EPL / 4], kf[EPL / 4];
+                for (int i = 0; i < EPL / 4; ++i) sc[c][i] = ld_state<NT>(sp + 4 * (gl + LPC * i));
+            }
+            const int lc = vbase - vb0;
+            float cs = 1.0f;
 #pragma unroll
-                    for (int i = 0; i < EPL / 4; ++i) {
-                        qf[i] = *reinterpret_cast<const f32x4*>(&shq[t][4 * (gl + LPC * i)]);
-                        kf[i] = *reinterpret_cast<const f32x4*>(&shk[t][4 * (gl + LPC * i)]);
-                    }
-                    float pk = 0.0f, pq = 0.0f;
+            for (int t = 0; t < TSH; ++t) {
+                if (t >= ntok) break;
+                f32x4 qf[EPL / 4], kf[EPL / 4];
+#pragma unroll
+                for (int i = 0; i < EPL / 4; ++i) {
+                    qf[i] = *reinterpret_cast<const f32x4*>(&shq[t][4 * (gl + LPC * i)]);
+                    kf[i] = *reinterpret_cast<const f32x4*>(&shk[t][4 * (gl + LPC * i)]);
+                }
+                const float g = shg[t], beta = shb[t], qk = shqk[t];
+                float cn = cs * g;
+                if (!(cn >= 1e-30f && cn <= 1e30f)) {
+                    // block-uniform: fold the scale, this token's decay included, into the kept state
+                    // (a zero or tiny decay leaves a zero state, as the recurrence does)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                        for (int i = 0; i < EPL / 4; ++i)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) sc[c][i][e] *= cn;
+                    cn = 1.0f;
+                }
+                cs = cn;
+                const float icn = 1.0f / cn;
+                float pk[CPL], pq[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    pk[c] = 0.0f;
+                    pq[c] = 0.0f;
 #pragma unroll
                     for (int i = 0; i < EPL / 4; ++i)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            pk = fmaf(sc[i][e], kf[i][e], pk);
-                            pq = fmaf(sc[i][e], qf[i][e], pq);
+                            pk[c] = fmaf(sc[c][i][e], kf[i][e], pk[c]);
+                            pq[c] = fmaf(sc[c][i][e], qf[i][e], pq[c]);
                         }
-                    pk = group_sum<LPC>(pk);
-                    pq = group_sum<LPC>(pq);
-                    const float g = shg[t], beta = shb[t];
-                    const float r = rmul * (g * pk);
+                }
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    pk[c] = group_sum<LPC>(pk[c]);
+                    pq[c] = group_sum<LPC>(pq[c]);
+                }
+                float mine = 0.0f, dm = 0.0f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const float r = rmul * (cn * pk[c]);
                     const float delta = beta * (shv[t][lc + c] - r);
-                    const float o = p.scale * fmaf(g, pq, delta * shqk[t]);
+                    const float o = p.scale * fmaf(cn, pq[c], delta * qk);
+                    const float dc = delta * icn;
 #pragma unroll
                     for (int i = 0; i < EPL / 4; ++i)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) sc[i][e] = fmaf(delta, kf[i][e], g * sc[i][e]);
+                        for (int e = 0; e < 4; ++e) sc[c][i][e] = fmaf(dc, kf[i][e], sc[c][i][e]);
                     if (gl == c) {
-                        mine[t] = o;
-                        dmine[t] = delta;
+                        mine = o;
+                        dm = delta;
                     }
                 }
-                float* sp = p.state_out + (col0 + vbase + c) * K;
-#pragma unroll
-                for (int i = 0; i < EPL / 4; ++i) st_state<NT>(sp + 4 * (gl + LPC * i), sc[i]);
+                if (gl < CPL) outp[((size_t)(start + t) * p.H + h) * p.V + vbase + gl] = from_f32<T>(mine);
+                if (cap_d && t < captured) crow.d(t, h)[vbase + gl] = dm;
             }
 #pragma unroll
-            for (int t = 0; t < TSH; ++t) {
-                if (t >= ntok) break;
-                if (gl < CPL) outp[((size_t)(start + t) * p.H + h) * p.V + vbase + gl] = from_f32<T>(mine[t]);
+            for (int c = 0; c < CPL; ++c) {
+                float* sp = p.state_out + (col0 + vbase + c) * K;
+#pragma unroll
+                for (int i = 0; i < EPL / 4; ++i) {
+                    f32x4 v = sc[c][i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] *= cs;
+                    st_state<NT>(sp + 4 * (gl + LPC * i), v);
+                }
             }
             if (p.cap > 0) {
 #pragma unroll
@@ -398,7 +424,6 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
 #pragma unroll
                             for (int e = 0; e < 4; ++e) kd[4 * (gl + LPC * m) + e] = shk[t][4 * (gl + LPC * m) + e];
                     }
-                    if (cap_d) crow.d(t, h)[vbase + gl] = dmine[t];
                 }
                 capture_zeros();
             }

@@ -104,3 +104,19 @@ def test_auto_takes_decode_for_short_batches(torch):
     assert used2 == "seq"
     assert_close(f64(out), f64(o2), TOL[w.io], "decode vs seq out")
     assert_close(f64(st), f64(s2), TOL[w.io], "decode vs seq state")
+
+
+def test_short_sequences_with_extreme_decays(torch):
+    """Raw log-decays from -200 (a decay that is 0 in fp32) to +10 (growth) on some tokens: the scaled
+    state of the short form folds its scale into the state whenever it leaves [1e-30, 1e30]."""
+    w = workloads.make(name="short_extreme", seed=840, lengths=[8, 6, 8, 3, 5, 8], HQ=1, H=2, K=64, V=64, io="f32",
+                       softplus=False, decay_range=(-1.0, 0.0))
+    a = workloads.from_raw(w.a, w.gate_dtype).astype(np.float32).copy()
+    rng = np.random.default_rng(841)
+    idx = rng.choice(a.size, size=a.size // 4, replace=False)
+    a.flat[idx] = rng.choice(np.array([-200.0, -80.0, -40.0, 4.0, 10.0], np.float32), size=idx.size)
+    w.a = workloads.to_raw(a, w.gate_dtype)
+    out, st, used = run(torch, w)
+    assert used == "decode"
+    assert np.all(np.isfinite(f64(out))) and np.all(np.isfinite(f64(st)))
+    check(w, out, st, what="extreme decays")
