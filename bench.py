@@ -393,8 +393,8 @@ def copy_calibration(torch, steps: int, warmup: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "long", "edge_fp16", "tiny_fp32", "verify"])
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "seq", "chunk"])
