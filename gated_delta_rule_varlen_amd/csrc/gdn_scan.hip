@@ -31,7 +31,8 @@
 //     the tokens' normalised q and k, gates, q^.k^ and its columns' v in LDS, once per block instead
 //     of once per lane group, then carries its whole column tile through the tokens with the state
 //     kept as s = c * s' (c the product of the decays so far, uniform over the block), so that a
-//     token costs the two dot products and one fused multiply-add per state element;
+//     token costs the two dot products and one fused multiply-add per state element (per-key
+//     decays are staged per channel too and applied to the tile directly);
 //   * with a per-key-channel decay (GDN_GATE_PER_KEY; "PK" instances) thread i of the block
 //     evaluates the decay of key channel i once per token into LDS (every wave of a block serves
 //     the same head), and each lane decays its state slice before the two dot products
@@ -159,7 +160,6 @@ __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int 
 template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK, bool SHORT>
 __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
     static_assert(!(PK && PREP), "the per-key decay is evaluated in-kernel from raw inputs");
-    static_assert(!(PK && SHORT), "per-key decays take the general loop");
     constexpr int EPL = K / LPC;  // state elements per lane per column
     static_assert(EPL % 4 == 0, "whole 16-byte chunks per lane");
     constexpr int GPW = 64 / LPC;  // lane groups per wave
@@ -238,6 +238,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
         __shared__ __align__(16) float shk[TSH][K];
         __shared__ float shv[TSH][BC];
         __shared__ float shg[TSH], shb[TSH], shqk[TSH];
+        __shared__ __align__(16) float shgk[PK ? TSH : 1][PK ? K : 1];  // PK: decays per key channel
         const int ntok = end - start;  // tokens of the sequence
         const bool full_tile = (vt * NW + NW) * WC <= p.V;
         if (ntok >= 2 && ntok <= TSH && full_tile && p.state_in != nullptr && p.state_out != nullptr) {
@@ -297,6 +298,14 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                         shq[t][j * EPT + e] = qv[e] * rq;
                         shk[t][j * EPT + e] = kv[e] * rk;
                     }
+                    if constexpr (PK) {
+                        const size_t gi = ((size_t)tt * p.H + h) * K + j * EPT;
+#pragma unroll
+                        for (int e = 0; e < EPT; ++e) {
+                            const float x = load_any(p.a, p.gate_dtype, gi + e);
+                            shgk[t][j * EPT + e] = softplus ? expf(a_mul * softplus_f(x + a_bias)) : expf(x);
+                        }
+                    }
                     if (j == 0) {
                         float g, beta;
                         const size_t gi = (size_t)tt * p.H + h;
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                             beta = p.gb_prep[(size_t)p.N * p.H + gi];
                         } else {
                             g = 1.0f;
-                            if (p.a) {
+                            if (!PK && p.a) {
                                 const float x = load_any(p.a, p.gate_dtype, gi);
                                 g = softplus ? expf(a_mul * softplus_f(x + a_bias)) : expf(x);
                             }
@@ -351,7 +360,17 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                 }
                 const float g = shg[t], beta = shb[t], qk = shqk[t];
                 float cn = cs * g;
-                if (!(cn >= 1e-30f && cn <= 1e30f)) {
+                if constexpr (PK) {
+                    // per-key decays (g is 1): decay each channel of the resident tile directly
+#pragma unroll
+                    for (int i = 0; i < EPL / 4; ++i) {
+                        const f32x4 gv = *reinterpret_cast<const f32x4*>(&shgk[t][4 * (gl + LPC * i)]);
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) sc[c][i][e] *= gv[e];
+                    }
+                } else if (!(cn >= 1e-30f && cn <= 1e30f)) {
                     // block-uniform: fold the scale, this token's decay included, into the kept state
                     // (a zero or tiny decay leaves a zero state, as the recurrence does)
 #pragma unroll
@@ -672,9 +691,8 @@ template <typename T, int K, bool PREP, bool PK>
 hipError_t launch_k(const ScanArgs& p, hipStream_t stream) {
     constexpr int LPC = K >= 64 ? 16 : 8;
     constexpr int CPL = K >= 256 ? (GDN_DECODE_CPL > 1 ? GDN_DECODE_CPL / 2 : 1) : GDN_DECODE_CPL;
-    // calls with more tokens than sequences hold short sequences: SHORT instances (per-key decays
-    // take the general loop of the plain instances)
-    if (!PK && p.N > p.B) return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, false, true>(p, stream);
+    // calls with more tokens than sequences hold short sequences: SHORT instances
+    if (p.N > p.B) return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, PK, true>(p, stream);
     return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, PK, false>(p, stream);
 }
 

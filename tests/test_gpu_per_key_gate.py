@@ -103,3 +103,12 @@ def test_auto_never_takes_chunk_with_per_key_gate(torch):
                                  dt_bias=dev(w.dt_bias, "f32"), gate_per_key=True)
     torch.cuda.synchronize()
     assert used == "seq"
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_per_key_gate_short_sequences(torch, io):
+    """Verification-step shape (2..8 tokens per sequence): the DECODE path's short-sequence form with
+    decays staged per key channel."""
+    w, a_pk = per_key_problem(f"pk_short_{io}", 624, [5, 2, 8, 3, 5, 7, 1, 0, 4, 6], HQ=2, H=4, K=128, V=64, io=io)
+    out, st = run(torch, w, a_pk, "decode")
+    check(w, a_pk, out, st, what=f"short {io}")

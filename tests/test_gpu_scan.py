@@ -2,7 +2,8 @@
 
 Every path (DECODE, SEQ) runs in both input modes (fused: norms and gates in-kernel; prepared:
 from gdn_prepare_qk_gates) on the five workloads at full size, in the launch configuration the
-benchmark uses; the oracle computes sampled heads and columns of the same launch.  Outputs use
+benchmark uses (plus the benchmark's speculative verification step); the oracle computes sampled
+heads and columns of the same launch.  Outputs use
 the dtype tolerance, the final fp32 state 1e-4 for fp32 I/O and 2e-2 otherwise."""
 import dataclasses
 
@@ -54,11 +55,14 @@ SAMPLES = {
     "prefill": ([0, 13, 31], None),
     "long": ([0, 9], [0, 1, 37, 64, 100, 127]),
     "edge_fp16": (None, None),
+    "verify": ([0, 5, 31], None),
 }
 PARITY = [(n, p, m) for n in cases.ALL for p in ("decode", "seq") for m in ("fused", "prepared")
           if not (n == "long" and p == "decode")]
 # the chunked path runs on fused bf16/fp16 inputs with the softplus gate and L2 norm
 PARITY += [("decode", "chunk", "fused"), ("prefill", "chunk", "fused"), ("long", "chunk", "fused")]
+# the speculative verification step (B=256 x 5 tokens) at full size: DECODE's short-sequence form and SEQ
+PARITY += [("verify", "decode", "fused"), ("verify", "decode", "prepared"), ("verify", "seq", "fused")]
 
 
 def check_against_oracle(w, name, out, st):
