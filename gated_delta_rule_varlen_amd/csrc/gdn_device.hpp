@@ -129,18 +129,6 @@ __device__ __forceinline__ void report_status(int32_t* dev_status, bool malforme
         *dev_status = malformed ? GDN_ERR_OFFSETS : GDN_OK;
 }
 
-// Sequence containing token t: the last b in [0, B) with offsets[b] <= t (offsets already valid,
-// t < N).  Zero-length sequences share their start with the next one and are skipped.
-__device__ __forceinline__ int find_sequence(const int32_t* __restrict__ offsets, int B, int t) {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (offsets[mid] <= t) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
 // Four consecutive gate inputs (element type T, the qkv type, or fp32), widened to fp32.
 template <typename T>
 __device__ __forceinline__ f32x4 load4_gate(const void* p, int gate_dtype, size_t i) {

@@ -55,7 +55,7 @@
 #ifndef GDN_DECODE_STREAM
 #define GDN_DECODE_STREAM 4
 #endif
-// Longest sequence the SHORT instances carry column by column with staged token operands.
+// Longest sequence the SHORT instances carry through their staged-operand form.
 #ifndef GDN_DECODE_SHORT
 #define GDN_DECODE_SHORT kDecodeShortTokens
 #endif
