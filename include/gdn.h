@@ -6,12 +6,19 @@
  *                         (W-1)*D window per (sequence, channel)
  *   gdn_prepare_qk_gates  per-token q/k L2 normalisation plus the decay and update-rate gates
  *   gdn_scan_varlen       the gated delta-rule recurrence with a per-(sequence, head) state
- * and one fusion of them for decode steps (at most one token per sequence):
+ * one fusion of them for decode steps (at most one token per sequence):
  *   gdn_decode_step       gdn_conv1d_varlen then gdn_scan_varlen in a single launch
+ * and variants of the same operations:
+ *   gdn_conv1d_varlen_capture, gdn_scan_varlen_capture   also record the first tokens of each
+ *                         sequence for speculative decoding
+ *   gdn_prepare_qk_gates_strided, gdn_scan_varlen_strided   read q, k and v as separate token
+ *                         streams with their own row strides
+ * plus gdn_scan_workspace_bytes, gdn_status_string and gdn_abi_version.
  *
  * Sources (docs.rs source pages): "onnxruntime-ep-mlx 0.31.1 src/ops/paged_ssm.rs" -- kernel strings
- * CONV, DELTA_PREPARE and DELTA, host functions conv(), delta() and the claim predicates; and
- * "mlx-c-rust compile/gated_delta_rate_activation.rs" -- the rate-activation graph.
+ * CONV, DELTA_PREPARE and DELTA, the capture strings, host functions conv(), delta() and the claim
+ * predicates; "mlx-c-rust compile/gated_delta_rate_activation.rs" -- the rate-activation graph; and
+ * "rlx-cpu 0.2.14 thunk/types.rs" -- Thunk::GatedDeltaNet's per-key-channel gate.
  *
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer owned by the caller; the library allocates nothing,
