@@ -518,9 +518,9 @@ struct OutFrags {
 //   U = U' - W S^T for token tile w, and S^T <- e^{G_C} S^T + Kd^T U for key tiles of wave w.  The
 //   state is held transposed (accumulator lane: 4 consecutive keys of one value column), which makes
 //   its LDS copy and its HBM load/store contiguous.
-//   Waves 4-7 ("output") compute chunk c-1's output O^T[v][i] = e^{G_i} (S qhat_i) + (U^T P^T)[v][i]
-//   for token tile w from the double-buffered S and U^T, off the serial chain, and write it as whole
-//   token rows through a per-wave LDS tile.
+//   Waves 4-7 ("output") compute chunk c's output O^T[v][i] = e^{G_i} (S qhat_i) + (U^T P^T)[v][i]
+//   for token tile w from the double-buffered S and U^T while the state waves update S, off the
+//   serial chain, and write it as whole token rows through a per-wave LDS tile.
 template <typename T, int K, int V, int NCT>
 __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
     using TS = typename T::storage;
@@ -695,9 +695,12 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
         }
     };
 
-    // Iteration c (c0 <= c <= c1): state waves process chunk c (when c < c1), output waves chunk c-1
-    // (when c > c0).  Every fetch is unconditional (chunk indices clamped into [c0, c1)), so the loads
-    // in flight are the same on every path and each wait covers only the data about to be used.
+    // Iteration c (c0 <= c <= c1) has two barriers.  State waves store S entering chunk c before the
+    // first, form U between them and update S after the second; output waves compute chunk c's
+    // output after the second barrier (S and U of chunk c are complete then and stay untouched until
+    // the next iteration's second barrier), alongside the state update.  Every fetch is
+    // unconditional (chunk indices clamped into [c0, c1)), so the loads in flight are the same on
+    // every path and each wait covers only the data about to be used.
     if (c0 < c1) {
         if (is_state) {
             StateFrags<K, NCT> fa, fb;
@@ -718,19 +721,21 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
                 if (c + 1 < c1) s_update((c + 1 - c0) & 1, fb);
             }
         } else {
-            // chunk j's operands live in fa (j - c0 even) or fb (odd): fetched in iteration j, used in
-            // iteration j + 1
+            // chunk j's output is computed right after the second barrier of iteration j (S entering
+            // chunk j and its U are complete then), alongside the state waves' update; its operands
+            // live in fa (j - c0 even) or fb (odd), fetched one iteration ahead
             OutFrags<K> fa, fb;
+            fetch_o(c0, fa);
             for (int c = c0; c <= c1; c += 2) {
-                fetch_o(min(c, c1 - 1), fa);
                 __syncthreads();
-                if (c > c0) o_tile(c - 1, (c - 1 - c0) & 1, fb);
-                __syncthreads();
-                if (c + 1 > c1) break;
                 fetch_o(min(c + 1, c1 - 1), fb);
                 __syncthreads();
-                o_tile(c, (c - c0) & 1, fa);
+                if (c < c1) o_tile(c, (c - c0) & 1, fa);
+                if (c + 1 > c1) break;
                 __syncthreads();
+                fetch_o(min(c + 2, c1 - 1), fa);
+                __syncthreads();
+                if (c + 1 < c1) o_tile(c + 1, (c + 1 - c0) & 1, fb);
             }
         }
     }
