@@ -15,7 +15,8 @@
 //
 // Kernels (all on the caller's stream; bf16 MFMA operands, fp32 accumulation, fp32 state):
 //   index  one block: checks the offsets (nothing is written anywhere when they are malformed),
-//          builds the table of each sequence's first chunk.
+//          builds the table of each sequence's first chunk and an order of the sequences by
+//          decreasing chunk count.
 //   prep   one block per (chunk, head), parallel: gates, G, the normalised q and k, A and the masked
 //          Q K^T by MFMA, T by blocked inversion (16x16 diagonal blocks by substitution, off-diagonal
 //          blocks by fp32 MFMA), W^T = X^T T^T and U' = T Y by MFMA.  Writes W, Kd^T =
@@ -79,7 +80,7 @@ constexpr int DT = 256;
 
 // Workspace layout (byte offsets), identical on host and device.  Per (chunk, head) "chh":
 struct WsLayout {
-    size_t hdr;      // int32: [0] status, [1] total chunks; cstart[B+1] at +64
+    size_t hdr;      // int32: [0] status, [1] total chunks; cstart[B+1] at +64, then order[B]
     size_t w;        // W     (CH x K, rows = tokens):      A tiles [4][K/32]
     size_t kdt;      // Kd^T  (K x CH, rows = keys):        A tiles [K/16][2], Kd = diag(e^{G_C - G}) Khat
     size_t qf;       // Qhat  (CH x K, rows = tokens):      A tiles [4][K/32]
@@ -95,7 +96,7 @@ __host__ __device__ inline WsLayout ws_layout(int B, int N, int H, int K, int V)
     const size_t nh = nch * (size_t)H;
     size_t o = 0;
     L.hdr = o;
-    o = align256(o + 64 + 4 * ((size_t)B + 1));
+    o = align256(o + 64 + 4 * (2 * (size_t)B + 1));
     L.w = o;
     o = align256(o + nh * CH * K * 2);
     L.kdt = o;
@@ -173,6 +174,28 @@ __global__ __launch_bounds__(1024) void chunk_index_kernel(ChunkArgs p) {
         __syncthreads();
         if (threadIdx.x == 1023) carry = before + incl;
         __syncthreads();
+    }
+    // The state kernel's blocks are long-lived and can outnumber the blocks resident at once, so
+    // they take the sequences longest first (list scheduling: the critical path is then close to the
+    // longest sequence rather than a late start plus it).  Up to 1024 sequences are ranked here;
+    // beyond that the order is the identity.
+    int32_t* order = cstart + p.B + 1;
+    __shared__ int s_cnt[1024];
+    if (p.B <= 1024) {
+        const int i = threadIdx.x;
+        if (i < p.B) s_cnt[i] = (p.offsets[i + 1] - p.offsets[i] + CH - 1) / CH;
+        __syncthreads();
+        if (i < p.B) {
+            const int ci = s_cnt[i];
+            int rank = 0;
+            for (int j = 0; j < p.B; ++j) {
+                const int cj = s_cnt[j];
+                rank += (cj > ci) || (cj == ci && j < i);
+            }
+            order[rank] = i;
+        }
+    } else {
+        for (int i = threadIdx.x; i < p.B; i += blockDim.x) order[i] = i;
     }
     if (threadIdx.x == 0) {
         cstart[p.B] = carry;
@@ -538,7 +561,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
     const int blk = xcd_remap((int)blockIdx.x, p.n_blocks, NVT);
     const int vt = blk % NVT;
     const int bh = blk / NVT;
-    const int h = bh % p.H, b = bh / p.H;
+    const int h = bh % p.H, b = cstart[p.B + 1 + bh / p.H];  // sequences longest first
     const int tid = threadIdx.x, lane = tid & 63;
     const bool is_state = tid < 256;
     const int wv = (tid >> 6) & 3;  // token / key tile of this wave within its group
