@@ -18,6 +18,7 @@
 //         r = g (k^.s),  delta = beta (v - r),  out = scale (g (q^.s) + delta (q^.k^)),
 //         s <- g s + delta k^;
 //   * outputs of a chunk are collected in LDS and written back as 16-byte vectors;
+//   * blocks take the sequences longest first (ranked in-block by length, for up to 64 sequences);
 //   * with a per-key-channel decay (GDN_GATE_PER_KEY; "PK" instances) the staging also evaluates
 //     the decay of every (token, key channel) once per block into LDS, and the recurrence decays
 //     each state slice channel by channel before the dot products;
@@ -88,6 +89,8 @@ struct Fetch {
     float gk[GKN];  // per-key decay inputs of the thread's q/k elements (PK only)
 };
 
+constexpr int kRankedSeqs = 64;  // sequences ranked by length in-block (more keep their order)
+
 template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool PK>
 __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     static_assert(!(PK && PREP), "the per-key decay is evaluated in-kernel from raw inputs");
@@ -113,9 +116,27 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     const int vt = blk % p.n_vtiles;
     const int bh = blk / p.n_vtiles;
     const int h = bh % p.H;
-    const int b = bh / p.H;
-    const int kh = h / p.G;
     const int tid = (int)threadIdx.x;
+    // Blocks live as long as their sequence and can outnumber the resident ones, so the sequences are
+    // taken longest first (list scheduling): with up to kRankedSeqs sequences every block ranks
+    // the lengths in LDS and serves the sequence whose rank is its logical index.
+    int b = bh / p.H;
+    if (p.B <= kRankedSeqs) {
+        __shared__ int s_len[kRankedSeqs];
+        __shared__ int s_pick;
+        for (int i = tid; i < p.B; i += NT) s_len[i] = p.offsets[i + 1] - p.offsets[i];
+        __syncthreads();
+        const int want = b;
+        for (int i = tid; i < p.B; i += NT) {
+            const int li = s_len[i];
+            int rank = 0;
+            for (int j = 0; j < p.B; ++j) rank += (s_len[j] > li) || (s_len[j] == li && j < i);
+            if (rank == want) s_pick = i;
+        }
+        __syncthreads();
+        b = s_pick;
+    }
+    const int kh = h / p.G;
     const int wave = tid / 64, lane = tid % 64;
     const int grp = lane / LPC, gl = lane % LPC;
     const int cw = wave * WC + grp * CPL;  // first block-local column of this lane group
