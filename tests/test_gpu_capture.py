@@ -292,3 +292,35 @@ def test_speculative_verification_step_replay(torch):
                                  sigmoid=True, counts=accepted[bsel:bsel + 1], cap=CAP)
         check_capsule(SimpleNamespace(B=1, HQ=HQ, H=H, K=K, V=V), f64(caps)[bsel:bsel + 1], cref, TOL["bf16"], f"verify b={bsel}")
     print(f"  replay err {err:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("path", ["decode", "seq"])
+def test_capture_at_capacity_eight(torch, path):
+    """cap = 8 (the capacity the pages' speculative decoding uses at most): sequences shorter than,
+    equal to and longer than the capacity, recorded in full, on both token-sequential paths (the
+    DECODE path's short form carries the sequences of up to 8 tokens)."""
+    import gated_delta_rule_varlen_amd as gdn
+
+    cap = 8
+    lens = [8, 3, 12, 8, 0, 9, 5, 1]
+    w = workloads.make(name=f"cap8_{path}", seed=560, lengths=lens, HQ=2, H=4, K=128, V=128, io="bf16")
+    counts = np.array([8, 8, 8, 5, 8, 100, 0, 8], np.int32)
+    qkv = dev(w.qkv, w.io)
+    kw = dict(HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=dev(w.a, w.gate_dtype), b=dev(w.b, w.gate_dtype),
+              A_log=dev(w.A_log, "f32"), dt_bias=dev(w.dt_bias, "f32"), state_in=dev(w.state, "f32"), path=path)
+    _, _, caps, used = gdn.scan_varlen_capture(qkv, dev_i32(w.offsets), cap=cap, counts=dev_i32(counts), **kw)
+    torch.cuda.synchronize()
+    assert used == path
+    _, _, ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io, gate_dtype=w.gate_dtype,
+                            a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias, state_in=w.state, counts=counts, cap=cap)
+    got = f64(caps)
+    assert np.all(got[ref == 0] == 0)
+    g_n, k_n = cap * w.H, cap * (w.H + w.HQ * w.K)
+    for part, sl in (("g", slice(0, g_n)), ("k^", slice(g_n, k_n)), ("delta", slice(k_n, None))):
+        assert_close(got[:, sl], ref[:, sl], TOL[w.io], f"cap8 {path} {part}")
+    upd = gdn.conv1d_varlen_capture(dev(w.x, w.io), dev(w.conv_w, w.io), dev_i32(w.offsets), cap=cap,
+                                    counts=dev_i32(counts), bias=dev(w.conv_bias, w.io),
+                                    state_in=dev(w.conv_state, w.conv_state_dtype), silu=w.silu,
+                                    state_dtype=getattr(torch, {"f32": "float32", "bf16": "bfloat16"}[w.conv_state_dtype]))[2]
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(upd), oracle.conv_capture(w.x, w.offsets, counts, cap=cap, x_dtype=w.io))

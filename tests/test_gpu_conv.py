@@ -104,3 +104,23 @@ def test_all_sequences_empty_copies_windows(torch):
     w0 = dataclasses.replace(w, N=0, offsets=np.zeros(w.B + 1, np.int32), x=w.x[:0], qkv=w.qkv[:0])
     _, st = gpu_conv(torch, w0)
     assert np.array_equal(bits(st), np.ascontiguousarray(w.conv_state).view(np.int16))
+
+
+SWEEP = [(W, D, io, sdt) for W in (2, 6, 8) for D in (1, 3) for io, sdt in (("bf16", "f32"), ("f16", "f16"), ("f32", "f32"))]
+
+
+@pytest.mark.parametrize("W,D,io,sdt", SWEEP)
+def test_conv_widths_and_dilations(torch, W, D, io, sdt):
+    """Conv widths up to the supported maximum (8) and dilations beyond 1, with window dtypes equal to
+    and wider than x: sequences empty, shorter than the window, and long (several body tiles)."""
+    lens = [0, 1, 2, 5, 40, 7, 0, 63]
+    w = workloads.make(name=f"conv_w{W}_d{D}_{io}", seed=900 + 10 * W + D, lengths=lens, HQ=1, H=1, K=32, V=64,
+                       W=W, D=D, io=io, conv_state_dtype=sdt)
+    print(f"[conv sweep] W={W} D={D} {io}/{sdt} L={w.L}", flush=True)
+    y, st = gpu_conv(torch, w)
+    y_ref, st_ref = oracle.conv(w.x, w.conv_w, w.offsets, W=w.W, D=w.D, x_dtype=w.io, bias=w.conv_bias,
+                                state_in=w.conv_state, state_dtype=w.conv_state_dtype, silu=w.silu)
+    assert_close(f64(y), y_ref, TOL[w.io], "y")
+    assert np.array_equal(f64(st), st_ref), "the new window is a copy"
+    y2, st2 = gpu_conv(torch, w, inplace=True)
+    assert np.array_equal(bits(y2), bits(y)) and np.array_equal(bits(st2), bits(st))
