@@ -9,8 +9,10 @@
 //   * "body" blocks own a tile of TT consecutive packed tokens and compute every token whose local
 //     index is >= L (all taps then fall inside the sequence); for dilation 1 the W taps slide
 //     through registers, so each token row is loaded once;
-//   * "head" blocks own one sequence: they compute its first min(L, len) tokens -- the only ones
-//     whose taps reach into the carried window -- and then write the new window.  The window is
+//   * "head" blocks own one sequence: they compute its first min(L + kHeadExtra, len) tokens -- the
+//     first L are the only ones whose taps reach into the carried window; the few after them make a
+//     short sequence (a decode or verification step) a head block's work alone -- and then write
+//     the new window.  The window is
 //     read and written by the same thread in that order, so state_out may alias state_in;
 //   * with capture (speculative decoding: paged_ssm.rs page, CONV_CAPTURE_INIT / _STEP) the head
 //     blocks also copy the sequence's first captured token rows into its update slots and zero the
@@ -28,6 +30,7 @@ namespace gdn {
 namespace {
 
 constexpr int kConvTile = 16;        // tokens per body block
+constexpr int kHeadExtra = 8;        // tokens a head block computes beyond the first L
 constexpr int kStagedOffsets = 2048;  // offsets kept in LDS when B + 1 fits
 
 struct ConvArgs {
@@ -165,8 +168,9 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     if (cvec >= p.n_cvec) return;
     const int C = p.C, D = p.D, L = p.L;
 
-    // Body blocks: which tokens of the tile have local index >= L (the rest belong to head blocks).
-    // A tile without any -- every tile of a batch of short sequences -- ends here, before any load.
+    // Body blocks: which tokens of the tile have local index >= L + kHeadExtra (the rest belong to
+    // head blocks).  A tile without any -- every tile of a batch of short sequences -- ends here,
+    // before any load.
     unsigned body_mask = 0;
     if (item >= p.B) {
         const int t0 = (item - p.B) * p.tile;
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
                 ++b;
                 next = off(b + 1);
             }
-            if (t - off(b) >= L) body_mask |= 1u << (t - t0);
+            if (t - off(b) >= L + kHeadExtra) body_mask |= 1u << (t - t0);
         }
         if (body_mask == 0) return;
     }
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
             for (int k = 0; k < NCH; ++k) win.v[k] = u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int l = 0; l < L1; ++l) {
+        for (int l = 0; l < L1 + kHeadExtra; ++l) {
             if (l >= len) break;
             float acc[VEC];
 #pragma unroll
@@ -321,14 +325,14 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     }
 
     if (item < p.B) {
-        // ---- head: the first min(L, len) tokens of sequence b, then the new window ----------------
+        // ---- head: the first min(L + kHeadExtra, len) tokens of sequence b, then the new window -----
         const int b = item;
         const int start = off(b);
         const int len = off(b + 1) - start;
         const SS* st_in = static_cast<const SS*>(p.state_in);
         SS* st_out = static_cast<SS*>(p.state_out);
         const size_t wrow = ((size_t)b * C + c0) * (size_t)L;  // window of channel c0 + i at wrow + i*L
-        const int nh = len < L ? len : L;
+        const int nh = len < L + kHeadExtra ? len : L + kHeadExtra;
         for (int l = 0; l < nh; ++l) {
             float acc[VEC];
 #pragma unroll
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
         return;
     }
 
-    // ---- body: tokens [t0, t1) with local index >= L ----------------------------------------------
+    // ---- body: tokens [t0, t1) with local index >= L + kHeadExtra ---------------------------------
     if constexpr (VEC > 1 && W > 1) {
         if (D == 1) {
             // dilation 1: all TILE + L rows of the tile are loaded up front (independent 16-byte loads
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     float ring[W][VEC];  // ring[j] = x[t - (W-1-j)*D]
     int ring_t = -2;
     for (int t = t0; t < t1; ++t) {
-        if (!(body_mask & (1u << (t - t0)))) continue;  // reaches into the window: a head block's
+        if (!(body_mask & (1u << (t - t0)))) continue;  // a head block's token
         if (D == 1 && ring_t == t - 1) {
 #pragma unroll
             for (int j = 0; j + 1 < W; ++j)
