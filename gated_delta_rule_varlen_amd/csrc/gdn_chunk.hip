@@ -19,11 +19,13 @@
 //          decreasing chunk count.
 //   prep   one block per (chunk, head), parallel: gates, G, the normalised q and k, A and the masked
 //          Q K^T by MFMA, T by blocked inversion (16x16 diagonal blocks by substitution, off-diagonal
-//          blocks by fp32 MFMA), W^T = X^T T^T and U' = T Y by MFMA.  Writes W, Kd^T =
-//          (diag(e^{G_C - G}) K)^T, Qhat, P = M o (Qhat Khat^T), U' and G to the workspace.
+//          blocks by fp32 MFMA), W^T = X^T T^T and U' = T Y by MFMA.  Writes W, P = M o (Qhat Khat^T),
+//          U' and G per (chunk, value head), and Qhat and Khat^T once per (chunk, key head): they do
+//          not depend on the decay, so the G value heads of a key head share them.
 //   state  one block per (sequence, head, column tile), sequential over the sequence's chunks:
-//          U = U' - W S^T, S <- e^{G_C} S + U^T Kd, with the fp32 state in MFMA accumulators; the
-//          output of the previous chunk from the same LDS copies of S and U on separate waves.
+//          U = U' - W S^T, S <- e^{G_C} S + (diag(e^{G_C - G}) U)^T Khat, with the fp32 state in
+//          MFMA accumulators; the output of the previous chunk from the same LDS copies of S and U
+//          on separate waves.
 //
 // Every MFMA operand the state kernel reads from the workspace is stored in fragment order: the
 // 16 x 32 bf16 block one instruction consumes is 64 consecutive 16-byte pieces, lane l's piece at
@@ -78,31 +80,32 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 constexpr int AT = 512;
 constexpr int DT = 256;
 
-// Workspace layout (byte offsets), identical on host and device.  Per (chunk, head) "chh":
+// Workspace layout (byte offsets), identical on host and device.  Per (chunk, value head) "chh",
+// or per (chunk, key head) "chk" where marked:
 struct WsLayout {
     size_t hdr;      // int32: [0] status, [1] total chunks; cstart[B+1] at +64, then order[B]
-    size_t w;        // W     (CH x K, rows = tokens):      A tiles [4][K/32]
-    size_t kdt;      // Kd^T  (K x CH, rows = keys):        A tiles [K/16][2], Kd = diag(e^{G_C - G}) Khat
-    size_t qf;       // Qhat  (CH x K, rows = tokens):      A tiles [4][K/32]
-    size_t pm;       // P     (CH x CH, rows = tokens i):   A tiles [4][2], P = M o (Qhat Khat^T)
-    size_t upt;      // U'    (CH x V):                     D tiles [4][V/16]
-    size_t gam;      // G     [CH] f32
+    size_t w;        // W      (CH x K, rows = tokens):      A tiles [4][K/32]
+    size_t kt;       // Khat^T (K x CH, rows = keys):        A tiles [K/16][2]        (chk)
+    size_t qf;       // Qhat   (CH x K, rows = tokens):      A tiles [4][K/32]        (chk)
+    size_t pm;       // P      (CH x CH, rows = tokens i):   A tiles [4][2], P = M o (Qhat Khat^T)
+    size_t upt;      // U'     (CH x V):                     D tiles [4][V/16]
+    size_t gam;      // G      [CH] f32
     size_t total;
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-__host__ __device__ inline WsLayout ws_layout(int B, int N, int H, int K, int V) {
+__host__ __device__ inline WsLayout ws_layout(int B, int N, int HQ, int H, int K, int V) {
     WsLayout L;
     const size_t nch = ((size_t)N + CH - 1) / CH + (size_t)B;  // upper bound on chunks over all sequences
-    const size_t nh = nch * (size_t)H;
+    const size_t nh = nch * (size_t)H, nk = nch * (size_t)HQ;
     size_t o = 0;
     L.hdr = o;
     o = align256(o + 64 + 4 * (2 * (size_t)B + 1));
     L.w = o;
     o = align256(o + nh * CH * K * 2);
-    L.kdt = o;
-    o = align256(o + nh * K * CH * 2);
+    L.kt = o;
+    o = align256(o + nk * K * CH * 2);
     L.qf = o;
-    o = align256(o + nh * CH * K * 2);
+    o = align256(o + nk * CH * K * 2);
     L.pm = o;
     o = align256(o + nh * CH * CH * 2);
     L.upt = o;
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
         float am[CH][CH + 4];      // A (fp32)
         uint16_t tb[CH][CH + PAD];  // T (bf16)
     } r2;
-    __shared__ float s_gam[CH], s_beta[CH], s_xs[CH], s_ks[CH];
+    __shared__ float s_gam[CH], s_beta[CH], s_xs[CH];
     auto& kn = r0.kn;
     auto& tm = r0.tm;
     auto& qn = r1.qn;
@@ -300,6 +303,9 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
     const int n = min(CH, p.offsets[b + 1] - t0);
     const int kh = h / p.G;
     const size_t chh = (size_t)cid * p.H + h;
+    const size_t chk = (size_t)cid * p.HQ + kh;
+    // Qhat and Khat^T are the same for every value head of the key head: the first one writes them
+    const bool shared_writer = (h % p.G) == 0;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int pc = lane % LPT, tsub = lane / LPT;
     const TS* const xq = static_cast<const TS*>(p.x.q);
@@ -307,8 +313,8 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
     const TS* const xv = static_cast<const TS*>(p.x.v);
     uint16_t* const wsb = reinterpret_cast<uint16_t*>(p.ws);
     uint16_t* const w_out = wsb + p.L.w / 2 + chh * CH * K;
-    uint16_t* const kd_out = wsb + p.L.kdt / 2 + chh * K * CH;
-    uint16_t* const q_out = wsb + p.L.qf / 2 + chh * CH * K;
+    uint16_t* const kt_out = wsb + p.L.kt / 2 + chk * K * CH;
+    uint16_t* const q_out = wsb + p.L.qf / 2 + chk * CH * K;
     uint16_t* const p_out = wsb + p.L.pm / 2 + chh * CH * CH;
     uint16_t* const u_out = wsb + p.L.upt / 2 + chh * CH * V;
 
@@ -348,11 +354,9 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
             const float y = __shfl_up(gam, d);
             if (lane >= d) gam += y;
         }
-        const float gC = __shfl(gam, CH - 1);
         s_gam[lane] = gam;
         s_beta[lane] = beta;
         s_xs[lane] = beta * expf(gam);
-        s_ks[lane] = expf(gC - gam);
         reinterpret_cast<float*>(p.ws + p.L.gam)[chh * CH + lane] = gam;
     }
     __syncthreads();  // gates ready
@@ -380,12 +384,14 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
     __syncthreads();  // kn, qn, vn ready
 
     // Qhat tiles (token tile wv) straight from its rows
+    if (shared_writer) {
 #pragma unroll
-    for (int kk = 0; kk < K / 32; ++kk)
-        *reinterpret_cast<u32x4*>(q_out + (size_t)(wv * (K / 32) + kk) * AT + 8 * lane) =
-            *reinterpret_cast<const u32x4*>(&qn[16 * wv + (lane & 15)][32 * kk + 8 * (lane >> 4)]);
+        for (int kk = 0; kk < K / 32; ++kk)
+            *reinterpret_cast<u32x4*>(q_out + (size_t)(wv * (K / 32) + kk) * AT + 8 * lane) =
+                *reinterpret_cast<const u32x4*>(&qn[16 * wv + (lane & 15)][32 * kk + 8 * (lane >> 4)]);
+    }
 
-    // Column fragments of key tiles kt = wv + 4m: Kd^T (stored) and X^T = (diag(b e^G) Khat)^T (kept
+    // Column fragments of key tiles kt = wv + 4m: Khat^T (stored) and X^T = (diag(b e^G) Khat)^T (kept
     // for W), and of value tiles vt = wv + 4m: Y (kept for U').  Lane l: index 16 kt + l%16, tokens
     // 32 c + 8(l/16) + e.
     bf16x8 xf[KT4][2], yf[KT4][2];
@@ -395,16 +401,16 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int tb0 = 32 * c + 8 * (lane >> 4);
-            float kx[8], kdv[8];
-            bf16x8 y;
+            float kx[8];
+            bf16x8 kc, y;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float kv = bf16_bits_to_f32(kn[tb0 + e][col]);
-                kx[e] = s_xs[tb0 + e] * kv;
-                kdv[e] = s_ks[tb0 + e] * kv;
+                const uint16_t kb = kn[tb0 + e][col];
+                kx[e] = s_xs[tb0 + e] * bf16_bits_to_f32(kb);
+                kc[e] = __builtin_bit_cast(__bf16, kb);
                 y[e] = __builtin_bit_cast(__bf16, vn[tb0 + e][col]);
             }
-            *reinterpret_cast<u32x4*>(kd_out + (size_t)(kt * 2 + c) * AT + 8 * lane) = pack8(kdv, 1.0f);
+            if (shared_writer) *reinterpret_cast<bf16x8*>(kt_out + (size_t)(kt * 2 + c) * AT + 8 * lane) = kc;
             const u32x4 xp = pack8(kx, 1.0f);
             xf[m][c] = __builtin_bit_cast(bf16x8, xp);
             yf[m][c] = y;
@@ -524,7 +530,8 @@ template <int K, int NCT>
 struct StateFrags {
     bf16x8 w[K / 32];          // W tiles of this wave's token tile
     u32x2 up[NCT];             // U' D-tile pieces, one per column tile
-    bf16x8 kd[K / 64][2];      // Kd^T tiles of this wave's key tiles
+    bf16x8 kt[K / 64][2];      // Khat^T tiles of this wave's key tiles
+    f32x4 gr;                  // G of this lane's four U rows (tokens 16 w + 4(l/16) .. +3)
     float gC;                  // G_C
 };
 template <int K>
@@ -536,11 +543,12 @@ struct OutFrags {
 
 // ---- state + output ---------------------------------------------------------------------------------
 // One block of 8 waves per (sequence, head, VT-column tile; VT = 16 NCT).  Loads of the chunk's
-// W, Kd, Qhat and P are shared by the block's NCT 16-column tiles.
+// W, Khat^T, Qhat and P are shared by the block's NCT 16-column tiles.
 //   Waves 0-3 ("state") carry the serial chain for chunk c: the entering state -> LDS (bf16),
-//   U = U' - W S^T for token tile w, and S^T <- e^{G_C} S^T + Kd^T U for key tiles of wave w.  The
-//   state is held transposed (accumulator lane: 4 consecutive keys of one value column), which makes
-//   its LDS copy and its HBM load/store contiguous.
+//   U = U' - W S^T for token tile w (to LDS as is, for the output, and with row i scaled by
+//   e^{G_C - G_i} <= 1, for the update), and S^T <- e^{G_C} S^T + Khat^T Ud for key tiles of wave w.
+//   The state is held transposed (accumulator lane: 4 consecutive keys of one value column), which
+//   makes its LDS copy and its HBM load/store contiguous.
 //   Waves 4-7 ("output") compute chunk c's output O^T[v][i] = e^{G_i} (S qhat_i) + (U^T P^T)[v][i]
 //   for token tile w from the double-buffered S and U^T while the state waves update S, off the
 //   serial chain, and write it as whole token rows through a per-wave LDS tile.
@@ -552,6 +560,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
     static_assert(V % VT == 0, "column tiles");
     __shared__ __align__(16) uint16_t sb[2][VT][K + PAD];   // S entering the chunk (bf16)
     __shared__ __align__(16) uint16_t ut[2][VT][CH + PAD];  // U^T (bf16)
+    __shared__ __align__(16) uint16_t ud[VT][CH + PAD];     // (diag(e^{G_C - G}) U)^T (bf16)
     __shared__ __align__(16) uint16_t ot[4][16][VT + 8];    // output rows, one tile per output wave
 
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws + p.L.hdr);
@@ -562,6 +571,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
     const int vt = blk % NVT;
     const int bh = blk / NVT;
     const int h = bh % p.H, b = cstart[p.B + 1 + bh / p.H];  // sequences longest first
+    const int kh = h / p.G;
     const int tid = threadIdx.x, lane = tid & 63;
     const bool is_state = tid < 256;
     const int wv = (tid >> 6) & 3;  // token / key tile of this wave within its group
@@ -572,7 +582,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
     const int seq_start = p.offsets[b], seq_end = p.offsets[b + 1];
     const uint16_t* const wsb = reinterpret_cast<const uint16_t*>(p.ws);
     const uint16_t* const wbase = wsb + p.L.w / 2;
-    const uint16_t* const kdbase = wsb + p.L.kdt / 2;
+    const uint16_t* const ktbase = wsb + p.L.kt / 2;
     const uint16_t* const qbase = wsb + p.L.qf / 2;
     const uint16_t* const pbase = wsb + p.L.pm / 2;
     const uint16_t* const ubase = wsb + p.L.upt / 2;
@@ -592,7 +602,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
 
     auto afrag = [&](const uint16_t* tile) { return *reinterpret_cast<const bf16x8*>(tile + 8 * lane); };
     auto fetch_s = [&](int c, StateFrags<K, NCT>& f) {
-        const size_t chh = (size_t)c * p.H + h;
+        const size_t chh = (size_t)c * p.H + h, chk = (size_t)c * p.HQ + kh;
         const uint16_t* wt = wbase + (chh * 4 + wv) * (K / 32) * AT;
 #pragma unroll
         for (int kk = 0; kk < K / 32; ++kk) f.w[kk] = afrag(wt + kk * AT);
@@ -602,12 +612,13 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
 #pragma unroll
         for (int t = 0; t < KTW; ++t)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) f.kd[t][jj] = afrag(kdbase + ((chh * (K / 16) + KTW * wv + t) * 2 + jj) * AT);
+            for (int jj = 0; jj < 2; ++jj) f.kt[t][jj] = afrag(ktbase + ((chk * (K / 16) + KTW * wv + t) * 2 + jj) * AT);
+        f.gr = *reinterpret_cast<const f32x4*>(gamb + chh * CH + 16 * wv + 4 * (lane >> 4));
         f.gC = gamb[chh * CH + CH - 1];
     };
     auto fetch_o = [&](int c, OutFrags<K>& f) {
-        const size_t chh = (size_t)c * p.H + h;
-        const uint16_t* qt = qbase + (chh * 4 + wv) * (K / 32) * AT;
+        const size_t chh = (size_t)c * p.H + h, chk = (size_t)c * p.HQ + kh;
+        const uint16_t* qt = qbase + (chk * 4 + wv) * (K / 32) * AT;
 #pragma unroll
         for (int kk = 0; kk < K / 32; ++kk) f.q[kk] = afrag(qt + kk * AT);
 #pragma unroll
@@ -640,6 +651,9 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) pw[ct] = mma_bf16(f.w[kk], sf[kk][ct], pw[ct]);
         order_reads_then_mfma<K / 32 * NCT, K / 32 * NCT>();
+        float ds[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ds[r] = expf(f.gC - f.gr[r]);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const float u0 = bf16_bits_to_f32(f.up[ct].x & 0xffffu) - pw[ct][0];
@@ -647,24 +661,26 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
             const float u2 = bf16_bits_to_f32(f.up[ct].y & 0xffffu) - pw[ct][2];
             const float u3 = bf16_bits_to_f32(f.up[ct].y >> 16) - pw[ct][3];
             *reinterpret_cast<u32x2*>(&ut[buf][16 * ct + (lane & 15)][16 * wv + 4 * (lane >> 4)]) = pack4(u0, u1, u2, u3);
+            *reinterpret_cast<u32x2*>(&ud[16 * ct + (lane & 15)][16 * wv + 4 * (lane >> 4)]) =
+                pack4(u0 * ds[0], u1 * ds[1], u2 * ds[2], u3 * ds[3]);
         }
     };
-    // state waves, after the second barrier: S^T <- e^{G_C} S^T + Kd^T U
-    auto s_update = [&](int buf, const StateFrags<K, NCT>& f) {
+    // state waves, after the second barrier: S^T <- e^{G_C} S^T + Khat^T Ud
+    auto s_update = [&](const StateFrags<K, NCT>& f) {
         const float gC = expf(f.gC);
         bf16x8 uf[NCT][2];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) uf[ct][jj] = frag(&ut[buf][16 * ct][32 * jj], CH + PAD, lane);
+            for (int jj = 0; jj < 2; ++jj) uf[ct][jj] = frag(&ud[16 * ct][32 * jj], CH + PAD, lane);
 #pragma unroll
         for (int t = 0; t < KTW; ++t)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = mma_bf16(f.kd[t][0], uf[ct][0], acc[t][ct] * gC);
+            for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = mma_bf16(f.kt[t][0], uf[ct][0], acc[t][ct] * gC);
 #pragma unroll
         for (int t = 0; t < KTW; ++t)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = mma_bf16(f.kd[t][1], uf[ct][1], acc[t][ct]);
+            for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = mma_bf16(f.kt[t][1], uf[ct][1], acc[t][ct]);
         order_reads_then_mfma<2 * NCT, 2 * KTW * NCT>();
     };
     // output waves: chunk c's output tiles (token tile wv, all column tiles) from sb[buf], ut[buf]
@@ -734,14 +750,14 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
                 __syncthreads();
                 if (c < c1) s_u((c - c0) & 1, fa);
                 __syncthreads();
-                if (c < c1) s_update((c - c0) & 1, fa);
+                if (c < c1) s_update(fa);
                 if (c + 1 > c1) break;
                 fetch_s(min(c + 2, c1 - 1), fa);
                 if (c + 1 < c1) s_store((c + 1 - c0) & 1);
                 __syncthreads();
                 if (c + 1 < c1) s_u((c + 1 - c0) & 1, fb);
                 __syncthreads();
-                if (c + 1 < c1) s_update((c + 1 - c0) & 1, fb);
+                if (c + 1 < c1) s_update(fb);
             }
         } else {
             // chunk j's output is computed right after the second barrier of iteration j (S entering
@@ -808,8 +824,7 @@ bool chunked_shape_supported(int K, int V, int qkv_dtype) {
 }
 
 size_t chunked_workspace_bytes(int B, int N, int HQ, int H, int K, int V) {
-    (void)HQ;
-    return ws_layout(B, N, H, K, V).total;
+    return ws_layout(B, N, HQ, H, K, V).total;
 }
 
 hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream) {
@@ -825,7 +840,7 @@ hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream) {
     p.offsets = a.offsets;
     p.dev_status = a.dev_status;
     p.ws = static_cast<char*>(a.workspace);
-    p.L = ws_layout(a.B, a.N, a.H, a.K, a.V);
+    p.L = ws_layout(a.B, a.N, a.HQ, a.H, a.K, a.V);
     p.B = a.B;
     p.N = a.N;
     p.HQ = a.HQ;
