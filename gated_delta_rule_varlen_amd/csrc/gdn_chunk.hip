@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
         float am[CH][CH + 4];      // A (fp32)
         uint16_t tb[CH][CH + PAD];  // T (bf16)
     } r2;
-    __shared__ float s_gam[CH], s_beta[CH], s_xs[CH];
+    __shared__ __align__(16) float s_gam[CH], s_beta[CH], s_xs[CH];
     auto& kn = r0.kn;
     auto& tm = r0.tm;
     auto& qn = r1.qn;
@@ -402,18 +402,24 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
         for (int c = 0; c < 2; ++c) {
             const int tb0 = 32 * c + 8 * (lane >> 4);
             float kx[8];
-            bf16x8 kc, y;
+            u32x4 kc, yp;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint16_t kb = kn[tb0 + e][col];
-                kx[e] = s_xs[tb0 + e] * bf16_bits_to_f32(kb);
-                kc[e] = __builtin_bit_cast(__bf16, kb);
-                y[e] = __builtin_bit_cast(__bf16, vn[tb0 + e][col]);
+            for (int e = 0; e < 4; ++e) {
+                const uint16_t k0 = kn[tb0 + 2 * e][col], k1 = kn[tb0 + 2 * e + 1][col];
+                kx[2 * e] = s_xs[tb0 + 2 * e] * bf16_bits_to_f32(k0);
+                kx[2 * e + 1] = s_xs[tb0 + 2 * e + 1] * bf16_bits_to_f32(k1);
+                kc[e] = (uint32_t)k0 | ((uint32_t)k1 << 16);
+                yp[e] = (uint32_t)vn[tb0 + 2 * e][col] | ((uint32_t)vn[tb0 + 2 * e + 1][col] << 16);
             }
-            if (shared_writer) *reinterpret_cast<bf16x8*>(kt_out + (size_t)(kt * 2 + c) * AT + 8 * lane) = kc;
-            const u32x4 xp = pack8(kx, 1.0f);
+            if (shared_writer) *reinterpret_cast<u32x4*>(kt_out + (size_t)(kt * 2 + c) * AT + 8 * lane) = kc;
+            u32x4 xp = pack8(kx, 1.0f);
+            // Pack here: left to itself the compiler keeps the eight 16-bit values of a fragment in
+            // eight registers until the products far below, which spills.  The empty statements
+            // (no instructions) pin the packed values at this point.
+            asm volatile("" : "+v"(xp));
+            asm volatile("" : "+v"(yp));
             xf[m][c] = __builtin_bit_cast(bf16x8, xp);
-            yf[m][c] = y;
+            yf[m][c] = __builtin_bit_cast(bf16x8, yp);
         }
     }
 
@@ -421,30 +427,45 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
 
     // Row block wv: A_ij = b_i e^{G_i - G_j} (khat_i . khat_j) for j < i, and
     // P_ij = e^{G_i - G_j} (qhat_i . khat_j) for j <= i (computed transposed: 4 consecutive j per lane).
-    // The tile loop stays rolled: the X and Y fragments are live across it, and unrolled it needs
-    // more registers than three blocks per compute unit leave.
+    // The masks are selects, not branches: the decay factor is evaluated for every entry with its
+    // exponent clamped at 0 (G never increases inside a chunk, so the clamp changes only entries the
+    // mask drops), and G and b are read as 4-vectors.  The tile loop stays rolled: the X and Y fragments are live across it, and unrolled it needs more
+    // registers than three blocks per compute unit leave.
+    {
+        const int ia = 16 * wv + 4 * (lane >> 4);  // rows of this lane's A entries
+        const int ip = 16 * wv + (lane & 15);      // row of this lane's P entries
 #pragma unroll 1
-    for (int jt = 0; jt < 4; ++jt) {
-        f32x4 a = zero4(), pt = zero4();
-        if (jt <= wv) {
+        for (int jt = 0; jt < 4; ++jt) {
+            f32x4 a = zero4(), pt = zero4();
+            if (jt <= wv) {
 #pragma unroll
-            for (int kk = 0; kk < K; kk += 32) {
-                const bf16x8 kj = frag(&kn[16 * jt][kk], K + PAD, lane);
-                a = mma_bf16(frag(&kn[16 * wv][kk], K + PAD, lane), kj, a);
-                pt = mma_bf16(kj, frag(&qn[16 * wv][kk], K + PAD, lane), pt);
+                for (int kk = 0; kk < K; kk += 32) {
+                    const bf16x8 kj = frag(&kn[16 * jt][kk], K + PAD, lane);
+                    a = mma_bf16(frag(&kn[16 * wv][kk], K + PAD, lane), kj, a);
+                    pt = mma_bf16(kj, frag(&qn[16 * wv][kk], K + PAD, lane), pt);
+                }
+                const int j = 16 * jt + (lane & 15);
+                const float g_j = s_gam[j];
+                const f32x4 g_ia = *reinterpret_cast<const f32x4*>(&s_gam[ia]);
+                const f32x4 b_ia = *reinterpret_cast<const f32x4*>(&s_beta[ia]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e = expf(fminf(g_ia[r] - g_j, 0.0f));
+                    am[ia + r][j] = (j < ia + r) ? b_ia[r] * e * a[r] : 0.0f;
+                }
             }
+            const int j = 16 * jt + 4 * (lane >> 4);
+            const f32x4 g_j = *reinterpret_cast<const f32x4*>(&s_gam[j]);
+            const float g_ip = s_gam[ip];
+            float pv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * wv + 4 * (lane >> 4) + r, j = 16 * jt + (lane & 15);
-                am[i][j] = (j < i) ? s_beta[i] * expf(s_gam[i] - s_gam[j]) * a[r] : 0.0f;
+                const float e = expf(fminf(g_ip - g_j[r], 0.0f));
+                pv[r] = (j + r <= ip) ? e * pt[r] : 0.0f;
             }
+            *reinterpret_cast<u32x2*>(p_out + (size_t)(wv * 2 + (jt >> 1)) * AT + a_tile_half_offset(lane, jt & 1)) =
+                pack4(pv[0], pv[1], pv[2], pv[3]);
         }
-        const int i = 16 * wv + (lane & 15), j = 16 * jt + 4 * (lane >> 4);
-        float pv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pv[r] = (j + r <= i) ? expf(s_gam[i] - s_gam[j + r]) * pt[r] : 0.0f;
-        *reinterpret_cast<u32x2*>(p_out + (size_t)(wv * 2 + (jt >> 1)) * AT + a_tile_half_offset(lane, jt & 1)) =
-            pack4(pv[0], pv[1], pv[2], pv[3]);
     }
     __syncthreads();  // A ready; Khat and Qhat rows dead (T and the scratch may be written)
 
