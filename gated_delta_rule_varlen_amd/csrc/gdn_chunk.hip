@@ -254,15 +254,16 @@ __device__ __forceinline__ u32x4 pack8(const float* x, float s) {
 }
 
 // ---- prep ----------------------------------------------------------------------------------------
-// Token rows are read whole: LPT = K/8 lanes per row, 8 elements (16 bytes) each, so one wave
-// instruction covers 64/LPT complete rows.  Column operands (8 consecutive tokens of one key or
-// value index) are gathered from the row-major LDS copies with 2-byte reads.
-// LDS is shared by lifetime (52 KB at K = 128, so three blocks fit on a compute unit):
+// k and v token rows are read whole: LPT = K/8 lanes per row, 8 elements (16 bytes) each, so one
+// wave instruction covers 64/LPT complete rows.  Column operands (8 consecutive tokens of one key or
+// value index) are gathered from the row-major LDS copies with 2-byte reads.  A wave needs only its
+// own 16 rows of Qhat, as MFMA fragments: they are loaded in fragment order and stay in registers.
+// LDS is shared by lifetime (39 KB at K = 128, so four blocks fit on a compute unit):
 //   region 0: Khat rows, until A and P are formed; then T (fp32)
-//   region 1: Qhat rows, until A and P are formed; then the inversion scratch
 //   region 2: Y rows, until their fragments are in registers; then A (fp32); then T (bf16)
+//   the off-diagonal inversion scratch has its own 4 KB
 template <typename T, int K, int V>
-__global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
+__global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
     using TS = typename T::storage;
     static_assert(K == V && (K == 64 || K == 128), "chunk tile shapes");
     constexpr int LPT = K / 8;     // lanes per token row
@@ -273,10 +274,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
         uint16_t kn[CH][K + PAD];  // Khat rows
         float tm[CH][CH + 4];      // T (fp32)
     } r0;
-    __shared__ __align__(16) union {
-        uint16_t qn[CH][K + PAD];  // Qhat rows
-        float scr[4][16][17];      // off-diagonal inversion scratch
-    } r1;
+    __shared__ float scr[4][16][17];  // off-diagonal inversion scratch
     __shared__ __align__(16) union {
         uint16_t vn[CH][V + PAD];  // Y = diag(b) V rows
         float am[CH][CH + 4];      // A (fp32)
@@ -285,8 +283,6 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
     __shared__ __align__(16) float s_gam[CH], s_beta[CH], s_xs[CH];
     auto& kn = r0.kn;
     auto& tm = r0.tm;
-    auto& qn = r1.qn;
-    auto& scr = r1.scr;
     auto& vn = r2.vn;
     auto& am = r2.am;
     auto& tb = r2.tb;
@@ -320,18 +316,28 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
 
     // this wave's 16 token rows (row 16 wv + TPI u + tsub), elements 8 pc .. 8 pc + 7, kept packed
     // (16-bit inputs) until the gates are known
-    u32x4 kr[NI], qr[NI], vr[NI];
+    u32x4 kr[NI], vr[NI];
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
         const int ti = 16 * wv + TPI * u + tsub;
         if (ti < n) {
             const size_t t = (size_t)(t0 + ti);
             kr[u] = *reinterpret_cast<const u32x4*>(xk + t * p.x.sk + (size_t)kh * K + 8 * pc);
-            qr[u] = *reinterpret_cast<const u32x4*>(xq + t * p.x.sq + (size_t)kh * K + 8 * pc);
             vr[u] = *reinterpret_cast<const u32x4*>(xv + t * p.x.sv + (size_t)h * V + 8 * pc);
         } else {
-            kr[u] = qr[u] = vr[u] = u32x4{0u, 0u, 0u, 0u};
+            kr[u] = vr[u] = u32x4{0u, 0u, 0u, 0u};
         }
+    }
+    // this wave's q rows in MFMA operand order: lane l holds row 16 wv + l%16, elements
+    // 32 kk + 8(l/16) .. +7 of fragment kk
+    u32x4 qr[K / 32];
+    {
+        const int ti = 16 * wv + (lane & 15);
+#pragma unroll
+        for (int kk = 0; kk < K / 32; ++kk)
+            qr[kk] = ti < n ? *reinterpret_cast<const u32x4*>(xq + (size_t)(t0 + ti) * p.x.sq + (size_t)kh * K + 32 * kk +
+                                                              8 * (lane >> 4))
+                            : u32x4{0u, 0u, 0u, 0u};
     }
 
     // gates and the cumulative log-decay (wave 0, one token per lane); padding tokens have b = 0
@@ -361,34 +367,48 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
     }
     __syncthreads();  // gates ready
 
-    // normalised rows -> LDS
+    // normalised k rows and Y = diag(b) V rows -> LDS
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
         const int ti = 16 * wv + TPI * u + tsub;
-        float kf[8], qf[8], vf[8];
+        float kf[8], vf[8];
         unpack8<T>(kr[u], kf);
-        unpack8<T>(qr[u], qf);
         unpack8<T>(vr[u], vf);
-        float sk = 0.0f, sq = 0.0f;
+        float sk = 0.0f;
 #pragma unroll
-        for (int z = 0; z < 8; ++z) {
-            sk = fmaf(kf[z], kf[z], sk);
-            sq = fmaf(qf[z], qf[z], sq);
-        }
+        for (int z = 0; z < 8; ++z) sk = fmaf(kf[z], kf[z], sk);
         sk = group_sum<LPT>(sk);
-        sq = group_sum<LPT>(sq);
         *reinterpret_cast<u32x4*>(&kn[ti][8 * pc]) = pack8(kf, rsqrtf(sk + 1e-12f));
-        *reinterpret_cast<u32x4*>(&qn[ti][8 * pc]) = pack8(qf, rsqrtf(sq + 1e-12f));
         *reinterpret_cast<u32x4*>(&vn[ti][8 * pc]) = pack8(vf, s_beta[ti]);
     }
-    __syncthreads();  // kn, qn, vn ready
+    // normalised q fragments (the four lanes l%16 + 16 j hold one row between them)
+    bf16x8 qw[K / 32];
+    {
+        float qf[K / 32][8];
+        float sq = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < K / 32; ++kk) {
+            unpack8<T>(qr[kk], qf[kk]);
+#pragma unroll
+            for (int z = 0; z < 8; ++z) sq = fmaf(qf[kk][z], qf[kk][z], sq);
+        }
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        const float rq = rsqrtf(sq + 1e-12f);
+#pragma unroll
+        for (int kk = 0; kk < K / 32; ++kk) {
+            u32x4 pq = pack8(qf[kk], rq);
+            asm volatile("" : "+v"(pq));  // pack now (see the column fragments below)
+            qw[kk] = __builtin_bit_cast(bf16x8, pq);
+        }
+    }
+    __syncthreads();  // kn, vn ready
 
-    // Qhat tiles (token tile wv) straight from its rows
+    // Qhat tiles (token tile wv)
     if (shared_writer) {
 #pragma unroll
         for (int kk = 0; kk < K / 32; ++kk)
-            *reinterpret_cast<u32x4*>(q_out + (size_t)(wv * (K / 32) + kk) * AT + 8 * lane) =
-                *reinterpret_cast<const u32x4*>(&qn[16 * wv + (lane & 15)][32 * kk + 8 * (lane >> 4)]);
+            *reinterpret_cast<bf16x8*>(q_out + (size_t)(wv * (K / 32) + kk) * AT + 8 * lane) = qw[kk];
     }
 
     // Column fragments of key tiles kt = wv + 4m: Khat^T (stored) and X^T = (diag(b e^G) Khat)^T (kept
@@ -442,7 +462,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
                 for (int kk = 0; kk < K; kk += 32) {
                     const bf16x8 kj = frag(&kn[16 * jt][kk], K + PAD, lane);
                     a = mma_bf16(frag(&kn[16 * wv][kk], K + PAD, lane), kj, a);
-                    pt = mma_bf16(kj, frag(&qn[16 * wv][kk], K + PAD, lane), pt);
+                    pt = mma_bf16(kj, qw[kk / 32], pt);
                 }
                 const int j = 16 * jt + (lane & 15);
                 const float g_j = s_gam[j];
@@ -467,7 +487,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs p) {
                 pack4(pv[0], pv[1], pv[2], pv[3]);
         }
     }
-    __syncthreads();  // A ready; Khat and Qhat rows dead (T and the scratch may be written)
+    __syncthreads();  // A ready; Khat rows dead (T may be written)
 
     // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution (wave w, lanes 0..15 own the
     // columns of block w); T is zero above the diagonal.
