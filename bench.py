@@ -450,8 +450,9 @@ def main():
     if not args.no_also and args.workload == "decode":
         del p
         torch.cuda.empty_cache()
-        line["also"] = {"prefill": secondary(torch, workloads.varlen_prefill(), max(3, args.steps // 10), 2),
-                        "long": secondary(torch, workloads.long_single(), 3, 1),
+        # warmups long enough for the clocks to settle (a 2-step warmup reads ~15% slow)
+        line["also"] = {"prefill": secondary(torch, workloads.varlen_prefill(), max(3, args.steps // 10), 20),
+                        "long": secondary(torch, workloads.long_single(), 5, 5),
                         "decode_step_fused_vs_two_call": fused_comparison(torch),
                         "speculative_verify_capture": verify_comparison(torch),
                         "per_key_decay": per_key_comparison(torch),
