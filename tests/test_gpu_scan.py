@@ -159,19 +159,21 @@ def test_ragged_multi_tile_small_case(torch):
             assert_close(f64(st), s_ref, 2e-2, f"ragged {path} {prepared} state")
 
 
-def chunk_ragged(K, H=4, io="bf16", seed=12):
+def chunk_ragged(K, H=4, io="bf16", seed=12, G=2):
     """Several chunks per sequence with ragged tails, a one-token and two zero-length sequences,
-    GQA 2: every shape corner of the chunked path.  With H*V/64 >= 256/7 value-column blocks the
-    state kernel takes its 64-column tile, else its 16-column tile."""
-    return workloads.make(name=f"chunk_ragged_k{K}_h{H}_{io}", seed=seed, lengths=[130, 0, 64, 1, 0, 200, 63],
-                          HQ=H // 2, H=H, K=K, V=K, io=io, conv_state_dtype="f32")
+    G value heads per key head (the chunked form stores q^ and k^ once per key head): every shape
+    corner of the chunked path.  With H*V/64 >= 256/7 value-column blocks the state kernel takes its
+    64-column tile, else its 16-column tile."""
+    return workloads.make(name=f"chunk_ragged_k{K}_h{H}_g{G}_{io}", seed=seed, lengths=[130, 0, 64, 1, 0, 200, 63],
+                          HQ=H // G, H=H, K=K, V=K, io=io, conv_state_dtype="f32")
 
 
-@pytest.mark.parametrize("K,H,io", [(64, 4, "bf16"), (128, 4, "bf16"), (128, 4, "f16"), (64, 64, "bf16"),
-                                    (128, 32, "f16")])
-def test_chunk_ragged_against_oracle_and_seq(torch, K, H, io):
-    w = chunk_ragged(K, H, io)
-    print(f"[chunk ragged] K={K} H={H} {io} N={w.N}", flush=True)
+@pytest.mark.parametrize("K,H,io,G", [(64, 4, "bf16", 2), (128, 4, "bf16", 2), (128, 4, "f16", 2), (64, 64, "bf16", 2),
+                                      (128, 32, "f16", 2), (128, 4, "bf16", 1), (128, 8, "bf16", 4),
+                                      (64, 8, "f16", 8), (128, 64, "bf16", 4)])
+def test_chunk_ragged_against_oracle_and_seq(torch, K, H, io, G):
+    w = chunk_ragged(K, H, io, G=G)
+    print(f"[chunk ragged] K={K} H={H} G={G} {io} N={w.N}", flush=True)
     out_c, st_c, used = gpu_scan(torch, w, "chunk", False)
     assert used == "chunk"
     out_s, st_s, _ = gpu_scan(torch, w, "seq", False)
