@@ -483,8 +483,10 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
                 const float e = expf(fminf(g_ip - g_j[r], 0.0f));
                 pv[r] = (j + r <= ip) ? e * pt[r] : 0.0f;
             }
-            *reinterpret_cast<u32x2*>(p_out + (size_t)(wv * 2 + (jt >> 1)) * AT + a_tile_half_offset(lane, jt & 1)) =
-                pack4(pv[0], pv[1], pv[2], pv[3]);
+            // (token tiles 0 and 1 have no nonzero entry past key 31; that fragment is never read)
+            if (wv >= 2 || jt < 2)
+                *reinterpret_cast<u32x2*>(p_out + (size_t)(wv * 2 + (jt >> 1)) * AT + a_tile_half_offset(lane, jt & 1)) =
+                    pack4(pv[0], pv[1], pv[2], pv[3]);
         }
     }
     __syncthreads();  // A ready; Khat rows dead (T may be written)
@@ -662,8 +664,10 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
         const uint16_t* qt = qbase + (chk * 4 + wv) * (K / 32) * AT;
 #pragma unroll
         for (int kk = 0; kk < K / 32; ++kk) f.q[kk] = afrag(qt + kk * AT);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) f.pm[jj] = afrag(pbase + ((chh * 4 + wv) * 2 + jj) * AT);
+        f.pm[0] = afrag(pbase + (chh * 4 + wv) * 2 * AT);
+        // token tiles 0 and 1 have no nonzero P entry past key 31: that fragment is neither
+        // stored nor loaded
+        if (wv >= 2) f.pm[1] = afrag(pbase + ((chh * 4 + wv) * 2 + 1) * AT);
         f.gi = gamb[chh * CH + 16 * wv + (lane & 15)];
     };
 
@@ -727,15 +731,17 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
     // output waves: chunk c's output tiles (token tile wv, all column tiles) from sb[buf], ut[buf]
     constexpr int LPR = VT / 8;         // lanes per output row (16 bytes each)
     constexpr int RPI = 64 / LPR;       // rows per store instruction
-    auto o_tile = [&](int c, int buf, const OutFrags<K>& f) {
+    // NJ: the P fragments of this token tile that can be nonzero (tiles 0 and 1 see only keys < 32)
+    auto o_tile = [&](auto nj, int c, int buf, const OutFrags<K>& f) {
+        constexpr int NJ = decltype(nj)::value;
         const float cs = expf(f.gi);
-        bf16x8 sf[NCT][K / 32], uf[NCT][2];
+        bf16x8 sf[NCT][K / 32], uf[NCT][NJ];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
             for (int kk = 0; kk < K / 32; ++kk) sf[ct][kk] = frag(&sb[buf][16 * ct][32 * kk], K + PAD, lane);
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) uf[ct][jj] = frag(&ut[buf][16 * ct][32 * jj], CH + PAD, lane);
+            for (int jj = 0; jj < NJ; ++jj) uf[ct][jj] = frag(&ut[buf][16 * ct][32 * jj], CH + PAD, lane);
         }
         f32x4 a1[NCT], a2[NCT];
 #pragma unroll
@@ -743,13 +749,15 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
             a1[ct] = mma_bf16(sf[ct][0], f.q[0], zero4());
             a2[ct] = mma_bf16(uf[ct][0], f.pm[0], zero4());
         }
+        if constexpr (NJ == 2) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) a2[ct] = mma_bf16(uf[ct][1], f.pm[1], a2[ct]);
+            for (int ct = 0; ct < NCT; ++ct) a2[ct] = mma_bf16(uf[ct][1], f.pm[1], a2[ct]);
+        }
 #pragma unroll
         for (int kk = 1; kk < K / 32; ++kk)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) a1[ct] = mma_bf16(sf[ct][kk], f.q[kk], a1[ct]);
-        order_reads_then_mfma<(K / 32 + 2) * NCT, (K / 32 + 2) * NCT>();
+        order_reads_then_mfma<(K / 32 + NJ) * NCT, (K / 32 + NJ) * NCT>();
         // lane: token 16 wv + l%16, columns 16 ct + 4(l/16) .. +3
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
@@ -810,12 +818,18 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
                 __syncthreads();
                 fetch_o(min(c + 1, c1 - 1), fb);
                 __syncthreads();
-                if (c < c1) o_tile(c, (c - c0) & 1, fa);
+                if (c < c1) {
+                    if (wv >= 2) o_tile(std::integral_constant<int, 2>{}, c, (c - c0) & 1, fa);
+                    else o_tile(std::integral_constant<int, 1>{}, c, (c - c0) & 1, fa);
+                }
                 if (c + 1 > c1) break;
                 __syncthreads();
                 fetch_o(min(c + 2, c1 - 1), fa);
                 __syncthreads();
-                if (c + 1 < c1) o_tile(c + 1, (c + 1 - c0) & 1, fb);
+                if (c + 1 < c1) {
+                    if (wv >= 2) o_tile(std::integral_constant<int, 2>{}, c + 1, (c + 1 - c0) & 1, fb);
+                    else o_tile(std::integral_constant<int, 1>{}, c + 1, (c + 1 - c0) & 1, fb);
+                }
             }
         }
     }
