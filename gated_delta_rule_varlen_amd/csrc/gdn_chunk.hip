@@ -547,8 +547,9 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
         const int kt = wv + 4 * m;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
+            // T is lower triangular: rows i < 32 have no entry at j >= 32
             f32x4 acc = mma_bf16(xf[m][0], frag(&tb[16 * it][0], CH + PAD, lane), zero4());
-            acc = mma_bf16(xf[m][1], frag(&tb[16 * it][32], CH + PAD, lane), acc);
+            if (it >= 2) acc = mma_bf16(xf[m][1], frag(&tb[16 * it][32], CH + PAD, lane), acc);
             *reinterpret_cast<u32x2*>(w_out + (size_t)(it * (K / 32) + (kt >> 1)) * AT + a_tile_half_offset(lane, kt & 1)) =
                 pack4(acc[0], acc[1], acc[2], acc[3]);
         }
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             f32x4 acc = mma_bf16(frag(&tb[16 * it][0], CH + PAD, lane), yf[m][0], zero4());
-            acc = mma_bf16(frag(&tb[16 * it][32], CH + PAD, lane), yf[m][1], acc);
+            if (it >= 2) acc = mma_bf16(frag(&tb[16 * it][32], CH + PAD, lane), yf[m][1], acc);
             *reinterpret_cast<u32x2*>(u_out + (size_t)(it * (V / 16) + vt) * DT + 4 * lane) = pack4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
