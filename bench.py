@@ -407,7 +407,7 @@ def main():
                     help="time a plain 1 GiB device-to-device copy (reference for HBM counters and achievable bandwidth)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards with no exchange across sequences or key-head groups; see the design notes)",
               file=sys.stderr)
         sys.exit(2)

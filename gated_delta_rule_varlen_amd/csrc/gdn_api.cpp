@@ -121,7 +121,7 @@ const char* gdn_status_string(gdn_status s) {
         case GDN_ERR_DTYPE: return "unknown or disallowed element type";
         case GDN_ERR_OVERFLOW: return "a size or launch grid exceeds the index range";
         case GDN_ERR_ALIGN: return "a tensor pointer or token row is not 16-byte aligned";
-        case GDN_ERR_UNSUPPORTED: return "shape, flag or path not supported by this build";
+        case GDN_ERR_UNSUPPORTED: return "shape, flag or path not supported by this library";
         case GDN_ERR_WORKSPACE: return "workspace missing or too small";
         case GDN_ERR_HIP: return "the HIP runtime rejected a launch";
         case GDN_ERR_OFFSETS: return "malformed offsets (device-detected; nothing written)";

@@ -145,7 +145,7 @@ gdn_status gdn_conv1d_varlen_capture(const gdn_conv_desc *desc, const void *x, c
  * A NULL decay input a means g = 1; a NULL rate input b means beta = 1.  Gate arithmetic is fp32
  * (gate inputs are widened to fp32 first).  scale <= 0 selects 1/sqrt(K).
  * Constraints: B >= 1, N >= 0, HQ >= 1, H >= 1, H % HQ == 0, 1 <= K <= 256 (the pages' limit),
- * V >= 1; this build instantiates K in {32, 64, 128, 256} (GDN_ERR_UNSUPPORTED otherwise).
+ * V >= 1; the library instantiates K in {32, 64, 128, 256} (GDN_ERR_UNSUPPORTED otherwise).
  * gate_dtype is GDN_F32 or qkv_dtype.
  * ---------------------------------------------------------------------------------------------- */
 #define GDN_L2NORM 1u
