@@ -449,8 +449,9 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
     // P_ij = e^{G_i - G_j} (qhat_i . khat_j) for j <= i (computed transposed: 4 consecutive j per lane).
     // The masks are selects, not branches: the decay factor is evaluated for every entry with its
     // exponent clamped at 0 (G never increases inside a chunk, so the clamp changes only entries the
-    // mask drops), and G and b are read as 4-vectors.  The tile loop stays rolled: the X and Y fragments are live across it, and unrolled it needs more
-    // registers than three blocks per compute unit leave.
+    // mask drops), and G and b are read as 4-vectors.  The tile loop stays rolled: the X and Y
+    // fragments are live across it, and unrolled it needs more registers than four blocks per
+    // compute unit leave.
     {
         const int ia = 16 * wv + 4 * (lane >> 4);  // rows of this lane's A entries
         const int ip = 16 * wv + (lane & 15);      // row of this lane's P entries
