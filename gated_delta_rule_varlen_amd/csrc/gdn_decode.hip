@@ -55,6 +55,8 @@ constexpr int kMaxL = 4;  // (W-1)*D handled by this kernel
 #ifndef GDN_DECODE_STEP_NW
 #define GDN_DECODE_STEP_NW 4
 #endif
+// Grids with fewer blocks than compute units run 8 waves per block instead.
+constexpr long long kSmallGridBlocks = 256;
 
 // Whole-call checks: the offsets (as everywhere) and, for this entry point, at most one token per
 // sequence.  Returns 0, GDN_ERR_OFFSETS or GDN_ERR_UNSUPPORTED; must be reached by all threads.
@@ -309,7 +311,13 @@ hipError_t launch_k(DecodeArgs p, hipStream_t stream) {
     if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
     p.n_blocks = (int)blocks;
     const size_t lds = decode_lds_bytes(K, p.G * p.V, p.L, p.W, sizeof(typename S::storage));
-    hipLaunchKernelGGL((decode_kernel<T, S, K, LPC, CPL, NW>), dim3((unsigned)blocks), dim3(64 * NW), lds, stream, p);
+    // A grid smaller than the chip (small batches, where this single launch is the faster form)
+    // gives each block 8 waves, so twice the column tiles of a block are in flight at once
+    // (B = 8: 25.3 -> 21.6 us per step; 16 waves spill and gain nothing more).
+    if (blocks < kSmallGridBlocks)
+        hipLaunchKernelGGL((decode_kernel<T, S, K, LPC, CPL, 8>), dim3((unsigned)blocks), dim3(64 * 8), lds, stream, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, S, K, LPC, CPL, NW>), dim3((unsigned)blocks), dim3(64 * NW), lds, stream, p);
     return hipGetLastError();
 }
 
