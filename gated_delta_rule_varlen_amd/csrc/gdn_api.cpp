@@ -88,9 +88,10 @@ gdn_status strided_streams(const gdn_scan_desc* d, const gdn_qkv_streams* s, boo
 // the softplus gate), and it relies on normalised keys for a well-conditioned (I + A); it computes
 // the gates and norms itself, so it runs on fused inputs only; its algebra is that of the rules
 // with the retrieval term and one decay per head.  Built for bf16/fp16 I/O with K = V = 64 or 128.
-// Capture is recorded by the token-sequential paths only.
+// Capture is recorded by the token-sequential paths only.  A call without tokens reads no decays
+// (its chunked form only copies the initial states), so there the decay input may be absent.
 bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay, bool capture) {
-    return !prepared && has_decay && !capture && (d->flags & GDN_SOFTPLUS) && (d->flags & GDN_L2NORM) &&
+    return !prepared && (has_decay || d->N == 0) && !capture && (d->flags & GDN_SOFTPLUS) && (d->flags & GDN_L2NORM) &&
            !(d->flags & (GDN_NO_RETRIEVE | GDN_GATE_PER_KEY)) &&
            gdn::chunked_shape_supported(d->K, d->V, d->qkv_dtype);
 }

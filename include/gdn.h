@@ -237,10 +237,9 @@ gdn_status gdn_prepare_qk_gates_strided(const gdn_scan_desc *desc, const gdn_qkv
  *   workspace  device scratch of ws_bytes bytes, needed only by GDN_PATH_CHUNK (query the size
  *              with gdn_scan_workspace_bytes); may be NULL otherwise
  *   dev_status [1] int32 (NULL ok); path_used: HOST int32 receiving the gdn_path that ran (NULL ok)
- * GDN_PATH_CHUNK requires fused mode with a decay input and GDN_SOFTPLUS (so every decay is
- * finite and positive), GDN_L2NORM, the retrieval term (no GDN_NO_RETRIEVE), bf16 or fp16 qkv, and
- * K = V = 64 or K = V = 128; otherwise
- * GDN_ERR_UNSUPPORTED.  Its intra-chunk contractions run on bf16 matrix cores with fp32
+ * GDN_PATH_CHUNK requires fused mode with a decay input (not needed when N = 0) and GDN_SOFTPLUS
+ * (so every decay is finite and positive), GDN_L2NORM, the retrieval term (no GDN_NO_RETRIEVE),
+ * bf16 or fp16 qkv, and K = V = 64 or K = V = 128; otherwise GDN_ERR_UNSUPPORTED.  Its intra-chunk contractions run on bf16 matrix cores with fp32
  * accumulation (the state itself stays fp32).
  * ---------------------------------------------------------------------------------------------- */
 gdn_status gdn_scan_varlen(const gdn_scan_desc *desc, const void *qkv, const float *qk_prep, const float *gb_prep,

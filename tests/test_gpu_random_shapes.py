@@ -1,0 +1,64 @@
+"""GPU parity of gdn_scan_varlen on seeded random shapes, every recurrence path against the oracle.
+
+Each case draws a batch size, ragged lengths (empty and one-token sequences included), key heads,
+value heads per key head (1, 2 or 4), K = V in {64, 128} and a half-precision dtype from its seed,
+then runs the DECODE, SEQ and CHUNK paths on the same inputs.  Outputs and final state are held to
+the half-precision tolerance; the state of an empty sequence must come back bit-identical."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import TOL, assert_close, bits, ensure_built, f64, require_gpu
+from test_gpu_scan import gpu_scan
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = list(range(301, 317))
+
+
+@pytest.fixture(scope="module")
+def torch():
+    ensure_built()
+    return require_gpu()
+
+
+def draw(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 7))
+    lengths = rng.integers(0, 261, size=B)
+    kind = rng.random(B)
+    lengths[kind < 0.2] = 0
+    lengths[(kind >= 0.2) & (kind < 0.3)] = 1
+    G = int(rng.choice([1, 2, 4]))
+    HQ = int(rng.choice([1, 2]))
+    K = int(rng.choice([64, 128]))
+    io = str(rng.choice(["bf16", "f16"]))
+    return workloads.make(name=f"random_{seed}", seed=seed, lengths=[int(x) for x in lengths], HQ=HQ, H=HQ * G,
+                          K=K, V=K, io=io, conv_state_dtype="f32")
+
+
+@pytest.fixture(scope="module")
+def references():
+    refs = {}
+    for seed in SEEDS:
+        w = draw(seed)
+        refs[seed] = (w, oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io,
+                                     gate_dtype=w.gate_dtype, a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias,
+                                     state_in=w.state))
+    return refs
+
+
+@pytest.mark.parametrize("path", ["decode", "seq", "chunk"])
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_shape_against_oracle(torch, references, seed, path):
+    w, (o_ref, s_ref) = references[seed]
+    lens = [int(x) for x in w.lengths]
+    print(f"[random {seed}] path={path} B={w.B} lengths={lens} HQ={w.HQ} H={w.H} K={w.K} {w.io}", flush=True)
+    out, st, used = gpu_scan(torch, w, path, False)
+    assert used == path
+    if w.N > 0:
+        assert_close(f64(out), o_ref, TOL[w.io], f"{path} out")
+    assert_close(f64(st), s_ref, TOL[w.io], f"{path} state")
+    empty = np.flatnonzero(w.lengths == 0)
+    assert np.array_equal(bits(st)[empty], w.state[empty].view(np.int32))
