@@ -227,7 +227,7 @@ gdn_status check_prepare(const gdn_scan_desc* d, const void* a, const float* A_l
     const gdn_status st = check_scan_desc(d);
     if (st != GDN_OK) return st;
     if (d->flags & GDN_GATE_PER_KEY) return GDN_ERR_UNSUPPORTED;  // its gate plane is one decay per head
-    if (qk_out == nullptr && gb_out == nullptr) return GDN_ERR_NULL;
+    if (d->N > 0 && qk_out == nullptr && gb_out == nullptr) return GDN_ERR_NULL;  // N = 0 writes nothing
     if (a != nullptr && (d->flags & GDN_SOFTPLUS) && (A_log == nullptr || dt_bias == nullptr)) return GDN_ERR_NULL;
     if (misaligned(qk_out) || misaligned(gb_out)) return GDN_ERR_ALIGN;
     return GDN_OK;

@@ -201,7 +201,7 @@ typedef struct gdn_qkv_streams {
  *   gb_out[0, t, h] = g,  gb_out[1, t, h] = beta   (fp32)
  * Tensors: qkv [N, C] qkv_dtype (required); a, b [N, H] gate_dtype (NULL = absent); A_log,
  * dt_bias [H] fp32 (required when a is given and GDN_SOFTPLUS is set); qk_out [2, N, HQ, K] fp32;
- * gb_out [2, N, H] fp32.  Either output may be NULL to skip it (not both).
+ * gb_out [2, N, H] fp32.  Either output may be NULL to skip it (not both, unless N = 0).
  * ---------------------------------------------------------------------------------------------- */
 gdn_status gdn_prepare_qk_gates(const gdn_scan_desc *desc, const void *qkv, const void *a, const void *b,
                                 const float *A_log, const float *dt_bias, float *qk_out, float *gb_out,

@@ -168,6 +168,9 @@ def test_prepare_host_validation(abi):
     assert L.gdn_prepare_qk_gates(ctypes.byref(d), P, None, None, None, None, P + 4, P, None) == abi.ERR_ALIGN
     bad = scan_desc(abi, K=100)
     assert L.gdn_prepare_qk_gates(ctypes.byref(bad), P, None, None, None, None, P, P, None) == abi.ERR_UNSUPPORTED
+    # a call without tokens writes nothing, so it needs no buffers at all (and launches nothing)
+    empty = scan_desc(abi, N=0)
+    assert L.gdn_prepare_qk_gates(ctypes.byref(empty), None, None, None, None, None, None, None, None) == abi.OK
 
 
 def test_workspace_query(abi):

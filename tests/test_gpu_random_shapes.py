@@ -62,3 +62,57 @@ def test_random_shape_against_oracle(torch, references, seed, path):
     assert_close(f64(st), s_ref, TOL[w.io], f"{path} state")
     empty = np.flatnonzero(w.lengths == 0)
     assert np.array_equal(bits(st)[empty], w.state[empty].view(np.int32))
+
+
+FLAG_SEEDS = list(range(401, 417))
+
+
+def draw_flags(seed):
+    """Wider flag space of the token-sequential paths: fp32 I/O, K != V, raw decay and rate inputs,
+    no q/k normalisation (unit-norm keys then keep the recurrence bounded), prepared inputs."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 6))
+    lengths = rng.integers(0, 140, size=B)
+    lengths[rng.random(B) < 0.2] = 0
+    G = int(rng.choice([1, 2, 4]))
+    HQ = int(rng.choice([1, 2]))
+    K = int(rng.choice([32, 64, 128, 256]))
+    V = int(rng.choice([32, 64, 128]))
+    io = str(rng.choice(["f32", "bf16", "f16"]))
+    l2norm = bool(rng.random() < 0.5)
+    softplus = bool(rng.random() < 0.5)
+    sigmoid = bool(rng.random() < 0.5)
+    prepared = bool(rng.random() < 0.5)
+    w = workloads.make(name=f"random_flags_{seed}", seed=seed, lengths=[int(x) for x in lengths], HQ=HQ, H=HQ * G,
+                       K=K, V=V, io=io, conv_state_dtype="f32", l2norm=l2norm, softplus=softplus, sigmoid=sigmoid,
+                       decay_range=None if softplus else (-1.0, 0.0), beta_range=None if sigmoid else (0.0, 1.0),
+                       unit_k_scan=not l2norm)
+    return w, prepared
+
+
+@pytest.fixture(scope="module")
+def flag_references():
+    refs = {}
+    for seed in FLAG_SEEDS:
+        w, prepared = draw_flags(seed)
+        refs[seed] = (w, prepared, oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io,
+                                               gate_dtype=w.gate_dtype, a=w.a, b=w.b, A_log=w.A_log,
+                                               dt_bias=w.dt_bias, state_in=w.state, l2norm=w.l2norm,
+                                               softplus=w.softplus, sigmoid=w.sigmoid, scale=w.scale))
+    return refs
+
+
+@pytest.mark.parametrize("path", ["decode", "seq"])
+@pytest.mark.parametrize("seed", FLAG_SEEDS)
+def test_random_flags_against_oracle(torch, flag_references, seed, path):
+    w, prepared, (o_ref, s_ref) = flag_references[seed]
+    lens = [int(x) for x in w.lengths]
+    print(f"[random flags {seed}] path={path} prepared={prepared} B={w.B} lengths={lens} HQ={w.HQ} H={w.H} "
+          f"K={w.K} V={w.V} {w.io} l2norm={w.l2norm} softplus={w.softplus} sigmoid={w.sigmoid}", flush=True)
+    out, st, used = gpu_scan(torch, w, path, prepared)
+    assert used == path
+    if w.N > 0:
+        assert_close(f64(out), o_ref, TOL[w.io], f"{path} out")
+    assert_close(f64(st), s_ref, TOL[w.io], f"{path} state")
+    empty = np.flatnonzero(w.lengths == 0)
+    assert np.array_equal(bits(st)[empty], w.state[empty].view(np.int32))
