@@ -1,9 +1,14 @@
-"""GPU parity of gdn_scan_varlen on seeded random shapes, every recurrence path against the oracle.
+"""GPU parity on seeded random shapes and flags, against the oracle.
 
-Each case draws a batch size, ragged lengths (empty and one-token sequences included), key heads,
-value heads per key head (1, 2 or 4), K = V in {64, 128} and a half-precision dtype from its seed,
-then runs the DECODE, SEQ and CHUNK paths on the same inputs.  Outputs and final state are held to
-the half-precision tolerance; the state of an empty sequence must come back bit-identical."""
+* Recurrence, every path: each case draws a batch size, ragged lengths (empty and one-token
+  sequences included), key heads, value heads per key head (1, 2 or 4), K = V in {64, 128} and a
+  half-precision dtype, then runs DECODE, SEQ and CHUNK on the same inputs.
+* Recurrence, wider flags (DECODE and SEQ): fp32 I/O, K != V, raw decay and rate inputs, no q/k
+  normalisation, prepared inputs.
+* Conv: widths 1..8, dilations 1..3, channel counts off the 16-byte vector width, every dtype with
+  its own or an fp32 window, bias and SiLU on or off, sequences shorter than the window.
+Outputs and final state are held to the dtype tolerance; the state of an empty sequence and the
+carried conv window must come back bit-identical."""
 import numpy as np
 import pytest
 
@@ -116,3 +121,42 @@ def test_random_flags_against_oracle(torch, flag_references, seed, path):
     assert_close(f64(st), s_ref, TOL[w.io], f"{path} state")
     empty = np.flatnonzero(w.lengths == 0)
     assert np.array_equal(bits(st)[empty], w.state[empty].view(np.int32))
+
+
+CONV_SEEDS = list(range(501, 517))
+
+
+def draw_conv(seed):
+    """Random conv calls: widths 1..8, dilations 1..3, channel counts that do and do not fill 16-byte
+    vectors, every I/O dtype with its own or an fp32 window, bias and SiLU on or off, short ragged
+    sequences (shorter than the window too) and empty ones."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 7))
+    lengths = rng.integers(0, 41, size=B)
+    lengths[rng.random(B) < 0.2] = 0
+    HQ = int(rng.choice([1, 2]))
+    H = HQ * int(rng.choice([1, 2]))
+    K = int(rng.choice([3, 8, 16, 32]))
+    V = int(rng.choice([2, 8, 16]))
+    io = str(rng.choice(["f32", "bf16", "f16"]))
+    return workloads.make(name=f"random_conv_{seed}", seed=seed, lengths=[int(x) for x in lengths], HQ=HQ, H=H,
+                          K=K, V=V, W=int(rng.integers(1, 9)), D=int(rng.integers(1, 4)), io=io,
+                          conv_state_dtype=str(rng.choice([io, "f32"])), silu=bool(rng.random() < 0.5),
+                          has_bias=bool(rng.random() < 0.5))
+
+
+@pytest.mark.parametrize("seed", CONV_SEEDS)
+def test_random_conv_against_oracle(torch, seed):
+    from test_gpu_conv import gpu_conv
+
+    w = draw_conv(seed)
+    lens = [int(x) for x in w.lengths]
+    print(f"[random conv {seed}] B={w.B} lengths={lens} C={w.C} W={w.W} D={w.D} {w.io} window={w.conv_state_dtype} "
+          f"bias={w.conv_bias is not None} silu={w.silu}", flush=True)
+    y, st = gpu_conv(torch, w)
+    y_ref, st_ref = oracle.conv(w.x, w.conv_w, w.offsets, W=w.W, D=w.D, x_dtype=w.io, bias=w.conv_bias,
+                                state_in=w.conv_state, silu=w.silu, state_dtype=w.conv_state_dtype)
+    if w.N > 0:
+        assert_close(f64(y), y_ref, TOL[w.io], "conv y")
+    if w.L > 0:
+        assert np.array_equal(f64(st), st_ref), "carried window"
