@@ -7,6 +7,8 @@
   normalisation, prepared inputs.
 * Conv: widths 1..8, dilations 1..3, channel counts off the 16-byte vector width, every dtype with
   its own or an fp32 window, bias and SiLU on or off, sequences shorter than the window.
+* Single-launch decode step: bit-identical to the two calls, on batches either side of its
+  small-grid launch.
 Outputs and final state are held to the dtype tolerance; the state of an empty sequence and the
 carried conv window must come back bit-identical."""
 import numpy as np
@@ -160,3 +162,39 @@ def test_random_conv_against_oracle(torch, seed):
         assert_close(f64(y), y_ref, TOL[w.io], "conv y")
     if w.L > 0:
         assert np.array_equal(f64(st), st_ref), "carried window"
+
+
+STEP_SEEDS = list(range(601, 613))
+
+
+def draw_step(seed):
+    """Random single-launch decode steps: batches on both sides of the small-grid launch (fewer
+    blocks than compute units), empty sequences, every key width and dtype, GQA 1..4, conv widths
+    1..5 and dilations with a window of at most 4."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 301))
+    lengths = (rng.random(B) >= 0.2).astype(int)
+    HQ = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 2, 4]))
+    K = int(rng.choice([32, 64, 128, 256]))
+    V = int(rng.choice([4, 32, 64, 128]))
+    W = int(rng.integers(1, 6))
+    D = int(rng.choice([1, 2])) if W <= 3 else 1
+    io = str(rng.choice(["f32", "bf16", "f16"]))
+    return workloads.make(name=f"random_step_{seed}", seed=seed, lengths=[int(x) for x in lengths], HQ=HQ,
+                          H=HQ * G, K=K, V=V, W=W, D=D, io=io, conv_state_dtype=str(rng.choice([io, "f32"])))
+
+
+@pytest.mark.parametrize("seed", STEP_SEEDS)
+def test_random_decode_step_matches_two_calls(torch, seed):
+    from test_gpu_decode_step import run_chain, run_fused
+
+    w = draw_step(seed)
+    print(f"[random step {seed}] B={w.B} N={w.N} HQ={w.HQ} H={w.H} K={w.K} V={w.V} W={w.W} D={w.D} {w.io} "
+          f"window={w.conv_state_dtype} blocks={w.B * w.HQ}", flush=True)
+    o2, s2, c2 = run_chain(torch, w)
+    o1, s1, c1 = run_fused(torch, w)
+    assert np.array_equal(bits(o1), bits(o2)), "out"
+    assert np.array_equal(bits(s1), bits(s2)), "state"
+    if w.L > 0:
+        assert np.array_equal(bits(c1), bits(c2)), "conv window"
