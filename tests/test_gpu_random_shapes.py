@@ -9,6 +9,7 @@
   its own or an fp32 window, bias and SiLU on or off, sequences shorter than the window.
 * Single-launch decode step: bit-identical to the two calls, on batches either side of its
   small-grid launch.
+* Every entry point on a batch of empty sequences (N = 0).
 Outputs and final state are held to the dtype tolerance; the state of an empty sequence and the
 carried conv window must come back bit-identical."""
 import numpy as np
@@ -16,7 +17,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import TOL, assert_close, bits, ensure_built, f64, require_gpu
+from gpu_util import TOL, assert_close, bits, dev, dev_i32, ensure_built, f64, require_gpu
 from test_gpu_scan import gpu_scan
 
 pytestmark = pytest.mark.gpu
@@ -198,3 +199,42 @@ def test_random_decode_step_matches_two_calls(torch, seed):
     assert np.array_equal(bits(s1), bits(s2)), "state"
     if w.L > 0:
         assert np.array_equal(bits(c1), bits(c2)), "conv window"
+
+
+def test_every_entry_point_accepts_a_call_without_tokens(torch):
+    """A batch of empty sequences (N = 0): every entry point returns, the final states are the
+    initial ones bit for bit, the conv windows are copied, and capture records only zeros."""
+    import gated_delta_rule_varlen_amd as gdn
+
+    w = workloads.make(name="all_empty", seed=701, lengths=[0, 0, 0], HQ=2, H=4, K=128, V=128, io="bf16",
+                       conv_state_dtype="f32")
+    assert w.N == 0
+    x, cw, cb = dev(w.x, w.io), dev(w.conv_w, w.io), dev(w.conv_bias, w.io)
+    cst, st, off = dev(w.conv_state, "f32"), dev(w.state, "f32"), dev_i32(w.offsets)
+    gates = dict(a=dev(w.a, w.gate_dtype), b=dev(w.b, w.gate_dtype), A_log=dev(w.A_log, "f32"),
+                 dt_bias=dev(w.dt_bias, "f32"))
+    dims = dict(HQ=w.HQ, H=w.H, K=w.K, V=w.V)
+    counts = torch.full((w.B,), 2, dtype=torch.int32, device="cuda")
+    st_bits, cst_bits = w.state.view(np.int32), w.conv_state.view(np.int32)
+
+    out, s1, c1 = gdn.decode_step(x, cw, off, bias=cb, conv_state_in=cst, state_in=st, **gates, **dims)
+    y, c2, upd = gdn.conv1d_varlen_capture(x, cw, off, cap=2, counts=counts, bias=cb, state_in=cst, silu=True,
+                                           state_dtype=torch.float32)
+    o3, s3, cap3, used3 = gdn.scan_varlen_capture(dev(w.qkv, w.io), off, cap=2, counts=counts, state_in=st,
+                                                  **gates, **dims)
+    HQK = w.HQ * w.K
+    qkv = dev(w.qkv, w.io)
+    q, k, v = qkv[:, :HQK], qkv[:, HQK:2 * HQK], qkv[:, 2 * HQK:]
+    qk, gb = gdn.prepare_qk_gates_strided(q, k, **gates, **dims)
+    results = [(s1, c1)]
+    for path in ("decode", "seq", "chunk"):
+        o4, s4, used4 = gdn.scan_varlen_strided(q, k, v, off, state_in=st, path=path, **gates, **dims)
+        assert used4 == path
+        results.append((s4, None))
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and y.numel() == 0 and o3.numel() == 0 and qk.numel() == 0 and gb.numel() == 0
+    for s, c in results + [(s3, c2)]:
+        assert np.array_equal(bits(s), st_bits)
+        if c is not None:
+            assert np.array_equal(bits(c), cst_bits)
+    assert not np.any(f64(upd)) and not np.any(f64(cap3))
