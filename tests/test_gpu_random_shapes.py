@@ -9,6 +9,7 @@
   its own or an fp32 window, bias and SiLU on or off, sequences shorter than the window.
 * Single-launch decode step: bit-identical to the two calls, on batches either side of its
   small-grid launch.
+* Speculative-decoding capture on random batches, lengths and counts.
 * Every entry point on a batch of empty sequences (N = 0).
 Outputs and final state are held to the dtype tolerance; the state of an empty sequence and the
 carried conv window must come back bit-identical."""
@@ -238,3 +239,29 @@ def test_every_entry_point_accepts_a_call_without_tokens(torch):
         if c is not None:
             assert np.array_equal(bits(c), cst_bits)
     assert not np.any(f64(upd)) and not np.any(f64(cap3))
+
+
+CAPTURE_SEEDS = list(range(801, 811))
+
+
+@pytest.mark.parametrize("path", ["decode", "seq"])
+@pytest.mark.parametrize("seed", CAPTURE_SEEDS)
+def test_random_capture_against_oracle(torch, seed, path):
+    """Speculative-decoding capture on random batches: lengths 0..12 (either side of the short
+    form's 8 tokens), random per-sequence counts (zero, negative, below and past the capacity and
+    the length), any key width and dtype; outputs and state unchanged by the capture."""
+    from test_gpu_capture import CAP, check_capsule, oracle_capsule, run_capture
+
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    lengths = [int(x) for x in rng.integers(0, 13, size=B)]
+    counts = rng.integers(-1, CAP + 3, size=B).astype(np.int32)
+    HQ = int(rng.choice([1, 2]))
+    K = int(rng.choice([32, 64, 128, 256]))
+    V = int(rng.choice([32, 64, 128]))
+    io = str(rng.choice(["f32", "bf16", "f16"]))
+    w = workloads.make(name=f"random_capture_{seed}", seed=seed, lengths=lengths, HQ=HQ,
+                       H=HQ * int(rng.choice([1, 2, 4])), K=K, V=V, io=io)
+    print(f"[random capture {seed}] {path} B={B} N={w.N} HQ={w.HQ} H={w.H} K={K} V={V} {io}", flush=True)
+    got = run_capture(torch, w, counts, path=path)
+    check_capsule(w, got, oracle_capsule(w, counts), TOL[w.io], f"random capture {seed}/{path}")
