@@ -293,6 +293,47 @@ def per_key_comparison(torch, steps: int = 50):
     return res
 
 
+def prepare_bytes(w) -> int:
+    """Algorithmic HBM bytes of one gdn_prepare_qk_gates launch: the q and k rows and the two gate
+    inputs read, the fp32 normalised q/k planes and the g/beta planes written."""
+    reads = w.N * (2 * w.HQ * w.K * sizeof(w.io) + 2 * w.H * sizeof(w.gate_dtype))
+    writes = w.N * (2 * w.HQ * w.K + 2 * w.H) * 4
+    return reads + writes
+
+
+def prepare_measurement(torch, steps: int = 50):
+    """gdn_prepare_qk_gates alone on the prefill and decode workloads: mean microseconds per launch
+    (HIP events on the launch stream, best of 3) against the HBM roofline of its algorithmic bytes."""
+    import gated_delta_rule_varlen_amd as gdn
+    import workloads
+
+    res = {}
+    for w in (workloads.varlen_prefill(), workloads.decode_step()):
+        p = Path(w, torch, "auto")
+        kw = dict(HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=p.a, b=p.b, A_log=p.A_log, dt_bias=p.dt_bias,
+                  l2norm=w.l2norm, softplus=w.softplus, sigmoid=w.sigmoid)
+        qk, gb = gdn.prepare_qk_gates(p.x, **kw)
+        best = None
+        for _ in range(3):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for _ in range(10):
+                gdn.prepare_qk_gates(p.x, qk_out=qk, gb_out=gb, **kw)
+            for a, b in evs:
+                a.record()
+                gdn.prepare_qk_gates(p.x, qk_out=qk, gb_out=gb, **kw)
+                b.record()
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+            best = us if best is None else min(best, us)
+        nbytes = prepare_bytes(w)
+        gbs = nbytes / (best * 1e-6) / 1e9
+        res[w.name] = {"us": round(best, 2), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del p, qk, gb
+    torch.cuda.empty_cache()
+    return res
+
+
 def cache_flushed_decode(torch, steps: int = 50, flush_mb: int = 512):
     """The decode step's recurrence timed with a flush_mb buffer written between steps, so that no
     state line can still sit in the 256 MB memory-side cache from the previous step: mean
@@ -485,7 +526,8 @@ def main():
                         "speculative_verify_capture": verify_comparison(torch),
                         "per_key_decay": per_key_comparison(torch),
                         "strided_qkv": strided_comparison(torch),
-                        "decode_cache_flushed": cache_flushed_decode(torch)}
+                        "decode_cache_flushed": cache_flushed_decode(torch),
+                        "prepare": prepare_measurement(torch)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
