@@ -334,32 +334,36 @@ def prepare_measurement(torch, steps: int = 50):
     return res
 
 
-def cache_flushed_decode(torch, steps: int = 50, flush_mb: int = 512):
-    """The decode step's recurrence timed with a flush_mb buffer written between steps, so that no
-    state line can still sit in the 256 MB memory-side cache from the previous step: mean
-    microseconds per recurrence launch (HIP events on the launch stream, flush outside the pair)
-    next to the back-to-back figure from the same setup."""
+def cache_flushed(torch, steps: int = 50, flush_mb: int = 512):
+    """The recurrence of the decode, prefill and edge workloads timed with a flush_mb buffer written
+    between steps, so that nothing the previous step touched can still sit in the 256 MB memory-side
+    cache: mean microseconds per recurrence launch (HIP events on the launch stream, the flush
+    outside the pair) next to the back-to-back figure from the same setup, and the flushed launch
+    against the HBM roofline of its algorithmic bytes."""
     import workloads
 
-    w = workloads.decode_step()
-    p = Path(w, torch, "decode")
+    res = {}
     scratch = torch.empty(flush_mb << 20, dtype=torch.uint8, device="cuda")
-    for _ in range(10):
-        p.step()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        scratch.fill_(i & 0xFF)
-        p.step(evs[i])
-    torch.cuda.synchronize()
-    flushed = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    _, back_to_back, _, _ = time_path(p, steps, 5)
-    del p, scratch
+    for w in (workloads.decode_step(), workloads.varlen_prefill(), workloads.edge_fp16()):
+        p = Path(w, torch, "auto")
+        for _ in range(10):
+            used = p.step()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            scratch.fill_(i & 0xFF)
+            p.step(evs[i])
+        torch.cuda.synchronize()
+        flushed = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        _, back_to_back, _, _ = time_path(p, steps, 5)
+        del p
+        gbs = scan_bytes(w) / (flushed * 1e-3) / 1e9
+        res[w.name] = {"path": used, "flush_mb": flush_mb, "scan_us_flushed": round(flushed * 1e3, 2),
+                       "scan_us_back_to_back": round(back_to_back * 1e3, 2), "scan_gbs_flushed": round(gbs, 1),
+                       "scan_hbm_frac_flushed": round(gbs / HBM_PEAK_GBS, 4)}
+    del scratch
     torch.cuda.empty_cache()
-    gbs = scan_bytes(w) / (flushed * 1e-3) / 1e9
-    return {"workload": w.name, "flush_mb": flush_mb, "scan_us_flushed": round(flushed * 1e3, 2),
-            "scan_us_back_to_back": round(back_to_back * 1e3, 2), "scan_gbs_flushed": round(gbs, 1),
-            "scan_hbm_frac_flushed": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def strided_comparison(torch, steps: int = 20):
@@ -526,7 +530,7 @@ def main():
                         "speculative_verify_capture": verify_comparison(torch),
                         "per_key_decay": per_key_comparison(torch),
                         "strided_qkv": strided_comparison(torch),
-                        "decode_cache_flushed": cache_flushed_decode(torch),
+                        "cache_flushed": cache_flushed(torch),
                         "prepare": prepare_measurement(torch)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
