@@ -448,35 +448,22 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
 
     __syncthreads();  // Y gathered: A may overwrite it
 
-    // Row block wv: A_ij = b_i e^{G_i - G_j} (khat_i . khat_j) for j < i, and
-    // P_ij = e^{G_i - G_j} (qhat_i . khat_j) for j <= i (computed transposed: 4 consecutive j per lane).
-    // The masks are selects, not branches: the decay factor is evaluated for every entry with its
-    // exponent clamped at 0 (G never increases inside a chunk, so the clamp changes only entries the
-    // mask drops), and G and b are read as 4-vectors.  The tile loop stays rolled: the X and Y
-    // fragments are live across it, and unrolled it needs more registers than four blocks per
-    // compute unit leave.
+    // A_ij = b_i e^{G_i - G_j} (khat_i . khat_j) for j < i, and P_ij = e^{G_i - G_j} (qhat_i . khat_j)
+    // for j <= i, in 16 x 16 blocks.  Wave wv forms the P blocks of its own row tile (it holds those
+    // Qhat rows; computed transposed: 4 consecutive j per lane) and the A blocks of column tile wv
+    // (rows it..3), so that every wave does 5 of the 20 nonzero blocks.  The masks are selects, not
+    // branches: the decay factor is evaluated for every entry with its exponent clamped at 0 (G never
+    // increases inside a chunk, so the clamp changes only entries the mask drops), and G and b are
+    // read as 4-vectors.  The tile loops stay rolled: the X and Y fragments are live across them,
+    // and unrolled they need more registers than four blocks per compute unit leave.
     {
-        const int ia = 16 * wv + 4 * (lane >> 4);  // rows of this lane's A entries
-        const int ip = 16 * wv + (lane & 15);      // row of this lane's P entries
+        const int ip = 16 * wv + (lane & 15);  // row of this lane's P entries
 #pragma unroll 1
         for (int jt = 0; jt < 4; ++jt) {
-            f32x4 a = zero4(), pt = zero4();
+            f32x4 pt = zero4();
             if (jt <= wv) {
 #pragma unroll
-                for (int kk = 0; kk < K; kk += 32) {
-                    const bf16x8 kj = frag(&kn[16 * jt][kk], K + PAD, lane);
-                    a = mma_bf16(frag(&kn[16 * wv][kk], K + PAD, lane), kj, a);
-                    pt = mma_bf16(kj, qw[kk / 32], pt);
-                }
-                const int j = 16 * jt + (lane & 15);
-                const float g_j = s_gam[j];
-                const f32x4 g_ia = *reinterpret_cast<const f32x4*>(&s_gam[ia]);
-                const f32x4 b_ia = *reinterpret_cast<const f32x4*>(&s_beta[ia]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e = expf(fminf(g_ia[r] - g_j, 0.0f));
-                    am[ia + r][j] = (j < ia + r) ? b_ia[r] * e * a[r] : 0.0f;
-                }
+                for (int kk = 0; kk < K; kk += 32) pt = mma_bf16(frag(&kn[16 * jt][kk], K + PAD, lane), qw[kk / 32], pt);
             }
             const int j = 16 * jt + 4 * (lane >> 4);
             const f32x4 g_j = *reinterpret_cast<const f32x4*>(&s_gam[j]);
@@ -491,6 +478,23 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
             if (wv >= 2 || jt < 2)
                 *reinterpret_cast<u32x2*>(p_out + (size_t)(wv * 2 + (jt >> 1)) * AT + a_tile_half_offset(lane, jt & 1)) =
                     pack4(pv[0], pv[1], pv[2], pv[3]);
+        }
+        const int ja = 16 * wv + (lane & 15);  // column of this lane's A entries
+        const float g_ja = s_gam[ja];
+#pragma unroll 1
+        for (int it = wv; it < 4; ++it) {
+            f32x4 a = zero4();
+#pragma unroll
+            for (int kk = 0; kk < K; kk += 32)
+                a = mma_bf16(frag(&kn[16 * it][kk], K + PAD, lane), frag(&kn[16 * wv][kk], K + PAD, lane), a);
+            const int ia = 16 * it + 4 * (lane >> 4);  // rows of this lane's A entries
+            const f32x4 g_ia = *reinterpret_cast<const f32x4*>(&s_gam[ia]);
+            const f32x4 b_ia = *reinterpret_cast<const f32x4*>(&s_beta[ia]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float e = expf(fminf(g_ia[r] - g_ja, 0.0f));
+                am[ia + r][ja] = (ja < ia + r) ? b_ia[r] * e * a[r] : 0.0f;
+            }
         }
     }
     __syncthreads();  // A ready; Khat rows dead (T may be written)
