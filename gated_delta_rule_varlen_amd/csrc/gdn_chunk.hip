@@ -501,7 +501,10 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
 
     // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution (wave w, lanes 0..15 own the
     // columns of block w); T is zero above the diagonal.
-    for (int idx = tid; idx < CH * CH; idx += 256) tm[idx / CH][idx % CH] = 0.0f;
+    // (thread t clears 16 consecutive entries of row t/4 with 16-byte stores)
+    static_assert(CH * CH == 256 * 16, "one 16-entry run per thread");
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(&tm[tid >> 2][16 * (tid & 3) + 4 * q]) = zero4();
     __syncthreads();
     if (lane < 16) {
         const int c = lane, o = 16 * wv;
@@ -543,9 +546,18 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
         __syncthreads();
     }
     // T to bf16 (overwrites A, which is dead)
-    for (int idx = tid; idx < CH * CH; idx += 256) {
-        const int i = idx / CH, j = idx % CH;
-        tb[i][j] = bf(tm[i][j]);
+    {
+        // thread t converts 16 consecutive entries of row t/4: four 16-byte reads, two 16-byte writes
+        const int i = tid >> 2, j0 = 16 * (tid & 3);
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&tm[i][j0 + 4 * q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+        }
+        *reinterpret_cast<u32x4*>(&tb[i][j0]) = pack8(v, 1.0f);
+        *reinterpret_cast<u32x4*>(&tb[i][j0 + 8]) = pack8(v + 8, 1.0f);
     }
     __syncthreads();
 
