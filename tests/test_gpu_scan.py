@@ -210,3 +210,20 @@ def test_chunk_rejects_ineligible_inputs(torch):
     with pytest.raises(gdn.GdnError) as ei:  # prepared inputs carry g, not log g
         gpu_scan(torch, w, "chunk", True)
     assert ei.value.status == -6
+
+
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_chunk_long_sequence_k64(torch, io):
+    """One 8192-token sequence (128 chunks in one serial chain) at K = V = 64, both half types:
+    the chunked form against the oracle and against the sequential form on the same inputs."""
+    w = workloads.make(name=f"chunk_long_k64_{io}", seed=141, lengths=[8192], HQ=4, H=8, K=64, V=64, io=io,
+                       conv_state_dtype="f32")
+    out_c, st_c, used = gpu_scan(torch, w, "chunk", False)
+    assert used == "chunk"
+    out_s, st_s, _ = gpu_scan(torch, w, "seq", False)
+    o_ref, s_ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io, gate_dtype=w.gate_dtype,
+                               a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias, state_in=w.state)
+    e1 = assert_close(f64(out_c), o_ref, TOL[w.io], "chunk out")
+    e2 = assert_close(f64(st_c), s_ref, 2e-2, "chunk state")
+    e3 = assert_close(f64(out_c), f64(out_s), TOL[w.io], "chunk vs seq out")
+    print(f"  long k64 {io}: out {e1:.2e} state {e2:.2e} vs-seq {e3:.2e}", flush=True)
