@@ -16,7 +16,7 @@ from . import _abi
 from ._abi import GdnError, PATH_NAMES, lib  # noqa: F401
 
 __all__ = ["conv1d_varlen", "conv1d_varlen_capture", "prepare_qk_gates", "prepare_qk_gates_strided", "scan_varlen",
-           "scan_varlen_capture", "scan_varlen_strided", "scan_workspace_bytes", "decode_step", "GdnError", "lib"]
+           "scan_varlen_capture", "scan_varlen_strided", "scan_varlen_noalloc", "scan_workspace_bytes", "decode_step", "GdnError", "lib"]
 
 _DTYPE = {torch.float32: _abi.F32, torch.bfloat16: _abi.BF16, torch.float16: _abi.F16}
 _TORCH = {v: k for k, v in _DTYPE.items()}
@@ -212,6 +212,31 @@ def scan_varlen(qkv: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K:
                                _ptr(offsets, "offsets"), _ptr(workspace, "workspace"), ws_bytes,
                                _ptr(dev_status, "dev_status"), ctypes.byref(used), _stream(qkv.device))
     _check(st, "gdn_scan_varlen")
+    return out, state_out, PATH_NAMES.get(used.value, str(used.value))
+
+
+def scan_varlen_noalloc(qkv: torch.Tensor, offsets: torch.Tensor, *, HQ: int, H: int, K: int, V: int, a=None, b=None,
+                        A_log=None, dt_bias=None, state_in=None, qk_prep=None, gb_prep=None, l2norm=True,
+                        softplus=True, sigmoid=True, scale: float = 0.0, path: str = "auto", out=None,
+                        state_out=None, dev_status=None, retrieve: bool = True, gate_per_key: bool = False):
+    """scan_varlen without a workspace argument (gdn_scan_varlen_noalloc): the chunked path's
+    workspace is the library's own device array, so the call allocates no device memory when out
+    and state_out are given.  Returns (out, state_out, path name that ran)."""
+    N = qkv.shape[0]
+    B = offsets.numel() - 1
+    if out is None:
+        out = torch.empty((N, H, V), dtype=qkv.dtype, device=qkv.device)
+    if state_out is None:
+        state_out = torch.empty((B, H, V, K), dtype=torch.float32, device=qkv.device)
+    d = _scan_desc(qkv, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, path, retrieve,
+                   gate_per_key)
+    used = ctypes.c_int32(-1)
+    st = lib().gdn_scan_varlen_noalloc(ctypes.byref(d), _ptr(qkv, "qkv"), _ptr(qk_prep, "qk_prep"),
+                                       _ptr(gb_prep, "gb_prep"), _ptr(a, "a"), _ptr(b, "b"), _ptr(A_log, "A_log"),
+                                       _ptr(dt_bias, "dt_bias"), _ptr(state_in, "state_in"), _ptr(out, "out"),
+                                       _ptr(state_out, "state_out"), _ptr(offsets, "offsets"),
+                                       _ptr(dev_status, "dev_status"), ctypes.byref(used), _stream(qkv.device))
+    _check(st, "gdn_scan_varlen_noalloc")
     return out, state_out, PATH_NAMES.get(used.value, str(used.value))
 
 

@@ -11,6 +11,8 @@ LIB_PATH = os.path.join(PKG, "libgdn.so")
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_OVERFLOW, ERR_ALIGN = -1, -2, -3, -4, -5
 ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_OFFSETS = -6, -7, -8, -9
+# the device array gdn_scan_varlen_noalloc uses as its workspace (GDN_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 # gdn_dtype
 F32, BF16, F16 = 0, 1, 2
 # flags
@@ -30,6 +32,7 @@ EXPORTS = (
     "gdn_scan_varlen",
     "gdn_scan_varlen_capture",
     "gdn_scan_varlen_strided",
+    "gdn_scan_varlen_noalloc",
     "gdn_scan_workspace_bytes",
     "gdn_decode_step",
     "gdn_status_string",
@@ -110,6 +113,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_scan_varlen_strided.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(QKVStreams)] + [vp] * 11 +
                                               [ctypes.c_size_t, vp, i32p, vp])
         L.gdn_scan_varlen_strided.restype = st
+        L.gdn_scan_varlen_noalloc.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 11 + [vp, i32p, vp]
+        L.gdn_scan_varlen_noalloc.restype = st
         L.gdn_decode_step.argtypes = [ctypes.POINTER(ConvDesc), ctypes.POINTER(ScanDesc)] + [vp] * 15
         L.gdn_decode_step.restype = st
         L.gdn_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(ctypes.c_size_t)]

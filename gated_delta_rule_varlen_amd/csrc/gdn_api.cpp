@@ -275,11 +275,14 @@ namespace {
 
 // gdn_scan_varlen with an optional capture (cap == 0: none; the capture arguments were checked).
 // The token streams x were checked by the caller (packed or strided); the rest is checked here.
+// The workspace is the caller's buffer, or, when `scratch` is given, the library's own device
+// scratch of ws_bytes bytes, which is looked up only after every host check has passed and only
+// when the resolved path uses a workspace.
 gdn_status scan_call(const gdn_scan_desc* d, const gdn::TokenStreams& x, const float* qk_prep, const float* gb_prep,
                      const void* a, const void* b, const float* A_log, const float* dt_bias, const float* state_in,
                      void* out, float* state_out, const int32_t* offsets, int cap, const int32_t* counts,
                      const int32_t* active, float* capsule, void* workspace, size_t ws_bytes, int32_t* dev_status,
-                     int32_t* path_used, hipStream_t stream) {
+                     int32_t* path_used, hipStream_t stream, gdn::ScratchFn scratch = nullptr) {
     if (offsets == nullptr) return GDN_ERR_NULL;
     if (d->N > 0 && out == nullptr) return GDN_ERR_NULL;
     if ((qk_prep == nullptr) != (gb_prep == nullptr)) return GDN_ERR_NULL;
@@ -295,11 +298,16 @@ gdn_status scan_call(const gdn_scan_desc* d, const gdn::TokenStreams& x, const f
         misaligned(state_out) || misaligned(workspace))
         return GDN_ERR_ALIGN;
     const bool capture = cap > 0;
-    const int path = resolve_path(d, prepared, a != nullptr, capture, workspace ? ws_bytes : 0);
+    const bool has_ws = workspace != nullptr || scratch != nullptr;
+    const int path = resolve_path(d, prepared, a != nullptr, capture, has_ws ? ws_bytes : 0);
     if (path == GDN_PATH_CHUNK) {
         if (!chunk_eligible(d, prepared, a != nullptr, capture)) return GDN_ERR_UNSUPPORTED;
-        if (workspace == nullptr || ws_bytes < gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
+        if (!has_ws || ws_bytes < gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
             return GDN_ERR_WORKSPACE;
+        if (scratch != nullptr) {
+            const gdn_status ss = scratch(&workspace);
+            if (ss != GDN_OK) return ss;
+        }
     }
     gdn::ScanLaunch s;
     s.x = x;
@@ -356,6 +364,28 @@ gdn_status gdn_scan_varlen(const gdn_scan_desc* d, const void* qkv, const float*
     return scan_call(d, x, qk_prep, gb_prep, a, b, A_log, dt_bias, state_in, out, state_out, offsets, 0, nullptr,
                      nullptr, nullptr, workspace, ws_bytes, dev_status, path_used, stream);
 }
+
+}  // extern "C"
+
+namespace gdn {
+
+gdn_status scan_varlen_scratch(const gdn_scan_desc* d, const void* qkv, const float* qk_prep, const float* gb_prep,
+                               const void* a, const void* b, const float* A_log, const float* dt_bias,
+                               const float* state_in, void* out, float* state_out, const int32_t* offsets,
+                               ScratchFn scratch, size_t scratch_bytes, int32_t* dev_status, int32_t* path_used,
+                               hipStream_t stream) {
+    gdn_status st = check_scan_desc(d);
+    if (st != GDN_OK) return st;
+    if (d->N > 0 && qkv == nullptr) return GDN_ERR_NULL;
+    gdn::TokenStreams x;
+    if ((st = packed_streams(d, qkv, &x)) != GDN_OK) return st;
+    return scan_call(d, x, qk_prep, gb_prep, a, b, A_log, dt_bias, state_in, out, state_out, offsets, 0, nullptr,
+                     nullptr, nullptr, nullptr, scratch_bytes, dev_status, path_used, stream, scratch);
+}
+
+}  // namespace gdn
+
+extern "C" {
 
 gdn_status gdn_scan_varlen_strided(const gdn_scan_desc* d, const gdn_qkv_streams* streams, const float* qk_prep,
                                    const float* gb_prep, const void* a, const void* b, const float* A_log,

@@ -110,6 +110,15 @@ hipError_t launch_decode_step(const DecodeStepLaunch& a, hipStream_t stream);
 bool decode_step_supported(int K, int V, int G, int W, int D);
 bool chunked_shape_supported(int K, int V, int qkv_dtype);
 
+// Supplies the library's own device scratch for the current device (allocation-free entry points).
+typedef gdn_status (*ScratchFn)(void** ptr);
+// gdn_scan_varlen on a packed row with the workspace taken from `scratch` (scratch_bytes bytes).
+gdn_status scan_varlen_scratch(const gdn_scan_desc* d, const void* qkv, const float* qk_prep, const float* gb_prep,
+                               const void* a, const void* b, const float* A_log, const float* dt_bias,
+                               const float* state_in, void* out, float* state_out, const int32_t* offsets,
+                               ScratchFn scratch, size_t scratch_bytes, int32_t* dev_status, int32_t* path_used,
+                               hipStream_t stream);
+
 // Longest sequence the DECODE kernel carries column by column with staged token operands; AUTO
 // takes DECODE while the average sequence is no longer than this.
 constexpr int kDecodeShortTokens = 8;

@@ -13,6 +13,8 @@
  *                         sequence for speculative decoding
  *   gdn_prepare_qk_gates_strided, gdn_scan_varlen_strided   read q, k and v as separate token
  *                         streams with their own row strides
+ *   gdn_scan_varlen_noalloc   gdn_scan_varlen with the library's own device scratch, for callers
+ *                         that cannot allocate
  * plus gdn_scan_workspace_bytes, gdn_status_string and gdn_abi_version.
  *
  * Sources (docs.rs source pages): "onnxruntime-ep-mlx 0.31.1 src/ops/paged_ssm.rs" -- kernel strings
@@ -22,7 +24,8 @@
  *
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer owned by the caller; the library allocates nothing,
- *     keeps no state between calls and is re-entrant.  Descriptor pointers and path_used are host
+ *     keeps no state between calls and is re-entrant (gdn_scan_varlen_noalloc alone uses a device
+ *     array of the library's own, see there).  Descriptor pointers and path_used are host
  *     pointers.  Calls return as soon as the work is queued on `stream` (NULL = default stream).
  *   - Packed tokens: offsets[B+1] (int32, device) delimit sequence b as tokens
  *     [offsets[b], offsets[b+1]).  Offsets are valid iff offsets[0] == 0, offsets[B] == N and they
@@ -308,6 +311,29 @@ gdn_status gdn_decode_step(const gdn_conv_desc *conv, const gdn_scan_desc *scan,
                            const void *conv_bias, const void *conv_state_in, void *conv_state_out, const void *a,
                            const void *b, const float *A_log, const float *dt_bias, const float *state_in, void *out,
                            float *state_out, const int32_t *offsets, int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * gdn_scan_varlen_noalloc -- gdn_scan_varlen for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * paths, results (bit for bit) and errors as gdn_scan_varlen on a packed row, without the workspace
+ * arguments: the chunked path's workspace is the library's own device array of
+ * GDN_NOALLOC_SCRATCH_BYTES, placed once per device by the HIP runtime and kept until the process
+ * ends.  The call allocates nothing.
+ *   - AUTO takes the chunked path only when its workspace fits the array; an explicit
+ *     GDN_PATH_CHUNK whose workspace (gdn_scan_workspace_bytes) exceeds it returns
+ *     GDN_ERR_WORKSPACE.
+ *   - The array of the CURRENT device is used (hipGetDevice), so `stream` must belong to it.  Its
+ *     address is looked up on the first call on each device (GDN_ERR_HIP if that fails).
+ *   - Every call on one device shares that device's array: calls that overlap in time on one device
+ *     (other streams, other host threads) race and must be serialised by the caller.  The array
+ *     keeps the last call's contents; nothing in it needs to start at zero.
+ * ---------------------------------------------------------------------------------------------- */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+gdn_status gdn_scan_varlen_noalloc(const gdn_scan_desc *desc, const void *qkv, const float *qk_prep,
+                                   const float *gb_prep, const void *a, const void *b, const float *A_log,
+                                   const float *dt_bias, const float *state_in, void *out, float *state_out,
+                                   const int32_t *offsets, int32_t *dev_status, int32_t *path_used, hipStream_t stream);
 
 /* Workspace bytes gdn_scan_varlen needs for `desc` (with its path resolved as AUTO would);
  * 0 when the resolved path needs none.  Returns the same argument errors as gdn_scan_varlen. */

@@ -298,3 +298,27 @@ def test_prepare_strided_host_validation(abi):
                                           None) == abi.ERR_NULL
     assert L.gdn_prepare_qk_gates_strided(ctypes.byref(d), ctypes.byref(good), None, None, None, None, P + 4, P,
                                           None) == abi.ERR_ALIGN
+
+
+@pytest.mark.parametrize(
+    "fields,kw,want",
+    [
+        (dict(B=0), {}, "ERR_SHAPE"),
+        (dict(K=48), {}, "ERR_UNSUPPORTED"),
+        (dict(path=3), {}, "ERR_UNSUPPORTED"),  # chunked path not eligible (fp32 I/O)
+        ({}, dict(qkv=None), "ERR_NULL"),
+        ({}, dict(off=None), "ERR_NULL"),
+        ({}, dict(out=P + 2), "ERR_ALIGN"),
+        # a chunked call whose workspace exceeds the library's device array
+        (dict(B=1, N=1 << 16, HQ=32, H=32, K=128, V=128, qkv_dtype=1, gate_dtype=1, path=3), dict(a=P, alog=P, dtb=P),
+         "ERR_WORKSPACE"),
+    ],
+)
+def test_scan_noalloc_host_validation(abi, fields, kw, want):
+    """gdn_scan_varlen_noalloc rejects these before it touches the device (no HIP call here)."""
+    d = scan_desc(abi, **fields)
+    a = dict(qkv=P, out=P, off=P, a=None, alog=None, dtb=None)
+    a.update(kw)
+    st = abi.lib().gdn_scan_varlen_noalloc(ctypes.byref(d), a["qkv"], None, None, a["a"], None, a["alog"], a["dtb"],
+                                           None, a["out"], None, a["off"], None, None, None)
+    assert st == getattr(abi, want)
