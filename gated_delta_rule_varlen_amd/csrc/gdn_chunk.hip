@@ -7,33 +7,41 @@
 // For one chunk of C = 64 tokens of one sequence and head, with G_i the cumulative log-decay inside
 // the chunk and S0 the state entering it:
 //     A_ij = b_i e^{G_i - G_j} (k_i . k_j)  (j < i),   T = (I + A)^{-1}   (unit lower triangular)
-//     W  = T diag(b e^G) K,      U' = T diag(b) V,      U = U' - W S0^T   (U row i = delta_i)
-//     O  = scale [ diag(e^G) Q S0^T + (M o Q K^T) U ],  M_ij = e^{G_i - G_j} (j <= i), else 0
-//     S_C = e^{G_C} S0 + U^T diag(e^{G_C - G}) K.
+//     R    = diag(b) V - diag(b e^G) K S0^T,          U = T R             (U row i = delta_i)
+//     O    = scale [ diag(e^G) Q S0^T + P U ],        P_ij = e^{G_i - G_j} (q_i . k_j) (j <= i)
+//     S_C^T = e^{G_C} S0^T + K^T diag(e^{G_C - G}) U.
 // Only decays that are finite and positive are allowed (log-decays are summed), which the softplus
 // gate guarantees.  Chunks never cross sequence boundaries.
 //
-// Kernels (all on the caller's stream; bf16 MFMA operands, fp32 accumulation, fp32 state):
-//   index  one block: checks the offsets (nothing is written anywhere when they are malformed),
-//          builds the table of each sequence's first chunk and an order of the sequences by
-//          decreasing chunk count.
-//   prep   one block per (chunk, head), parallel: gates, G, the normalised q and k, A and the masked
-//          Q K^T by MFMA, T by blocked inversion (16x16 diagonal blocks by substitution, off-diagonal
-//          blocks by fp32 MFMA), W^T = X^T T^T and U' = T Y by MFMA.  Writes W, P = M o (Qhat Khat^T),
-//          U' and G per (chunk, value head), and Qhat and Khat^T once per (chunk, key head): they do
-//          not depend on the decay, so the G value heads of a key head share them.
-//   state  one block per (sequence, head, column tile), sequential over the sequence's chunks:
-//          U = U' - W S^T, S <- e^{G_C} S + (diag(e^{G_C - G}) U)^T Khat, with the fp32 state in
-//          MFMA accumulators; the output of the previous chunk from the same LDS copies of S and U
-//          on separate waves.
-//
-// Every MFMA operand the state kernel reads from the workspace is stored in fragment order: the
-// 16 x 32 bf16 block one instruction consumes is 64 consecutive 16-byte pieces, lane l's piece at
-// 16 l (operand lane layout of v_mfma_f32_16x16x32_bf16: lane l holds row l%16, inner elements
-// 8*(l/16)..+7; accumulator lane l holds rows 4*(l/16)..+3 of column l%16).  A wave then loads a
-// fragment as one contiguous 1 KB access: a row-major fragment touches sixteen 128-byte lines per
-// instruction, and on gfx950 that pattern moves about a third of the bytes per clock per compute unit
-// that a contiguous one does.
+// Kernels, in stream order:
+//   index    one block: checks the offsets (nothing is written anywhere when they are malformed)
+//            and builds the tables (chunks per sequence, sequences longest first, segments).
+//   tmat     one block per (chunk, head), fully parallel: the gates and G, A by MFMA and
+//            T = (I + A)^{-1} by blocked inversion, stored as the six 16 x 32 bf16 operand
+//            fragments the chain reads (6 KB), plus G and b (512 B).  This is the only per-chunk
+//            data that goes through memory.
+//   summary  (long sequences only, below)
+//   combine  (long sequences only, below)
+//   main     one block of four waves per (sequence or segment, head), serial over its chunks.
+//            Wave w owns value columns [w V/4, (w+1) V/4) and keeps their fp32 state S0^T in MFMA
+//            accumulators.  An accumulator holds 4 consecutive rows of one column per lane; read as
+//            the B operand of the next product it supplies inner elements in the order
+//            {4g..4g+3, 16+4g..16+4g+3} (g = lane/16) of each 32-block, so A operands are read in
+//            that same order ("split" fragments) and K S0^T, Q S0^T, T R, P U and K^T U chain
+//            from accumulator to operand in registers, with no barrier.  P is formed by each wave
+//            directly in that operand order.  The normalised q and k rows (k also transposed) and
+//            the transposed v of the next chunk go to a second LDS buffer while the current one is
+//            read, so a chunk costs one barrier; the next chunk's rows and T fragments are in
+//            flight meanwhile.
+// Long sequences with few heads leave most compute units idle, so they are cut into segments of
+// seglen chunks that run in parallel.  A segment's effect on the state is affine,
+// S_end^T = Phi S_start^T + N^T, and its (Phi, N) come from the same chain run from S = 0 on the
+// value columns (N) and from S = I on K extra columns with v = 0 (Phi):
+//   summary  one block per (non-last segment, head): Phi and N into the workspace;
+//   combine  one block per (sequence, head, 16 value rows): S_start of every segment, in order,
+//            in fp32;
+//   main     then runs every segment from its S_start.
+#include <climits>
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -43,86 +51,149 @@ namespace gdn {
 namespace {
 
 constexpr int CH = 64;  // tokens per chunk
-// LDS rows holding MFMA fragments are padded by 16 bytes: a fragment read has the 16 lanes of a
-// group on 16 consecutive rows, and unpadded 128- or 256-byte rows would put them all on the same
-// four banks (a 16-way conflict); the pad shifts each row by four banks.
-constexpr int PAD = 8;  // bf16 elements
+constexpr int NW = 4;   // waves per block
+// LDS rows holding MFMA operands are padded by 16 bytes so that the 16 rows a fragment read touches
+// do not all start on the same banks.
+constexpr int PAD = 8;  // 16-bit elements
+constexpr int NTF = 6;  // T fragments per chunk: (token tile, 32-block) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-// Scheduling hint for the current region: NR LDS reads first, then NM matrix products.  Issuing all
-// reads of a phase up front lets their latencies overlap instead of stalling before every product.
-template <int NR, int NM>
-__device__ __forceinline__ void order_reads_then_mfma() {
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-}
 __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-// 16 rows x 32 inner elements starting at `base` (row stride ld elements): this lane's fragment.
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ uint32_t bf(float x) { return f32_to_bf16_bits(x); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// two values rounded to bf16 (nearest even) in one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t bf2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+// two values rounded to the I/O type (nearest even)
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    if constexpr (std::is_same<T, BF16>::value) return bf2(lo, hi);
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+// eight 16-bit inputs of the I/O type as bf16 MFMA operand bits (bf16 inputs are used as they are)
+template <typename T>
+__device__ __forceinline__ u32x4 to_bf16x8(u32x4 raw) {
+    if constexpr (std::is_same<T, BF16>::value) {
+        return raw;
+    } else {
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // (the element goes through a scalar: a bit cast of the subscript itself was compiled to
+            // read element 0)
+            const uint32_t x = raw[e];
+            const f16x2 hv = __builtin_bit_cast(f16x2, x);
+            o[e] = bf2((float)hv[0], (float)hv[1]);
+        }
+        return o;
+    }
+}
+// sum of squares of eight 16-bit inputs, fp32 (plain FMAs; v_dot2 would need a bit cast of each
+// vector element, which was compiled to read element 0 every time)
+template <typename T>
+__device__ __forceinline__ float sumsq8(u32x4 raw) {
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float lo = to_f32<T>((uint16_t)(raw[e] & 0xffffu)), hi = to_f32<T>((uint16_t)(raw[e] >> 16));
+        s = fmaf(lo, lo, s);
+        s = fmaf(hi, hi, s);
+    }
+    return s;
+}
+// e^x through the hardware 2^x (about 1 ulp): for decay factors that are rounded to bf16 or scale
+// a whole chunk
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ int tf_tile(int f) { return f < 2 ? f : 2 + (f - 2) / 2; }  // token tile of T fragment f
+__device__ __forceinline__ int tf_blk(int f) { return f < 2 ? 0 : (f - 2) % 2; }    // its 32-block
+
+// Operand lane layout of v_mfma_f32_16x16x32_bf16: lane l holds row l%16 and inner elements
+// 8(l/16)..+7; the accumulator lane l holds rows 4(l/16)..+3 of column l%16.
+// Plain fragment: 16 rows x 32 inner elements from `base` (row stride ld).
 __device__ __forceinline__ bf16x8 frag(const uint16_t* base, int ld, int lane) {
     return *reinterpret_cast<const bf16x8*>(base + (lane & 15) * ld + 8 * (lane >> 4));
 }
-__device__ __forceinline__ uint16_t bf(float x) { return f32_to_bf16_bits(x); }
-__device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
-    return u32x2{(uint32_t)bf(a) | ((uint32_t)bf(b) << 16), (uint32_t)bf(c) | ((uint32_t)bf(d) << 16)};
+// Accumulator tiles for rows 0..15 (lo) and 16..31 (hi) of a 32-row block, as one operand whose
+// inner order is the split order.
+__device__ __forceinline__ bf16x8 pack_acc(f32x4 lo, f32x4 hi) {
+    return __builtin_bit_cast(bf16x8, u32x4{bf2(lo[0], lo[1]), bf2(lo[2], lo[3]), bf2(hi[0], hi[1]), bf2(hi[2], hi[3])});
 }
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// Fragment tiles.  An A tile is one 16 x 32 bf16 operand block in lane order (lane l: row l%16,
-// inner elements 8(l/16)..+7; 512 elements).  A D tile is one 16 x 16 block in accumulator order
-// (lane l: rows 4(l/16)..+3 of column l%16; 256 elements).
-constexpr int AT = 512;
-constexpr int DT = 256;
-
-// Workspace layout (byte offsets), identical on host and device.  Per (chunk, value head) "chh",
-// or per (chunk, key head) "chk" where marked:
+__device__ __forceinline__ u32x4 pack8(const float* x, float s) {
+    return u32x4{bf2(x[0] * s, x[1] * s), bf2(x[2] * s, x[3] * s), bf2(x[4] * s, x[5] * s), bf2(x[6] * s, x[7] * s)};
+}
+template <typename T>
+__device__ __forceinline__ void unpack8(u32x4 raw, float (&v)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = to_f32<T>((uint16_t)(raw[e] & 0xffffu));
+        v[2 * e + 1] = to_f32<T>((uint16_t)(raw[e] >> 16));
+    }
+}
+__device__ __forceinline__ uint16_t half_of(u32x4 w, int e) {
+    return (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+}
+// ---- workspace ----------------------------------------------------------------------------------
+// int32 header: [0] status, [1] main units, [2] summary units, [3] chunks, then the tables at +16:
+//   order[B]     sequences by decreasing chunk count (rank -> sequence)
+//   ustart[B+1]  first main unit of each rank (nseg * H units per sequence)
+//   sstart[B+1]  first summary unit of each sequence ((nseg - 1) * H units when nseg > 1)
+//   slot0[B+1]   first slot of each sequence (nseg slots when nseg > 1, else none)
+//   nchunk[B]    chunks of each sequence
+//   cstart[B+1]  first chunk of each sequence
+// Per (chunk, head): the T fragments (6 x 512 bf16, lane order) and G, b, 1/|k| (3 x 64 f32).
+// Slots: per (slot, head) Phi [K][K] then N [V][K], fp32 (a row per column, K contiguous).  Slot
+// s < nseg-1 of a sequence holds the summary of segment s, and after the combine kernel its N holds
+// S_start(s+1); the N of slot nseg-1 holds S_start(0).
 struct WsLayout {
-    size_t hdr;      // int32: [0] status, [1] total chunks; cstart[B+1] at +64, then order[B]
-    size_t w;        // W      (CH x K, rows = tokens):      A tiles [4][K/32]
-    size_t kt;       // Khat^T (K x CH, rows = keys):        A tiles [K/16][2]        (chk)
-    size_t qf;       // Qhat   (CH x K, rows = tokens):      A tiles [4][K/32]        (chk)
-    size_t pm;       // P      (CH x CH, rows = tokens i):   A tiles [4][2], P = M o (Qhat Khat^T)
-    size_t upt;      // U'     (CH x V):                     D tiles [4][V/16]
-    size_t gam;      // G      [CH] f32
-    size_t total;
+    size_t hdr, tfr, gates, slots, total;
+    size_t nslots;  // slots available
+    int seglen;     // chunks per segment; INT_MAX = one segment per sequence
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-__host__ __device__ inline WsLayout ws_layout(int B, int N, int HQ, int H, int K, int V) {
+
+// Segments are used when fewer than a quarter of the compute units would hold a (sequence, head)
+// unit; then each sequence is cut into about 256 / (B H) segments of at least 16 chunks.
+constexpr int kChipUnits = 256;
+inline long long chunk_bound(int B, int N) { return ((long long)N + CH - 1) / CH + B; }
+inline int segment_length(int B, int N, int H) {
+    const long long units = (long long)B * H;
+    const long long per = kChipUnits / units;
+    if (per < 4) return INT_MAX;
+    const long long nch = chunk_bound(B, N);
+    const long long avg = (nch + B - 1) / B;
+    long long sl = (avg + per - 1) / per;
+    if (sl < 16) sl = 16;
+    return (int)sl;
+}
+inline WsLayout ws_layout(int B, int N, int H, int K, int V) {
     WsLayout L;
-    const size_t nch = ((size_t)N + CH - 1) / CH + (size_t)B;  // upper bound on chunks over all sequences
-    const size_t nh = nch * (size_t)H, nk = nch * (size_t)HQ;
+    L.seglen = segment_length(B, N, H);
+    const long long nch = chunk_bound(B, N);
+    L.nslots = 0;
+    if (L.seglen != INT_MAX) {
+        const long long multi = nch / (L.seglen + 1);  // sequences with more than one segment
+        L.nslots = (size_t)(nch / L.seglen + 1 + (multi < B ? multi : B));
+    }
     size_t o = 0;
     L.hdr = o;
-    o = align256(o + 64 + 4 * (2 * (size_t)B + 1));
-    L.w = o;
-    o = align256(o + nh * CH * K * 2);
-    L.kt = o;
-    o = align256(o + nk * K * CH * 2);
-    L.qf = o;
-    o = align256(o + nk * CH * K * 2);
-    L.pm = o;
-    o = align256(o + nh * CH * CH * 2);
-    L.upt = o;
-    o = align256(o + nh * CH * V * 2);
-    L.gam = o;
-    o = align256(o + nh * CH * 4);
+    o = align256(o + 4 * (16 + 6 * (size_t)B + 4));
+    L.tfr = o;
+    o = align256(o + (size_t)nch * H * NTF * 512 * 2);
+    L.gates = o;
+    o = align256(o + (size_t)nch * H * 3 * CH * 4);
+    L.slots = o;
+    o = align256(o + L.nslots * (size_t)H * ((size_t)K * K + (size_t)V * K) * 4);
     L.total = o;
     return L;
-}
-
-// Half of an A tile's lane piece from an accumulator: an accumulator lane holding rows 4(l/16)..+3
-// of column l%16 of the 16 x 16 block at inner offset 16*half of a 32-wide A tile writes elements
-// [4(l/16) + 16 half, +4) of row l%16, which is lane piece (l%16) + 16*(2 half + (l/16)/2) at
-// element 4*((l/16)%2).  Returns the element offset inside the tile.
-__device__ __forceinline__ int a_tile_half_offset(int lane, int half) {
-    const int g = lane >> 4;
-    return ((lane & 15) + 16 * (2 * half + (g >> 1))) * 8 + 4 * (g & 1);
 }
 
 struct ChunkArgs {
@@ -143,50 +214,81 @@ struct ChunkArgs {
     uint32_t flags;
     float scale;
     int n_blocks;
+    int cap;
+    const int32_t* counts;
+    const int32_t* active;
+    float* capsule;
 };
 
-// ---- index: offsets check and the first-chunk table --------------------------------------------
-__global__ __launch_bounds__(1024) void chunk_index_kernel(ChunkArgs p) {
-    const bool malformed = offsets_malformed(p.offsets, p.B, p.N);
-    report_status(p.dev_status, malformed);
-    int32_t* hdr = reinterpret_cast<int32_t*>(p.ws + p.L.hdr);
-    int32_t* cstart = hdr + 16;
-    if (malformed) {
-        if (threadIdx.x == 0) hdr[0] = GDN_ERR_OFFSETS;
-        return;
+struct Tables {
+    int32_t *order, *ustart, *sstart, *slot0, *nchunk, *cstart;
+};
+__device__ __forceinline__ Tables tables(char* ws, int B) {
+    int32_t* t = reinterpret_cast<int32_t*>(ws) + 16;
+    return Tables{t, t + B, t + 2 * B + 1, t + 3 * B + 2, t + 4 * B + 3, t + 5 * B + 3};
+}
+__device__ __forceinline__ int nseg_of(int nch, int seglen) {
+    return (seglen == INT_MAX || nch <= seglen) ? 1 : (nch + seglen - 1) / seglen;
+}
+// last index r in [0, n) with start[r] <= u (start[0] = 0 <= u)
+__device__ __forceinline__ int find_start(const int32_t* start, int n, int u) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (start[mid] <= u) lo = mid;
+        else hi = mid - 1;
     }
-    __shared__ int warp_tot[16];
-    __shared__ int carry;
-    if (threadIdx.x == 0) carry = 0;
-    __syncthreads();
+    return lo;
+}
+
+// Exclusive scan over i < n of val(i) into out[i] (out[n] = total), by one block of 1024 threads.
+template <typename F>
+__device__ void block_scan(int n, F val, int32_t* out, int* s_tot, int* s_carry) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    for (int base = 0; base < p.B; base += 1024) {
+    if (threadIdx.x == 0) *s_carry = 0;
+    __syncthreads();
+    for (int base = 0; base < n; base += 1024) {
         const int i = base + (int)threadIdx.x;
-        const int cnt = i < p.B ? (p.offsets[i + 1] - p.offsets[i] + CH - 1) / CH : 0;
-        int incl = cnt;  // inclusive scan inside the wave
+        const int v = i < n ? val(i) : 0;
+        int incl = v;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const int y = __shfl_up(incl, d);
             if (lane >= d) incl += y;
         }
-        if (lane == 63) warp_tot[wv] = incl;
+        if (lane == 63) s_tot[wv] = incl;
         __syncthreads();
-        int before = carry;
-        for (int k = 0; k < wv; ++k) before += warp_tot[k];
-        if (i < p.B) cstart[i] = before + incl - cnt;
+        int before = *s_carry;
+        for (int k = 0; k < wv; ++k) before += s_tot[k];
+        if (i < n) out[i] = before + incl - v;
         __syncthreads();
-        if (threadIdx.x == 1023) carry = before + incl;
+        if (threadIdx.x == 1023) *s_carry = before + incl;
         __syncthreads();
     }
-    // The state kernel's blocks are long-lived and can outnumber the blocks resident at once, so
-    // they take the sequences longest first (list scheduling: the critical path is then close to the
-    // longest sequence rather than a late start plus it).  Up to 1024 sequences are ranked here;
-    // beyond that the order is the identity.
-    int32_t* order = cstart + p.B + 1;
+    if (threadIdx.x == 0) out[n] = *s_carry;
+    __syncthreads();
+}
+
+// ---- index --------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void chunk_index_kernel(ChunkArgs p) {
+    const bool malformed = offsets_malformed(p.offsets, p.B, p.N);
+    report_status(p.dev_status, malformed);
+    int32_t* hdr = reinterpret_cast<int32_t*>(p.ws);
+    if (malformed) {
+        if (threadIdx.x == 0) hdr[0] = GDN_ERR_OFFSETS;
+        return;
+    }
+    __shared__ int s_tot[16], s_carry;
     __shared__ int s_cnt[1024];
+    const Tables tb = tables(p.ws, p.B);
+    const int sl = p.L.seglen;
+    for (int i = threadIdx.x; i < p.B; i += blockDim.x)
+        tb.nchunk[i] = (p.offsets[i + 1] - p.offsets[i] + CH - 1) / CH;
+    __syncthreads();
+    // sequences longest first (list scheduling of the long-lived main blocks); up to 1024 ranked
     if (p.B <= 1024) {
         const int i = threadIdx.x;
-        if (i < p.B) s_cnt[i] = (p.offsets[i + 1] - p.offsets[i] + CH - 1) / CH;
+        if (i < p.B) s_cnt[i] = tb.nchunk[i];
         __syncthreads();
         if (i < p.B) {
             const int ci = s_cnt[i];
@@ -195,162 +297,74 @@ __global__ __launch_bounds__(1024) void chunk_index_kernel(ChunkArgs p) {
                 const int cj = s_cnt[j];
                 rank += (cj > ci) || (cj == ci && j < i);
             }
-            order[rank] = i;
+            tb.order[rank] = i;
         }
     } else {
-        for (int i = threadIdx.x; i < p.B; i += blockDim.x) order[i] = i;
+        for (int i = threadIdx.x; i < p.B; i += blockDim.x) tb.order[i] = i;
     }
+    __syncthreads();
+    const int H = p.H;
+    const int32_t* nchunk = tb.nchunk;
+    const int32_t* order = tb.order;
+    block_scan(p.B, [&](int r) { return nseg_of(nchunk[order[r]], sl) * H; }, tb.ustart, s_tot, &s_carry);
+    block_scan(p.B, [&](int i) { const int s = nseg_of(nchunk[i], sl); return s > 1 ? (s - 1) * H : 0; }, tb.sstart,
+               s_tot, &s_carry);
+    block_scan(p.B, [&](int i) { const int s = nseg_of(nchunk[i], sl); return s > 1 ? s : 0; }, tb.slot0, s_tot,
+               &s_carry);
+    block_scan(p.B, [&](int i) { return nchunk[i]; }, tb.cstart, s_tot, &s_carry);
     if (threadIdx.x == 0) {
-        cstart[p.B] = carry;
-        hdr[1] = carry;
+        hdr[1] = tb.ustart[p.B];
+        hdr[2] = tb.sstart[p.B];
+        hdr[3] = tb.cstart[p.B];
         hdr[0] = GDN_OK;
     }
 }
 
-// Sequence owning global chunk `cid` (the last b with cstart[b] <= cid); cid < total.
-__device__ __forceinline__ int chunk_owner(const int32_t* cstart, int B, int cid) {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cstart[mid] <= cid) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
-template <typename T>
-__device__ __forceinline__ void load8(const typename T::storage* p, float (&v)[8]) {
-    if constexpr (std::is_same<T, F32>::value) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[e] = a[e];
-            v[4 + e] = b[e];
-        }
-    } else {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[2 * e] = to_f32<T>((uint16_t)(raw[e] & 0xffffu));
-            v[2 * e + 1] = to_f32<T>((uint16_t)(raw[e] >> 16));
-        }
-    }
-}
-
-// Eight 16-bit values packed in 16 bytes -> fp32.
-template <typename T>
-__device__ __forceinline__ void unpack8(u32x4 raw, float (&v)[8]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[2 * e] = to_f32<T>((uint16_t)(raw[e] & 0xffffu));
-        v[2 * e + 1] = to_f32<T>((uint16_t)(raw[e] >> 16));
-    }
-}
-
-__device__ __forceinline__ u32x4 pack8(const float* x, float s) {
-    return u32x4{(uint32_t)bf(x[0] * s) | ((uint32_t)bf(x[1] * s) << 16), (uint32_t)bf(x[2] * s) | ((uint32_t)bf(x[3] * s) << 16),
-                 (uint32_t)bf(x[4] * s) | ((uint32_t)bf(x[5] * s) << 16), (uint32_t)bf(x[6] * s) | ((uint32_t)bf(x[7] * s) << 16)};
-}
-
-// ---- prep ----------------------------------------------------------------------------------------
-// k and v token rows are read whole: LPT = K/8 lanes per row, 8 elements (16 bytes) each, so one
-// wave instruction covers 64/LPT complete rows.  Column operands (8 consecutive tokens of one key or
-// value index) are gathered from the row-major LDS copies with 2-byte reads.  A wave needs only its
-// own 16 rows of Qhat, as MFMA fragments: they are loaded in fragment order and stay in registers.
-// LDS is shared by lifetime (39 KB at K = 128, so four blocks fit on a compute unit):
-//   region 0: Khat rows, until A and P are formed; then T (fp32)
-//   region 2: Y rows, until their fragments are in registers; then A (fp32); then T (bf16)
-//   the off-diagonal inversion scratch has its own 4 KB
-template <typename T, int K, int V>
-__global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
+// ---- tmat: gates, G and the T fragments of every (chunk, head) -----------------------------------
+// k rows are read whole (K/8 lanes per row, 16 bytes each); wave w normalises token rows
+// 16w..16w+15.  A is formed in 16 x 16 blocks by MFMA (wave w: column tile w).  T: the diagonal
+// blocks by substitution (wave w, block w), then wave w walks down its block column,
+// T_iw = -T_ii sum_{w <= m < i} A_im T_mw, which needs only its own earlier blocks and the diagonal
+// ones (one barrier).
+template <typename T, int K>
+__global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     using TS = typename T::storage;
-    static_assert(K == V && (K == 64 || K == 128), "chunk tile shapes");
-    constexpr int LPT = K / 8;     // lanes per token row
-    constexpr int TPI = 64 / LPT;  // token rows per wave instruction
-    constexpr int NI = 16 / TPI;   // instructions per wave for its 16 rows
-    constexpr int KT4 = K / 64;    // 16-wide key (value) tiles per wave
+    constexpr int LPT = K / 8, TPI = 64 / LPT, NI = 16 / TPI;
     __shared__ __align__(16) union {
-        uint16_t kn[CH][K + PAD];  // Khat rows
+        uint16_t kn[CH][K + PAD];  // normalised k rows, until A is formed
         float tm[CH][CH + 4];      // T (fp32)
     } r0;
-    __shared__ float scr[4][16][17];  // off-diagonal inversion scratch
-    __shared__ __align__(16) union {
-        uint16_t vn[CH][V + PAD];  // Y = diag(b) V rows
-        float am[CH][CH + 4];      // A (fp32)
-        uint16_t tb[CH][CH + PAD];  // T (bf16)
-    } r2;
-    __shared__ __align__(16) float s_gam[CH], s_beta[CH], s_xs[CH];
-    auto& kn = r0.kn;
-    auto& tm = r0.tm;
-    auto& vn = r2.vn;
-    auto& am = r2.am;
-    auto& tb = r2.tb;
+    __shared__ __align__(16) float am[CH][CH + 4];
+    __shared__ float scr[NW][16][17];
+    __shared__ __align__(16) float s_gam[CH], s_beta[CH], s_rk[CH];
 
-    const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws + p.L.hdr);
+    const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws);
     if (hdr[0] != GDN_OK) return;
-    const int total = hdr[1];
+    const Tables tab = tables(p.ws, p.B);
     const int blk = xcd_remap((int)blockIdx.x, p.n_blocks, p.G);
-    // Chunks are taken last first: the operands written last are the likeliest still to sit in the
-    // 256 MB memory-side cache when the state kernel starts, and it starts from the first chunks
-    // (one long sequence: 1477 -> 1429 us for the whole call).
-    const int cid = p.n_blocks / p.H - 1 - blk / p.H, h = blk % p.H;
-    if (cid >= total) return;
-    const int32_t* cstart = hdr + 16;
-    const int b = chunk_owner(cstart, p.B, cid);
-    const int t0 = p.offsets[b] + (cid - cstart[b]) * CH;
+    const int cid = blk / p.H, h = blk % p.H, kh = h / p.G;
+    if (cid >= hdr[3]) return;
+    const int b = find_start(tab.cstart, p.B, cid);
+    const int local = cid - tab.cstart[b];
+    const int t0 = p.offsets[b] + local * CH;
     const int n = min(CH, p.offsets[b + 1] - t0);
-    const int kh = h / p.G;
-    const size_t chh = (size_t)cid * p.H + h;
-    const size_t chk = (size_t)cid * p.HQ + kh;
-    // Qhat and Khat^T are the same for every value head of the key head: the first one writes them
-    const bool shared_writer = (h % p.G) == 0;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
     const int pc = lane % LPT, tsub = lane / LPT;
-    const TS* const xq = static_cast<const TS*>(p.x.q);
     const TS* const xk = static_cast<const TS*>(p.x.k);
-    const TS* const xv = static_cast<const TS*>(p.x.v);
-    uint16_t* const wsb = reinterpret_cast<uint16_t*>(p.ws);
-    uint16_t* const w_out = wsb + p.L.w / 2 + chh * CH * K;
-    uint16_t* const kt_out = wsb + p.L.kt / 2 + chk * K * CH;
-    uint16_t* const q_out = wsb + p.L.qf / 2 + chk * CH * K;
-    uint16_t* const p_out = wsb + p.L.pm / 2 + chh * CH * CH;
-    uint16_t* const u_out = wsb + p.L.upt / 2 + chh * CH * V;
 
-    // this wave's 16 token rows (row 16 wv + TPI u + tsub), elements 8 pc .. 8 pc + 7, kept packed
-    // (16-bit inputs) until the gates are known
-    u32x4 kr[NI], vr[NI];
+    u32x4 kr[NI];
 #pragma unroll
-    for (int u = 0; u < NI; ++u) {
-        const int ti = 16 * wv + TPI * u + tsub;
-        if (ti < n) {
-            const size_t t = (size_t)(t0 + ti);
-            kr[u] = *reinterpret_cast<const u32x4*>(xk + t * p.x.sk + (size_t)kh * K + 8 * pc);
-            vr[u] = *reinterpret_cast<const u32x4*>(xv + t * p.x.sv + (size_t)h * V + 8 * pc);
-        } else {
-            kr[u] = vr[u] = u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int i = 0; i < NI; ++i) {
+        const int ti = 16 * w + TPI * i + tsub;
+        kr[i] = ti < n ? *reinterpret_cast<const u32x4*>(xk + (size_t)(t0 + ti) * p.x.sk + (size_t)kh * K + 8 * pc)
+                       : u32x4{0u, 0u, 0u, 0u};
     }
-    // this wave's q rows in MFMA operand order: lane l holds row 16 wv + l%16, elements
-    // 32 kk + 8(l/16) .. +7 of fragment kk
-    u32x4 qr[K / 32];
-    {
-        const int ti = 16 * wv + (lane & 15);
-#pragma unroll
-        for (int kk = 0; kk < K / 32; ++kk)
-            qr[kk] = ti < n ? *reinterpret_cast<const u32x4*>(xq + (size_t)(t0 + ti) * p.x.sq + (size_t)kh * K + 32 * kk +
-                                                              8 * (lane >> 4))
-                            : u32x4{0u, 0u, 0u, 0u};
-    }
-
-    // gates and the cumulative log-decay (wave 0, one token per lane); padding tokens have b = 0
-    // and no decay
-    if (wv == 0) {
+    const size_t ch = (size_t)cid * p.H + h;
+    if (w == 0) {  // gates and the cumulative log-decay; padding tokens: no decay, no update
         float ell = 0.0f, beta = 0.0f;
         if (lane < n) {
             const size_t gi = (size_t)(t0 + lane) * p.H + h;
-            const float x = load_any(p.a, p.gate_dtype, gi);
-            ell = -expf(p.A_log[h]) * softplus_f(x + p.dt_bias[h]);
+            ell = -expf(p.A_log[h]) * softplus_f(load_any(p.a, p.gate_dtype, gi) + p.dt_bias[h]);
             beta = 1.0f;
             if (p.b) {
                 beta = load_any(p.b, p.gate_dtype, gi);
@@ -365,524 +379,646 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(ChunkArgs p) {
         }
         s_gam[lane] = gam;
         s_beta[lane] = beta;
-        s_xs[lane] = beta * expf(gam);
-        reinterpret_cast<float*>(p.ws + p.L.gam)[chh * CH + lane] = gam;
+        float* const gout = reinterpret_cast<float*>(p.ws + p.L.gates) + ch * 3 * CH;
+        gout[lane] = gam;
+        gout[CH + lane] = beta;
     }
-    __syncthreads();  // gates ready
-
-    // normalised k rows and Y = diag(b) V rows -> LDS
+    // raw k rows (bf16 operands); the norms 1/|k| scale A's entries instead
+    float* const rkout = reinterpret_cast<float*>(p.ws + p.L.gates) + ch * 3 * CH + 2 * CH;
 #pragma unroll
-    for (int u = 0; u < NI; ++u) {
-        const int ti = 16 * wv + TPI * u + tsub;
-        float kf[8], vf[8];
-        unpack8<T>(kr[u], kf);
-        unpack8<T>(vr[u], vf);
-        float sk = 0.0f;
-#pragma unroll
-        for (int z = 0; z < 8; ++z) sk = fmaf(kf[z], kf[z], sk);
-        sk = group_sum<LPT>(sk);
-        *reinterpret_cast<u32x4*>(&kn[ti][8 * pc]) = pack8(kf, rsqrtf(sk + 1e-12f));
-        *reinterpret_cast<u32x4*>(&vn[ti][8 * pc]) = pack8(vf, s_beta[ti]);
-    }
-    // normalised q fragments (the four lanes l%16 + 16 j hold one row between them)
-    bf16x8 qw[K / 32];
-    {
-        float qf[K / 32][8];
-        float sq = 0.0f;
-#pragma unroll
-        for (int kk = 0; kk < K / 32; ++kk) {
-            unpack8<T>(qr[kk], qf[kk]);
-#pragma unroll
-            for (int z = 0; z < 8; ++z) sq = fmaf(qf[kk][z], qf[kk][z], sq);
-        }
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
-        const float rq = rsqrtf(sq + 1e-12f);
-#pragma unroll
-        for (int kk = 0; kk < K / 32; ++kk) {
-            u32x4 pq = pack8(qf[kk], rq);
-            asm volatile("" : "+v"(pq));  // pack now (see the column fragments below)
-            qw[kk] = __builtin_bit_cast(bf16x8, pq);
+    for (int i = 0; i < NI; ++i) {
+        const int ti = 16 * w + TPI * i + tsub;
+        const float rk = rsqrtf(group_sum<LPT>(sumsq8<T>(kr[i])) + 1e-12f);
+        *reinterpret_cast<u32x4*>(&r0.kn[ti][8 * pc]) = to_bf16x8<T>(kr[i]);
+        if (pc == 0) {
+            s_rk[ti] = rk;
+            rkout[ti] = rk;
         }
     }
-    __syncthreads();  // kn, vn ready
-
-    // Qhat tiles (token tile wv)
-    if (shared_writer) {
-#pragma unroll
-        for (int kk = 0; kk < K / 32; ++kk)
-            *reinterpret_cast<bf16x8*>(q_out + (size_t)(wv * (K / 32) + kk) * AT + 8 * lane) = qw[kk];
-    }
-
-    // Column fragments of key tiles kt = wv + 4m: Khat^T (stored) and X^T = (diag(b e^G) Khat)^T (kept
-    // for W), and of value tiles vt = wv + 4m: Y (kept for U').  Lane l: index 16 kt + l%16, tokens
-    // 32 c + 8(l/16) + e.
-    bf16x8 xf[KT4][2], yf[KT4][2];
-#pragma unroll
-    for (int m = 0; m < KT4; ++m) {
-        const int kt = wv + 4 * m, col = 16 * kt + (lane & 15);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int tb0 = 32 * c + 8 * (lane >> 4);
-            float kx[8];
-            u32x4 kc, yp;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint16_t k0 = kn[tb0 + 2 * e][col], k1 = kn[tb0 + 2 * e + 1][col];
-                kx[2 * e] = s_xs[tb0 + 2 * e] * bf16_bits_to_f32(k0);
-                kx[2 * e + 1] = s_xs[tb0 + 2 * e + 1] * bf16_bits_to_f32(k1);
-                kc[e] = (uint32_t)k0 | ((uint32_t)k1 << 16);
-                yp[e] = (uint32_t)vn[tb0 + 2 * e][col] | ((uint32_t)vn[tb0 + 2 * e + 1][col] << 16);
-            }
-            if (shared_writer) *reinterpret_cast<u32x4*>(kt_out + (size_t)(kt * 2 + c) * AT + 8 * lane) = kc;
-            u32x4 xp = pack8(kx, 1.0f);
-            // Pack here: left to itself the compiler keeps the eight 16-bit values of a fragment in
-            // eight registers until the products far below, which spills.  The empty statements
-            // (no instructions) pin the packed values at this point.
-            asm volatile("" : "+v"(xp));
-            asm volatile("" : "+v"(yp));
-            xf[m][c] = __builtin_bit_cast(bf16x8, xp);
-            yf[m][c] = __builtin_bit_cast(bf16x8, yp);
-        }
-    }
-
-    __syncthreads();  // Y gathered: A may overwrite it
-
-    // A_ij = b_i e^{G_i - G_j} (khat_i . khat_j) for j < i, and P_ij = e^{G_i - G_j} (qhat_i . khat_j)
-    // for j <= i, in 16 x 16 blocks.  Wave wv forms the P blocks of its own row tile (it holds those
-    // Qhat rows; computed transposed: 4 consecutive j per lane) and the A blocks of column tile wv
-    // (rows it..3), so that every wave does 5 of the 20 nonzero blocks.  The masks are selects, not
-    // branches: the decay factor is evaluated for every entry with its exponent clamped at 0 (G never
-    // increases inside a chunk, so the clamp changes only entries the mask drops), and G and b are
-    // read as 4-vectors.  The tile loops stay rolled: the X and Y fragments are live across them,
-    // and unrolled they need more registers than four blocks per compute unit leave.
-    {
-        const int ip = 16 * wv + (lane & 15);  // row of this lane's P entries
+    __syncthreads();
+    {  // A, column tile w, rows it = w..3
+        const int ja = 16 * w + (lane & 15);
+        const float g_ja = s_gam[ja], r_ja = s_rk[ja];
 #pragma unroll 1
-        for (int jt = 0; jt < 4; ++jt) {
-            f32x4 pt = zero4();
-            if (jt <= wv) {
-#pragma unroll
-                for (int kk = 0; kk < K; kk += 32) pt = mma_bf16(frag(&kn[16 * jt][kk], K + PAD, lane), qw[kk / 32], pt);
-            }
-            const int j = 16 * jt + 4 * (lane >> 4);
-            const f32x4 g_j = *reinterpret_cast<const f32x4*>(&s_gam[j]);
-            const float g_ip = s_gam[ip];
-            float pv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float e = expf(fminf(g_ip - g_j[r], 0.0f));
-                pv[r] = (j + r <= ip) ? e * pt[r] : 0.0f;
-            }
-            // (token tiles 0 and 1 have no nonzero entry past key 31; that fragment is never read)
-            if (wv >= 2 || jt < 2)
-                *reinterpret_cast<u32x2*>(p_out + (size_t)(wv * 2 + (jt >> 1)) * AT + a_tile_half_offset(lane, jt & 1)) =
-                    pack4(pv[0], pv[1], pv[2], pv[3]);
-        }
-        const int ja = 16 * wv + (lane & 15);  // column of this lane's A entries
-        const float g_ja = s_gam[ja];
-#pragma unroll 1
-        for (int it = wv; it < 4; ++it) {
+        for (int it = w; it < 4; ++it) {
             f32x4 a = zero4();
 #pragma unroll
             for (int kk = 0; kk < K; kk += 32)
-                a = mma_bf16(frag(&kn[16 * it][kk], K + PAD, lane), frag(&kn[16 * wv][kk], K + PAD, lane), a);
-            const int ia = 16 * it + 4 * (lane >> 4);  // rows of this lane's A entries
+                a = mma_bf16(frag(&r0.kn[16 * it][kk], K + PAD, lane), frag(&r0.kn[16 * w][kk], K + PAD, lane), a);
+            const int ia = 16 * it + 4 * g;
             const f32x4 g_ia = *reinterpret_cast<const f32x4*>(&s_gam[ia]);
             const f32x4 b_ia = *reinterpret_cast<const f32x4*>(&s_beta[ia]);
+            const f32x4 r_ia = *reinterpret_cast<const f32x4*>(&s_rk[ia]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float e = expf(fminf(g_ia[r] - g_ja, 0.0f));
-                am[ia + r][ja] = (ja < ia + r) ? b_ia[r] * e * a[r] : 0.0f;
+                const float e = fexp(fminf(g_ia[r] - g_ja, 0.0f));
+                am[ia + r][ja] = (ja < ia + r) ? (b_ia[r] * r_ia[r] * r_ja) * e * a[r] : 0.0f;
             }
         }
     }
-    __syncthreads();  // A ready; Khat rows dead (T may be written)
-
-    // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution (wave w, lanes 0..15 own the
-    // columns of block w); T is zero above the diagonal.
-    // (thread t clears 16 consecutive entries of row t/4 with 16-byte stores)
-    static_assert(CH * CH == 256 * 16, "one 16-entry run per thread");
-#pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(&tm[tid >> 2][16 * (tid & 3) + 4 * q]) = zero4();
-    __syncthreads();
-    if (lane < 16) {
-        const int c = lane, o = 16 * wv;
+    __syncthreads();  // A ready; k rows dead: T may be written
+    auto& tm = r0.tm;
+    if (lane < 16) {  // diagonal block w by forward substitution, lane = column
+        const int cc = lane, o = 16 * w;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float v = (i == c) ? 1.0f : 0.0f;
+            float v = (i == cc) ? 1.0f : 0.0f;
 #pragma unroll
             for (int m = 0; m < i; ++m) v = fmaf(-am[o + i][o + m], x[m], v);
             x[i] = v;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tm[o + i][o + c] = x[i];
+        for (int i = 0; i < 16; ++i) tm[o + i][o + cc] = x[i];
     }
-    __syncthreads();
-    // Off-diagonal blocks, one block diagonal at a time: T_ij = -T_ii sum_{j<=m<i} A_im T_mj.
-    for (int d = 1; d < 4; ++d) {
-        const int bj = wv, bi = wv + d;
-        const bool act = bi < 4;
-        if (act) {
-            f32x4 y = zero4();
-            for (int m = bj; m < bi; ++m)
-#pragma unroll
-                for (int kk = 0; kk < 16; kk += 4)
-                    y = mma_f32(am[16 * bi + (lane & 15)][16 * m + kk + (lane >> 4)],
-                                tm[16 * m + kk + (lane >> 4)][16 * bj + (lane & 15)], y);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) scr[wv][4 * (lane >> 4) + r][lane & 15] = y[r];
-        }
-        __syncthreads();
-        if (act) {
-            f32x4 z = zero4();
+    __syncthreads();  // diagonal blocks ready
+    // block column w, top down; the wave's own writes are read back by other lanes of the wave
+    for (int i = w + 1; i < 4; ++i) {
+        f32x4 y = zero4();
+        for (int m = w; m < i; ++m)
 #pragma unroll
             for (int kk = 0; kk < 16; kk += 4)
-                z = mma_f32(tm[16 * bi + (lane & 15)][16 * bi + kk + (lane >> 4)], scr[wv][kk + (lane >> 4)][lane & 15], z);
+                y = mma_f32(am[16 * i + (lane & 15)][16 * m + kk + g], tm[16 * m + kk + g][16 * w + (lane & 15)], y);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) tm[16 * bi + 4 * (lane >> 4) + r][16 * bj + (lane & 15)] = -z[r];
-        }
-        __syncthreads();
-    }
-    // T to bf16 (overwrites A, which is dead)
-    {
-        // thread t converts 16 consecutive entries of row t/4: four 16-byte reads, two 16-byte writes
-        const int i = tid >> 2, j0 = 16 * (tid & 3);
-        float v[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(&tm[i][j0 + 4 * q]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
-        }
-        *reinterpret_cast<u32x4*>(&tb[i][j0]) = pack8(v, 1.0f);
-        *reinterpret_cast<u32x4*>(&tb[i][j0 + 8]) = pack8(v + 8, 1.0f);
-    }
-    __syncthreads();
-
-    // W^T = X^T T^T for key tiles kt = wv + 4m: lane holds W[i][k..k+3], half of a W tile piece
-#pragma unroll
-    for (int m = 0; m < KT4; ++m) {
-        const int kt = wv + 4 * m;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            // T is lower triangular: rows i < 32 have no entry at j >= 32
-            f32x4 acc = mma_bf16(xf[m][0], frag(&tb[16 * it][0], CH + PAD, lane), zero4());
-            if (it >= 2) acc = mma_bf16(xf[m][1], frag(&tb[16 * it][32], CH + PAD, lane), acc);
-            *reinterpret_cast<u32x2*>(w_out + (size_t)(it * (K / 32) + (kt >> 1)) * AT + a_tile_half_offset(lane, kt & 1)) =
-                pack4(acc[0], acc[1], acc[2], acc[3]);
-        }
-    }
-    // U' = T Y for value tiles vt = wv + 4m: accumulator order is the D tile order
-#pragma unroll
-    for (int m = 0; m < KT4; ++m) {
-        const int vt = wv + 4 * m;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            f32x4 acc = mma_bf16(frag(&tb[16 * it][0], CH + PAD, lane), yf[m][0], zero4());
-            if (it >= 2) acc = mma_bf16(frag(&tb[16 * it][32], CH + PAD, lane), yf[m][1], acc);
-            *reinterpret_cast<u32x2*>(u_out + (size_t)(it * (V / 16) + vt) * DT + 4 * lane) = pack4(acc[0], acc[1], acc[2], acc[3]);
-        }
-    }
-}
-
-// Operands of one chunk as one lane reads them.  Two of each alternate (ping-pong): while one chunk
-// is processed the next chunk's loads are in flight, and nothing is derived from a fetched value
-// until it is used, so no wait is forced early.  State waves use StateFrags, output waves OutFrags.
-template <int K, int NCT>
-struct StateFrags {
-    bf16x8 w[K / 32];          // W tiles of this wave's token tile
-    u32x2 up[NCT];             // U' D-tile pieces, one per column tile
-    bf16x8 kt[K / 64][2];      // Khat^T tiles of this wave's key tiles
-    f32x4 gr;                  // G of this lane's four U rows (tokens 16 w + 4(l/16) .. +3)
-    float gC;                  // G_C
-};
-template <int K>
-struct OutFrags {
-    bf16x8 q[K / 32];          // Qhat tiles of this wave's token tile
-    bf16x8 pm[2];              // P tiles of this wave's token tile
-    float gi;                  // G_i of this lane's output token
-};
-
-// ---- state + output ---------------------------------------------------------------------------------
-// One block of 8 waves per (sequence, head, VT-column tile; VT = 16 NCT).  Loads of the chunk's
-// W, Khat^T, Qhat and P are shared by the block's NCT 16-column tiles.
-//   Waves 0-3 ("state") carry the serial chain for chunk c: the entering state -> LDS (bf16),
-//   U = U' - W S^T for token tile w (to LDS as is, for the output, and with row i scaled by
-//   e^{G_C - G_i} <= 1, for the update), and S^T <- e^{G_C} S^T + Khat^T Ud for key tiles of wave w.
-//   The state is held transposed (accumulator lane: 4 consecutive keys of one value column), which
-//   makes its LDS copy and its HBM load/store contiguous.
-//   Waves 4-7 ("output") compute chunk c's output O^T[v][i] = e^{G_i} (S qhat_i) + (U^T P^T)[v][i]
-//   for token tile w from the double-buffered S and U^T while the state waves update S, off the
-//   serial chain, and write it as whole token rows through a per-wave LDS tile.
-template <typename T, int K, int V, int NCT>
-__global__ __launch_bounds__(512) void chunk_state_kernel(ChunkArgs p) {
-    using TS = typename T::storage;
-    constexpr int VT = 16 * NCT;
-    constexpr int KTW = K / 64;  // 16-wide key tiles per state wave
-    static_assert(V % VT == 0, "column tiles");
-    __shared__ __align__(16) uint16_t sb[2][VT][K + PAD];   // S entering the chunk (bf16)
-    __shared__ __align__(16) uint16_t ut[2][VT][CH + PAD];  // U^T (bf16)
-    __shared__ __align__(16) uint16_t ud[VT][CH + PAD];     // (diag(e^{G_C - G}) U)^T (bf16)
-    __shared__ __align__(16) uint16_t ot[4][16][VT + 8];    // output rows, one tile per output wave
-
-    const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws + p.L.hdr);
-    if (hdr[0] != GDN_OK) return;
-    const int32_t* cstart = hdr + 16;
-    constexpr int NVT = V / VT;
-    const int blk = xcd_remap((int)blockIdx.x, p.n_blocks, NVT);
-    const int vt = blk % NVT;
-    const int bh = blk / NVT;
-    const int h = bh % p.H, b = cstart[p.B + 1 + bh / p.H];  // sequences longest first
-    const int kh = h / p.G;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const bool is_state = tid < 256;
-    const int wv = (tid >> 6) & 3;  // token / key tile of this wave within its group
-    const int v0 = vt * VT;
-    const size_t col0 = ((size_t)b * p.H + h) * V + v0;  // first state row of the block
-    TS* outp = static_cast<TS*>(p.out);
-    const int c0 = cstart[b], c1 = cstart[b + 1];
-    const int seq_start = p.offsets[b], seq_end = p.offsets[b + 1];
-    const uint16_t* const wsb = reinterpret_cast<const uint16_t*>(p.ws);
-    const uint16_t* const wbase = wsb + p.L.w / 2;
-    const uint16_t* const ktbase = wsb + p.L.kt / 2;
-    const uint16_t* const qbase = wsb + p.L.qf / 2;
-    const uint16_t* const pbase = wsb + p.L.pm / 2;
-    const uint16_t* const ubase = wsb + p.L.upt / 2;
-    const float* gamb = reinterpret_cast<const float*>(p.ws + p.L.gam);
-
-    // transposed state tiles (state waves): acc[t][ct][r] = S[v0 + 16 ct + l%16][16 (KTW w + t) + 4(l/16) + r]
-    f32x4 acc[KTW][NCT];
-    if (is_state) {
-#pragma unroll
-        for (int t = 0; t < KTW; ++t)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const size_t off = (col0 + 16 * ct + (lane & 15)) * K + 16 * (KTW * wv + t) + 4 * (lane >> 4);
-                acc[t][ct] = p.state_in ? *reinterpret_cast<const f32x4*>(p.state_in + off) : zero4();
-            }
-    }
-
-    auto afrag = [&](const uint16_t* tile) { return *reinterpret_cast<const bf16x8*>(tile + 8 * lane); };
-    auto fetch_s = [&](int c, StateFrags<K, NCT>& f) {
-        const size_t chh = (size_t)c * p.H + h, chk = (size_t)c * p.HQ + kh;
-        const uint16_t* wt = wbase + (chh * 4 + wv) * (K / 32) * AT;
-#pragma unroll
-        for (int kk = 0; kk < K / 32; ++kk) f.w[kk] = afrag(wt + kk * AT);
-        const uint16_t* ud = ubase + ((chh * 4 + wv) * (V / 16) + vt * NCT) * DT + 4 * lane;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) f.up[ct] = *reinterpret_cast<const u32x2*>(ud + ct * DT);
-#pragma unroll
-        for (int t = 0; t < KTW; ++t)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) f.kt[t][jj] = afrag(ktbase + ((chk * (K / 16) + KTW * wv + t) * 2 + jj) * AT);
-        f.gr = *reinterpret_cast<const f32x4*>(gamb + chh * CH + 16 * wv + 4 * (lane >> 4));
-        f.gC = gamb[chh * CH + CH - 1];
-    };
-    auto fetch_o = [&](int c, OutFrags<K>& f) {
-        const size_t chh = (size_t)c * p.H + h, chk = (size_t)c * p.HQ + kh;
-        const uint16_t* qt = qbase + (chk * 4 + wv) * (K / 32) * AT;
-#pragma unroll
-        for (int kk = 0; kk < K / 32; ++kk) f.q[kk] = afrag(qt + kk * AT);
-        f.pm[0] = afrag(pbase + (chh * 4 + wv) * 2 * AT);
-        // token tiles 0 and 1 have no nonzero P entry past key 31: that fragment is neither
-        // stored nor loaded
-        if (wv >= 2) f.pm[1] = afrag(pbase + ((chh * 4 + wv) * 2 + 1) * AT);
-        f.gi = gamb[chh * CH + 16 * wv + (lane & 15)];
-    };
-
-    // state waves, before the first barrier: S entering the chunk -> LDS (one 8-byte store per tile)
-    auto s_store = [&](int buf) {
-#pragma unroll
-        for (int t = 0; t < KTW; ++t)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-                *reinterpret_cast<u32x2*>(&sb[buf][16 * ct + (lane & 15)][16 * (KTW * wv + t) + 4 * (lane >> 4)]) =
-                    pack4(acc[t][ct][0], acc[t][ct][1], acc[t][ct][2], acc[t][ct][3]);
-    };
-    // state waves, between the barriers: U = U' - W S^T for token tile wv.  All LDS fragments are read
-    // before the first product so that the NCT accumulation chains run back to back.
-    auto s_u = [&](int buf, const StateFrags<K, NCT>& f) {
-        bf16x8 sf[K / 32][NCT];
-#pragma unroll
-        for (int kk = 0; kk < K / 32; ++kk)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) sf[kk][ct] = frag(&sb[buf][16 * ct][32 * kk], K + PAD, lane);
-        f32x4 pw[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) pw[ct] = mma_bf16(f.w[0], sf[0][ct], zero4());
-#pragma unroll
-        for (int kk = 1; kk < K / 32; ++kk)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) pw[ct] = mma_bf16(f.w[kk], sf[kk][ct], pw[ct]);
-        order_reads_then_mfma<K / 32 * NCT, K / 32 * NCT>();
-        float ds[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ds[r] = expf(f.gC - f.gr[r]);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const float u0 = bf16_bits_to_f32(f.up[ct].x & 0xffffu) - pw[ct][0];
-            const float u1 = bf16_bits_to_f32(f.up[ct].x >> 16) - pw[ct][1];
-            const float u2 = bf16_bits_to_f32(f.up[ct].y & 0xffffu) - pw[ct][2];
-            const float u3 = bf16_bits_to_f32(f.up[ct].y >> 16) - pw[ct][3];
-            *reinterpret_cast<u32x2*>(&ut[buf][16 * ct + (lane & 15)][16 * wv + 4 * (lane >> 4)]) = pack4(u0, u1, u2, u3);
-            *reinterpret_cast<u32x2*>(&ud[16 * ct + (lane & 15)][16 * wv + 4 * (lane >> 4)]) =
-                pack4(u0 * ds[0], u1 * ds[1], u2 * ds[2], u3 * ds[3]);
-        }
-    };
-    // state waves, after the second barrier: S^T <- e^{G_C} S^T + Khat^T Ud
-    auto s_update = [&](const StateFrags<K, NCT>& f) {
-        const float gC = expf(f.gC);
-        bf16x8 uf[NCT][2];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) uf[ct][jj] = frag(&ud[16 * ct][32 * jj], CH + PAD, lane);
-#pragma unroll
-        for (int t = 0; t < KTW; ++t)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = mma_bf16(f.kt[t][0], uf[ct][0], acc[t][ct] * gC);
-#pragma unroll
-        for (int t = 0; t < KTW; ++t)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = mma_bf16(f.kt[t][1], uf[ct][1], acc[t][ct]);
-        order_reads_then_mfma<2 * NCT, 2 * KTW * NCT>();
-    };
-    // output waves: chunk c's output tiles (token tile wv, all column tiles) from sb[buf], ut[buf]
-    constexpr int LPR = VT / 8;         // lanes per output row (16 bytes each)
-    constexpr int RPI = 64 / LPR;       // rows per store instruction
-    // NJ: the P fragments of this token tile that can be nonzero (tiles 0 and 1 see only keys < 32)
-    auto o_tile = [&](auto nj, int c, int buf, const OutFrags<K>& f) {
-        constexpr int NJ = decltype(nj)::value;
-        const float cs = expf(f.gi);
-        bf16x8 sf[NCT][K / 32], uf[NCT][NJ];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-            for (int kk = 0; kk < K / 32; ++kk) sf[ct][kk] = frag(&sb[buf][16 * ct][32 * kk], K + PAD, lane);
-#pragma unroll
-            for (int jj = 0; jj < NJ; ++jj) uf[ct][jj] = frag(&ut[buf][16 * ct][32 * jj], CH + PAD, lane);
-        }
-        f32x4 a1[NCT], a2[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            a1[ct] = mma_bf16(sf[ct][0], f.q[0], zero4());
-            a2[ct] = mma_bf16(uf[ct][0], f.pm[0], zero4());
-        }
-        if constexpr (NJ == 2) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) a2[ct] = mma_bf16(uf[ct][1], f.pm[1], a2[ct]);
-        }
-#pragma unroll
-        for (int kk = 1; kk < K / 32; ++kk)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) a1[ct] = mma_bf16(sf[ct][kk], f.q[kk], a1[ct]);
-        order_reads_then_mfma<(K / 32 + NJ) * NCT, (K / 32 + NJ) * NCT>();
-        // lane: token 16 wv + l%16, columns 16 ct + 4(l/16) .. +3
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            float o[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = p.scale * fmaf(cs, a1[ct][r], a2[ct][r]);
-            *reinterpret_cast<u32x2*>(&ot[wv][lane & 15][16 * ct + 4 * (lane >> 4)]) =
-                u32x2{(uint32_t)from_f32<T>(o[0]) | ((uint32_t)from_f32<T>(o[1]) << 16),
-                      (uint32_t)from_f32<T>(o[2]) | ((uint32_t)from_f32<T>(o[3]) << 16)};
-        }
-        // the tile is this wave's alone: LDS keeps one wave's accesses in order, the fence keeps the
-        // compiler from moving the reads above the writes
+        for (int r = 0; r < 4; ++r) scr[w][4 * g + r][lane & 15] = y[r];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int tbase = seq_start + (c - c0) * CH + 16 * wv;
+        f32x4 z = zero4();
 #pragma unroll
-        for (int r0 = 0; r0 < 16; r0 += RPI) {
-            const int row = r0 + lane / LPR;
-            if (row < 16 && tbase + row < seq_end)
-                *reinterpret_cast<u32x4*>(outp + ((size_t)(tbase + row) * p.H + h) * V + v0 + 8 * (lane % LPR)) =
-                    *reinterpret_cast<const u32x4*>(&ot[wv][row][8 * (lane % LPR)]);
-        }
-    };
-
-    // Iteration c (c0 <= c <= c1) has two barriers.  State waves store S entering chunk c before the
-    // first, form U between them and update S after the second; output waves compute chunk c's
-    // output after the second barrier (S and U of chunk c are complete then and stay untouched until
-    // the next iteration's second barrier), alongside the state update.  Every fetch is
-    // unconditional (chunk indices clamped into [c0, c1)), so the loads in flight are the same on
-    // every path and each wait covers only the data about to be used.
-    if (c0 < c1) {
-        if (is_state) {
-            StateFrags<K, NCT> fa, fb;
-            fetch_s(c0, fa);
-            for (int c = c0; c <= c1; c += 2) {
-                fetch_s(min(c + 1, c1 - 1), fb);
-                if (c < c1) s_store((c - c0) & 1);
-                __syncthreads();
-                if (c < c1) s_u((c - c0) & 1, fa);
-                __syncthreads();
-                if (c < c1) s_update(fa);
-                if (c + 1 > c1) break;
-                fetch_s(min(c + 2, c1 - 1), fa);
-                if (c + 1 < c1) s_store((c + 1 - c0) & 1);
-                __syncthreads();
-                if (c + 1 < c1) s_u((c + 1 - c0) & 1, fb);
-                __syncthreads();
-                if (c + 1 < c1) s_update(fb);
-            }
-        } else {
-            // chunk j's output is computed right after the second barrier of iteration j (S entering
-            // chunk j and its U are complete then), alongside the state waves' update; its operands
-            // live in fa (j - c0 even) or fb (odd), fetched one iteration ahead
-            OutFrags<K> fa, fb;
-            fetch_o(c0, fa);
-            for (int c = c0; c <= c1; c += 2) {
-                __syncthreads();
-                fetch_o(min(c + 1, c1 - 1), fb);
-                __syncthreads();
-                if (c < c1) {
-                    if (wv >= 2) o_tile(std::integral_constant<int, 2>{}, c, (c - c0) & 1, fa);
-                    else o_tile(std::integral_constant<int, 1>{}, c, (c - c0) & 1, fa);
-                }
-                if (c + 1 > c1) break;
-                __syncthreads();
-                fetch_o(min(c + 2, c1 - 1), fa);
-                __syncthreads();
-                if (c + 1 < c1) {
-                    if (wv >= 2) o_tile(std::integral_constant<int, 2>{}, c + 1, (c + 1 - c0) & 1, fb);
-                    else o_tile(std::integral_constant<int, 1>{}, c + 1, (c + 1 - c0) & 1, fb);
-                }
-            }
-        }
+        for (int kk = 0; kk < 16; kk += 4)
+            z = mma_f32(tm[16 * i + (lane & 15)][16 * i + kk + g], scr[w][kk + g][lane & 15], z);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tm[16 * i + 4 * g + r][16 * w + (lane & 15)] = -z[r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    if (is_state && p.state_out != nullptr) {
+    __syncthreads();  // T complete
+    // fragments f = w and w + 4: lane l holds row 16 it + l%16, columns 32 jj + {4g.., 16+4g..}; the
+    // blocks above the diagonal are zero
+    uint16_t* const tout = reinterpret_cast<uint16_t*>(p.ws + p.L.tfr) + ch * NTF * 512;
+    for (int f = w; f < NTF; f += NW) {
+        const int it = tf_tile(f), jj = tf_blk(f);
+        const int i = 16 * it + (lane & 15);
+        const int j0 = 32 * jj + 4 * g, j1 = j0 + 16;
+        float v[8];
 #pragma unroll
-        for (int t = 0; t < KTW; ++t)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const size_t off = (col0 + 16 * ct + (lane & 15)) * K + 16 * (KTW * wv + t) + 4 * (lane >> 4);
-                *reinterpret_cast<f32x4*>(p.state_out + off) = acc[t][ct];
-            }
+        for (int e = 0; e < 4; ++e) {
+            v[e] = (j0 >> 4) <= it ? tm[i][j0 + e] : 0.0f;
+            v[4 + e] = (j1 >> 4) <= it ? tm[i][j1 + e] : 0.0f;
+        }
+        *reinterpret_cast<u32x4*>(tout + f * 512 + 8 * lane) = pack8(v, 1.0f);
     }
 }
 
+// ---- summary and main -----------------------------------------------------------------------------
+// LDS layouts of one chunk (all 16-bit elements):
+//   kn, qn  [token][key]: the raw k and q rows as bf16 operands (the L2 norms 1/|k|, 1/|q| scale
+//           per-token factors instead), keys of every 32-block in the split order (physical slot
+//           8g + e holds key 4g + e for e < 4 and 16 + 4g + e - 4 otherwise), so a split fragment
+//           is one 16-byte read; products between two such rows are unchanged.
+//   kt, vt  [key or value column][token]: transposed, tokens of every 32-block in the split order,
+//           in 16-byte units (8 tokens = one lane group's split fragment) placed at unit u ^ (idx/8 % 8)
+//           so that the stores of one row-major lane (8 consecutive indices) spread over the banks.
+//   pb      P, [row i][column j] with the columns in the split order.
+__device__ __forceinline__ int split_key_slot(int pc) {  // slot of keys 8pc..8pc+3 (then +8 for 8pc+4..+7)
+    const int a = pc & 3;
+    return 32 * (pc >> 2) + 16 * (a & 1) + 4 * (a >> 1);
+}
+// element offset of token t in row idx of a transposed tile
+__device__ __forceinline__ int tpos(int idx, int t) {
+    const int q = (t >> 2) & 7;
+    const int unit = 4 * (t >> 5) + (q & 3);
+    return 8 * (unit ^ ((idx >> 3) & 7)) + 4 * (q >> 2) + (t & 3);
+}
+// split fragment of a transposed tile: rows idx0 + l%16, the tokens of 32-block jj
+__device__ __forceinline__ bf16x8 frag_t(const uint16_t* tile, int ld, int idx0, int jj, int lane) {
+    const int idx = idx0 + (lane & 15);
+    return *reinterpret_cast<const bf16x8*>(tile + idx * ld + 8 * ((4 * jj + (lane >> 4)) ^ ((idx >> 3) & 7)));
+}
+
+template <int K, int V, bool Q>
+struct ChunkBuf {
+    uint16_t kn[CH][K + PAD];
+    uint16_t qn[Q ? CH : 1][K + PAD];
+    uint16_t kt[K][CH + PAD];
+    uint16_t vt[V][CH + PAD];
+    // per token: G; b; scale e^G; b e^G / |k|; e^{G_C - G} / |k|; 1/|k|; 1/|q|; and e^{G_C}
+    float gam[CH], beta[CH], eg[CH], bx[CH], ud[CH], rk[CH], rq[CH], gc[4];
+};
+template <int K, int V, bool SUMMARY>
+struct FusedLds {
+    ChunkBuf<K, V, !SUMMARY> buf[2];
+    uint16_t pb[SUMMARY ? 1 : CH][CH + PAD];
+};
+
+// MODE: kMain, kMainCapture (also records the first tokens of each sequence) or kSummary.
+constexpr int kMain = 0, kMainCapture = 1, kSummary = 2;
+
+// One wave per VTW 16-column value tiles.  Staging: wave w stages token rows RPW w .. RPW w + RPW-1.
+template <typename T, int K, int V, int MODE, int VTW>
+__global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(ChunkArgs p) {
+    using TS = typename T::storage;
+    constexpr bool SUMMARY = MODE == kSummary, CAPTURE = MODE == kMainCapture;
+    constexpr int NWV = V / (16 * VTW);  // waves
+    static_assert(K % 32 == 0 && V % (16 * VTW) == 0 && K % (16 * NWV) == 0, "tile shapes");
+    constexpr int NPHI = SUMMARY ? K / (16 * NWV) : 0;  // Phi column tiles per wave in a summary
+    constexpr int NCT = VTW + NPHI;
+    constexpr int KT = K / 16, KK = K / 32;
+    constexpr int RPW = CH / NWV;  // token rows staged per wave
+    constexpr int LPT = K / 8, TPI = 64 / LPT;  // k/q rows: lanes per row, rows per instruction
+    constexpr int LPV = V / 8, TPV = 64 / LPV;
+    static_assert(RPW % TPI == 0 && RPW % TPV == 0, "staging tiles");
+    constexpr int NI = RPW / TPI, NV = RPW / TPV;
+    __shared__ __align__(16) FusedLds<K, V, SUMMARY> sm;
+
+    int32_t* hdr = reinterpret_cast<int32_t*>(p.ws);
+    if (hdr[0] != GDN_OK) return;
+    const Tables tab = tables(p.ws, p.B);
+    const int u = xcd_remap((int)blockIdx.x, p.n_blocks, p.G);
+    if (u >= hdr[SUMMARY ? 2 : 1]) return;
+    int b, local;
+    if constexpr (SUMMARY) {
+        b = find_start(tab.sstart, p.B, u);
+        local = u - tab.sstart[b];
+    } else {
+        const int r = find_start(tab.ustart, p.B, u);
+        b = tab.order[r];
+        local = u - tab.ustart[r];
+    }
+    const int seg = local / p.H, h = local % p.H, kh = h / p.G;
+    const int sl = p.L.seglen;
+    const int nch = tab.nchunk[b];
+    const int nseg = nseg_of(nch, sl);
+    const int cb = nseg == 1 ? 0 : seg * sl;
+    const int ce = nseg == 1 ? nch : min(nch, cb + sl);
+    const int seq_start = p.offsets[b], len = p.offsets[b + 1] - seq_start;
+    const int cid0 = tab.cstart[b];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+    const size_t slot_stride = ((size_t)K * K + (size_t)V * K);
+    float* const slots = reinterpret_cast<float*>(p.ws + p.L.slots);
+    auto slot_phi = [&](int s) { return slots + ((size_t)s * p.H + h) * slot_stride; };
+    auto slot_n = [&](int s) { return slot_phi(s) + (size_t)K * K; };
+
+    // column of tile ct of this lane: value column 16 (VTW w + ct) + l%16 (ct < VTW), or (summary) Phi
+    // column 16 (NPHI w + ct - VTW) + l%16
+    auto col_of = [&](int ct) {
+        return ct < VTW ? 16 * (VTW * w + ct) + l16 : V + 16 * (NPHI * w + ct - VTW) + l16;
+    };
+
+    // ---- entering state: sacc[kt][ct] = S0^T[16 kt + 4g .. +3][col]
+    f32x4 sacc[KT][NCT];
+    {
+        const float* src = nullptr;
+        if constexpr (!SUMMARY) {
+            if (nseg == 1) src = p.state_in ? p.state_in + ((size_t)b * p.H + h) * V * K : nullptr;
+            else src = slot_n(tab.slot0[b] + (seg == 0 ? nseg - 1 : seg - 1));
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int c = col_of(ct);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                if (ct < VTW) {
+                    sacc[kt][ct] = src ? *reinterpret_cast<const f32x4*>(src + (size_t)c * K + 16 * kt + 4 * g) : zero4();
+                } else {  // Phi starts as the identity
+                    const int cc = c - V, k0 = 16 * kt + 4 * g;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sacc[kt][ct][r] = (k0 + r == cc) ? 1.0f : 0.0f;
+                }
+            }
+        }
+    }
+
+    // ---- capture (first segment): zero the unrecorded slots
+    int captured = 0;
+    CaptureRow crow{};
+    if constexpr (CAPTURE) {
+        if (seg == 0) {
+            captured = captured_tokens(p.counts, p.active, p.cap, b, len);
+            crow = capture_row(p.capsule, b, p.cap, p.H, p.HQ, K, V);
+            for (int i = captured; i < p.cap; ++i) {
+                if (tid == 0) *crow.g(i, h) = 0.0f;
+                for (int j = tid; j < V; j += blockDim.x) crow.d(i, h)[j] = 0.0f;
+                if (h % p.G == 0)
+                    for (int j = tid; j < K; j += blockDim.x) crow.k(i, kh)[j] = 0.0f;
+            }
+        }
+    }
+
+    const TS* const xq = static_cast<const TS*>(p.x.q);
+    const TS* const xk = static_cast<const TS*>(p.x.k);
+    const TS* const xv = static_cast<const TS*>(p.x.v);
+    const uint16_t* const tfr = reinterpret_cast<const uint16_t*>(p.ws + p.L.tfr);
+    const float* const gts = reinterpret_cast<const float*>(p.ws + p.L.gates);
+    const int pc = lane % LPT, tsub = lane / LPT;
+    const int pv = lane % LPV, vsub = lane / LPV;
+    const int ks0 = split_key_slot(pc);
+    constexpr int RSRC = 0x00020000;  // raw buffer resource (gfx9 family)
+
+    // Rows of one chunk (range-checked buffer loads: rows at or past the chunk's end read as zero),
+    // its T fragments and the tokens' G, b and 1/|k| (lane = token).
+    struct Rows {
+        u32x4 k[NI], q[SUMMARY ? 1 : NI], v[NV];
+        u32x4 tf[NTF];
+        float gam, beta, rk;
+    };
+    auto load_rows = [&](int c, Rows& R) {
+        const int t0 = seq_start + c * CH, n = min(CH, len - c * CH);
+        const size_t ch = (size_t)(cid0 + c) * p.H + h;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<TS*>(xk + (size_t)t0 * p.x.sk + (size_t)kh * K), 0, n * (int)p.x.sk * (int)sizeof(TS), RSRC);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<TS*>(xv + (size_t)t0 * p.x.sv + (size_t)h * V), 0, n * (int)p.x.sv * (int)sizeof(TS), RSRC);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int ti = RPW * w + TPI * i + tsub;
+            R.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rk, (ti * (int)p.x.sk + 8 * pc) * (int)sizeof(TS), 0, 0));
+        }
+        if constexpr (!SUMMARY) {
+            const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<TS*>(xq + (size_t)t0 * p.x.sq + (size_t)kh * K), 0, n * (int)p.x.sq * (int)sizeof(TS), RSRC);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int ti = RPW * w + TPI * i + tsub;
+                R.q[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rq, (ti * (int)p.x.sq + 8 * pc) * (int)sizeof(TS), 0, 0));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int ti = RPW * w + TPV * i + vsub;
+            R.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rv, (ti * (int)p.x.sv + 8 * pv) * (int)sizeof(TS), 0, 0));
+        }
+#pragma unroll
+        for (int f = 0; f < NTF; ++f) R.tf[f] = *reinterpret_cast<const u32x4*>(tfr + (ch * NTF + f) * 512 + 8 * lane);
+        R.gam = gts[ch * 3 * CH + lane];
+        R.beta = gts[ch * 3 * CH + CH + lane];
+        R.rk = gts[ch * 3 * CH + 2 * CH + lane];
+    };
+    // raw rows, transposes, norms and per-token factors of chunk c into buffer Bf
+    auto stage = [&](int c, const Rows& R, ChunkBuf<K, V, !SUMMARY>& Bf) {
+        const bool cap_chunk = CAPTURE && c == 0 && captured > 0;
+        if (w == 0) {
+            const float gC = __shfl(R.gam, CH - 1);
+            const float eg = fexp(R.gam);
+            Bf.gam[lane] = R.gam;
+            Bf.beta[lane] = R.beta;
+            Bf.eg[lane] = p.scale * eg;
+            Bf.bx[lane] = R.beta * eg * R.rk;
+            Bf.ud[lane] = fexp(gC - R.gam) * R.rk;
+            Bf.rk[lane] = R.rk;
+            if (lane == 0) Bf.gc[0] = fexp(gC);
+            if (cap_chunk && lane < captured) {
+                const float gp = lane > 0 ? __shfl(R.gam, lane - 1) : 0.0f;
+                *crow.g(lane, h) = expf(R.gam - gp);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int ti = RPW * w + TPI * i + tsub;
+            const u32x4 kb = to_bf16x8<T>(R.k[i]);
+            *reinterpret_cast<u32x2*>(&Bf.kn[ti][ks0]) = u32x2{kb[0], kb[1]};
+            *reinterpret_cast<u32x2*>(&Bf.kn[ti][ks0 + 8]) = u32x2{kb[2], kb[3]};
+            const int tp = tpos(8 * pc, ti);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Bf.kt[8 * pc + e][tp] = half_of(kb, e);
+            if constexpr (!SUMMARY) {
+                if (cap_chunk && ti < captured && h % p.G == 0) {
+                    const float rk = rsqrtf(group_sum<LPT>(sumsq8<T>(R.k[i])) + 1e-12f);
+                    float kf[8];
+                    unpack8<T>(R.k[i], kf);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) crow.k(ti, kh)[8 * pc + e] = kf[e] * rk;
+                }
+                const u32x4 qb = to_bf16x8<T>(R.q[i]);
+                *reinterpret_cast<u32x2*>(&Bf.qn[ti][ks0]) = u32x2{qb[0], qb[1]};
+                *reinterpret_cast<u32x2*>(&Bf.qn[ti][ks0 + 8]) = u32x2{qb[2], qb[3]};
+                const float rq = rsqrtf(group_sum<LPT>(sumsq8<T>(R.q[i])) + 1e-12f);
+                if (pc == 0) Bf.rq[ti] = rq;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int ti = RPW * w + TPV * i + vsub;
+            const int tp = tpos(8 * pv, ti);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Bf.vt[8 * pv + e][tp] = half_of(R.v[i], e);
+        }
+    };
+
+    if constexpr (!SUMMARY) {  // P blocks (0,1) and (2,3) are read as zeros by the U^T P^T products
+        for (int z = tid; z < 128; z += blockDim.x) {
+            const int blk2 = z >> 6, rr = (z & 63) >> 2, cc = z & 3;
+            *reinterpret_cast<u32x2*>(&sm.pb[32 * blk2 + rr][32 * blk2 + 8 * cc + 4]) = u32x2{0u, 0u};
+        }
+    }
+    TS* const outp = static_cast<TS*>(p.out);
+
+    // One chunk; Bf holds it, Bn receives the next one (the two buffers alternate)
+    Rows R;
+    auto step = [&](int c, ChunkBuf<K, V, !SUMMARY>& Bf, ChunkBuf<K, V, !SUMMARY>& Bn) {
+        const int t0 = seq_start + c * CH, n = min(CH, len - c * CH);
+        const bool cap_chunk = CAPTURE && c == 0 && captured > 0;
+        bf16x8 tf[NTF];
+#pragma unroll
+        for (int f = 0; f < NTF; ++f) tf[f] = __builtin_bit_cast(bf16x8, R.tf[f]);
+        if (c + 1 < ce) load_rows(c + 1, R);  // in flight during this chunk
+
+        // ---- P = M o (Q K^T) / (|q_i| |k_j|): the ten nonzero 16 x 16 blocks (it, jt <= it), block n by
+        // wave n % NWV, formed transposed (K_jt Q_it^T; lane: 4 consecutive j = 16 jt + 4g + r of row
+        // i = 16 it + l%16)
+        if constexpr (!SUMMARY) {
+#pragma unroll
+            for (int nb = w; nb < 10; nb += NWV) {
+                const int it = nb < 1 ? 0 : nb < 3 ? 1 : nb < 6 ? 2 : 3;
+                const int jt = nb - it * (it + 1) / 2;
+                f32x4 pt = zero4();
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    pt = mma_bf16(frag(&Bf.kn[16 * jt][32 * kk], K + PAD, lane), frag(&Bf.qn[16 * it][32 * kk], K + PAD, lane), pt);
+                const int i = 16 * it + l16, j0 = 16 * jt + 4 * g;
+                const float g_i = Bf.gam[i], q_i = Bf.rq[i];
+                const f32x4 g_j = *reinterpret_cast<const f32x4*>(&Bf.gam[j0]);
+                const f32x4 r_j = *reinterpret_cast<const f32x4*>(&Bf.rk[j0]);
+                float pv4[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    pv4[r] = (j0 + r <= i) ? fexp(fminf(g_i - g_j[r], 0.0f)) * (q_i * r_j[r]) * pt[r] : 0.0f;
+                *reinterpret_cast<u32x2*>(&sm.pb[i][32 * (jt >> 1) + 8 * g + 4 * (jt & 1)]) =
+                    u32x2{bf2(pv4[0], pv4[1]), bf2(pv4[2], pv4[3])};
+            }
+        }
+
+        // ---- chain: S0^T -> K S0^T (and S0 Q^T) -> R -> U -> S
+        bf16x8 sbf[KK][NCT];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) sbf[kk][ct] = pack_acc(sacc[2 * kk][ct], sacc[2 * kk + 1][ct]);
+        f32x4 ks[4][NCT];
+        f32x4 oq[SUMMARY ? 1 : 4][VTW];  // (S0 Q^T) tiles: rows = value columns, columns = tokens
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) ks[it][ct] = zero4();
+            if constexpr (!SUMMARY) {
+#pragma unroll
+                for (int ct = 0; ct < VTW; ++ct) oq[it][ct] = zero4();
+            }
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const bf16x8 kf = frag(&Bf.kn[16 * it][32 * kk], K + PAD, lane);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) ks[it][ct] = mma_bf16(kf, sbf[kk][ct], ks[it][ct]);
+                if constexpr (!SUMMARY) {
+                    const bf16x8 qf = frag(&Bf.qn[16 * it][32 * kk], K + PAD, lane);
+#pragma unroll
+                    for (int ct = 0; ct < VTW; ++ct) oq[it][ct] = mma_bf16(sbf[kk][ct], qf, oq[it][ct]);
+                }
+            }
+        }
+        // R = diag(b) V - diag(b e^G / |k|) (K S0^T), in place of ks (rows 16 it + 4g + r)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int i0 = 16 * it + 4 * g;
+            const f32x4 bet = *reinterpret_cast<const f32x4*>(&Bf.beta[i0]);
+            const f32x4 bxv = *reinterpret_cast<const f32x4*>(&Bf.bx[i0]);
+#pragma unroll
+            for (int ct = 0; ct < VTW; ++ct) {
+                const int cc = col_of(ct);
+                const u32x2 vr = *reinterpret_cast<const u32x2*>(&Bf.vt[cc][tpos(cc, i0)]);
+                const float vv[4] = {to_f32<T>((uint16_t)(vr.x & 0xffffu)), to_f32<T>((uint16_t)(vr.x >> 16)),
+                                     to_f32<T>((uint16_t)(vr.y & 0xffffu)), to_f32<T>((uint16_t)(vr.y >> 16))};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ks[it][ct][r] = fmaf(bet[r], vv[r], -bxv[r] * ks[it][ct][r]);
+            }
+#pragma unroll
+            for (int ct = VTW; ct < NCT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ks[it][ct][r] = -bxv[r] * ks[it][ct][r];
+        }
+        // U = T R (T lower triangular: token tiles 0 and 1 need only the first 32-block)
+        f32x4 ua[4][NCT];
+        {
+            bf16x8 rb[2][NCT];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) rb[jj][ct] = pack_acc(ks[2 * jj][ct], ks[2 * jj + 1][ct]);
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) ua[it][ct] = zero4();
+#pragma unroll
+            for (int f = 0; f < NTF; ++f) {
+                const int it = tf_tile(f), jj = tf_blk(f);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) ua[it][ct] = mma_bf16(tf[f], rb[jj][ct], ua[it][ct]);
+            }
+        }
+        if constexpr (!SUMMARY) {
+            __syncthreads();  // P complete
+            // O^T = (S0 Q^T) diag(scale e^G / |q|) + scale U^T P^T (the first factor is eg / |q|).
+            // Lane: value columns 16 w + 4g .. +3 of token 16 it + l%16, stored as 8 bytes; rows at or
+            // past the chunk's end are dropped by the range-checked buffer (so every store is issued
+            // and the waits stay exact)
+            bf16x8 ub[2][VTW];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int ct = 0; ct < VTW; ++ct) ub[jj][ct] = pack_acc(ua[2 * jj][ct], ua[2 * jj + 1][ct]);
+            const __amdgpu_buffer_rsrc_t orsrc =
+                __builtin_amdgcn_make_buffer_rsrc(outp + (size_t)t0 * p.H * V, 0, n * p.H * V * (int)sizeof(TS), RSRC);
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int i = 16 * it + l16;
+                const bf16x8 p0 = frag(&sm.pb[16 * it][0], CH + PAD, lane);
+                bf16x8 p1;
+                if (it >= 2) p1 = frag(&sm.pb[16 * it][32], CH + PAD, lane);
+                const float qf = Bf.eg[i] * Bf.rq[i];
+#pragma unroll
+                for (int ct = 0; ct < VTW; ++ct) {
+                    f32x4 o = mma_bf16(ub[0][ct], p0, zero4());
+                    if (it >= 2) o = mma_bf16(ub[1][ct], p1, o);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = fmaf(oq[it][ct][r], qf, p.scale * o[r]);
+                    const u32x2 piece = u32x2{pack2<T>(o[0], o[1]), pack2<T>(o[2], o[3])};
+                    const int off = (((16 * it + l16) * p.H + h) * V + 16 * (VTW * w + ct) + 4 * g) * (int)sizeof(TS);
+                    __builtin_amdgcn_raw_buffer_store_b64(piece, orsrc, off, 0, 0);
+                }
+            }
+            if (cap_chunk) {  // delta of the recorded tokens: rows of U
+#pragma unroll
+                for (int ct = 0; ct < VTW; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * g + r < captured) crow.d(4 * g + r, h)[col_of(ct)] = ua[0][ct][r];
+            }
+        }
+        // S0^T <- e^{G_C} S0^T + K^T diag(e^{G_C - G} / |k|) U
+        {
+            bf16x8 udb[2][NCT];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const f32x4 d0 = *reinterpret_cast<const f32x4*>(&Bf.ud[32 * jj + 4 * g]);
+                const f32x4 d1 = *reinterpret_cast<const f32x4*>(&Bf.ud[32 * jj + 16 + 4 * g]);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) udb[jj][ct] = pack_acc(ua[2 * jj][ct] * d0, ua[2 * jj + 1][ct] * d1);
+            }
+            const float gC = Bf.gc[0];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const bf16x8 a0 = frag_t(&Bf.kt[0][0], CH + PAD, 16 * kt, 0, lane);
+                const bf16x8 a1 = frag_t(&Bf.kt[0][0], CH + PAD, 16 * kt, 1, lane);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    f32x4 s = sacc[kt][ct] * gC;
+                    s = mma_bf16(a0, udb[0][ct], s);
+                    sacc[kt][ct] = mma_bf16(a1, udb[1][ct], s);
+                }
+            }
+        }
+        // the next chunk into the other buffer (last read before the previous barrier)
+        if (c + 1 < ce) stage(c + 1, R, Bn);
+        __syncthreads();
+    };
+
+    if (cb < ce) {
+        load_rows(cb, R);
+        stage(cb, R, sm.buf[0]);
+    }
+    // nothing may be in flight when the loop starts: the compiler then has to wait in the loop only
+    // for what the loop itself issued
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int c = cb; c < ce; ++c) {
+        const int bi = (c - cb) & 1;
+        step(c, sm.buf[bi], sm.buf[bi ^ 1]);
+    }
+
+    // ---- leaving state
+    if constexpr (SUMMARY) {
+        float* const phi = slot_phi(tab.slot0[b] + seg);
+        float* const nst = slot_n(tab.slot0[b] + seg);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int c = col_of(ct);
+            float* dst = ct < VTW ? nst + (size_t)c * K : phi + (size_t)(c - V) * K;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) *reinterpret_cast<f32x4*>(dst + 16 * kt + 4 * g) = sacc[kt][ct];
+        }
+    } else {
+        if (seg == nseg - 1 && p.state_out != nullptr) {
+            float* const dst = p.state_out + ((size_t)b * p.H + h) * V * K;
+#pragma unroll
+            for (int ct = 0; ct < VTW; ++ct) {
+                const int c = col_of(ct);
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) *reinterpret_cast<f32x4*>(dst + (size_t)c * K + 16 * kt + 4 * g) = sacc[kt][ct];
+            }
+        }
+    }
+}
+
+// ---- combine: S_start of every segment, in order ------------------------------------------------
+// One block per (sequence, head, 16 value rows); a thread owns key column k = t % K of rows
+// t / K + (256 / K) j.  S_start(s+1) = S_start(s) Phi_s + N_s  (rows v: S[v][k] = sum_c S[v][c]
+// phi[c][k] + N[v][k]), in fp32.
+template <int K, int V>
+__global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs p) {
+    constexpr int RG = 256 / K;   // row groups
+    constexpr int RPT = 16 / RG;  // rows per thread
+    static_assert(256 % K == 0 && 16 % RG == 0, "combine tiling");
+    const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws);
+    if (hdr[0] != GDN_OK) return;
+    const Tables tab = tables(p.ws, p.B);
+    constexpr int NVT = V / 16;
+    const int blk = blockIdx.x;
+    const int vt = blk % NVT, bh = blk / NVT;
+    const int h = bh % p.H, b = bh / p.H;
+    const int nseg = nseg_of(tab.nchunk[b], p.L.seglen);
+    if (nseg <= 1) return;
+    __shared__ float s[16][K + 1];
+    const int tid = threadIdx.x, k = tid % K, rg = tid / K;
+    const size_t slot_stride = ((size_t)K * K + (size_t)V * K);
+    float* const slots = reinterpret_cast<float*>(p.ws + p.L.slots);
+    auto slot_phi = [&](int sidx) { return slots + ((size_t)sidx * p.H + h) * slot_stride; };
+    const int s0 = tab.slot0[b];
+    float acc[RPT];
+    {
+        float* const st0 = slot_phi(s0 + nseg - 1) + (size_t)K * K;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            const int v = 16 * vt + rg + RG * j;
+            acc[j] = p.state_in ? p.state_in[(((size_t)b * p.H + h) * V + v) * K + k] : 0.0f;
+            s[rg + RG * j][k] = acc[j];
+            st0[(size_t)v * K + k] = acc[j];
+        }
+    }
+    __syncthreads();
+    for (int sg = 0; sg + 1 < nseg; ++sg) {
+        const float* const phi = slot_phi(s0 + sg);
+        float* const nst = slot_phi(s0 + sg) + (size_t)K * K;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) acc[j] = nst[(size_t)(16 * vt + rg + RG * j) * K + k];
+#pragma unroll 8
+        for (int c = 0; c < K; ++c) {
+            const float pk = phi[(size_t)c * K + k];
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) acc[j] = fmaf(s[rg + RG * j][c], pk, acc[j]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            s[rg + RG * j][k] = acc[j];
+            nst[(size_t)(16 * vt + rg + RG * j) * K + k] = acc[j];
+        }
+        __syncthreads();
+    }
+}
+
+#ifndef GDN_CHUNK_VTW
+#define GDN_CHUNK_VTW 1
+#endif
+constexpr int kValueTilesPerWave = GDN_CHUNK_VTW;  // 16-column value tiles per wave of the main kernel
+
 template <typename T, int K, int V>
 hipError_t launch_kv(ChunkArgs p, hipStream_t stream) {
-    const long long nch = ((long long)p.N + CH - 1) / CH + p.B;
-    const long long par_blocks = nch * p.H;
-    // Column tile of the state kernel: 64 columns share one load of the chunk's operands, 16 columns
-    // give four times the blocks.  Wide tiles win once they still fill every compute unit.
-    const long long wide_blocks = (long long)p.B * p.H * (V / 64);
-    const bool wide = wide_blocks >= 256;
-    const long long seq_blocks = wide ? wide_blocks : (long long)p.B * p.H * (V / 16);
-    if (par_blocks > kMaxBlocks || seq_blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
+    const int sl = p.L.seglen;
+    const long long nch = chunk_bound(p.B, p.N);
+    long long main_units = (long long)p.B * p.H, sum_units = 0;
+    if (sl != INT_MAX) {
+        main_units = (nch / sl + p.B) * p.H;
+        sum_units = (nch / sl) * p.H;
+    }
+    // token rows are addressed through 32-bit buffer offsets within a chunk
+    if ((p.x.sq > (1 << 23)) || (p.x.sk > (1 << 23)) || (p.x.sv > (1 << 23)) || (long long)CH * p.H * V > (1 << 29))
+        return hipErrorInvalidConfiguration;
+    const long long tm_blocks = nch * p.H;
+    const long long comb_blocks = (long long)p.B * p.H * (V / 16);
+    if (main_units > kMaxBlocks || comb_blocks > kMaxBlocks || tm_blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(1024), 0, stream, p);
-    p.n_blocks = (int)par_blocks;
-    hipLaunchKernelGGL((chunk_prep_kernel<T, K, V>), dim3((unsigned)par_blocks), dim3(256), 0, stream, p);
-    p.n_blocks = (int)seq_blocks;
-    if (wide)
-        hipLaunchKernelGGL((chunk_state_kernel<T, K, V, 4>), dim3((unsigned)seq_blocks), dim3(512), 0, stream, p);
+    if (p.N > 0) {
+        p.n_blocks = (int)tm_blocks;
+        hipLaunchKernelGGL((chunk_tmat_kernel<T, K>), dim3((unsigned)tm_blocks), dim3(256), 0, stream, p);
+    }
+    constexpr int VTW = kValueTilesPerWave;
+    constexpr int NT = 64 * (V / (16 * VTW));
+    if (sum_units > 0) {
+        p.n_blocks = (int)sum_units;
+        hipLaunchKernelGGL((chunk_fused_kernel<T, K, V, kSummary, VTW>), dim3((unsigned)sum_units), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((chunk_combine_kernel<K, V>), dim3((unsigned)comb_blocks), dim3(256), 0, stream, p);
+    }
+    p.n_blocks = (int)main_units;
+    if (p.cap > 0)
+        hipLaunchKernelGGL((chunk_fused_kernel<T, K, V, kMainCapture, VTW>), dim3((unsigned)main_units), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((chunk_state_kernel<T, K, V, 1>), dim3((unsigned)seq_blocks), dim3(512), 0, stream, p);
+        hipLaunchKernelGGL((chunk_fused_kernel<T, K, V, kMain, VTW>), dim3((unsigned)main_units), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -900,7 +1036,8 @@ bool chunked_shape_supported(int K, int V, int qkv_dtype) {
 }
 
 size_t chunked_workspace_bytes(int B, int N, int HQ, int H, int K, int V) {
-    return ws_layout(B, N, HQ, H, K, V).total;
+    (void)HQ;
+    return ws_layout(B, N, H, K, V).total;
 }
 
 hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream) {
@@ -916,7 +1053,7 @@ hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream) {
     p.offsets = a.offsets;
     p.dev_status = a.dev_status;
     p.ws = static_cast<char*>(a.workspace);
-    p.L = ws_layout(a.B, a.N, a.HQ, a.H, a.K, a.V);
+    p.L = ws_layout(a.B, a.N, a.H, a.K, a.V);
     p.B = a.B;
     p.N = a.N;
     p.HQ = a.HQ;
@@ -928,6 +1065,10 @@ hipError_t launch_scan_chunked(const ScanLaunch& a, hipStream_t stream) {
     p.flags = a.flags;
     p.scale = a.scale;
     p.n_blocks = 0;
+    p.cap = a.cap;
+    p.counts = a.counts;
+    p.active = a.active;
+    p.capsule = a.capsule;
     if (a.qkv_dtype == GDN_BF16) return launch_t<BF16>(p, stream);
     if (a.qkv_dtype == GDN_F16) return launch_t<F16>(p, stream);
     return hipErrorInvalidValue;
