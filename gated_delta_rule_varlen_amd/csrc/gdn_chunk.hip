@@ -54,7 +54,10 @@ constexpr int CH = 64;  // tokens per chunk
 constexpr int NW = 4;   // waves per block
 // LDS rows holding MFMA operands are padded by 16 bytes so that the 16 rows a fragment read touches
 // do not all start on the same banks.
-constexpr int PAD = 8;  // 16-bit elements
+// Row pitches (16-bit elements) of the LDS tiles: K + kPadRow for k/q rows, CH + kPadT for 64-token
+// rows.  An odd number of 16-byte units per row makes the 16 x 16 fragment reads 2-way bank
+// conflicted on gfx950; these pads give an even count and conflict-free reads.
+constexpr int kPadRow = 16, kPadT = 16;
 constexpr int NTF = 6;  // T fragments per chunk: (token tile, 32-block) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -140,6 +143,15 @@ __device__ __forceinline__ void unpack8(u32x4 raw, float (&v)[8]) {
 }
 __device__ __forceinline__ uint16_t half_of(u32x4 w, int e) {
     return (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+}
+// 4 x 4 transpose of 32-bit words across the four 16-lane rows of the wave: row r receives word r
+// of rows 0..3 (out[j] = word r of row j), by two cross-half and two cross-row swaps
+__device__ __forceinline__ u32x4 transpose_rows4(u32x4 x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    return u32x4{c[0], c[1], d[0], d[1]};
 }
 // ---- workspace ----------------------------------------------------------------------------------
 // int32 header: [0] status, [1] main units, [2] summary units, [3] chunks, then the tables at +16:
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     using TS = typename T::storage;
     constexpr int LPT = K / 8, TPI = 64 / LPT, NI = 16 / TPI;
     __shared__ __align__(16) union {
-        uint16_t kn[CH][K + PAD];  // normalised k rows, until A is formed
+        uint16_t kn[CH][K + kPadRow];  // normalised k rows, until A is formed
         float tm[CH][CH + 4];      // T (fp32)
     } r0;
     __shared__ __align__(16) float am[CH][CH + 4];
@@ -404,7 +416,7 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
             f32x4 a = zero4();
 #pragma unroll
             for (int kk = 0; kk < K; kk += 32)
-                a = mma_bf16(frag(&r0.kn[16 * it][kk], K + PAD, lane), frag(&r0.kn[16 * w][kk], K + PAD, lane), a);
+                a = mma_bf16(frag(&r0.kn[16 * it][kk], K + kPadRow, lane), frag(&r0.kn[16 * w][kk], K + kPadRow, lane), a);
             const int ia = 16 * it + 4 * g;
             const f32x4 g_ia = *reinterpret_cast<const f32x4*>(&s_gam[ia]);
             const f32x4 b_ia = *reinterpret_cast<const f32x4*>(&s_beta[ia]);
@@ -486,31 +498,39 @@ __device__ __forceinline__ int split_key_slot(int pc) {  // slot of keys 8pc..8p
     const int a = pc & 3;
     return 32 * (pc >> 2) + 16 * (a & 1) + 4 * (a >> 1);
 }
+#ifndef GDN_TSWZ
+#define GDN_TSWZ 4
+#endif
+constexpr int kSwz = GDN_TSWZ;
 // element offset of token t in row idx of a transposed tile
 __device__ __forceinline__ int tpos(int idx, int t) {
     const int q = (t >> 2) & 7;
     const int unit = 4 * (t >> 5) + (q & 3);
-    return 8 * (unit ^ ((idx >> 3) & 7)) + 4 * (q >> 2) + (t & 3);
+    return 8 * (unit ^ ((idx >> kSwz) & 7)) + 4 * (q >> 2) + (t & 3);
 }
 // split fragment of a transposed tile: rows idx0 + l%16, the tokens of 32-block jj
 __device__ __forceinline__ bf16x8 frag_t(const uint16_t* tile, int ld, int idx0, int jj, int lane) {
     const int idx = idx0 + (lane & 15);
-    return *reinterpret_cast<const bf16x8*>(tile + idx * ld + 8 * ((4 * jj + (lane >> 4)) ^ ((idx >> 3) & 7)));
+    return *reinterpret_cast<const bf16x8*>(tile + idx * ld + 8 * ((4 * jj + (lane >> 4)) ^ ((idx >> kSwz) & 7)));
 }
 
-template <int K, int V, bool Q>
+// kn, qn and vt are last read before a chunk's middle barrier and are written for the next chunk
+// after it, so one copy serves; kt and the per-token factors are read after that barrier and have two.
+template <int K>
 struct ChunkBuf {
-    uint16_t kn[CH][K + PAD];
-    uint16_t qn[Q ? CH : 1][K + PAD];
-    uint16_t kt[K][CH + PAD];
-    uint16_t vt[V][CH + PAD];
+    uint16_t kt[K][CH + kPadT];
     // per token: G; b; scale e^G; b e^G / |k|; e^{G_C - G} / |k|; 1/|k|; 1/|q|; and e^{G_C}
     float gam[CH], beta[CH], eg[CH], bx[CH], ud[CH], rk[CH], rq[CH], gc[4];
 };
 template <int K, int V, bool SUMMARY>
 struct FusedLds {
-    ChunkBuf<K, V, !SUMMARY> buf[2];
-    uint16_t pb[SUMMARY ? 1 : CH][CH + PAD];
+    uint16_t kn[CH][K + kPadRow];
+    uint16_t qn[SUMMARY ? 1 : CH][K + kPadRow];
+    uint16_t vt[V][CH + kPadT];
+    uint16_t tf[NTF][512];  // T fragments (lane order), read before the middle barrier
+    ChunkBuf<K> buf[2];
+    uint16_t pb[SUMMARY ? 1 : CH][CH + kPadT];
+    uint16_t ob[SUMMARY ? 1 : CH][V + 8];  // output rows of the previous chunk, stored whole
 };
 
 // MODE: kMain, kMainCapture (also records the first tokens of each sequence) or kSummary.
@@ -619,10 +639,12 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
     constexpr int RSRC = 0x00020000;  // raw buffer resource (gfx9 family)
 
     // Rows of one chunk (range-checked buffer loads: rows at or past the chunk's end read as zero),
-    // its T fragments and the tokens' G, b and 1/|k| (lane = token).
+    // T fragments w, w + NWV, .. (one copy per block; fragments past the last read as zero) and, in
+    // wave 0 only, the tokens' G, b and 1/|k| (lane = token; the other waves' range is empty).
+    constexpr int NTFW = (NTF + NWV - 1) / NWV;
     struct Rows {
         u32x4 k[NI], q[SUMMARY ? 1 : NI], v[NV];
-        u32x4 tf[NTF];
+        u32x4 tf[NTFW];
         float gam, beta, rk;
     };
     auto load_rows = [&](int c, Rows& R) {
@@ -654,15 +676,23 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
             R.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                    rv, (ti * (int)p.x.sv + 8 * pv) * (int)sizeof(TS), 0, 0));
         }
+        const __amdgpu_buffer_rsrc_t rt =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(tfr + ch * NTF * 512), 0, NTF * 1024, RSRC);
 #pragma unroll
-        for (int f = 0; f < NTF; ++f) R.tf[f] = *reinterpret_cast<const u32x4*>(tfr + (ch * NTF + f) * 512 + 8 * lane);
-        R.gam = gts[ch * 3 * CH + lane];
-        R.beta = gts[ch * 3 * CH + CH + lane];
-        R.rk = gts[ch * 3 * CH + 2 * CH + lane];
+        for (int j = 0; j < NTFW; ++j)
+            R.tf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, ((w + NWV * j) * 512 + 8 * lane) * 2, 0, 0));
+        const __amdgpu_buffer_rsrc_t rgt =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(gts + ch * 3 * CH), 0, w == 0 ? 3 * CH * 4 : 0, RSRC);
+        R.gam = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgt, lane * 4, 0, 0));
+        R.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgt, (CH + lane) * 4, 0, 0));
+        R.rk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgt, (2 * CH + lane) * 4, 0, 0));
     };
     // raw rows, transposes, norms and per-token factors of chunk c into buffer Bf
-    auto stage = [&](int c, const Rows& R, ChunkBuf<K, V, !SUMMARY>& Bf) {
+    auto stage = [&](int c, const Rows& R, ChunkBuf<K>& Bf) {
         const bool cap_chunk = CAPTURE && c == 0 && captured > 0;
+#pragma unroll
+        for (int j = 0; j < NTFW; ++j)
+            if (w + NWV * j < NTF) *reinterpret_cast<u32x4*>(&sm.tf[w + NWV * j][8 * lane]) = R.tf[j];
         if (w == 0) {
             const float gC = __shfl(R.gam, CH - 1);
             const float eg = fexp(R.gam);
@@ -682,11 +712,22 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
         for (int i = 0; i < NI; ++i) {
             const int ti = RPW * w + TPI * i + tsub;
             const u32x4 kb = to_bf16x8<T>(R.k[i]);
-            *reinterpret_cast<u32x2*>(&Bf.kn[ti][ks0]) = u32x2{kb[0], kb[1]};
-            *reinterpret_cast<u32x2*>(&Bf.kn[ti][ks0 + 8]) = u32x2{kb[2], kb[3]};
-            const int tp = tpos(8 * pc, ti);
+            *reinterpret_cast<u32x2*>(&sm.kn[ti][ks0]) = u32x2{kb[0], kb[1]};
+            *reinterpret_cast<u32x2*>(&sm.kn[ti][ks0 + 8]) = u32x2{kb[2], kb[3]};
+            if constexpr (TPI == 4) {
+                // lanes pc, pc + 16, pc + 32, pc + 48 hold four consecutive tokens: after the
+                // transpose, row tsub has keys 8 pc + 2 tsub and + 1 of all four (8 bytes per key)
+                const u32x4 y = transpose_rows4(kb);
+                const int r0 = 8 * pc + 2 * tsub, t0 = RPW * w + TPI * i;
+                *reinterpret_cast<u32x2*>(&Bf.kt[r0][tpos(r0, t0)]) =
+                    u32x2{(y[0] & 0xffffu) | (y[1] << 16), (y[2] & 0xffffu) | (y[3] << 16)};
+                *reinterpret_cast<u32x2*>(&Bf.kt[r0 + 1][tpos(r0 + 1, t0)]) =
+                    u32x2{(y[0] >> 16) | (y[1] & 0xffff0000u), (y[2] >> 16) | (y[3] & 0xffff0000u)};
+            } else {
+                const int tp = tpos(8 * pc, ti);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Bf.kt[8 * pc + e][tp] = half_of(kb, e);
+                for (int e = 0; e < 8; ++e) Bf.kt[8 * pc + e][tp] = half_of(kb, e);
+            }
             if constexpr (!SUMMARY) {
                 if (cap_chunk && ti < captured && h % p.G == 0) {
                     const float rk = rsqrtf(group_sum<LPT>(sumsq8<T>(R.k[i])) + 1e-12f);
@@ -696,8 +737,8 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
                     for (int e = 0; e < 8; ++e) crow.k(ti, kh)[8 * pc + e] = kf[e] * rk;
                 }
                 const u32x4 qb = to_bf16x8<T>(R.q[i]);
-                *reinterpret_cast<u32x2*>(&Bf.qn[ti][ks0]) = u32x2{qb[0], qb[1]};
-                *reinterpret_cast<u32x2*>(&Bf.qn[ti][ks0 + 8]) = u32x2{qb[2], qb[3]};
+                *reinterpret_cast<u32x2*>(&sm.qn[ti][ks0]) = u32x2{qb[0], qb[1]};
+                *reinterpret_cast<u32x2*>(&sm.qn[ti][ks0 + 8]) = u32x2{qb[2], qb[3]};
                 const float rq = rsqrtf(group_sum<LPT>(sumsq8<T>(R.q[i])) + 1e-12f);
                 if (pc == 0) Bf.rq[ti] = rq;
             }
@@ -705,9 +746,18 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int ti = RPW * w + TPV * i + vsub;
-            const int tp = tpos(8 * pv, ti);
+            if constexpr (TPV == 4) {
+                const u32x4 y = transpose_rows4(R.v[i]);
+                const int r0 = 8 * pv + 2 * vsub, t0 = RPW * w + TPV * i;
+                *reinterpret_cast<u32x2*>(&sm.vt[r0][tpos(r0, t0)]) =
+                    u32x2{(y[0] & 0xffffu) | (y[1] << 16), (y[2] & 0xffffu) | (y[3] << 16)};
+                *reinterpret_cast<u32x2*>(&sm.vt[r0 + 1][tpos(r0 + 1, t0)]) =
+                    u32x2{(y[0] >> 16) | (y[1] & 0xffff0000u), (y[2] >> 16) | (y[3] & 0xffff0000u)};
+            } else {
+                const int tp = tpos(8 * pv, ti);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Bf.vt[8 * pv + e][tp] = half_of(R.v[i], e);
+                for (int e = 0; e < 8; ++e) sm.vt[8 * pv + e][tp] = half_of(R.v[i], e);
+            }
         }
     };
 
@@ -718,15 +768,29 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
         }
     }
     TS* const outp = static_cast<TS*>(p.out);
+    // Output rows of chunk c (written to LDS by its O step, read after the next barrier): wave w
+    // stores token rows RPW w .. + RPW-1 whole, 16 bytes a lane; rows at or past the chunk's end
+    // are dropped by the range-checked buffer (so every store is issued and the waits stay exact)
+    auto flush_out = [&](int c) {
+        if constexpr (!SUMMARY) {
+            const int t0 = seq_start + c * CH, n = min(CH, len - c * CH);
+            const __amdgpu_buffer_rsrc_t orsrc =
+                __builtin_amdgcn_make_buffer_rsrc(outp + (size_t)t0 * p.H * V, 0, n * p.H * V * (int)sizeof(TS), RSRC);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int ti = RPW * w + TPV * i + vsub;
+                const u32x4 val = *reinterpret_cast<const u32x4*>(&sm.ob[ti][8 * pv]);
+                __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, ((ti * p.H + h) * V + 8 * pv) * (int)sizeof(TS), 0, 0);
+            }
+        }
+    };
 
     // One chunk; Bf holds it, Bn receives the next one (the two buffers alternate)
     Rows R;
-    auto step = [&](int c, ChunkBuf<K, V, !SUMMARY>& Bf, ChunkBuf<K, V, !SUMMARY>& Bn) {
+    auto step = [&](int c, ChunkBuf<K>& Bf, ChunkBuf<K>& Bn) {
         const int t0 = seq_start + c * CH, n = min(CH, len - c * CH);
         const bool cap_chunk = CAPTURE && c == 0 && captured > 0;
-        bf16x8 tf[NTF];
-#pragma unroll
-        for (int f = 0; f < NTF; ++f) tf[f] = __builtin_bit_cast(bf16x8, R.tf[f]);
+        if (c > cb) flush_out(c - 1);
         if (c + 1 < ce) load_rows(c + 1, R);  // in flight during this chunk
 
         // ---- P = M o (Q K^T) / (|q_i| |k_j|): the ten nonzero 16 x 16 blocks (it, jt <= it), block n by
@@ -740,7 +804,7 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
                 f32x4 pt = zero4();
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    pt = mma_bf16(frag(&Bf.kn[16 * jt][32 * kk], K + PAD, lane), frag(&Bf.qn[16 * it][32 * kk], K + PAD, lane), pt);
+                    pt = mma_bf16(frag(&sm.kn[16 * jt][32 * kk], K + kPadRow, lane), frag(&sm.qn[16 * it][32 * kk], K + kPadRow, lane), pt);
                 const int i = 16 * it + l16, j0 = 16 * jt + 4 * g;
                 const float g_i = Bf.gam[i], q_i = Bf.rq[i];
                 const f32x4 g_j = *reinterpret_cast<const f32x4*>(&Bf.gam[j0]);
@@ -772,11 +836,11 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
             }
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const bf16x8 kf = frag(&Bf.kn[16 * it][32 * kk], K + PAD, lane);
+                const bf16x8 kf = frag(&sm.kn[16 * it][32 * kk], K + kPadRow, lane);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) ks[it][ct] = mma_bf16(kf, sbf[kk][ct], ks[it][ct]);
                 if constexpr (!SUMMARY) {
-                    const bf16x8 qf = frag(&Bf.qn[16 * it][32 * kk], K + PAD, lane);
+                    const bf16x8 qf = frag(&sm.qn[16 * it][32 * kk], K + kPadRow, lane);
 #pragma unroll
                     for (int ct = 0; ct < VTW; ++ct) oq[it][ct] = mma_bf16(sbf[kk][ct], qf, oq[it][ct]);
                 }
@@ -791,7 +855,7 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
 #pragma unroll
             for (int ct = 0; ct < VTW; ++ct) {
                 const int cc = col_of(ct);
-                const u32x2 vr = *reinterpret_cast<const u32x2*>(&Bf.vt[cc][tpos(cc, i0)]);
+                const u32x2 vr = *reinterpret_cast<const u32x2*>(&sm.vt[cc][tpos(cc, i0)]);
                 const float vv[4] = {to_f32<T>((uint16_t)(vr.x & 0xffffu)), to_f32<T>((uint16_t)(vr.x >> 16)),
                                      to_f32<T>((uint16_t)(vr.y & 0xffffu)), to_f32<T>((uint16_t)(vr.y >> 16))};
 #pragma unroll
@@ -805,6 +869,9 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
         // U = T R (T lower triangular: token tiles 0 and 1 need only the first 32-block)
         f32x4 ua[4][NCT];
         {
+            bf16x8 tf[NTF];
+#pragma unroll
+            for (int f = 0; f < NTF; ++f) tf[f] = *reinterpret_cast<const bf16x8*>(&sm.tf[f][8 * lane]);
             bf16x8 rb[2][NCT];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
@@ -821,25 +888,23 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
                 for (int ct = 0; ct < NCT; ++ct) ua[it][ct] = mma_bf16(tf[f], rb[jj][ct], ua[it][ct]);
             }
         }
+        // P is complete, and kn, qn and vt of this chunk have been read for the last time (the next
+        // chunk's rows are staged into them after the state update)
+        __syncthreads();
         if constexpr (!SUMMARY) {
-            __syncthreads();  // P complete
             // O^T = (S0 Q^T) diag(scale e^G / |q|) + scale U^T P^T (the first factor is eg / |q|).
-            // Lane: value columns 16 w + 4g .. +3 of token 16 it + l%16, stored as 8 bytes; rows at or
-            // past the chunk's end are dropped by the range-checked buffer (so every store is issued
-            // and the waits stay exact)
+            // Lane: value columns 16 w + 4g .. +3 of token 16 it + l%16, into the LDS output rows
             bf16x8 ub[2][VTW];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                 for (int ct = 0; ct < VTW; ++ct) ub[jj][ct] = pack_acc(ua[2 * jj][ct], ua[2 * jj + 1][ct]);
-            const __amdgpu_buffer_rsrc_t orsrc =
-                __builtin_amdgcn_make_buffer_rsrc(outp + (size_t)t0 * p.H * V, 0, n * p.H * V * (int)sizeof(TS), RSRC);
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int i = 16 * it + l16;
-                const bf16x8 p0 = frag(&sm.pb[16 * it][0], CH + PAD, lane);
+                const bf16x8 p0 = frag(&sm.pb[16 * it][0], CH + kPadT, lane);
                 bf16x8 p1;
-                if (it >= 2) p1 = frag(&sm.pb[16 * it][32], CH + PAD, lane);
+                if (it >= 2) p1 = frag(&sm.pb[16 * it][32], CH + kPadT, lane);
                 const float qf = Bf.eg[i] * Bf.rq[i];
 #pragma unroll
                 for (int ct = 0; ct < VTW; ++ct) {
@@ -847,9 +912,8 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
                     if (it >= 2) o = mma_bf16(ub[1][ct], p1, o);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) o[r] = fmaf(oq[it][ct][r], qf, p.scale * o[r]);
-                    const u32x2 piece = u32x2{pack2<T>(o[0], o[1]), pack2<T>(o[2], o[3])};
-                    const int off = (((16 * it + l16) * p.H + h) * V + 16 * (VTW * w + ct) + 4 * g) * (int)sizeof(TS);
-                    __builtin_amdgcn_raw_buffer_store_b64(piece, orsrc, off, 0, 0);
+                    *reinterpret_cast<u32x2*>(&sm.ob[16 * it + l16][16 * (VTW * w + ct) + 4 * g]) =
+                        u32x2{pack2<T>(o[0], o[1]), pack2<T>(o[2], o[3])};
                 }
             }
             if (cap_chunk) {  // delta of the recorded tokens: rows of U
@@ -873,8 +937,8 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
             const float gC = Bf.gc[0];
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const bf16x8 a0 = frag_t(&Bf.kt[0][0], CH + PAD, 16 * kt, 0, lane);
-                const bf16x8 a1 = frag_t(&Bf.kt[0][0], CH + PAD, 16 * kt, 1, lane);
+                const bf16x8 a0 = frag_t(&Bf.kt[0][0], CH + kPadT, 16 * kt, 0, lane);
+                const bf16x8 a1 = frag_t(&Bf.kt[0][0], CH + kPadT, 16 * kt, 1, lane);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     f32x4 s = sacc[kt][ct] * gC;
@@ -900,6 +964,7 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
         const int bi = (c - cb) & 1;
         step(c, sm.buf[bi], sm.buf[bi ^ 1]);
     }
+    if (cb < ce) flush_out(ce - 1);  // after the last step's barrier
 
     // ---- leaving state
     if constexpr (SUMMARY) {
@@ -926,24 +991,30 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
 }
 
 // ---- combine: S_start of every segment, in order ------------------------------------------------
-// One block per (sequence, head, 16 value rows); a thread owns key column k = t % K of rows
+// One block per (sequence, head, 8 value rows); a thread owns key column k = t % K of rows
 // t / K + (256 / K) j.  S_start(s+1) = S_start(s) Phi_s + N_s  (rows v: S[v][k] = sum_c S[v][c]
-// phi[c][k] + N[v][k]), in fp32.
+// phi[c][k] + N[v][k]), in fp32.  Phi is staged through LDS in tiles of CT rows; the next tile (and
+// the next N rows) are loaded into registers while the current one is used.
 template <int K, int V>
 __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs p) {
-    constexpr int RG = 256 / K;   // row groups
-    constexpr int RPT = 16 / RG;  // rows per thread
-    static_assert(256 % K == 0 && 16 % RG == 0, "combine tiling");
+    constexpr int VR = 8;          // value rows per block
+    constexpr int RG = 256 / K;    // row groups
+    constexpr int RPT = VR / RG;   // rows per thread
+    constexpr int CT = K * K <= 16384 ? K : 16384 / K;  // Phi rows per tile
+    constexpr int NCT = K / CT;
+    constexpr int NLD = CT * K / (4 * 256);  // 16-byte loads per thread per tile
+    static_assert(256 % K == 0 && VR % RG == 0 && NLD >= 1 && V % VR == 0, "combine tiling");
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws);
     if (hdr[0] != GDN_OK) return;
     const Tables tab = tables(p.ws, p.B);
-    constexpr int NVT = V / 16;
+    constexpr int NVT = V / VR;
     const int blk = blockIdx.x;
     const int vt = blk % NVT, bh = blk / NVT;
     const int h = bh % p.H, b = bh / p.H;
     const int nseg = nseg_of(tab.nchunk[b], p.L.seglen);
     if (nseg <= 1) return;
-    __shared__ float s[16][K + 1];
+    __shared__ __align__(16) float phs[CT * K];
+    __shared__ __align__(16) float s[VR][K];
     const int tid = threadIdx.x, k = tid % K, rg = tid / K;
     const size_t slot_stride = ((size_t)K * K + (size_t)V * K);
     float* const slots = reinterpret_cast<float*>(p.ws + p.L.slots);
@@ -954,31 +1025,55 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs p) {
         float* const st0 = slot_phi(s0 + nseg - 1) + (size_t)K * K;
 #pragma unroll
         for (int j = 0; j < RPT; ++j) {
-            const int v = 16 * vt + rg + RG * j;
+            const int v = VR * vt + rg + RG * j;
             acc[j] = p.state_in ? p.state_in[(((size_t)b * p.H + h) * V + v) * K + k] : 0.0f;
             s[rg + RG * j][k] = acc[j];
             st0[(size_t)v * K + k] = acc[j];
         }
     }
-    __syncthreads();
-    for (int sg = 0; sg + 1 < nseg; ++sg) {
-        const float* const phi = slot_phi(s0 + sg);
-        float* const nst = slot_phi(s0 + sg) + (size_t)K * K;
+    f32x4 pre[NLD];
+    float npre[RPT];
+    auto fetch = [&](int sg, int ct) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(slot_phi(s0 + sg) + (size_t)ct * CT * K);
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) acc[j] = nst[(size_t)(16 * vt + rg + RG * j) * K + k];
-#pragma unroll 8
-        for (int c = 0; c < K; ++c) {
-            const float pk = phi[(size_t)c * K + k];
+        for (int i = 0; i < NLD; ++i) pre[i] = src[tid + 256 * i];
+        if (ct == 0) {
+            const float* const nst = slot_phi(s0 + sg) + (size_t)K * K;
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) acc[j] = fmaf(s[rg + RG * j][c], pk, acc[j]);
+            for (int j = 0; j < RPT; ++j) npre[j] = nst[(size_t)(VR * vt + rg + RG * j) * K + k];
         }
-        __syncthreads();
+    };
+    fetch(0, 0);
+    for (int sg = 0; sg + 1 < nseg; ++sg) {
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) acc[j] = npre[j];
+        for (int ct = 0; ct < NCT; ++ct) {
+            __syncthreads();  // the previous tile (and the rows of s) have been read
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) reinterpret_cast<f32x4*>(phs)[tid + 256 * i] = pre[i];
+            __syncthreads();
+            if (ct + 1 < NCT) fetch(sg, ct + 1);
+            else if (sg + 2 < nseg) fetch(sg + 1, 0);
+#pragma unroll 4
+            for (int c = 0; c < CT; c += 4) {
+                float pk[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pk[e] = phs[(c + e) * K + k];
+#pragma unroll
+                for (int j = 0; j < RPT; ++j) {
+                    const f32x4 sv = *reinterpret_cast<const f32x4*>(&s[rg + RG * j][ct * CT + c]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[j] = fmaf(sv[e], pk[e], acc[j]);
+                }
+            }
+        }
+        __syncthreads();  // every thread is done with s
+        float* const nst = slot_phi(s0 + sg) + (size_t)K * K;
 #pragma unroll
         for (int j = 0; j < RPT; ++j) {
             s[rg + RG * j][k] = acc[j];
-            nst[(size_t)(16 * vt + rg + RG * j) * K + k] = acc[j];
+            nst[(size_t)(VR * vt + rg + RG * j) * K + k] = acc[j];
         }
-        __syncthreads();
     }
 }
 
@@ -1000,7 +1095,7 @@ hipError_t launch_kv(ChunkArgs p, hipStream_t stream) {
     if ((p.x.sq > (1 << 23)) || (p.x.sk > (1 << 23)) || (p.x.sv > (1 << 23)) || (long long)CH * p.H * V > (1 << 29))
         return hipErrorInvalidConfiguration;
     const long long tm_blocks = nch * p.H;
-    const long long comb_blocks = (long long)p.B * p.H * (V / 16);
+    const long long comb_blocks = (long long)p.B * p.H * (V / 8);
     if (main_units > kMaxBlocks || comb_blocks > kMaxBlocks || tm_blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(1024), 0, stream, p);
     if (p.N > 0) {
