@@ -284,9 +284,10 @@ def scan_varlen_capture(qkv: torch.Tensor, offsets: torch.Tensor, *, cap: int, c
                         K: int, V: int, active=None, capsule=None, a=None, b=None, A_log=None, dt_bias=None,
                         state_in=None, qk_prep=None, gb_prep=None, l2norm=True, softplus=True, sigmoid=True,
                         scale: float = 0.0, path: str = "auto", out=None, state_out=None, write_state: bool = True,
-                        dev_status=None, retrieve: bool = True):
+                        workspace=None, dev_status=None, retrieve: bool = True):
     """scan_varlen that also records g, k^ and delta of the first min(counts[b], cap, len) tokens of
-    each sequence (gdn_scan_varlen_capture); active int32 [1] or None.
+    each sequence (gdn_scan_varlen_capture); active int32 [1] or None.  The workspace is allocated as
+    in scan_varlen when absent.
     Returns (out, state_out, capsule [B, cap*(H + HQ*K + H*V)] fp32, path name that ran)."""
     N = qkv.shape[0]
     B = offsets.numel() - 1
@@ -297,13 +298,20 @@ def scan_varlen_capture(qkv: torch.Tensor, offsets: torch.Tensor, *, cap: int, c
     if capsule is None:
         capsule = torch.empty((B, capsule_width(cap, HQ=HQ, H=H, K=K, V=V)), dtype=torch.float32, device=qkv.device)
     d = _scan_desc(qkv, B, HQ, H, K, V, a if a is not None else b, l2norm, softplus, sigmoid, scale, path, retrieve)
+    if workspace is None and path in ("auto", "chunk"):
+        n = ctypes.c_size_t(0)
+        _check(lib().gdn_scan_workspace_bytes(ctypes.byref(d), ctypes.byref(n)), "gdn_scan_workspace_bytes")
+        if n.value > 0:
+            workspace = torch.empty(int(n.value), dtype=torch.uint8, device=qkv.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     used = ctypes.c_int32(-1)
     st = lib().gdn_scan_varlen_capture(ctypes.byref(d), _ptr(qkv, "qkv"), _ptr(qk_prep, "qk_prep"),
                                        _ptr(gb_prep, "gb_prep"), _ptr(a, "a"), _ptr(b, "b"), _ptr(A_log, "A_log"),
                                        _ptr(dt_bias, "dt_bias"), _ptr(state_in, "state_in"), _ptr(out, "out"),
                                        _ptr(state_out, "state_out"), _ptr(offsets, "offsets"), int(cap),
-                                       _ptr(counts, "counts"), _ptr(active, "active"), _ptr(capsule, "capsule"), None,
-                                       0, _ptr(dev_status, "dev_status"), ctypes.byref(used), _stream(qkv.device))
+                                       _ptr(counts, "counts"), _ptr(active, "active"), _ptr(capsule, "capsule"),
+                                       _ptr(workspace, "workspace"), ws_bytes, _ptr(dev_status, "dev_status"),
+                                       ctypes.byref(used), _stream(qkv.device))
     _check(st, "gdn_scan_varlen_capture")
     return out, state_out, capsule, PATH_NAMES.get(used.value, str(used.value))
 

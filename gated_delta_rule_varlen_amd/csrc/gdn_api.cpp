@@ -88,10 +88,11 @@ gdn_status strided_streams(const gdn_scan_desc* d, const gdn_qkv_streams* s, boo
 // the softplus gate), and it relies on normalised keys for a well-conditioned (I + A); it computes
 // the gates and norms itself, so it runs on fused inputs only; its algebra is that of the rules
 // with the retrieval term and one decay per head.  Built for bf16/fp16 I/O with K = V = 64 or 128.
-// Capture is recorded by the token-sequential paths only.  A call without tokens reads no decays
-// (its chunked form only copies the initial states), so there the decay input may be absent.
-bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay, bool capture) {
-    return !prepared && (has_decay || d->N == 0) && !capture && (d->flags & GDN_SOFTPLUS) && (d->flags & GDN_L2NORM) &&
+// It records a capture from its first chunk, so at most 64 slots.  A call without tokens reads no
+// decays (its chunked form only copies the initial states), so there the decay input may be absent.
+bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay, int cap) {
+    return !prepared && (has_decay || d->N == 0) && cap <= gdn::kChunkTokens && (d->flags & GDN_SOFTPLUS) &&
+           (d->flags & GDN_L2NORM) &&
            !(d->flags & (GDN_NO_RETRIEVE | GDN_GATE_PER_KEY)) &&
            gdn::chunked_shape_supported(d->K, d->V, d->qkv_dtype);
 }
@@ -99,10 +100,10 @@ bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay, bool 
 // AUTO: DECODE for at most kDecodeShortTokens tokens per sequence on average (single tokens and
 // short blocks stream the state once); CHUNK when eligible, the average sequence fills at least one
 // chunk of 64 tokens and the workspace suffices; SEQ otherwise.
-int resolve_path(const gdn_scan_desc* d, bool prepared, bool has_decay, bool capture, size_t ws_bytes) {
+int resolve_path(const gdn_scan_desc* d, bool prepared, bool has_decay, int cap, size_t ws_bytes) {
     if (d->path != GDN_PATH_AUTO) return d->path;
     if ((long long)d->N <= (long long)gdn::kDecodeShortTokens * d->B) return GDN_PATH_DECODE;
-    if (chunk_eligible(d, prepared, has_decay, capture) && (long long)d->N >= 64ll * d->B &&
+    if (chunk_eligible(d, prepared, has_decay, cap) && (long long)d->N >= 64ll * d->B &&
         ws_bytes >= gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
         return GDN_PATH_CHUNK;
     return GDN_PATH_SEQ;
@@ -297,11 +298,10 @@ gdn_status scan_call(const gdn_scan_desc* d, const gdn::TokenStreams& x, const f
     if (misaligned(qk_prep) || misaligned(gb_prep) || misaligned(state_in) || misaligned(out) ||
         misaligned(state_out) || misaligned(workspace))
         return GDN_ERR_ALIGN;
-    const bool capture = cap > 0;
     const bool has_ws = workspace != nullptr || scratch != nullptr;
-    const int path = resolve_path(d, prepared, a != nullptr, capture, has_ws ? ws_bytes : 0);
+    const int path = resolve_path(d, prepared, a != nullptr, cap, has_ws ? ws_bytes : 0);
     if (path == GDN_PATH_CHUNK) {
-        if (!chunk_eligible(d, prepared, a != nullptr, capture)) return GDN_ERR_UNSUPPORTED;
+        if (!chunk_eligible(d, prepared, a != nullptr, cap)) return GDN_ERR_UNSUPPORTED;
         if (!has_ws || ws_bytes < gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
             return GDN_ERR_WORKSPACE;
         if (scratch != nullptr) {
@@ -414,7 +414,6 @@ gdn_status gdn_scan_varlen_capture(const gdn_scan_desc* d, const void* qkv, cons
     if ((long long)cap * ((long long)d->H + (long long)d->HQ * d->K + (long long)d->H * d->V) > INT_MAX)
         return GDN_ERR_OVERFLOW;
     if (misaligned(capsule)) return GDN_ERR_ALIGN;
-    if (d->path == GDN_PATH_CHUNK) return GDN_ERR_UNSUPPORTED;
     if (d->N > 0 && qkv == nullptr) return GDN_ERR_NULL;
     gdn::TokenStreams x;
     gdn_status ps = packed_streams(d, qkv, &x);

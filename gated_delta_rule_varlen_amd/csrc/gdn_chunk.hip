@@ -50,7 +50,7 @@
 namespace gdn {
 namespace {
 
-constexpr int CH = 64;  // tokens per chunk
+constexpr int CH = kChunkTokens;  // tokens per chunk
 constexpr int NW = 4;   // waves per block
 // LDS rows holding MFMA operands are padded by 16 bytes so that the 16 rows a fragment read touches
 // do not all start on the same banks.
@@ -703,10 +703,10 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
             Bf.ud[lane] = fexp(gC - R.gam) * R.rk;
             Bf.rk[lane] = R.rk;
             if (lane == 0) Bf.gc[0] = fexp(gC);
-            if (cap_chunk && lane < captured) {
-                const float gp = lane > 0 ? __shfl(R.gam, lane - 1) : 0.0f;
-                *crow.g(lane, h) = expf(R.gam - gp);
-            }
+            // the previous token's G, read by the whole wave (a lane shuffle from an inactive lane
+            // would read zero)
+            const float gprev = __shfl(R.gam, (lane + CH - 1) & (CH - 1));
+            if (cap_chunk && lane < captured) *crow.g(lane, h) = expf(R.gam - (lane > 0 ? gprev : 0.0f));
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -916,12 +916,14 @@ __global__ __launch_bounds__(64 * (V / (16 * VTW))) void chunk_fused_kernel(Chun
                         u32x2{pack2<T>(o[0], o[1]), pack2<T>(o[2], o[3])};
                 }
             }
-            if (cap_chunk) {  // delta of the recorded tokens: rows of U
+            if (cap_chunk) {  // delta of the recorded tokens (at most one chunk): rows of U
 #pragma unroll
-                for (int ct = 0; ct < VTW; ++ct)
+                for (int it = 0; it < 4; ++it)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (4 * g + r < captured) crow.d(4 * g + r, h)[col_of(ct)] = ua[0][ct][r];
+                    for (int ct = 0; ct < VTW; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (16 * it + 4 * g + r < captured) crow.d(16 * it + 4 * g + r, h)[col_of(ct)] = ua[it][ct][r];
             }
         }
         // S0^T <- e^{G_C} S0^T + K^T diag(e^{G_C - G} / |k|) U

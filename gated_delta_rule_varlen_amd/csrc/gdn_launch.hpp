@@ -123,6 +123,9 @@ gdn_status scan_varlen_scratch(const gdn_scan_desc* d, const void* qkv, const fl
 // takes DECODE while the average sequence is no longer than this.
 constexpr int kDecodeShortTokens = 8;
 
+// Tokens per chunk of the chunked form (it records a capture from a sequence's first chunk).
+constexpr int kChunkTokens = 64;
+
 // Limits of the launch grids (checked by the entry points before launching).
 constexpr long long kMaxBlocks = (1ll << 31) - 1;
 

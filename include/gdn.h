@@ -278,8 +278,10 @@ gdn_status gdn_scan_varlen_strided(const gdn_scan_desc *desc, const gdn_qkv_stre
  *   counts     [B] int32 device, required
  *   active     [1] int32 device, NULL = always active
  *   capsule    [B, cap*(H + HQ*K + H*V)] fp32 device, required, 16-byte aligned
- * Recorded by the DECODE and SEQ paths; AUTO never selects CHUNK for a capture and an explicit
- * GDN_PATH_CHUNK is GDN_ERR_UNSUPPORTED.  Malformed offsets write nothing.
+ * Recorded by every path.  CHUNK records from a sequence's first chunk of 64 tokens, so it takes
+ * cap <= 64 (a larger cap sends AUTO to SEQ, and an explicit GDN_PATH_CHUNK is
+ * GDN_ERR_UNSUPPORTED); its delta slots carry the chunked form's rounding (bf16 operands).
+ * Malformed offsets write nothing.
  * ---------------------------------------------------------------------------------------------- */
 gdn_status gdn_scan_varlen_capture(const gdn_scan_desc *desc, const void *qkv, const float *qk_prep,
                                    const float *gb_prep, const void *a, const void *b, const float *A_log,

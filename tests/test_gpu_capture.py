@@ -10,6 +10,10 @@ gdn_scan_varlen_capture) through the C ABI.
   and SEQ paths (the single-token streaming form included), fused and prepared inputs, GQA ratios,
   key widths, ragged column tiles and the rules without the retrieval term; unused slots are exact
   zeros; an inactive step records zeros only.
+* The chunked form records from its first chunk (capacities 4, 16 and 64, counts past the
+  capacity and the length): capsule against the oracle, outputs and state bit-identical to the
+  call without capture; AUTO keeps a prefill-shaped capture on the chunked form, and a capacity
+  past one chunk goes to SEQ (forced CHUNK: unsupported).
 * Replaying the recorded updates from the initial state reaches the state a run over the accepted
   prefix produces, at the size of a speculative verification step.
 * Malformed offsets write nothing."""
@@ -204,21 +208,80 @@ def test_scan_capture_without_final_state(torch):
         check_capsule(w, got, oracle_capsule(w, counts), TOL[w.io], f"nostate/{path}")
 
 
-def test_auto_path_records_on_the_sequential_form(torch):
-    """A prefill-shaped call that AUTO would give to the chunked form runs token-sequentially when
-    it records."""
+def test_auto_path_records_on_the_chunked_form(torch):
+    """A prefill-shaped call that AUTO gives to the chunked form records there (the capacity fits one
+    chunk); a capacity past one chunk sends it to the token-sequential form."""
     import gated_delta_rule_varlen_amd as gdn
 
     w = workloads.make(name="cap_auto", seed=544, lengths=[200, 150], HQ=1, H=2, K=64, V=64, io="bf16")
-    counts = np.array([CAP, 2], np.int32)
     qkv = dev(w.qkv, w.io)
-    _, _, caps, used = gdn.scan_varlen_capture(qkv, dev_i32(w.offsets), cap=CAP, counts=dev_i32(counts), HQ=w.HQ,
-                                               H=w.H, K=w.K, V=w.V, a=dev(w.a, w.gate_dtype),
-                                               b=dev(w.b, w.gate_dtype), A_log=dev(w.A_log, "f32"),
-                                               dt_bias=dev(w.dt_bias, "f32"), state_in=dev(w.state, "f32"))
+    kw = dict(HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=dev(w.a, w.gate_dtype), b=dev(w.b, w.gate_dtype),
+              A_log=dev(w.A_log, "f32"), dt_bias=dev(w.dt_bias, "f32"), state_in=dev(w.state, "f32"))
+    for cap, counts, path in ((CAP, np.array([CAP, 2], np.int32), "chunk"), (65, np.array([65, 70], np.int32), "seq")):
+        _, _, caps, used = gdn.scan_varlen_capture(qkv, dev_i32(w.offsets), cap=cap, counts=dev_i32(counts), **kw)
+        torch.cuda.synchronize()
+        assert used == path
+        _, _, ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io,
+                                gate_dtype=w.gate_dtype, a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias,
+                                state_in=w.state, counts=counts, cap=cap)
+        got = f64(caps)
+        assert np.all(got[ref == 0] == 0)
+        assert_close(got, ref, TOL[w.io], f"auto cap={cap}")
+
+
+CHUNK_CAPTURE_CASES = {
+    # (lengths, counts, cap, geometry): first chunks cut short, whole, and past the capacity
+    "bf16_k128_g2_cap64": ([70, 5, 0, 130, 1, 64, 3], [64, 5, 4, 80, 1, 63, -1], 64,
+                           dict(HQ=2, H=4, K=128, V=128, io="bf16")),
+    "f16_k64_g1_cap16": ([20, 0, 200, 7, 16], [16, 3, 9, 100, 16], 16, dict(HQ=2, H=2, K=64, V=64, io="f16")),
+    "bf16_k64_g4_cap4": ([100, 2, 64, 65], [4, 4, 0, 3], 4, dict(HQ=1, H=4, K=64, V=64, io="bf16")),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CHUNK_CAPTURE_CASES))
+def test_chunk_capture_matches_oracle(torch, name):
+    """The chunked form records g, k^ and delta (rows of its U = T R, the per-token deltas) of the
+    first chunk; the capsule matches the oracle to the half-precision tolerance and recording
+    changes neither outputs nor final state (bit for bit)."""
+    import gated_delta_rule_varlen_amd as gdn
+
+    lens, counts, cap, geo = CHUNK_CAPTURE_CASES[name]
+    w = workloads.make(name=name, seed=570 + sorted(CHUNK_CAPTURE_CASES).index(name), lengths=lens, **geo)
+    counts = np.array(counts, np.int32)
+    print(f"[capture chunk] {name} cap={cap} counts={counts.tolist()}", flush=True)
+    qkv = dev(w.qkv, w.io)
+    kw = dict(HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=dev(w.a, w.gate_dtype), b=dev(w.b, w.gate_dtype),
+              A_log=dev(w.A_log, "f32"), dt_bias=dev(w.dt_bias, "f32"), state_in=dev(w.state, "f32"), path="chunk")
+    off = dev_i32(w.offsets)
+    o1, s1, used1 = gdn.scan_varlen(qkv, off, out=sentinel((w.N, w.H, w.V), w.io),
+                                    state_out=sentinel((w.B, w.H, w.V, w.K), "f32"), **kw)
+    o2, s2, caps, used2 = gdn.scan_varlen_capture(
+        qkv, off, cap=cap, counts=dev_i32(counts),
+        capsule=sentinel((w.B, cap * (w.H + w.HQ * w.K + w.H * w.V)), "f32"), out=sentinel((w.N, w.H, w.V), w.io),
+        state_out=sentinel((w.B, w.H, w.V, w.K), "f32"), **kw)
     torch.cuda.synchronize()
-    assert used == "seq"
-    check_capsule(w, f64(caps), oracle_capsule(w, counts), TOL[w.io], "auto")
+    assert used1 == used2 == "chunk"
+    assert np.array_equal(bits(o1), bits(o2)), "capture changed the outputs"
+    assert np.array_equal(bits(s1), bits(s2)), "capture changed the final state"
+    _, _, ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io, gate_dtype=w.gate_dtype,
+                            a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias, state_in=w.state, counts=counts, cap=cap)
+    got = f64(caps)
+    assert np.all(got[ref == 0] == 0), "unused slots must be zero"
+    g_n, k_n = cap * w.H, cap * (w.H + w.HQ * w.K)
+    for part, sl in (("g", slice(0, g_n)), ("k^", slice(g_n, k_n)), ("delta", slice(k_n, None))):
+        assert_close(got[:, sl], ref[:, sl], TOL[w.io], f"{name} {part}")
+
+
+def test_chunk_capture_past_one_chunk_is_unsupported(torch):
+    import gated_delta_rule_varlen_amd as gdn
+    from gated_delta_rule_varlen_amd import _abi
+
+    w = workloads.make(name="cap_chunk65", seed=575, lengths=[100, 70], HQ=1, H=2, K=64, V=64, io="bf16")
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.scan_varlen_capture(dev(w.qkv, w.io), dev_i32(w.offsets), cap=65, counts=dev_i32(np.array([65, 65], np.int32)),
+                                HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=dev(w.a, w.gate_dtype), b=dev(w.b, w.gate_dtype),
+                                A_log=dev(w.A_log, "f32"), dt_bias=dev(w.dt_bias, "f32"), path="chunk")
+    assert e.value.status == _abi.ERR_UNSUPPORTED
 
 
 def test_scan_capture_malformed_offsets_write_nothing(torch):

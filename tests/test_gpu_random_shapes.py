@@ -5,6 +5,7 @@
   half-precision dtype, then runs DECODE, SEQ and CHUNK on the same inputs.
 * Recurrence, wider flags (DECODE and SEQ): fp32 I/O, K != V, raw decay and rate inputs, no q/k
   normalisation, prepared inputs.
+* CHUNK gate inputs: raw rates, no rate input, fp32 gate inputs (against the oracle and SEQ).
 * Conv: widths 1..8, dilations 1..3, channel counts off the 16-byte vector width, every dtype with
   its own or an fp32 window, bias and SiLU on or off, sequences shorter than the window.
 * Single-launch decode step: bit-identical to the two calls, on batches either side of its
@@ -125,6 +126,41 @@ def test_random_flags_against_oracle(torch, flag_references, seed, path):
     assert_close(f64(st), s_ref, TOL[w.io], f"{path} state")
     empty = np.flatnonzero(w.lengths == 0)
     assert np.array_equal(bits(st)[empty], w.state[empty].view(np.int32))
+
+
+CHUNK_GATE_CASES = {
+    # the chunked form's gate inputs beyond the sigmoid-of-logits default: raw rates in [0, 1], no
+    # rate input (beta = 1), fp32 gate inputs with half-precision q/k/v, and their mixtures
+    "raw_rate_bf16_k128_g2": dict(HQ=2, H=4, K=128, V=128, io="bf16", sigmoid=False, beta_range=(0.0, 1.0)),
+    "no_rate_f16_k64": dict(HQ=2, H=2, K=64, V=64, io="f16", has_beta=False),
+    "f32_gates_bf16_k128": dict(HQ=1, H=2, K=128, V=128, io="bf16", gate_dtype="f32"),
+    "f32_raw_rate_f16_k64_g4_no_state": dict(HQ=1, H=4, K=64, V=64, io="f16", gate_dtype="f32", sigmoid=False,
+                                             beta_range=(0.0, 1.0), state_std=None),
+    "f32_gates_no_rate_bf16_k64": dict(HQ=2, H=4, K=64, V=64, io="bf16", gate_dtype="f32", has_beta=False),
+}
+CHUNK_GATE_LENS = [200, 64, 1, 0, 130, 65, 17]
+
+
+@pytest.mark.parametrize("name", sorted(CHUNK_GATE_CASES))
+def test_chunk_gate_variants_against_oracle_and_seq(torch, name):
+    """CHUNK with raw rates (no sigmoid), without a rate input, and with fp32 gate inputs: outputs
+    and final state against the oracle and against SEQ on the same inputs."""
+    w = workloads.make(name=name, seed=450 + sorted(CHUNK_GATE_CASES).index(name), lengths=CHUNK_GATE_LENS,
+                       **CHUNK_GATE_CASES[name])
+    print(f"[chunk gates] {name} lengths={CHUNK_GATE_LENS} b={'none' if w.b is None else w.gate_dtype} "
+          f"sigmoid={w.sigmoid}", flush=True)
+    o_ref, s_ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io,
+                               gate_dtype=w.gate_dtype, a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias,
+                               state_in=w.state, l2norm=w.l2norm, softplus=w.softplus, sigmoid=w.sigmoid,
+                               scale=w.scale)
+    out, st, used = gpu_scan(torch, w, "chunk", False, use_state=w.state is not None)
+    assert used == "chunk"
+    assert_close(f64(out), o_ref, TOL[w.io], f"{name} chunk out")
+    assert_close(f64(st), s_ref, TOL[w.io], f"{name} chunk state")
+    o_seq, s_seq, used = gpu_scan(torch, w, "seq", False, use_state=w.state is not None)
+    assert used == "seq"
+    assert_close(f64(out), f64(o_seq), TOL[w.io], f"{name} chunk vs seq out")
+    assert_close(f64(st), f64(s_seq), TOL[w.io], f"{name} chunk vs seq state")
 
 
 CONV_SEEDS = list(range(501, 517))
