@@ -333,7 +333,7 @@ gdn_status scan_call(const gdn_scan_desc* d, const gdn::TokenStreams& x, const f
     s.qkv_dtype = d->qkv_dtype;
     s.gate_dtype = d->gate_dtype;
     s.flags = d->flags;
-    s.scale = (d->scale > 0.0f && std::isfinite(d->scale)) ? d->scale : 1.0f / std::sqrt((float)d->K);
+    s.scale = d->scale != 0.0f ? d->scale : 1.0f / std::sqrt((float)d->K);  // zero: the default
     s.path = path;
     s.cap = cap;
     s.counts = counts;
@@ -480,7 +480,7 @@ gdn_status gdn_decode_step(const gdn_conv_desc* cd, const gdn_scan_desc* sd, con
     l.gate_dtype = sd->gate_dtype;
     l.flags = sd->flags;
     l.silu = (cd->flags & GDN_CONV_SILU) != 0;
-    l.scale = (sd->scale > 0.0f && std::isfinite(sd->scale)) ? sd->scale : 1.0f / std::sqrt((float)sd->K);
+    l.scale = sd->scale != 0.0f ? sd->scale : 1.0f / std::sqrt((float)sd->K);  // zero: the default
     return from_hip(gdn::launch_decode_step(l, stream));
 }
 

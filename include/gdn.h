@@ -146,7 +146,8 @@ gdn_status gdn_conv1d_varlen_capture(const gdn_conv_desc *desc, const void *x, c
  *                 SEQ paths only: prepare, prepared scans, CHUNK, capture and gdn_decode_step reject
  *                 it (GDN_ERR_UNSUPPORTED); a must then be 16-byte aligned.
  * A NULL decay input a means g = 1; a NULL rate input b means beta = 1.  Gate arithmetic is fp32
- * (gate inputs are widened to fp32 first).  scale <= 0 selects 1/sqrt(K).
+ * (gate inputs are widened to fp32 first).  scale == 0 selects 1/sqrt(K); any other value, negative
+ * included, is applied as given.
  * Constraints: B >= 1, N >= 0, HQ >= 1, H >= 1, H % HQ == 0, 1 <= K <= 256 (the pages' limit),
  * V >= 1; the library instantiates K in {32, 64, 128, 256} (GDN_ERR_UNSUPPORTED otherwise).
  * gate_dtype is GDN_F32 or qkv_dtype.
@@ -169,7 +170,7 @@ typedef struct gdn_scan_desc {
     int32_t qkv_dtype;  /* gdn_dtype of qkv and out */
     int32_t gate_dtype; /* gdn_dtype of a and b: GDN_F32 or qkv_dtype */
     uint32_t flags;     /* GDN_L2NORM | GDN_SOFTPLUS | GDN_SIGMOID | GDN_NO_RETRIEVE | GDN_GATE_PER_KEY */
-    float scale;        /* output scale; <= 0 selects 1/sqrt(K) */
+    float scale;        /* output scale; 0 selects 1/sqrt(K), any other value is applied */
     int32_t path;       /* gdn_path */
 } gdn_scan_desc;
 

@@ -245,7 +245,8 @@ int gdn_oracle_conv_capture(int B, int N, int C, int cap, int x_dtype, const voi
  * Thunk::GatedDeltaNet with gate_per_channel: g shaped like the keys): a is [N,H,K] and the first step
  * becomes s[i] <- g_i * s[i] with g_i = decay_gate(a[t,h,i]) (A_log and dt_bias stay per head);
  * in matrix form S <- S diag(g) (I - beta k^ k^T) + beta v k^T.  Not combined with a capture.
- * scale <= 0 selects 1/sqrt(K) (host fn delta(): a zero scale attribute means 1/sqrt(K)).
+ * scale == 0 selects 1/sqrt(K); any other value, negative included, is applied as given (host fn
+ * delta(): a zero scale attribute means 1/sqrt(K)).
  * Layouts: qkv [N, 2*HQ*K + H*V]; out [N,H,V]; state [B,H,V,K] float32 in, fp64 out.
  * Returns 0 on success, 1 when the offsets are malformed (then nothing is written), 2 when out of
  * memory, 3 for a per-key gate with a capture.  Parallel over independent (b, h) pairs with OpenMP
@@ -258,7 +259,7 @@ int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, in
                     const int32_t *counts, const int32_t *active, int cap, double *capsule) {
     if (!gdn_oracle_offsets_valid(offsets, B, N)) return 1;
     if (gate_per_key && a && capsule) return 3;
-    if (scale <= 0.0) scale = 1.0 / sqrt((double)K);
+    if (scale == 0.0) scale = 1.0 / sqrt((double)K);
     const size_t C = (size_t)2 * HQ * K + (size_t)H * V;
     const void *a_head = gate_per_key ? NULL : a; /* per-head decay input, evaluated by prepare */
     const int G = H / HQ;

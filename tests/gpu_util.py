@@ -12,6 +12,26 @@ import workloads
 TORCH_DT = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
 TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2}  # max relative error per output tensor
 PREP_TOL = 1e-4  # fp32 prepare outputs from exactly decoded inputs
+# fp32 final state of the token-sequential paths (DECODE, SEQ, the fused decode step): computed in
+# fp32 from exactly decoded inputs whatever the I/O dtype, so fp32 accumulation bounds it; the
+# chunked form rounds its operands to bf16 and keeps the I/O tolerance
+SEQ_STATE_TOL = 1e-4
+# a state downstream of a conv output that was rounded to bf16/fp16 (the chained decode step): the
+# kernel's fp32 tap sum and the oracle's fp64 sum can round an element one unit apart, which moves
+# the state by at most that unit relative to it (2^-8 for bf16)
+CHAIN_STATE_TOL = 2.0 ** -8
+# per (sequence, head) slice, the chunked form's bf16 operand rounding is relative to the slice's
+# intermediate terms, not its (possibly smaller) outputs
+CHUNK_SLICE_TOL = 5e-2
+
+
+def state_tol(io: str, path: str) -> float:
+    return TOL[io] if path == "chunk" else SEQ_STATE_TOL
+
+
+# achieved errors of this process's comparisons (test id, what, normwise, elementwise, gate); written
+# as JSON lines at the end of the session when GDN_ERR_LOG names a file
+RECORD: list = []
 
 
 def require_gpu():
@@ -79,10 +99,54 @@ def max_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(num / den) if den > 0 else float(num)
 
 
+def elementwise_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """Diagnostic: max |got - ref| / (|ref| + 1e-3 max |ref|), elementwise."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    d = np.abs(got - ref)
+    if not np.all(np.isfinite(d)):
+        return float("inf")
+    return float(np.max(d / (np.abs(ref) + 1e-3 * np.max(np.abs(ref)) + 1e-300)))
+
+
 def assert_close(got, ref, tol, what):
     err = max_rel_err(got, ref)
+    eerr = elementwise_err(got, ref)
+    RECORD.append((os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], what, err, eerr, tol))
+    print(f"[err] {what}: normwise {err:.3e} elementwise {eerr:.3e} (gate {tol:.1e})", flush=True)
     assert err <= tol, f"{what}: max relative error {err:.3e} > {tol:.1e}"
     return err
+
+
+def assert_close_slices(got, ref, lengths, tol, what, *, token_major=True):
+    """The normwise error of each (sequence, head) slice against that slice's own max |ref|, so an
+    error confined to one short or small sequence or head cannot hide under another's magnitude.
+    Token-major arrays are [N, H, ...] split by the sequence lengths; otherwise [B, H, ...]."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    worst = 0.0
+    if token_major:
+        start = 0
+        for b, n in enumerate(lengths):
+            for h in range(ref.shape[1]):
+                r = ref[start:start + n, h]
+                if r.size and np.max(np.abs(r)) > 0:
+                    e = max_rel_err(got[start:start + n, h], r)
+                    worst = max(worst, e)
+                    assert e <= tol, f"{what}: sequence {b} head {h}: max relative error {e:.3e} > {tol:.1e}"
+            start += n
+    else:
+        for b in range(ref.shape[0]):
+            for h in range(ref.shape[1]):
+                r = ref[b, h]
+                if np.max(np.abs(r)) > 0:
+                    e = max_rel_err(got[b, h], r)
+                    worst = max(worst, e)
+                    assert e <= tol, f"{what}: sequence {b} head {h}: max relative error {e:.3e} > {tol:.1e}"
+    RECORD.append((os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], what + " per slice", worst, worst, tol))
+    return worst
 
 
 def sentinel(shape, dtype, device="cuda"):

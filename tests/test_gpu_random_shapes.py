@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import TOL, assert_close, bits, dev, dev_i32, ensure_built, f64, require_gpu
+from gpu_util import CHUNK_SLICE_TOL, SEQ_STATE_TOL, TOL, assert_close, assert_close_slices, state_tol, bits, dev, dev_i32, ensure_built, f64, require_gpu
 from test_gpu_scan import gpu_scan
 
 pytestmark = pytest.mark.gpu
@@ -69,7 +69,11 @@ def test_random_shape_against_oracle(torch, references, seed, path):
     assert used == path
     if w.N > 0:
         assert_close(f64(out), o_ref, TOL[w.io], f"{path} out")
-    assert_close(f64(st), s_ref, TOL[w.io], f"{path} state")
+        assert_close_slices(f64(out), o_ref, w.lengths, CHUNK_SLICE_TOL if path == "chunk" else TOL[w.io],
+                            f"{path} out")
+    assert_close(f64(st), s_ref, state_tol(w.io, path), f"{path} state")
+    assert_close_slices(f64(st), s_ref, w.lengths, CHUNK_SLICE_TOL if path == "chunk" else SEQ_STATE_TOL,
+                        f"{path} state", token_major=False)
     empty = np.flatnonzero(w.lengths == 0)
     assert np.array_equal(bits(st)[empty], w.state[empty].view(np.int32))
 
@@ -123,7 +127,7 @@ def test_random_flags_against_oracle(torch, flag_references, seed, path):
     assert used == path
     if w.N > 0:
         assert_close(f64(out), o_ref, TOL[w.io], f"{path} out")
-    assert_close(f64(st), s_ref, TOL[w.io], f"{path} state")
+    assert_close(f64(st), s_ref, SEQ_STATE_TOL, f"{path} state")
     empty = np.flatnonzero(w.lengths == 0)
     assert np.array_equal(bits(st)[empty], w.state[empty].view(np.int32))
 
@@ -156,11 +160,28 @@ def test_chunk_gate_variants_against_oracle_and_seq(torch, name):
     out, st, used = gpu_scan(torch, w, "chunk", False, use_state=w.state is not None)
     assert used == "chunk"
     assert_close(f64(out), o_ref, TOL[w.io], f"{name} chunk out")
+    assert_close_slices(f64(out), o_ref, w.lengths, CHUNK_SLICE_TOL, f"{name} chunk out")
     assert_close(f64(st), s_ref, TOL[w.io], f"{name} chunk state")
+    assert_close_slices(f64(st), s_ref, w.lengths, CHUNK_SLICE_TOL, f"{name} chunk state", token_major=False)
     o_seq, s_seq, used = gpu_scan(torch, w, "seq", False, use_state=w.state is not None)
     assert used == "seq"
     assert_close(f64(out), f64(o_seq), TOL[w.io], f"{name} chunk vs seq out")
     assert_close(f64(st), f64(s_seq), TOL[w.io], f"{name} chunk vs seq state")
+
+
+@pytest.mark.parametrize("path", ["decode", "seq", "chunk"])
+def test_negative_scale_is_applied(torch, path):
+    """A nonzero scale is applied as given, negative included (only zero selects 1/sqrt(K))."""
+    w = workloads.make(name="neg_scale", seed=470, lengths=[90, 3, 0, 70], HQ=2, H=4, K=64, V=64, io="bf16")
+    w.scale = -0.4
+    o_ref, s_ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io,
+                               gate_dtype=w.gate_dtype, a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias,
+                               state_in=w.state, scale=w.scale)
+    out, st, used = gpu_scan(torch, w, path, False)
+    assert used == path
+    assert_close(f64(out), o_ref, TOL[w.io], f"{path} out")
+    assert_close(f64(st), s_ref, state_tol(w.io, path), f"{path} state")
+    assert np.sum(f64(out) * o_ref) > 0  # the sign follows the scale
 
 
 CONV_SEEDS = list(range(501, 517))

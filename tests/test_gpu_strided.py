@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import TOL, assert_close, bits, dev, dev_i32, ensure_built, f64, require_gpu
+from gpu_util import SEQ_STATE_TOL, TOL, assert_close, bits, dev, dev_i32, ensure_built, f64, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -106,5 +106,5 @@ def test_strided_unpackable_value_width_matches_oracle(torch, path):
                                a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias, state_in=w.state, l2norm=w.l2norm,
                                softplus=w.softplus, sigmoid=w.sigmoid, scale=w.scale)
     e1 = assert_close(f64(out), o_ref, TOL[w.io], "out")
-    e2 = assert_close(f64(st), s_ref, TOL[w.io], "state")
+    e2 = assert_close(f64(st), s_ref, SEQ_STATE_TOL, "state")
     print(f"  v33 {path}: out {e1:.2e} state {e2:.2e}", flush=True)

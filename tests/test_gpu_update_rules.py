@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import TOL, assert_close, bits, dev, dev_i32, ensure_built, f64, require_gpu, sentinel
+from gpu_util import SEQ_STATE_TOL, TOL, assert_close, bits, dev, dev_i32, ensure_built, f64, require_gpu, sentinel
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +53,7 @@ def test_no_retrieval_matches_oracle(torch, io, decay, path, prepared):
     o_ref, s_ref = oracle_ref(w)
     tol = TOL[w.io]
     e1 = assert_close(f64(out), o_ref, tol, "out")
-    e2 = assert_close(f64(st), s_ref, tol, "state")
+    e2 = assert_close(f64(st), s_ref, SEQ_STATE_TOL, "state")
     print(f"  {io} decay={decay} {path} prepared={prepared}: out {e1:.2e} state {e2:.2e}", flush=True)
 
 

@@ -278,3 +278,18 @@ def test_default_scale_is_inverse_sqrt_k():
     o_def, _ = run(p, 1, 1, 16, 2, scale=0.0)
     o_one, _ = run(p, 1, 1, 16, 2, scale=1.0)
     np.testing.assert_allclose(o_def, o_one / 4.0, rtol=1e-15)
+
+
+def test_scale_zero_selects_inverse_sqrt_k_and_other_values_apply():
+    """The host fn delta() substitutes 1/sqrt(K) for a zero scale attribute only: any other value,
+    negative included, multiplies the readout.  The state never depends on the scale."""
+    HQ, H, K, V = 1, 2, 16, 6
+    p = rand_problem(7, [11, 5, 0], HQ, H, K, V)
+    o0, s0 = run(p, HQ, H, K, V, scale=0.0)
+    o1, s1 = run(p, HQ, H, K, V, scale=1.0)
+    on, sn = run(p, HQ, H, K, V, scale=-0.375)
+    op, sp = run(p, HQ, H, K, V, scale=0.375)
+    assert np.allclose(o0, o1 / np.sqrt(K), rtol=1e-12, atol=0)
+    assert np.array_equal(on, -op)
+    for s in (s1, sn, sp):
+        assert np.array_equal(s, s0)

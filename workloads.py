@@ -77,7 +77,7 @@ class Workload:
     A_log: Optional[np.ndarray]  # [H] f32
     dt_bias: Optional[np.ndarray]  # [H] f32
     state: Optional[np.ndarray]  # [B, H, V, K] f32
-    scale: float = 0.0  # <= 0 selects 1/sqrt(K)
+    scale: float = 0.0  # 0 selects 1/sqrt(K); any other value is applied
 
     @property
     def C(self) -> int:
