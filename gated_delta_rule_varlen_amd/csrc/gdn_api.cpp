@@ -37,7 +37,6 @@ gdn_status check_scan_desc(const gdn_scan_desc* d) {
     const long long C = 2ll * d->HQ * d->K + (long long)d->H * d->V;
     if (C > INT_MAX) return GDN_ERR_OVERFLOW;
     if ((long long)d->B * d->H > INT_MAX) return GDN_ERR_OVERFLOW;
-    if (d->K != 32 && d->K != 64 && d->K != 128 && d->K != 256) return GDN_ERR_UNSUPPORTED;
     if (d->path < GDN_PATH_AUTO || d->path > GDN_PATH_CHUNK) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }

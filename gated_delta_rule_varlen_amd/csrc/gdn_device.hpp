@@ -84,6 +84,64 @@ __device__ __forceinline__ f32x4 load4<F16>(const uint16_t* p) {
                  f16_bits_to_f32(w.y >> 16)};
 }
 
+// Slices of K-wide rows (state columns, q/k rows) for kernels compiled for a width KP >= K.
+// KX: K == KP, plain 16-byte (or 8-byte) accesses.  Otherwise elements at or past Kr read as zero
+// and are not written, element by element (rows of any width and 4-byte alignment).
+template <bool KX, bool NT>
+__device__ __forceinline__ f32x4 ld_row4(const float* row, int e0, int Kr) {
+    if constexpr (KX) {
+        if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0));
+        else return *reinterpret_cast<const f32x4*>(row + e0);
+    } else {
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = e0 + e < Kr ? row[e0 + e] : 0.0f;
+        return r;
+    }
+}
+template <bool KX, bool NT>
+__device__ __forceinline__ void st_row4(float* row, int e0, int Kr, f32x4 v) {
+    if constexpr (KX) {
+        if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(row + e0));
+        else *reinterpret_cast<f32x4*>(row + e0) = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e0 + e < Kr) row[e0 + e] = v[e];
+    }
+}
+template <typename T, bool KX>
+__device__ __forceinline__ f32x4 ld_in4(const typename T::storage* row, int e0, int Kr) {
+    if constexpr (KX) {
+        return load4<T>(row + e0);
+    } else {
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = e0 + e < Kr ? to_f32<T>(row[e0 + e]) : 0.0f;
+        return r;
+    }
+}
+// 16 raw bytes (VEC elements of type TS) of a row from element e0, elements at or past Kr zero.
+template <typename TS, int VEC, bool KX>
+__device__ __forceinline__ u32x4 ld_raw16(const TS* row, int e0, int Kr) {
+    static_assert(VEC * sizeof(TS) == 16, "16 bytes");
+    if constexpr (KX) {
+        return *reinterpret_cast<const u32x4*>(row + e0);
+    } else {
+        union {
+            u32x4 v;
+            TS e[VEC];
+        } u;
+        u.v = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            if (e0 + e < Kr) u.e[e] = row[e0 + e];
+        return u.v;
+    }
+}
+// Compiled key width for a row width K <= 256: the next of 32, 64, 128, 256.
+constexpr int padded_key_width(int K) { return K <= 32 ? 32 : K <= 64 ? 64 : K <= 128 ? 128 : 256; }
+
 // DPP lane permutation of a float within rows of 16 lanes.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {

@@ -47,9 +47,12 @@ __device__ __forceinline__ void gate_rate(const PrepArgs& p, long long i, int h,
     }
 }
 
-template <typename T, int K>
+template <typename T, int K, bool KX>
 __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs p) {
     using TS = typename T::storage;
+    // K is the compiled row width; rows are Kr wide (Kr < K: the lanes' elements past Kr read as
+    // zero and are not written)
+    const int Kr = KX ? K : p.K;
     constexpr int VEC = 16 / (int)sizeof(TS);  // elements per 16-byte load
     constexpr int RL = K / VEC;                // lanes per row
     static_assert(RL >= 1 && RL <= 64 && (RL & (RL - 1)) == 0, "row must map onto a power-of-two lane group");
@@ -63,12 +66,11 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs p) {
         const long long rr = live ? row : 0;
         const long long t = rr / (2 * p.HQ);
         const int r = (int)(rr % (2 * p.HQ));  // 0..HQ-1: q rows, HQ..2HQ-1: k rows
-        const TS* src = (r < p.HQ ? static_cast<const TS*>(p.x.q) + (size_t)t * p.x.sq + (size_t)r * K
-                                  : static_cast<const TS*>(p.x.k) + (size_t)t * p.x.sk + (size_t)(r - p.HQ) * K) +
-                        lane * VEC;
+        const TS* src = r < p.HQ ? static_cast<const TS*>(p.x.q) + (size_t)t * p.x.sq + (size_t)r * Kr
+                                 : static_cast<const TS*>(p.x.k) + (size_t)t * p.x.sk + (size_t)(r - p.HQ) * Kr;
         float v[VEC];
         {
-            const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
+            const u32x4 raw = ld_raw16<TS, VEC, KX>(src, lane * VEC, Kr);
             if constexpr (std::is_same<T, F32>::value) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(raw[i]);
@@ -87,10 +89,11 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs p) {
         const float scale = (p.flags & GDN_L2NORM) ? rsqrtf(ss + 1e-12f) : 1.0f;
         if (!live) return;
         const int plane = r / p.HQ, hq = r % p.HQ;
-        float* dst = p.qk_out + (((size_t)plane * p.N + (size_t)t) * p.HQ + hq) * K + lane * VEC;
+        float* dst = p.qk_out + (((size_t)plane * p.N + (size_t)t) * p.HQ + hq) * Kr;
 #pragma unroll
         for (int i = 0; i < VEC; i += 4)
-            *reinterpret_cast<f32x4*>(dst + i) = f32x4{v[i] * scale, v[i + 1] * scale, v[i + 2] * scale, v[i + 3] * scale};
+            st_row4<KX, false>(dst, lane * VEC + i, Kr,
+                               f32x4{v[i] * scale, v[i + 1] * scale, v[i + 2] * scale, v[i + 3] * scale});
         return;
     }
     if (p.gb_out == nullptr) return;
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs p) {
     p.gb_out[(size_t)p.N * p.H + i] = beta;
 }
 
-template <typename T, int K>
+template <typename T, int K, bool KX>
 hipError_t launch_k(const PrepArgs& p0, hipStream_t stream) {
     PrepArgs p = p0;
     constexpr int VEC = 16 / (int)sizeof(typename T::storage);
@@ -113,18 +116,26 @@ hipError_t launch_k(const PrepArgs& p0, hipStream_t stream) {
     const long long blocks = p.n_row_blocks + gate_blocks;
     if (blocks == 0) return hipSuccess;
     if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prepare_kernel<T, K>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((prepare_kernel<T, K, KX>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_t(const PrepArgs& p, hipStream_t stream) {
     switch (p.K) {
-        case 32: return launch_k<T, 32>(p, stream);
-        case 64: return launch_k<T, 64>(p, stream);
-        case 128: return launch_k<T, 128>(p, stream);
-        case 256: return launch_k<T, 256>(p, stream);
-        default: return hipErrorInvalidValue;
+        case 32: return launch_k<T, 32, true>(p, stream);
+        case 64: return launch_k<T, 64, true>(p, stream);
+        case 128: return launch_k<T, 128, true>(p, stream);
+        case 256: return launch_k<T, 256, true>(p, stream);
+        default: break;
+    }
+    // any other width up to 256: the next of them, with the elements past K masked
+    if (p.K < 1 || p.K > 256) return hipErrorInvalidValue;
+    switch (padded_key_width(p.K)) {
+        case 32: return launch_k<T, 32, false>(p, stream);
+        case 64: return launch_k<T, 64, false>(p, stream);
+        case 128: return launch_k<T, 128, false>(p, stream);
+        default: return launch_k<T, 256, false>(p, stream);
     }
 }
 

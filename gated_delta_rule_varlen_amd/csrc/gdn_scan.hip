@@ -43,6 +43,9 @@
 //     lane that writes the column's output); the slots after them are zeroed by the same lanes.
 //
 // DECODE instances stream the state with non-temporal loads/stores (read once, written once).
+// Key widths other than 32, 64, 128 and 256 run on the next compiled width ("KX = false"
+// instances): the lanes' elements past K read as zero and are never written, so dot products,
+// norms and updates are those of the K-wide rows.
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -88,17 +91,6 @@ struct ScanArgs {
     float* capsule;         // [B, cap*(H + HQ*K + H*V)]
 };
 
-template <bool NT>
-__device__ __forceinline__ f32x4 ld_state(const float* p) {
-    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    else return *reinterpret_cast<const f32x4*>(p);
-}
-template <bool NT>
-__device__ __forceinline__ void st_state(float* p, f32x4 v) {
-    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
-    else *reinterpret_cast<f32x4*>(p) = v;
-}
-
 // Operands of one token as seen by one lane.
 template <int EPL, int CPL, bool PK>
 struct TokenOps {
@@ -110,18 +102,19 @@ struct TokenOps {
     float gkr;              // PK: raw decay input of key channel threadIdx.x (threads below K)
 };
 
-template <typename T, int K, int LPC, int CPL, bool PREP, bool PK>
+template <typename T, int K, int LPC, int CPL, bool PREP, bool PK, bool KX>
 __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int kh, int gl, int vbase,
                                            TokenOps<K / LPC, CPL, PK>& o) {
     constexpr int EPL = K / LPC;
     using TS = typename T::storage;
+    const int Kr = KX ? K : p.K;
     if constexpr (PREP) {
-        const float* qp = p.qk_prep + ((size_t)t * p.HQ + kh) * K;
-        const float* kp = p.qk_prep + (((size_t)p.N + t) * p.HQ + kh) * K;
+        const float* qp = p.qk_prep + ((size_t)t * p.HQ + kh) * Kr;
+        const float* kp = p.qk_prep + (((size_t)p.N + t) * p.HQ + kh) * Kr;
 #pragma unroll
         for (int i = 0; i < EPL / 4; ++i) {
-            const f32x4 qv = *reinterpret_cast<const f32x4*>(qp + 4 * (gl + LPC * i));
-            const f32x4 kv = *reinterpret_cast<const f32x4*>(kp + 4 * (gl + LPC * i));
+            const f32x4 qv = ld_row4<KX, false>(qp, 4 * (gl + LPC * i), Kr);
+            const f32x4 kv = ld_row4<KX, false>(kp, 4 * (gl + LPC * i), Kr);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 o.q[4 * i + e] = qv[e];
@@ -131,12 +124,12 @@ __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int 
         o.ga = p.gb_prep[(size_t)t * p.H + h];
         o.gb = p.gb_prep[((size_t)p.N + t) * p.H + h];
     } else {
-        const TS* qp = static_cast<const TS*>(p.x.q) + (size_t)t * p.x.sq + (size_t)kh * K;
-        const TS* kp = static_cast<const TS*>(p.x.k) + (size_t)t * p.x.sk + (size_t)kh * K;
+        const TS* qp = static_cast<const TS*>(p.x.q) + (size_t)t * p.x.sq + (size_t)kh * Kr;
+        const TS* kp = static_cast<const TS*>(p.x.k) + (size_t)t * p.x.sk + (size_t)kh * Kr;
 #pragma unroll
         for (int i = 0; i < EPL / 4; ++i) {
-            const f32x4 qv = load4<T>(qp + 4 * (gl + LPC * i));
-            const f32x4 kv = load4<T>(kp + 4 * (gl + LPC * i));
+            const f32x4 qv = ld_in4<T, KX>(qp, 4 * (gl + LPC * i), Kr);
+            const f32x4 kv = ld_in4<T, KX>(kp, 4 * (gl + LPC * i), Kr);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 o.q[4 * i + e] = qv[e];
@@ -146,7 +139,7 @@ __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int 
         const size_t gi = (size_t)t * p.H + h;
         if constexpr (PK) {
             o.ga = 0.0f;
-            o.gkr = (int)threadIdx.x < K ? load_any(p.a, p.gate_dtype, gi * K + threadIdx.x) : 0.0f;
+            o.gkr = (int)threadIdx.x < Kr ? load_any(p.a, p.gate_dtype, gi * Kr + threadIdx.x) : 0.0f;
         } else {
             o.ga = p.a ? load_any(p.a, p.gate_dtype, gi) : 0.0f;
         }
@@ -157,9 +150,11 @@ __device__ __forceinline__ void load_token(const ScanArgs& p, int t, int h, int 
     for (int c = 0; c < CPL; ++c) o.v[c] = (vbase + c < p.V) ? to_f32<T>(vp[c]) : 0.0f;
 }
 
-template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK, bool SHORT>
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK, bool SHORT, bool KX>
 __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
     static_assert(!(PK && PREP), "the per-key decay is evaluated in-kernel from raw inputs");
+    // K is the compiled key width; rows are Kr wide (Kr < K: the lanes' elements past Kr are zero)
+    const int Kr = KX ? K : p.K;
     constexpr int EPL = K / LPC;  // state elements per lane per column
     static_assert(EPL % 4 == 0, "whole 16-byte chunks per lane");
     constexpr int GPW = 64 / LPC;  // lane groups per wave
@@ -198,7 +193,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
     CaptureRow crow{};
     if (p.cap > 0) {
         captured = captured_tokens(p.counts, p.active, p.cap, b, end - start);
-        crow = capture_row(p.capsule, b, p.cap, p.H, p.HQ, K, p.V);
+        crow = capture_row(p.capsule, b, p.cap, p.H, p.HQ, Kr, p.V);
     }
     const bool cap_g = vt == 0 && wave == 0 && lane == 0;
     const bool cap_k = vt == 0 && wave == 0 && grp == 0 && h == kh * p.G;
@@ -211,7 +206,8 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
 #pragma unroll
             for (int m = 0; m < EPL / 4; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) kd[4 * (gl + LPC * m) + e] = kv[4 * m + e] * rk;
+                for (int e = 0; e < 4; ++e)
+                    if (KX || 4 * (gl + LPC * m) + e < Kr) kd[4 * (gl + LPC * m) + e] = kv[4 * m + e] * rk;
         }
         if (cap_d) crow.d(i, h)[vbase + gl] = dmine;
     };
@@ -223,7 +219,8 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
 #pragma unroll
                 for (int m = 0; m < EPL / 4; ++m)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) kd[4 * (gl + LPC * m) + e] = 0.0f;
+                    for (int e = 0; e < 4; ++e)
+                        if (KX || 4 * (gl + LPC * m) + e < Kr) kd[4 * (gl + LPC * m) + e] = 0.0f;
             }
             if (cap_d) crow.d(i, h)[vbase + gl] = 0.0f;
         }
@@ -250,18 +247,25 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                 const bool live = t < ntok;
                 const int tt = start + (live ? t : 0);
                 float qv[EPT], kv[EPT];
+                const int ej = j * EPT;  // first element of the thread's slice
                 if constexpr (PREP) {
-                    const float* qp = p.qk_prep + ((size_t)tt * p.HQ + kh) * K + j * EPT;
-                    const float* kp = p.qk_prep + (((size_t)p.N + tt) * p.HQ + kh) * K + j * EPT;
+                    const float* qp = p.qk_prep + ((size_t)tt * p.HQ + kh) * Kr + ej;
+                    const float* kp = p.qk_prep + (((size_t)p.N + tt) * p.HQ + kh) * Kr + ej;
 #pragma unroll
                     for (int e = 0; e < EPT; ++e) {
-                        qv[e] = qp[e];
-                        kv[e] = kp[e];
+                        qv[e] = (KX || ej + e < Kr) ? qp[e] : 0.0f;
+                        kv[e] = (KX || ej + e < Kr) ? kp[e] : 0.0f;
                     }
                 } else {
-                    const TS* qp = static_cast<const TS*>(p.x.q) + (size_t)tt * p.x.sq + (size_t)kh * K + j * EPT;
-                    const TS* kp = static_cast<const TS*>(p.x.k) + (size_t)tt * p.x.sk + (size_t)kh * K + j * EPT;
-                    if constexpr (EPT % 4 == 0) {
+                    const TS* qp = static_cast<const TS*>(p.x.q) + (size_t)tt * p.x.sq + (size_t)kh * Kr + ej;
+                    const TS* kp = static_cast<const TS*>(p.x.k) + (size_t)tt * p.x.sk + (size_t)kh * Kr + ej;
+                    if constexpr (!KX) {
+#pragma unroll
+                        for (int e = 0; e < EPT; ++e) {
+                            qv[e] = ej + e < Kr ? to_f32<T>(qp[e]) : 0.0f;
+                            kv[e] = ej + e < Kr ? to_f32<T>(kp[e]) : 0.0f;
+                        }
+                    } else if constexpr (EPT % 4 == 0) {
 #pragma unroll
                         for (int e = 0; e < EPT; e += 4) {
                             const f32x4 a4 = load4<T>(qp + e), b4 = load4<T>(kp + e);
@@ -299,10 +303,10 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                         shk[t][j * EPT + e] = kv[e] * rk;
                     }
                     if constexpr (PK) {
-                        const size_t gi = ((size_t)tt * p.H + h) * K + j * EPT;
+                        const size_t gi = ((size_t)tt * p.H + h) * Kr + ej;
 #pragma unroll
                         for (int e = 0; e < EPT; ++e) {
-                            const float x = load_any(p.a, p.gate_dtype, gi + e);
+                            const float x = (KX || ej + e < Kr) ? load_any(p.a, p.gate_dtype, gi + e) : 0.0f;
                             shgk[t][j * EPT + e] = softplus ? expf(a_mul * softplus_f(x + a_bias)) : expf(x);
                         }
                     }
@@ -343,9 +347,9 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
             f32x4 sc[CPL][EPL / 4];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const float* sp = p.state_in + (col0 + vbase + c) * K;
+                const float* sp = p.state_in + (col0 + vbase + c) * Kr;
 #pragma unroll
-                for (int i = 0; i < EPL / 4; ++i) sc[c][i] = ld_state<NT>(sp + 4 * (gl + LPC * i));
+                for (int i = 0; i < EPL / 4; ++i) sc[c][i] = ld_row4<KX, NT>(sp, 4 * (gl + LPC * i), Kr);
             }
             const int lc = vbase - vb0;
             float cs = 1.0f;
@@ -422,13 +426,13 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
             }
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                float* sp = p.state_out + (col0 + vbase + c) * K;
+                float* sp = p.state_out + (col0 + vbase + c) * Kr;
 #pragma unroll
                 for (int i = 0; i < EPL / 4; ++i) {
                     f32x4 v = sc[c][i];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] *= cs;
-                    st_state<NT>(sp + 4 * (gl + LPC * i), v);
+                    st_row4<KX, NT>(sp, 4 * (gl + LPC * i), Kr, v);
                 }
             }
             if (p.cap > 0) {
@@ -441,7 +445,9 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
 #pragma unroll
                         for (int m = 0; m < EPL / 4; ++m)
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) kd[4 * (gl + LPC * m) + e] = shk[t][4 * (gl + LPC * m) + e];
+                            for (int e = 0; e < 4; ++e)
+                                if (KX || 4 * (gl + LPC * m) + e < Kr)
+                                    kd[4 * (gl + LPC * m) + e] = shk[t][4 * (gl + LPC * m) + e];
                     }
                 }
                 capture_zeros();
@@ -458,12 +464,12 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
         const bool full_tile = (vt * NW + NW) * WC <= p.V;
         if (end - start == 1 && full_tile && p.state_in != nullptr && p.state_out != nullptr) {
             TokenOps<EPL, CPL, PK> tok;
-            load_token<T, K, LPC, CPL, PREP, PK>(p, start, h, kh, gl, vbase, tok);
+            load_token<T, K, LPC, CPL, PREP, PK, KX>(p, start, h, kh, gl, vbase, tok);
             f32x4 ring[PD + 1][EPL / 4];
             auto load_col = [&](int c, f32x4 (&dst)[EPL / 4]) {
-                const float* sp = p.state_in + (col0 + vbase + c) * K;
+                const float* sp = p.state_in + (col0 + vbase + c) * Kr;
 #pragma unroll
-                for (int i = 0; i < EPL / 4; ++i) dst[i] = ld_state<NT>(sp + 4 * (gl + LPC * i));
+                for (int i = 0; i < EPL / 4; ++i) dst[i] = ld_row4<KX, NT>(sp, 4 * (gl + LPC * i), Kr);
             };
 #pragma unroll
             for (int c = 0; c < PD; ++c) load_col(c, ring[c]);
@@ -532,13 +538,13 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
                 const float delta = beta * (tok.v[c] - r);
                 const float dk = delta * rk;
                 const float o = oscale * fmaf(g, pq, dk * qk);
-                float* sp = p.state_out + (col0 + vbase + c) * K;
+                float* sp = p.state_out + (col0 + vbase + c) * Kr;
 #pragma unroll
                 for (int i = 0; i < EPL / 4; ++i) {
                     f32x4 nv;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) nv[e] = fmaf(dk, tok.k[4 * i + e], PK ? sc[i][e] : g * sc[i][e]);
-                    st_state<NT>(sp + 4 * (gl + LPC * i), nv);
+                    st_row4<KX, NT>(sp, 4 * (gl + LPC * i), Kr, nv);
                 }
                 if (gl == c) {
                     mine = o;
@@ -558,20 +564,20 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const bool valid = (vbase + c < p.V) && p.state_in != nullptr;
-        const float* sp = p.state_in + (col0 + vbase + c) * K;
+        const float* sp = p.state_in + (col0 + vbase + c) * Kr;
 #pragma unroll
         for (int i = 0; i < EPL / 4; ++i) {
-            const f32x4 v = valid ? ld_state<NT>(sp + 4 * (gl + LPC * i)) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 v = valid ? ld_row4<KX, NT>(sp, 4 * (gl + LPC * i), Kr) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[c][4 * i + e] = v[e];
         }
     }
 
     TokenOps<EPL, CPL, PK> cur;
-    if (start < end) load_token<T, K, LPC, CPL, PREP, PK>(p, start, h, kh, gl, vbase, cur);
+    if (start < end) load_token<T, K, LPC, CPL, PREP, PK, KX>(p, start, h, kh, gl, vbase, cur);
     for (int t = start; t < end; ++t) {
         TokenOps<EPL, CPL, PK> nxt;
-        if (t + 1 < end) load_token<T, K, LPC, CPL, PREP, PK>(p, t + 1, h, kh, gl, vbase, nxt);
+        if (t + 1 < end) load_token<T, K, LPC, CPL, PREP, PK, KX>(p, t + 1, h, kh, gl, vbase, nxt);
 
         float g, beta;
         if constexpr (PREP) {
@@ -657,24 +663,24 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             if (vbase + c >= p.V) continue;
-            float* sp = p.state_out + (col0 + vbase + c) * K;
+            float* sp = p.state_out + (col0 + vbase + c) * Kr;
 #pragma unroll
             for (int i = 0; i < EPL / 4; ++i)
-                st_state<NT>(sp + 4 * (gl + LPC * i),
-                             f32x4{s[c][4 * i], s[c][4 * i + 1], s[c][4 * i + 2], s[c][4 * i + 3]});
+                st_row4<KX, NT>(sp, 4 * (gl + LPC * i), Kr,
+                                f32x4{s[c][4 * i], s[c][4 * i + 1], s[c][4 * i + 2], s[c][4 * i + 3]});
         }
     }
     if (p.cap > 0) capture_zeros();
 }
 
-template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK, bool SHORT>
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool NT, bool PK, bool SHORT, bool KX>
 hipError_t launch_tile(ScanArgs p, hipStream_t stream) {
     constexpr int BC = (64 / LPC) * CPL * NW;  // columns per block
     p.n_vtiles = (p.V + BC - 1) / BC;
     const long long blocks = (long long)p.B * p.H * p.n_vtiles;
     if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
     p.n_blocks = (int)blocks;
-    hipLaunchKernelGGL((scan_kernel<T, K, LPC, CPL, NW, PREP, NT, PK, SHORT>), dim3((unsigned)blocks), dim3(64 * NW), 0,
+    hipLaunchKernelGGL((scan_kernel<T, K, LPC, CPL, NW, PREP, NT, PK, SHORT, KX>), dim3((unsigned)blocks), dim3(64 * NW), 0,
                        stream, p);
     return hipGetLastError();
 }
@@ -687,23 +693,32 @@ hipError_t launch_tile(ScanArgs p, hipStream_t stream) {
 #ifndef GDN_DECODE_NW
 #define GDN_DECODE_NW 4
 #endif
-template <typename T, int K, bool PREP, bool PK>
+template <typename T, int K, bool PREP, bool PK, bool KX>
 hipError_t launch_k(const ScanArgs& p, hipStream_t stream) {
     constexpr int LPC = K >= 64 ? 16 : 8;
     constexpr int CPL = K >= 256 ? (GDN_DECODE_CPL > 1 ? GDN_DECODE_CPL / 2 : 1) : GDN_DECODE_CPL;
     // calls with more tokens than sequences hold short sequences: SHORT instances
-    if (p.N > p.B) return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, PK, true>(p, stream);
-    return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, PK, false>(p, stream);
+    if (p.N > p.B) return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, PK, true, KX>(p, stream);
+    return launch_tile<T, K, LPC, CPL, GDN_DECODE_NW, PREP, true, PK, false, KX>(p, stream);
 }
 
+// Key widths 32, 64, 128 and 256 run exactly; any other width up to 256 runs on the next of them
+// with the lanes' elements past K zero (element-wise row accesses).
 template <typename T, bool PREP, bool PK>
 hipError_t launch_t(const ScanArgs& p, hipStream_t stream) {
     switch (p.K) {
-        case 32: return launch_k<T, 32, PREP, PK>(p, stream);
-        case 64: return launch_k<T, 64, PREP, PK>(p, stream);
-        case 128: return launch_k<T, 128, PREP, PK>(p, stream);
-        case 256: return launch_k<T, 256, PREP, PK>(p, stream);
-        default: return hipErrorInvalidValue;
+        case 32: return launch_k<T, 32, PREP, PK, true>(p, stream);
+        case 64: return launch_k<T, 64, PREP, PK, true>(p, stream);
+        case 128: return launch_k<T, 128, PREP, PK, true>(p, stream);
+        case 256: return launch_k<T, 256, PREP, PK, true>(p, stream);
+        default: break;
+    }
+    if (p.K < 1 || p.K > 256) return hipErrorInvalidValue;
+    switch (padded_key_width(p.K)) {
+        case 32: return launch_k<T, 32, PREP, PK, false>(p, stream);
+        case 64: return launch_k<T, 64, PREP, PK, false>(p, stream);
+        case 128: return launch_k<T, 128, PREP, PK, false>(p, stream);
+        default: return launch_k<T, 256, PREP, PK, false>(p, stream);
     }
 }
 

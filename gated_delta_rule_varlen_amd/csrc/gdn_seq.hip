@@ -18,6 +18,8 @@
 //         r = g (k^.s),  delta = beta (v - r),  out = scale (g (q^.s) + delta (q^.k^)),
 //         s <- g s + delta k^;
 //   * outputs of a chunk are collected in LDS and written back as 16-byte vectors;
+//   * key widths other than 32, 64, 128 and 256 run on the next compiled width with the elements
+//     past K zero (element-wise q/k and state accesses; "KX = false" instances);
 //   * blocks take the sequences longest first (ranked in-block by length, for up to 64 sequences);
 //   * with a per-key-channel decay (GDN_GATE_PER_KEY; "PK" instances) the staging also evaluates
 //     the decay of every (token, key channel) once per block into LDS, and the recurrence decays
@@ -91,9 +93,11 @@ struct Fetch {
 
 constexpr int kRankedSeqs = 64;  // sequences ranked by length in-block (more keep their order)
 
-template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool PK>
+template <typename T, int K, int LPC, int CPL, int NW, bool PREP, bool PK, bool KX>
 __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     static_assert(!(PK && PREP), "the per-key decay is evaluated in-kernel from raw inputs");
+    // K is the compiled key width; rows are Kr wide (Kr < K: the elements past Kr are zero)
+    const int Kr = KX ? K : p.K;
     using C_ = Cfg<T, K, LPC, CPL, NW, PREP, PK>;
     using TS = typename C_::TS;
     constexpr int EPL = C_::EPL, WC = C_::WC, BC = C_::BC, TC = C_::TC;
@@ -147,10 +151,10 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const bool valid = (v0 + cw + c < p.V) && p.state_in != nullptr;
-        const float* sp = p.state_in + (col0 + v0 + cw + c) * K;
+        const float* sp = p.state_in + (col0 + v0 + cw + c) * Kr;
 #pragma unroll
         for (int i = 0; i < EPL / 4; ++i) {
-            const f32x4 v = valid ? *reinterpret_cast<const f32x4*>(sp + 4 * (gl + LPC * i)) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 v = valid ? ld_row4<KX, false>(sp, 4 * (gl + LPC * i), Kr) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[c][4 * i + e] = v[e];
         }
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     CaptureRow crow{};
     if (p.cap > 0) {
         captured = captured_tokens(p.counts, p.active, p.cap, b, end - start);
-        crow = capture_row(p.capsule, b, p.cap, p.H, p.HQ, K, p.V);
+        crow = capture_row(p.capsule, b, p.cap, p.H, p.HQ, Kr, p.V);
     }
     const bool cap_d = gl < CPL && v0 + cw + gl < p.V;  // this lane records delta of its output column
 
@@ -187,23 +191,29 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
 #pragma unroll
                 for (int e = 0; e < SVEC; ++e) f.gk[ps * SVEC + e] = 0.0f;
                 if (ti < n && ti < TC) {
-                    const size_t gi = ((size_t)(t0 + ti) * p.H + h) * K + rl * SVEC;
+                    const size_t gi = ((size_t)(t0 + ti) * p.H + h) * Kr + rl * SVEC;
+                    if constexpr (KX) {
 #pragma unroll
-                    for (int e = 0; e < SVEC; e += 4) {
-                        const f32x4 av = load4_gate<T>(p.a, p.gate_dtype, gi + e);
+                        for (int e = 0; e < SVEC; e += 4) {
+                            const f32x4 av = load4_gate<T>(p.a, p.gate_dtype, gi + e);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) f.gk[ps * SVEC + e + j] = av[j];
+                            for (int j = 0; j < 4; ++j) f.gk[ps * SVEC + e + j] = av[j];
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < SVEC; ++e)
+                            if (rl * SVEC + e < Kr) f.gk[ps * SVEC + e] = load_any(p.a, p.gate_dtype, gi + e);
                     }
                 }
             }
             if (ti < n) {
                 const size_t t = (size_t)(t0 + ti);
                 if constexpr (PREP) {
-                    f.q[ps] = *reinterpret_cast<const u32x4*>(p.qk_prep + (t * p.HQ + kh) * K + rl * SVEC);
-                    f.k[ps] = *reinterpret_cast<const u32x4*>(p.qk_prep + (((size_t)p.N + t) * p.HQ + kh) * K + rl * SVEC);
+                    f.q[ps] = ld_raw16<float, 4, KX>(p.qk_prep + (t * p.HQ + kh) * Kr, rl * SVEC, Kr);
+                    f.k[ps] = ld_raw16<float, 4, KX>(p.qk_prep + (((size_t)p.N + t) * p.HQ + kh) * Kr, rl * SVEC, Kr);
                 } else {
-                    f.q[ps] = *reinterpret_cast<const u32x4*>(xq + t * p.x.sq + (size_t)kh * K + rl * SVEC);
-                    f.k[ps] = *reinterpret_cast<const u32x4*>(xk + t * p.x.sk + (size_t)kh * K + rl * SVEC);
+                    f.q[ps] = ld_raw16<TS, SVEC, KX>(xq + t * p.x.sq + (size_t)kh * Kr, rl * SVEC, Kr);
+                    f.k[ps] = ld_raw16<TS, SVEC, KX>(xk + t * p.x.sk + (size_t)kh * Kr, rl * SVEC, Kr);
                 }
             }
         }
@@ -352,8 +362,8 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
                 const int nc = min(n, captured - (t0 - start));
                 for (int idx = tid; idx < nc; idx += NT) *crow.g(t0 - start + idx, h) = sg[buf][idx];
                 if (h == kh * p.G)
-                    for (int idx = tid; idx < nc * K; idx += NT)
-                        crow.k(t0 - start + idx / K, kh)[idx % K] = sk[buf][idx / K][idx % K];
+                    for (int idx = tid; idx < nc * Kr; idx += NT)
+                        crow.k(t0 - start + idx / Kr, kh)[idx % Kr] = sk[buf][idx / Kr][idx % Kr];
             }
             for (int i = 0; i < n; ++i) {
                 float q[EPL], k[EPL];
@@ -438,11 +448,11 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             if (v0 + cw + c >= p.V) continue;
-            float* sp = p.state_out + (col0 + v0 + cw + c) * K;
+            float* sp = p.state_out + (col0 + v0 + cw + c) * Kr;
 #pragma unroll
             for (int i = 0; i < EPL / 4; ++i)
-                *reinterpret_cast<f32x4*>(sp + 4 * (gl + LPC * i)) =
-                    f32x4{s[c][4 * i], s[c][4 * i + 1], s[c][4 * i + 2], s[c][4 * i + 3]};
+                st_row4<KX, false>(sp, 4 * (gl + LPC * i), Kr,
+                                   f32x4{s[c][4 * i], s[c][4 * i + 1], s[c][4 * i + 2], s[c][4 * i + 3]});
         }
     }
 
@@ -453,7 +463,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
             if (vt == 0) {
                 if (tid == 0) *crow.g(i, h) = 0.0f;
                 if (h == kh * p.G)
-                    for (int j = tid; j < K; j += NT) crow.k(i, kh)[j] = 0.0f;
+                    for (int j = tid; j < Kr; j += NT) crow.k(i, kh)[j] = 0.0f;
             }
             for (int j = tid; j < BC; j += NT)
                 if (v0 + j < p.V) crow.d(i, h)[v0 + j] = 0.0f;
@@ -461,7 +471,7 @@ __global__ __launch_bounds__(64 * NW) void seq_kernel(SeqArgs p) {
     }
 }
 
-template <typename T, int K, int LPC, int CPL, bool PREP, bool PK>
+template <typename T, int K, int LPC, int CPL, bool PREP, bool PK, bool KX>
 hipError_t launch_tile(SeqArgs p, hipStream_t stream) {
     constexpr int NW = 4;
     using C_ = Cfg<T, K, LPC, CPL, NW, PREP, PK>;
@@ -470,33 +480,42 @@ hipError_t launch_tile(SeqArgs p, hipStream_t stream) {
     if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
     p.n_blocks = (int)blocks;
     p.vec_ok = (p.V % C_::VVEC) == 0;
-    hipLaunchKernelGGL((seq_kernel<T, K, LPC, CPL, NW, PREP, PK>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((seq_kernel<T, K, LPC, CPL, NW, PREP, PK, KX>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
 // Tile choice: two columns per lane group when that still gives 4 blocks per CU, else one; for
 // K >= 128 and very few columns, 32-lane groups halve the columns per block once more.
-template <typename T, int K, bool PREP, bool PK>
+template <typename T, int K, bool PREP, bool PK, bool KX>
 hipError_t launch_k(const SeqArgs& p, hipStream_t stream) {
     constexpr int LPC = K >= 64 ? 16 : 8;
     constexpr int BC2 = 4 * (64 / LPC) * 2;
     const long long bh = (long long)p.B * p.H;
-    if (bh * ((p.V + BC2 - 1) / BC2) >= 1024) return launch_tile<T, K, LPC, 2, PREP, PK>(p, stream);
+    if (bh * ((p.V + BC2 - 1) / BC2) >= 1024) return launch_tile<T, K, LPC, 2, PREP, PK, KX>(p, stream);
     if constexpr (K >= 128) {
         constexpr int BC1 = 4 * (64 / LPC);
-        if (bh * ((p.V + BC1 - 1) / BC1) < 1024) return launch_tile<T, K, 32, 1, PREP, PK>(p, stream);
+        if (bh * ((p.V + BC1 - 1) / BC1) < 1024) return launch_tile<T, K, 32, 1, PREP, PK, KX>(p, stream);
     }
-    return launch_tile<T, K, LPC, 1, PREP, PK>(p, stream);
+    return launch_tile<T, K, LPC, 1, PREP, PK, KX>(p, stream);
 }
 
+// Key widths 32, 64, 128 and 256 run exactly; any other width up to 256 runs on the next of them
+// with the elements past K zero (element-wise row accesses).
 template <typename T, bool PREP, bool PK>
 hipError_t launch_t(const SeqArgs& p, hipStream_t stream) {
     switch (p.K) {
-        case 32: return launch_k<T, 32, PREP, PK>(p, stream);
-        case 64: return launch_k<T, 64, PREP, PK>(p, stream);
-        case 128: return launch_k<T, 128, PREP, PK>(p, stream);
-        case 256: return launch_k<T, 256, PREP, PK>(p, stream);
-        default: return hipErrorInvalidValue;
+        case 32: return launch_k<T, 32, PREP, PK, true>(p, stream);
+        case 64: return launch_k<T, 64, PREP, PK, true>(p, stream);
+        case 128: return launch_k<T, 128, PREP, PK, true>(p, stream);
+        case 256: return launch_k<T, 256, PREP, PK, true>(p, stream);
+        default: break;
+    }
+    if (p.K < 1 || p.K > 256) return hipErrorInvalidValue;
+    switch (padded_key_width(p.K)) {
+        case 32: return launch_k<T, 32, PREP, PK, false>(p, stream);
+        case 64: return launch_k<T, 64, PREP, PK, false>(p, stream);
+        case 128: return launch_k<T, 128, PREP, PK, false>(p, stream);
+        default: return launch_k<T, 256, PREP, PK, false>(p, stream);
     }
 }
 

@@ -149,7 +149,9 @@ gdn_status gdn_conv1d_varlen_capture(const gdn_conv_desc *desc, const void *x, c
  * (gate inputs are widened to fp32 first).  scale == 0 selects 1/sqrt(K); any other value, negative
  * included, is applied as given.
  * Constraints: B >= 1, N >= 0, HQ >= 1, H >= 1, H % HQ == 0, 1 <= K <= 256 (the pages' limit),
- * V >= 1; the library instantiates K in {32, 64, 128, 256} (GDN_ERR_UNSUPPORTED otherwise).
+ * V >= 1.  Every K in that range runs on DECODE, SEQ and prepare: K = 32, 64, 128 and 256 exactly,
+ * any other K on the next of those widths with the lanes' elements past K zero (element-wise row
+ * accesses, so those widths are slower); CHUNK and gdn_decode_step keep their own width lists.
  * gate_dtype is GDN_F32 or qkv_dtype.
  * ---------------------------------------------------------------------------------------------- */
 #define GDN_L2NORM 1u

@@ -90,7 +90,6 @@ def scan(abi, d, qkv=P, qk=None, gb=None, a=None, b=None, alog=None, dtb=None, s
         (dict(B=0), {}, "ERR_SHAPE"),
         (dict(HQ=3, H=4), {}, "ERR_SHAPE"),  # H % HQ != 0
         (dict(K=512), {}, "ERR_SHAPE"),  # the pages' limit: K <= 256
-        (dict(K=48), {}, "ERR_UNSUPPORTED"),  # valid, not instantiated
         (dict(V=0), {}, "ERR_SHAPE"),
         (dict(qkv_dtype=5), {}, "ERR_DTYPE"),
         (dict(qkv_dtype=1, gate_dtype=2), {}, "ERR_DTYPE"),
@@ -139,7 +138,7 @@ def decode_step(abi, cfields=None, sfields=None, x=P, w=P, out=P, off=P, a=None,
         (dict(W=9), {}, {}, "ERR_UNSUPPORTED"),
         (dict(flags=4), {}, {}, "ERR_UNSUPPORTED"),
         (dict(C=4 * 32 + 2 * 30), dict(V=30), {}, "ERR_UNSUPPORTED"),  # V % 4 != 0
-        ({}, dict(K=48), {}, "ERR_UNSUPPORTED"),
+        (dict(C=2 * 2 * 48 + 2 * 32), dict(K=48), {}, "ERR_UNSUPPORTED"),  # a width the fused step does not take
         ({}, dict(HQ=3), {}, "ERR_SHAPE"),
         ({}, {}, dict(w=None), "ERR_NULL"),
         ({}, {}, dict(off=None), "ERR_NULL"),
@@ -166,8 +165,8 @@ def test_prepare_host_validation(abi):
     assert L.gdn_prepare_qk_gates(ctypes.byref(d), P, None, None, None, None, None, None, None) == abi.ERR_NULL
     assert L.gdn_prepare_qk_gates(ctypes.byref(d), P, P, None, None, None, P, P, None) == abi.ERR_NULL
     assert L.gdn_prepare_qk_gates(ctypes.byref(d), P, None, None, None, None, P + 4, P, None) == abi.ERR_ALIGN
-    bad = scan_desc(abi, K=100)
-    assert L.gdn_prepare_qk_gates(ctypes.byref(bad), P, None, None, None, None, P, P, None) == abi.ERR_UNSUPPORTED
+    bad = scan_desc(abi, K=300)
+    assert L.gdn_prepare_qk_gates(ctypes.byref(bad), P, None, None, None, None, P, P, None) == abi.ERR_SHAPE
     # a call without tokens writes nothing, so it needs no buffers at all (and launches nothing)
     empty = scan_desc(abi, N=0)
     assert L.gdn_prepare_qk_gates(ctypes.byref(empty), None, None, None, None, None, None, None, None) == abi.OK
@@ -228,8 +227,8 @@ def scan_capture(abi, d, cap=4, counts=P, active=None, capsule=P, qkv=P, out=P, 
         ({}, dict(capsule=None), "ERR_NULL"),
         ({}, dict(capsule=P + 4), "ERR_ALIGN"),
         ({}, dict(cap=2**24), "ERR_OVERFLOW"),  # the capsule row width must be an int32
-        (dict(path=3), {}, "ERR_UNSUPPORTED"),  # capture is not recorded by the chunked form
-        (dict(K=48), {}, "ERR_UNSUPPORTED"),  # the recurrence's own checks still apply
+        (dict(path=3), {}, "ERR_UNSUPPORTED"),  # a shape the chunked form does not take
+        (dict(K=512), {}, "ERR_SHAPE"),  # the recurrence's own checks still apply
         ({}, dict(off=None), "ERR_NULL"),
         ({}, dict(out=None), "ERR_NULL"),
     ],
@@ -304,7 +303,7 @@ def test_prepare_strided_host_validation(abi):
     "fields,kw,want",
     [
         (dict(B=0), {}, "ERR_SHAPE"),
-        (dict(K=48), {}, "ERR_UNSUPPORTED"),
+        (dict(K=300), {}, "ERR_SHAPE"),
         (dict(path=3), {}, "ERR_UNSUPPORTED"),  # chunked path not eligible (fp32 I/O)
         ({}, dict(qkv=None), "ERR_NULL"),
         ({}, dict(off=None), "ERR_NULL"),
