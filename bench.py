@@ -411,6 +411,43 @@ def strided_comparison(torch, steps: int = 20):
     return res
 
 
+def mixed_comparison(torch, steps: int = 10):
+    """A serving batch of 255 single tokens and one 4096-token prefill (HQ=16, H=32, K=V=128, bf16):
+    the recurrence call on AUTO and on each forced path, microseconds per call with the workspace
+    allocated once (best of 3), and AUTO's time over the fastest forced path's."""
+    import workloads
+
+    w = workloads.mixed_batch()
+    p = Path(w, torch, "auto")
+    gdn = p.gdn
+    n = gdn.scan_workspace_bytes(p.y, w.B, HQ=w.HQ, H=w.H, K=w.K, V=w.V)
+    ws = torch.empty(max(int(n), 1), dtype=torch.uint8, device="cuda")
+    p.step()  # the conv output feeds the recurrence
+    torch.cuda.synchronize()
+    rec = {"workload": w.name, "N": w.N}
+    for path in ("auto", "decode", "seq", "chunk"):
+        kw = dict(HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=p.a, b=p.b, A_log=p.A_log, dt_bias=p.dt_bias, state_in=p.state,
+                  path=path, out=p.out, state_out=p.state, workspace=ws)
+        _, _, used = gdn.scan_varlen(p.y, p.offsets, **kw)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                gdn.scan_varlen(p.y, p.offsets, **kw)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            best = us if best is None else min(best, us)
+        rec[path] = {"path": used, "us": round(best, 1), "tokens_per_s": round(w.N / (best * 1e-6), 1)}
+    fastest = min(rec[q]["us"] for q in ("decode", "seq", "chunk"))
+    rec["auto_over_fastest_forced"] = round(rec["auto"]["us"] / fastest, 3)
+    del p, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle (conv + scan, fp64, OpenMP) on a bounded sample of the same workload:
     whole sequences, taken in order until about budget_s seconds of CPU work."""
@@ -469,7 +506,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "long", "edge_fp16", "tiny_fp32", "verify"])
+                    choices=["decode", "prefill", "long", "edge_fp16", "tiny_fp32", "verify", "mixed"])
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "seq", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="skip the secondary prefill measurement")
@@ -528,6 +565,7 @@ def main():
                         "long": secondary(torch, workloads.long_single(), 5, 5),
                         "decode_step_fused_vs_two_call": fused_comparison(torch),
                         "speculative_verify_capture": verify_comparison(torch),
+                        "mixed_batch": mixed_comparison(torch),
                         "per_key_decay": per_key_comparison(torch),
                         "strided_qkv": strided_comparison(torch),
                         "cache_flushed": cache_flushed(torch),

@@ -97,12 +97,15 @@ bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay, int c
 }
 
 // AUTO: DECODE for at most kDecodeShortTokens tokens per sequence on average (single tokens and
-// short blocks stream the state once); CHUNK when eligible, the average sequence fills at least one
-// chunk of 64 tokens and the workspace suffices; SEQ otherwise.
+// short blocks stream the state once); past that CHUNK when eligible and the workspace suffices,
+// SEQ otherwise.  The lengths themselves stay on the device, so the choice sees only N and B: at
+// B = 256 (H = 32, K = V = 128) the chunked form ties SEQ at 12 tokens per sequence, is ahead from
+// 16 on, and keeps a batch that mixes single tokens with one long prefill off the token-sequential
+// chain of the long sequence (about 4.5x faster than SEQ with one 4096-token sequence).
 int resolve_path(const gdn_scan_desc* d, bool prepared, bool has_decay, int cap, size_t ws_bytes) {
     if (d->path != GDN_PATH_AUTO) return d->path;
     if ((long long)d->N <= (long long)gdn::kDecodeShortTokens * d->B) return GDN_PATH_DECODE;
-    if (chunk_eligible(d, prepared, has_decay, cap) && (long long)d->N >= 64ll * d->B &&
+    if (chunk_eligible(d, prepared, has_decay, cap) &&
         ws_bytes >= gdn::chunked_workspace_bytes(d->B, d->N, d->HQ, d->H, d->K, d->V))
         return GDN_PATH_CHUNK;
     return GDN_PATH_SEQ;

@@ -161,7 +161,7 @@ gdn_status gdn_conv1d_varlen_capture(const gdn_conv_desc *desc, const void *x, c
 #define GDN_GATE_PER_KEY 16u
 
 typedef enum gdn_path {
-    GDN_PATH_AUTO = 0,   /* DECODE when N <= 8*B; else CHUNK when eligible, N >= 64*B and ws_bytes suffices; else SEQ */
+    GDN_PATH_AUTO = 0,   /* DECODE when N <= 8*B; else CHUNK when eligible and ws_bytes suffices; else SEQ */
     GDN_PATH_DECODE = 1, /* state streamed once per call; sequences of up to 8 tokens streamed column by column */
     GDN_PATH_SEQ = 2,    /* token-sequential recurrence with the state resident in registers */
     GDN_PATH_CHUNK = 3   /* chunked WY form (chunk 64); needs a workspace and positive decays */

@@ -10,3 +10,5 @@ def get(name: str) -> workloads.Workload:
 
 
 ALL = ("tiny_fp32", "decode", "prefill", "long", "edge_fp16")
+# further full-size workloads: the speculative verification step and a mixed decode/prefill batch
+EXTRA = ("verify", "mixed")

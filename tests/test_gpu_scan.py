@@ -56,6 +56,7 @@ SAMPLES = {
     "long": ([0, 9], [0, 1, 37, 64, 100, 127]),
     "edge_fp16": (None, None),
     "verify": ([0, 5, 31], None),
+    "mixed": ([0, 17, 31], None),
 }
 PARITY = [(n, p, m) for n in cases.ALL for p in ("decode", "seq") for m in ("fused", "prepared")
           if not (n == "long" and p == "decode")]
@@ -63,6 +64,8 @@ PARITY = [(n, p, m) for n in cases.ALL for p in ("decode", "seq") for m in ("fus
 PARITY += [("decode", "chunk", "fused"), ("prefill", "chunk", "fused"), ("long", "chunk", "fused")]
 # the speculative verification step (B=256 x 5 tokens) at full size: DECODE's short-sequence form and SEQ
 PARITY += [("verify", "decode", "fused"), ("verify", "decode", "prepared"), ("verify", "seq", "fused")]
+# a serving batch mixing 255 single tokens with one 4096-token prefill, on every path
+PARITY += [("mixed", "decode", "fused"), ("mixed", "seq", "fused"), ("mixed", "chunk", "fused"), ("mixed", "auto", "fused")]
 
 
 def check_against_oracle(w, name, out, st, path):
@@ -86,13 +89,13 @@ def test_scan_matches_oracle(torch, name, path, mode):
     w = cases.get(name)
     print(f"[scan parity] {name} path={path} mode={mode} B={w.B} N={w.N} H={w.H} K={w.K} V={w.V}", flush=True)
     out, st, used = gpu_scan(torch, w, path, mode == "prepared")
-    assert used == path
+    assert used == path or path == "auto"
     assert np.all(np.isfinite(f64(out))), "an output element was left unwritten"
-    check_against_oracle(w, name, out, st, path)
+    check_against_oracle(w, name, out, st, used)
 
 
 @pytest.mark.parametrize("name,want", [("tiny_fp32", "seq"), ("decode", "decode"), ("edge_fp16", "seq"),
-                                       ("prefill", "chunk")])
+                                       ("prefill", "chunk"), ("verify", "decode"), ("mixed", "chunk")])
 def test_auto_path_choice(torch, name, want):
     w = cases.get(name)
     _, _, used = gpu_scan(torch, w, "auto", False)

@@ -210,6 +210,13 @@ def spec_verify(seed: int = 106) -> Workload:
                 D=1, io="bf16", conv_state_dtype="f32", conv_state_std=1.0, state_std=0.1)
 
 
+def mixed_batch(seed: int = 107) -> Workload:
+    """A serving batch that mixes decode and prefill: 255 sequences x 1 token and one 4096-token
+    sequence (N = 4351), HQ=16, H=32, K=V=128, bf16, fp32 state and conv window."""
+    return make(name="mixed_b256_255x1_1x4096_h32_k128", seed=seed, lengths=[1] * 255 + [4096], HQ=16, H=32,
+                K=128, V=128, W=4, D=1, io="bf16", conv_state_dtype="f32", conv_state_std=1.0, state_std=0.1)
+
+
 NAMED = {
     "tiny_fp32": tiny_fp32,
     "decode": decode_step,
@@ -217,6 +224,7 @@ NAMED = {
     "long": long_single,
     "edge_fp16": edge_fp16,
     "verify": spec_verify,
+    "mixed": mixed_batch,
 }
 
 # Offsets patterns that every entry point must reject by writing nothing.
