@@ -1,11 +1,11 @@
 """Benchmark of the varlen gated delta-rule hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of seeded synthetic input, with inputs resident
-in HBM: the varlen causal conv1d (its window updated in place) followed by the gated delta-rule
+in HBM: the varlen causal conv1d (its window carried to the next step) followed by the gated delta-rule
 recurrence (state updated in place).  The default workload is the decode step (B=256 sequences x 1
-token, HQ=16, H=32, K=V=128, bf16, fp32 state): gdn_conv1d_varlen then gdn_scan_varlen on its DECODE
-path (--fused-step runs the single-launch gdn_decode_step instead; "also" compares the two forms at
-several batch sizes).
+token, HQ=16, H=32, K=V=128, bf16, fp32 state) as one gdn_decode_step launch, the new conv window
+written to a second buffer that swaps with the first every step (--two-call runs gdn_conv1d_varlen
+then gdn_scan_varlen on its DECODE path instead; "also" compares the forms at several batch sizes).
 The prefill workload (B=8, lengths ~ U[512, 4096]) and the long single sequence (N=65536, H=16) are
 measured too and reported in "also", with the arithmetic roofline of the path they take, and so is a
 speculative verification step (B=256 x 5 tokens) with and without the capture of 4 tokens per
@@ -86,10 +86,12 @@ def measured_traffic(record: str, sources=SCAN_SOURCES):
 class Path:
     """Device-resident inputs of one workload and one step of the hot path."""
 
-    def __init__(self, w, torch, path: str, fused_step: bool = False, cap: int = 0, gate_per_key: bool = False):
+    def __init__(self, w, torch, path: str, fused_step: bool = False, cap: int = 0, gate_per_key: bool = False,
+                 window_in_place: bool = False):
         import gated_delta_rule_varlen_amd as gdn
 
         self.gdn, self.torch, self.w, self.path, self.fused_step, self.cap = gdn, torch, w, path, fused_step, cap
+        self.window_in_place = window_in_place
         self.gate_per_key = gate_per_key
         dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -117,6 +119,10 @@ class Path:
         self.state = dev(w.state, "f32")
         if self.state is None:
             self.state = torch.zeros((w.B, w.H, w.V, w.K), dtype=torch.float32, device="cuda")
+        # the fused step writes the new window into a second buffer and the two swap every step
+        # (with an in-place window it takes its key-head form, which is slower at large batches)
+        self.conv_state_next = (self.conv_state.clone() if fused_step and not window_in_place
+                                and self.conv_state is not None else self.conv_state)
         self.y = torch.empty_like(self.x)
         self.out = torch.empty((w.N, w.H, w.V), dtype=self.x.dtype, device="cuda")
         if cap > 0:
@@ -133,12 +139,13 @@ class Path:
             if ev is not None:
                 ev[0].record()
             gdn.decode_step(self.x, self.conv_w, self.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, bias=self.conv_b,
-                            conv_state_in=self.conv_state, conv_state_out=self.conv_state, dilation=w.D,
+                            conv_state_in=self.conv_state, conv_state_out=self.conv_state_next, dilation=w.D,
                             silu=w.silu, a=self.a, b=self.b, A_log=self.A_log, dt_bias=self.dt_bias,
                             state_in=self.state, state_out=self.state, l2norm=w.l2norm, softplus=w.softplus,
                             sigmoid=w.sigmoid, out=self.out)
             if ev is not None:
                 ev[1].record()
+            self.conv_state, self.conv_state_next = self.conv_state_next, self.conv_state
             return "decode_step"
         scan_kw = dict(HQ=w.HQ, H=w.H, K=w.K, V=w.V, a=self.a, b=self.b, A_log=self.A_log, dt_bias=self.dt_bias,
                        state_in=self.state, l2norm=w.l2norm, softplus=w.softplus, sigmoid=w.sigmoid, path=self.path,
@@ -166,24 +173,30 @@ class Path:
         return used
 
 
+EV_EVERY = 8
+
+
 def time_path(p: "Path", steps: int, warmup: int):
     torch = p.torch
     for _ in range(warmup):
         used = p.step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # the recurrence launch is bracketed by events on every EV_EVERY-th step of the timed region
+    # (events on every step add a few microseconds to each short step)
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in range(0, steps, EV_EVERY)}
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        used = p.step(evs[i])
+        used = p.step(evs.get(i))
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
-    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs.values()]))
     return total_ms / steps, scan_ms, used, wall
 
 
@@ -230,8 +243,9 @@ def secondary(torch, wl, steps: int, warmup: int):
 
 
 def fused_comparison(torch, batches=(1, 8, 256), steps: int = 100):
-    """Whole decode steps (HQ=16, H=32, K=V=128, bf16) as one gdn_decode_step launch and as two
-    launches, at several batch sizes: microseconds per step, launch cost included (best of 3)."""
+    """Whole decode steps (HQ=16, H=32, K=V=128, bf16) as one gdn_decode_step launch (new window in a
+    second buffer, and in place) and as two launches, at several batch sizes: microseconds per
+    step, launch cost included (best of 3)."""
     import workloads
 
     res = {}
@@ -239,9 +253,10 @@ def fused_comparison(torch, batches=(1, 8, 256), steps: int = 100):
         w = workloads.make(name=f"decode_b{B}", seed=102, lengths=[1] * B, HQ=16, H=32, K=128, V=128, W=4, D=1,
                            io="bf16", conv_state_dtype="f32", conv_state_std=1.0, state_std=0.1)
         rec = {}
-        for fused in (False, True):
-            p = Path(w, torch, "decode", fused_step=fused)
-            rec["fused_us" if fused else "two_call_us"] = round(min(time_path(p, steps, 10)[0] for _ in range(3)) * 1e3, 2)
+        for name, fused, inplace in (("two_call_us", False, True), ("fused_us", True, False),
+                                     ("fused_window_in_place_us", True, True)):
+            p = Path(w, torch, "decode", fused_step=fused, window_in_place=inplace)
+            rec[name] = round(min(time_path(p, steps, 10)[0] for _ in range(3)) * 1e3, 2)
             del p
         res[f"B{B}"] = rec
     torch.cuda.empty_cache()
@@ -510,9 +525,9 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "seq", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="skip the secondary prefill measurement")
-    ap.add_argument("--fused-step", action="store_true",
-                    help="decode: run the step as one gdn_decode_step launch instead of gdn_conv1d_varlen + "
-                         "gdn_scan_varlen (faster for small batches, slower at B=256)")
+    ap.add_argument("--two-call", action="store_true",
+                    help="decode: run the step as gdn_conv1d_varlen + gdn_scan_varlen instead of one "
+                         "gdn_decode_step launch (the default, faster at every batch size measured)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device-to-device copy (reference for HBM counters and achievable bandwidth)")
     args = ap.parse_args()
@@ -532,7 +547,7 @@ def main():
         return
     w = workloads.NAMED[args.workload]()
     # a decode step (at most one token per sequence) can run as one fused launch
-    fused = (args.fused_step and args.workload == "decode" and args.path in ("auto", "decode")
+    fused = (not args.two_call and args.workload == "decode" and args.path in ("auto", "decode")
              and int(np.max(np.diff(w.offsets))) <= 1)
     p = Path(w, torch, args.path, fused_step=fused)
     ms, scan_ms, used, _ = time_path(p, args.steps, args.warmup)
@@ -552,7 +567,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "HQ": w.HQ, "H": w.H, "K": w.K, "V": w.V,
                    "conv_W": w.W, "conv_D": w.D, "path": used, "parallelism": "single GPU"},
-        "roofline": roofline(w, scan_ms, args.workload, "decode_kernel (conv + recurrence)" if fused else "scan_kernel",
+        "roofline": roofline(w, scan_ms, args.workload, "decode_col_kernel (conv + recurrence)" if fused else "scan_kernel",
                              fused_step=fused),
     }
     if used not in ("decode", "decode_step"):

@@ -162,6 +162,30 @@ def test_decode_workload_full_size(torch):
     assert_close(f64(s1)[:nb], s_ref, CHAIN_STATE_TOL, "state")
 
 
+@pytest.mark.parametrize("state_inplace", [False, True])
+def test_decode_workload_full_size_separate_window(torch, state_inplace):
+    """The benchmark's decode step with the new window in a separate buffer (the column-tile form of
+    large batches; the state updated in place or not): identical to the two-call chain, bit for bit,
+    and sampled sequences against the oracle."""
+    import gated_delta_rule_varlen_amd as gdn
+
+    w = cases.get("decode")
+    o2, s2, c2 = run_chain(torch, w)
+    t = inputs(w)
+    cst_out = sentinel((w.B, w.C, w.L), w.conv_state_dtype)
+    st_out = t["st"] if state_inplace else sentinel((w.B, w.H, w.V, w.K), "f32")
+    o1, s1, c1 = gdn.decode_step(t["x"], t["cw"], t["off"], HQ=w.HQ, H=w.H, K=w.K, V=w.V, bias=t["cb"],
+                                 conv_state_in=t["cst"], conv_state_out=cst_out, dilation=w.D, silu=w.silu,
+                                 conv_state_dtype=torch.float32, a=t["a"], b=t["b"], A_log=t["A_log"],
+                                 dt_bias=t["dtb"], state_in=t["st"], state_out=st_out, l2norm=w.l2norm,
+                                 softplus=w.softplus, sigmoid=w.sigmoid, scale=w.scale,
+                                 out=sentinel((w.N, w.H, w.V), w.io))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o1), bits(o2))
+    assert np.array_equal(bits(s1), bits(s2))
+    assert np.array_equal(bits(c1), bits(c2))
+
+
 def test_malformed_offsets_and_long_sequences_write_nothing(torch):
     w = small("contract", 399, lengths=[1, 1, 0, 1], HQ=1, H=2, K=64, V=64)
     import gated_delta_rule_varlen_amd as gdn  # noqa: F401
