@@ -57,6 +57,8 @@ def lib():
             L.gdn_oracle_scan.restype = i32
             L.gdn_oracle_threads.argtypes = []
             L.gdn_oracle_threads.restype = i32
+            L.gdn_oracle_set_threads.argtypes = [i32]
+            L.gdn_oracle_set_threads.restype = None
             del f64p
             _lib = L
     return _lib
@@ -188,3 +190,8 @@ def scan(qkv, offsets, *, HQ, H, K, V, qkv_dtype, gate_dtype=None, a=None, b=Non
 
 def threads() -> int:
     return int(lib().gdn_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the following calls (for timing the oracle at a chosen width)."""
+    lib().gdn_oracle_set_threads(int(n))

@@ -341,6 +341,15 @@ int gdn_oracle_scan(int B, int N, int HQ, int H, int K, int V, int qkv_dtype, in
     return failed ? 2 : 0;
 }
 
+/* Threads for the following calls (test infrastructure: timing the oracle at a chosen width). */
+void gdn_oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of OpenMP threads the scan will use (1 without OpenMP). */
 int gdn_oracle_threads(void) {
 #ifdef _OPENMP
