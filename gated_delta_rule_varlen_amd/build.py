@@ -17,6 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_conv.hip", "gdn_prepare.hip", "gdn_scan.hip", "gdn_seq.hip", "gdn_chunk.hip",
+           "gdn_chunk_k64.hip", "gdn_chunk_k128.hip", "gdn_chunk_k256.hip",
            "gdn_decode.hip", "gdn_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

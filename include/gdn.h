@@ -151,7 +151,8 @@ gdn_status gdn_conv1d_varlen_capture(const gdn_conv_desc *desc, const void *x, c
  * Constraints: B >= 1, N >= 0, HQ >= 1, H >= 1, H % HQ == 0, 1 <= K <= 256 (the pages' limit),
  * V >= 1.  Every K in that range runs on DECODE, SEQ and prepare: K = 32, 64, 128 and 256 exactly,
  * any other K on the next of those widths with the lanes' elements past K zero (element-wise row
- * accesses, so those widths are slower); CHUNK and gdn_decode_step keep their own width lists.
+ * accesses, so those widths are slower); CHUNK (K and V multiples of 8) and gdn_decode_step keep
+ * their own width rules.
  * gate_dtype is GDN_F32 or qkv_dtype.
  * ---------------------------------------------------------------------------------------------- */
 #define GDN_L2NORM 1u
@@ -245,8 +246,13 @@ gdn_status gdn_prepare_qk_gates_strided(const gdn_scan_desc *desc, const gdn_qkv
  *   dev_status [1] int32 (NULL ok); path_used: HOST int32 receiving the gdn_path that ran (NULL ok)
  * GDN_PATH_CHUNK requires fused mode with a decay input (not needed when N = 0) and GDN_SOFTPLUS
  * (so every decay is finite and positive), GDN_L2NORM, the retrieval term (no GDN_NO_RETRIEVE),
- * bf16 or fp16 qkv, and K = V = 64 or K = V = 128; otherwise GDN_ERR_UNSUPPORTED.  Its intra-chunk contractions run on bf16 matrix cores with fp32
- * accumulation (the state itself stays fp32).
+ * bf16 or fp16 qkv, and K and V multiples of 8 (the chunked rule of the paged_ssm.rs page's host
+ * fn delta(): K != V included); otherwise GDN_ERR_UNSUPPORTED.  K runs on the next of 64, 128 and
+ * 256 and V in parts of at most 128 columns (one block each), with the keys and columns past K and
+ * V zero.  Long sequences are cut into segments that run in parallel at K <= 64 with V <= 64 and at
+ * 65 <= K <= 128 with 33 <= V <= 128; other widths run each sequence in one piece.  Its
+ * intra-chunk contractions run on bf16 matrix cores with fp32 accumulation (the state itself
+ * stays fp32).
  * ---------------------------------------------------------------------------------------------- */
 gdn_status gdn_scan_varlen(const gdn_scan_desc *desc, const void *qkv, const float *qk_prep, const float *gb_prep,
                            const void *a, const void *b, const float *A_log, const float *dt_bias,
