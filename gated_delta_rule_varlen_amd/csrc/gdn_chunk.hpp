@@ -173,44 +173,40 @@ struct ChunkArgs {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
+// MFMA operands of an I/O type: bf16 I/O runs on bf16 operands (v_mfma_f32_16x16x32_bf16) and fp16
+// I/O on fp16 operands (v_mfma_f32_16x16x32_f16, same rate), so the raw q, k and v rows are
+// operands as they are and, with fp16 I/O, every operand keeps fp16's 11-bit significand.  pk
+// rounds two fp32 values to the type (nearest even, one v_cvt_pk_*_f32); it also rounds outputs.
+template <typename T>
+struct Op;
+template <>
+struct Op<BF16> {
+    using v8 = bf16x8;
+    static __device__ __forceinline__ f32x4 mma(v8 a, v8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pk(float lo, float hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+    }
+};
+template <>
+struct Op<F16> {
+    using v8 = f16x8;
+    static __device__ __forceinline__ f32x4 mma(v8 a, v8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pk(float lo, float hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+    }
+};
 __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-// two values rounded to bf16 (nearest even) in one v_cvt_pk_bf16_f32
-__device__ __forceinline__ uint32_t bf2(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
-// two values rounded to the I/O type (nearest even)
-template <typename T>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    if constexpr (std::is_same<T, BF16>::value) return bf2(lo, hi);
-    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
-}
-// eight 16-bit inputs of the I/O type as bf16 MFMA operand bits (bf16 inputs are used as they are)
-template <typename T>
-__device__ __forceinline__ u32x4 to_bf16x8(u32x4 raw) {
-    if constexpr (std::is_same<T, BF16>::value) {
-        return raw;
-    } else {
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // (the element goes through a scalar: a bit cast of the subscript itself was compiled to
-            // read element 0)
-            const uint32_t x = raw[e];
-            const f16x2 hv = __builtin_bit_cast(f16x2, x);
-            o[e] = bf2((float)hv[0], (float)hv[1]);
-        }
-        return o;
-    }
-}
 // sum of squares of eight 16-bit inputs, fp32 (plain FMAs; v_dot2 would need a bit cast of each
 // vector element, which was compiled to read element 0 every time)
 template <typename T>
@@ -230,19 +226,24 @@ __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x
 __device__ __forceinline__ int tf_tile(int f) { return f < 2 ? f : 2 + (f - 2) / 2; }  // token tile of T fragment f
 __device__ __forceinline__ int tf_blk(int f) { return f < 2 ? 0 : (f - 2) % 2; }    // its 32-block
 
-// Operand lane layout of v_mfma_f32_16x16x32_bf16: lane l holds row l%16 and inner elements
+// Operand lane layout of v_mfma_f32_16x16x32_{bf16,f16}: lane l holds row l%16 and inner elements
 // 8(l/16)..+7; the accumulator lane l holds rows 4(l/16)..+3 of column l%16.
 // Plain fragment: 16 rows x 32 inner elements from `base` (row stride ld).
-__device__ __forceinline__ bf16x8 frag(const uint16_t* base, int ld, int lane) {
-    return *reinterpret_cast<const bf16x8*>(base + (lane & 15) * ld + 8 * (lane >> 4));
+template <typename T>
+__device__ __forceinline__ typename Op<T>::v8 frag(const uint16_t* base, int ld, int lane) {
+    return *reinterpret_cast<const typename Op<T>::v8*>(base + (lane & 15) * ld + 8 * (lane >> 4));
 }
 // Accumulator tiles for rows 0..15 (lo) and 16..31 (hi) of a 32-row block, as one operand whose
 // inner order is the split order.
-__device__ __forceinline__ bf16x8 pack_acc(f32x4 lo, f32x4 hi) {
-    return __builtin_bit_cast(bf16x8, u32x4{bf2(lo[0], lo[1]), bf2(lo[2], lo[3]), bf2(hi[0], hi[1]), bf2(hi[2], hi[3])});
+template <typename T>
+__device__ __forceinline__ typename Op<T>::v8 pack_acc(f32x4 lo, f32x4 hi) {
+    return __builtin_bit_cast(typename Op<T>::v8, u32x4{Op<T>::pk(lo[0], lo[1]), Op<T>::pk(lo[2], lo[3]),
+                                                        Op<T>::pk(hi[0], hi[1]), Op<T>::pk(hi[2], hi[3])});
 }
+template <typename T>
 __device__ __forceinline__ u32x4 pack8(const float* x, float s) {
-    return u32x4{bf2(x[0] * s, x[1] * s), bf2(x[2] * s, x[3] * s), bf2(x[4] * s, x[5] * s), bf2(x[6] * s, x[7] * s)};
+    return u32x4{Op<T>::pk(x[0] * s, x[1] * s), Op<T>::pk(x[2] * s, x[3] * s), Op<T>::pk(x[4] * s, x[5] * s),
+                 Op<T>::pk(x[6] * s, x[7] * s)};
 }
 template <typename T>
 __device__ __forceinline__ void unpack8(u32x4 raw, float (&v)[8]) {
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     for (int i = 0; i < NI; ++i) {
         const int ti = 16 * w + TPI * i + tsub;
         const float rk = rsqrtf(group_sum<LPT>(sumsq8<T>(kr[i])) + 1e-12f);
-        *reinterpret_cast<u32x4*>(&r0.kn[ti][8 * pc]) = to_bf16x8<T>(kr[i]);
+        *reinterpret_cast<u32x4*>(&r0.kn[ti][8 * pc]) = kr[i];
         if (pc == 0) {
             s_rk[ti] = rk;
             rkout[ti] = rk;
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
             f32x4 a = zero4();
 #pragma unroll
             for (int kk = 0; kk < K; kk += 32)
-                a = mma_bf16(frag(&r0.kn[16 * it][kk], K + kPadRow, lane), frag(&r0.kn[16 * w][kk], K + kPadRow, lane), a);
+                a = Op<T>::mma(frag<T>(&r0.kn[16 * it][kk], K + kPadRow, lane), frag<T>(&r0.kn[16 * w][kk], K + kPadRow, lane), a);
             const int ia = 16 * it + 4 * g;
             const f32x4 g_ia = *reinterpret_cast<const f32x4*>(&s_gam[ia]);
             const f32x4 b_ia = *reinterpret_cast<const f32x4*>(&s_beta[ia]);
@@ -513,7 +514,7 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
             v[e] = (j0 >> 4) <= it ? tm[i][j0 + e] : 0.0f;
             v[4 + e] = (j1 >> 4) <= it ? tm[i][j1 + e] : 0.0f;
         }
-        *reinterpret_cast<u32x4*>(tout + f * 512 + 8 * lane) = pack8(v, 1.0f);
+        *reinterpret_cast<u32x4*>(tout + f * 512 + 8 * lane) = pack8<T>(v, 1.0f);
     }
 }
 
@@ -542,9 +543,10 @@ __device__ __forceinline__ int tpos(int idx, int t) {
     return 8 * (unit ^ ((idx >> kSwz) & 7)) + 4 * (q >> 2) + (t & 3);
 }
 // split fragment of a transposed tile: rows idx0 + l%16, the tokens of 32-block jj
-__device__ __forceinline__ bf16x8 frag_t(const uint16_t* tile, int ld, int idx0, int jj, int lane) {
+template <typename T>
+__device__ __forceinline__ typename Op<T>::v8 frag_t(const uint16_t* tile, int ld, int idx0, int jj, int lane) {
     const int idx = idx0 + (lane & 15);
-    return *reinterpret_cast<const bf16x8*>(tile + idx * ld + 8 * ((4 * jj + (lane >> 4)) ^ ((idx >> kSwz) & 7)));
+    return *reinterpret_cast<const typename Op<T>::v8*>(tile + idx * ld + 8 * ((4 * jj + (lane >> 4)) ^ ((idx >> kSwz) & 7)));
 }
 
 // kn, qn and vt are last read before a chunk's middle barrier and are written for the next chunk
@@ -588,6 +590,7 @@ constexpr int kMain = 0, kMainCapture = 1, kSummary = 2;
 template <typename T, int K, int VT, int MODE, int VTW>
 __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(ChunkArgs p) {
     using TS = typename T::storage;
+    using OpV = typename Op<T>::v8;
     constexpr bool SUMMARY = MODE == kSummary, CAPTURE = MODE == kMainCapture;
     constexpr int NWV = VT / (16 * VTW);  // waves
     static_assert(K % 32 == 0 && VT % (16 * VTW) == 0 && (!SUMMARY || K % (16 * NWV) == 0), "tile shapes");
@@ -770,7 +773,7 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
             Bf.beta[lane] = R.beta;
             Bf.eg[lane] = p.scale * eg;
             Bf.bx[lane] = R.beta * eg * R.rk;
-            Bf.ud[lane] = fexp(gC - R.gam) * R.rk;
+            Bf.ud[lane] = std::is_same<T, F16>::value ? fexp(gC - R.gam) : fexp(gC - R.gam) * R.rk;
             Bf.rk[lane] = R.rk;
             if (lane == 0) Bf.gc[0] = fexp(gC);
             // the previous token's G, read by the whole wave (a lane shuffle from an inactive lane
@@ -781,13 +784,22 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int ti = RPW * w + TPI * i + tsub;
-            const u32x4 kb = to_bf16x8<T>(R.k[i]);
+            const u32x4 kb = R.k[i];
             *reinterpret_cast<u32x2*>(&sm.kn[ti][ks0]) = u32x2{kb[0], kb[1]};
             *reinterpret_cast<u32x2*>(&sm.kn[ti][ks0 + 8]) = u32x2{kb[2], kb[3]};
+            // K^T: raw rows on bf16 operands (1/|k| goes with U); on fp16 operands the rows are
+            // normalised here, so that U's factor stays within 1 whatever |k| is
+            u32x4 ktb = kb;
+            if constexpr (std::is_same<T, F16>::value) {
+                const float rk = rsqrtf(group_sum<LPT>(sumsq8<T>(kb)) + 1e-12f);
+                float kf[8];
+                unpack8<T>(kb, kf);
+                ktb = pack8<T>(kf, rk);
+            }
             if constexpr (TPI == 4) {
                 // lanes pc, pc + 16, pc + 32, pc + 48 hold four consecutive tokens: after the
                 // transpose, row tsub has keys 8 pc + 2 tsub and + 1 of all four (8 bytes per key)
-                const u32x4 y = transpose_rows4(kb);
+                const u32x4 y = transpose_rows4(ktb);
                 const int r0 = 8 * pc + 2 * tsub, t0 = RPW * w + TPI * i;
                 *reinterpret_cast<u32x2*>(&kt[r0][tpos(r0, t0)]) =
                     u32x2{(y[0] & 0xffffu) | (y[1] << 16), (y[2] & 0xffffu) | (y[3] << 16)};
@@ -796,7 +808,7 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
             } else {
                 const int tp = tpos(8 * pc, ti);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kt[8 * pc + e][tp] = half_of(kb, e);
+                for (int e = 0; e < 8; ++e) kt[8 * pc + e][tp] = half_of(ktb, e);
             }
             if constexpr (!SUMMARY) {
                 if (cap_chunk && ti < captured && h % p.G == 0 && vp == 0) {  // (uniform over the row's lanes)
@@ -807,7 +819,7 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
 #pragma unroll
                         for (int e = 0; e < 8; ++e) crow.k(ti, kh)[8 * pc + e] = kf[e] * rk;
                 }
-                const u32x4 qb = to_bf16x8<T>(R.q[i]);
+                const u32x4 qb = R.q[i];
                 *reinterpret_cast<u32x2*>(&sm.qn[ti][ks0]) = u32x2{qb[0], qb[1]};
                 *reinterpret_cast<u32x2*>(&sm.qn[ti][ks0 + 8]) = u32x2{qb[2], qb[3]};
                 const float rq = rsqrtf(group_sum<LPT>(sumsq8<T>(R.q[i])) + 1e-12f);
@@ -877,7 +889,7 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
                 f32x4 pt = zero4();
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    pt = mma_bf16(frag(&sm.kn[16 * jt][32 * kk], K + kPadRow, lane), frag(&sm.qn[16 * it][32 * kk], K + kPadRow, lane), pt);
+                    pt = Op<T>::mma(frag<T>(&sm.kn[16 * jt][32 * kk], K + kPadRow, lane), frag<T>(&sm.qn[16 * it][32 * kk], K + kPadRow, lane), pt);
                 const int i = 16 * it + l16, j0 = 16 * jt + 4 * g;
                 const float g_i = Bf.gam[i], q_i = Bf.rq[i];
                 const f32x4 g_j = *reinterpret_cast<const f32x4*>(&Bf.gam[j0]);
@@ -887,16 +899,16 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
                 for (int r = 0; r < 4; ++r)
                     pv4[r] = (j0 + r <= i) ? fexp(fminf(g_i - g_j[r], 0.0f)) * (q_i * r_j[r]) * pt[r] : 0.0f;
                 *reinterpret_cast<u32x2*>(&sm.pb[i][32 * (jt >> 1) + 8 * g + 4 * (jt & 1)]) =
-                    u32x2{bf2(pv4[0], pv4[1]), bf2(pv4[2], pv4[3])};
+                    u32x2{Op<T>::pk(pv4[0], pv4[1]), Op<T>::pk(pv4[2], pv4[3])};
             }
         }
 
         // ---- chain: S0^T -> K S0^T (and S0 Q^T) -> R -> U -> S
-        bf16x8 sbf[KK][NCT];
+        OpV sbf[KK][NCT];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) sbf[kk][ct] = pack_acc(sacc[2 * kk][ct], sacc[2 * kk + 1][ct]);
+            for (int ct = 0; ct < NCT; ++ct) sbf[kk][ct] = pack_acc<T>(sacc[2 * kk][ct], sacc[2 * kk + 1][ct]);
         f32x4 ks[4][NCT];
         f32x4 oq[SUMMARY ? 1 : 4][VTW];  // (S0 Q^T) tiles: rows = value columns, columns = tokens
 #pragma unroll
@@ -909,13 +921,13 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
             }
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const bf16x8 kf = frag(&sm.kn[16 * it][32 * kk], K + kPadRow, lane);
+                const OpV kf = frag<T>(&sm.kn[16 * it][32 * kk], K + kPadRow, lane);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) ks[it][ct] = mma_bf16(kf, sbf[kk][ct], ks[it][ct]);
+                for (int ct = 0; ct < NCT; ++ct) ks[it][ct] = Op<T>::mma(kf, sbf[kk][ct], ks[it][ct]);
                 if constexpr (!SUMMARY) {
-                    const bf16x8 qf = frag(&sm.qn[16 * it][32 * kk], K + kPadRow, lane);
+                    const OpV qf = frag<T>(&sm.qn[16 * it][32 * kk], K + kPadRow, lane);
 #pragma unroll
-                    for (int ct = 0; ct < VTW; ++ct) oq[it][ct] = mma_bf16(sbf[kk][ct], qf, oq[it][ct]);
+                    for (int ct = 0; ct < VTW; ++ct) oq[it][ct] = Op<T>::mma(sbf[kk][ct], qf, oq[it][ct]);
                 }
             }
         }
@@ -942,14 +954,14 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
         // U = T R (T lower triangular: token tiles 0 and 1 need only the first 32-block)
         f32x4 ua[4][NCT];
         {
-            bf16x8 tf[NTF];
+            OpV tf[NTF];
 #pragma unroll
-            for (int f = 0; f < NTF; ++f) tf[f] = *reinterpret_cast<const bf16x8*>(&sm.tf[f][8 * lane]);
-            bf16x8 rb[2][NCT];
+            for (int f = 0; f < NTF; ++f) tf[f] = *reinterpret_cast<const OpV*>(&sm.tf[f][8 * lane]);
+            OpV rb[2][NCT];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) rb[jj][ct] = pack_acc(ks[2 * jj][ct], ks[2 * jj + 1][ct]);
+                for (int ct = 0; ct < NCT; ++ct) rb[jj][ct] = pack_acc<T>(ks[2 * jj][ct], ks[2 * jj + 1][ct]);
 #pragma unroll
             for (int it = 0; it < 4; ++it)
 #pragma unroll
@@ -958,7 +970,7 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
             for (int f = 0; f < NTF; ++f) {
                 const int it = tf_tile(f), jj = tf_blk(f);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) ua[it][ct] = mma_bf16(tf[f], rb[jj][ct], ua[it][ct]);
+                for (int ct = 0; ct < NCT; ++ct) ua[it][ct] = Op<T>::mma(tf[f], rb[jj][ct], ua[it][ct]);
             }
         }
         // P is complete, and kn, qn and vt of this chunk have been read for the last time (the next
@@ -967,25 +979,25 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
         if constexpr (!SUMMARY) {
             // O^T = (S0 Q^T) diag(scale e^G / |q|) + scale U^T P^T (the first factor is eg / |q|).
             // Lane: value columns 16 w + 4g .. +3 of token 16 it + l%16, into the LDS output rows
-            bf16x8 ub[2][VTW];
+            OpV ub[2][VTW];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                for (int ct = 0; ct < VTW; ++ct) ub[jj][ct] = pack_acc(ua[2 * jj][ct], ua[2 * jj + 1][ct]);
+                for (int ct = 0; ct < VTW; ++ct) ub[jj][ct] = pack_acc<T>(ua[2 * jj][ct], ua[2 * jj + 1][ct]);
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int i = 16 * it + l16;
-                const bf16x8 p0 = frag(&sm.pb[16 * it][0], CH + kPadT, lane);
-                bf16x8 p1;
-                if (it >= 2) p1 = frag(&sm.pb[16 * it][32], CH + kPadT, lane);
+                const OpV p0 = frag<T>(&sm.pb[16 * it][0], CH + kPadT, lane);
+                OpV p1;
+                if (it >= 2) p1 = frag<T>(&sm.pb[16 * it][32], CH + kPadT, lane);
                 const float qf = Bf.eg[i] * Bf.rq[i];
 #pragma unroll
                 for (int ct = 0; ct < VTW; ++ct) {
-                    f32x4 o = mma_bf16(ub[0][ct], p0, zero4());
-                    if (it >= 2) o = mma_bf16(ub[1][ct], p1, o);
+                    f32x4 o = Op<T>::mma(ub[0][ct], p0, zero4());
+                    if (it >= 2) o = Op<T>::mma(ub[1][ct], p1, o);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) o[r] = fmaf(oq[it][ct][r], qf, p.scale * o[r]);
-                    const u32x2 ov = u32x2{pack2<T>(o[0], o[1]), pack2<T>(o[2], o[3])};
+                    const u32x2 ov = u32x2{Op<T>::pk(o[0], o[1]), Op<T>::pk(o[2], o[3])};
                     const int oc = 16 * (VTW * w + ct) + 4 * g;
                     if constexpr (SO) {
                         *reinterpret_cast<u32x2*>(&sm.ob[16 * it + l16][oc]) = ov;
@@ -1007,24 +1019,24 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
         }
         // S0^T <- e^{G_C} S0^T + K^T diag(e^{G_C - G} / |k|) U
         {
-            bf16x8 udb[2][NCT];
+            OpV udb[2][NCT];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const f32x4 d0 = *reinterpret_cast<const f32x4*>(&Bf.ud[32 * jj + 4 * g]);
                 const f32x4 d1 = *reinterpret_cast<const f32x4*>(&Bf.ud[32 * jj + 16 + 4 * g]);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) udb[jj][ct] = pack_acc(ua[2 * jj][ct] * d0, ua[2 * jj + 1][ct] * d1);
+                for (int ct = 0; ct < NCT; ++ct) udb[jj][ct] = pack_acc<T>(ua[2 * jj][ct] * d0, ua[2 * jj + 1][ct] * d1);
             }
             const float gC = Bf.gc[0];
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const bf16x8 a0 = frag_t(&ktf[0][0], CH + kPadT, 16 * kt, 0, lane);
-                const bf16x8 a1 = frag_t(&ktf[0][0], CH + kPadT, 16 * kt, 1, lane);
+                const OpV a0 = frag_t<T>(&ktf[0][0], CH + kPadT, 16 * kt, 0, lane);
+                const OpV a1 = frag_t<T>(&ktf[0][0], CH + kPadT, 16 * kt, 1, lane);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     f32x4 s = sacc[kt][ct] * gC;
-                    s = mma_bf16(a0, udb[0][ct], s);
-                    sacc[kt][ct] = mma_bf16(a1, udb[1][ct], s);
+                    s = Op<T>::mma(a0, udb[0][ct], s);
+                    sacc[kt][ct] = Op<T>::mma(a1, udb[1][ct], s);
                 }
             }
         }

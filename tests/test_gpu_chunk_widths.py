@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import (CHUNK_SLICE_TOL, TOL, assert_close, assert_close_slices, bits, dev, dev_i32, ensure_built, f64,
+from gpu_util import (CHUNK_SEQ_TOL, CHUNK_SLICE_TOL, CHUNK_TOL, TOL, assert_close, assert_close_slices, bits, dev, dev_i32, ensure_built, f64,
                       require_gpu, sentinel)
 from test_gpu_scan import gpu_scan
 
@@ -51,16 +51,16 @@ def check_chunk(torch, w, label):
     o_ref, s_ref = reference(w)
     out, st, used = gpu_scan(torch, w, "chunk", False)
     assert used == "chunk"
-    assert_close(f64(out), o_ref, TOL[w.io], f"{label} chunk out")
-    assert_close_slices(f64(out), o_ref, w.lengths, CHUNK_SLICE_TOL, f"{label} chunk out")
-    assert_close(f64(st), s_ref, TOL[w.io], f"{label} chunk state")
-    assert_close_slices(f64(st), s_ref, w.lengths, CHUNK_SLICE_TOL, f"{label} chunk state", token_major=False)
+    assert_close(f64(out), o_ref, CHUNK_TOL[w.io], f"{label} chunk out")
+    assert_close_slices(f64(out), o_ref, w.lengths, CHUNK_SLICE_TOL[w.io], f"{label} chunk out")
+    assert_close(f64(st), s_ref, CHUNK_TOL[w.io], f"{label} chunk state")
+    assert_close_slices(f64(st), s_ref, w.lengths, CHUNK_SLICE_TOL[w.io], f"{label} chunk state", token_major=False)
     empty = np.flatnonzero(w.lengths == 0)
     assert np.array_equal(bits(st)[empty], w.state[empty].view(np.int32)), "empty sequences keep their state"
     o_seq, s_seq, used = gpu_scan(torch, w, "seq", False)
     assert used == "seq"
-    assert_close(f64(out), f64(o_seq), TOL[w.io], f"{label} chunk vs seq out")
-    assert_close(f64(st), f64(s_seq), TOL[w.io], f"{label} chunk vs seq state")
+    assert_close(f64(out), f64(o_seq), CHUNK_SEQ_TOL[w.io], f"{label} chunk vs seq out")
+    assert_close(f64(st), f64(s_seq), CHUNK_SEQ_TOL[w.io], f"{label} chunk vs seq state")
 
 
 @pytest.mark.parametrize("name", sorted(WIDTHS))
@@ -118,7 +118,7 @@ def test_chunk_width_capture_against_oracle(torch, name):
     assert np.all(got[ref == 0] == 0), "unused slots must be zero"
     g_n, k_n = cap * w.H, cap * (w.H + w.HQ * w.K)
     for part, sl in (("g", slice(0, g_n)), ("k^", slice(g_n, k_n)), ("delta", slice(k_n, None))):
-        assert_close(got[:, sl], ref[:, sl], TOL[w.io], f"{name} {part}")
+        assert_close(got[:, sl], ref[:, sl], CHUNK_TOL[w.io], f"{name} {part}")
 
 
 def test_auto_takes_chunk_at_page_widths(torch):
@@ -128,4 +128,4 @@ def test_auto_takes_chunk_at_page_widths(torch):
         out, st, used = gpu_scan(torch, w, "auto", False)
         assert used == "chunk", geo
         o_ref, s_ref = reference(w)
-        assert_close(f64(out), o_ref, TOL[w.io], f"auto K={w.K} V={w.V} out")
+        assert_close(f64(out), o_ref, CHUNK_TOL[w.io], f"auto K={w.K} V={w.V} out")

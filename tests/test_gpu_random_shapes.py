@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import CHUNK_SLICE_TOL, SEQ_STATE_TOL, TOL, assert_close, assert_close_slices, state_tol, bits, dev, dev_i32, ensure_built, f64, require_gpu
+from gpu_util import CHUNK_SEQ_TOL, CHUNK_SLICE_TOL, CHUNK_TOL, SEQ_STATE_TOL, TOL, out_tol, assert_close, assert_close_slices, state_tol, bits, dev, dev_i32, ensure_built, f64, require_gpu
 from test_gpu_scan import gpu_scan
 
 pytestmark = pytest.mark.gpu
@@ -68,11 +68,11 @@ def test_random_shape_against_oracle(torch, references, seed, path):
     out, st, used = gpu_scan(torch, w, path, False)
     assert used == path
     if w.N > 0:
-        assert_close(f64(out), o_ref, TOL[w.io], f"{path} out")
-        assert_close_slices(f64(out), o_ref, w.lengths, CHUNK_SLICE_TOL if path == "chunk" else TOL[w.io],
+        assert_close(f64(out), o_ref, out_tol(w.io, path), f"{path} out")
+        assert_close_slices(f64(out), o_ref, w.lengths, CHUNK_SLICE_TOL[w.io] if path == "chunk" else TOL[w.io],
                             f"{path} out")
     assert_close(f64(st), s_ref, state_tol(w.io, path), f"{path} state")
-    assert_close_slices(f64(st), s_ref, w.lengths, CHUNK_SLICE_TOL if path == "chunk" else SEQ_STATE_TOL,
+    assert_close_slices(f64(st), s_ref, w.lengths, CHUNK_SLICE_TOL[w.io] if path == "chunk" else SEQ_STATE_TOL,
                         f"{path} state", token_major=False)
     empty = np.flatnonzero(w.lengths == 0)
     assert np.array_equal(bits(st)[empty], w.state[empty].view(np.int32))
@@ -159,14 +159,14 @@ def test_chunk_gate_variants_against_oracle_and_seq(torch, name):
                                scale=w.scale)
     out, st, used = gpu_scan(torch, w, "chunk", False, use_state=w.state is not None)
     assert used == "chunk"
-    assert_close(f64(out), o_ref, TOL[w.io], f"{name} chunk out")
-    assert_close_slices(f64(out), o_ref, w.lengths, CHUNK_SLICE_TOL, f"{name} chunk out")
-    assert_close(f64(st), s_ref, TOL[w.io], f"{name} chunk state")
-    assert_close_slices(f64(st), s_ref, w.lengths, CHUNK_SLICE_TOL, f"{name} chunk state", token_major=False)
+    assert_close(f64(out), o_ref, CHUNK_TOL[w.io], f"{name} chunk out")
+    assert_close_slices(f64(out), o_ref, w.lengths, CHUNK_SLICE_TOL[w.io], f"{name} chunk out")
+    assert_close(f64(st), s_ref, CHUNK_TOL[w.io], f"{name} chunk state")
+    assert_close_slices(f64(st), s_ref, w.lengths, CHUNK_SLICE_TOL[w.io], f"{name} chunk state", token_major=False)
     o_seq, s_seq, used = gpu_scan(torch, w, "seq", False, use_state=w.state is not None)
     assert used == "seq"
-    assert_close(f64(out), f64(o_seq), TOL[w.io], f"{name} chunk vs seq out")
-    assert_close(f64(st), f64(s_seq), TOL[w.io], f"{name} chunk vs seq state")
+    assert_close(f64(out), f64(o_seq), CHUNK_SEQ_TOL[w.io], f"{name} chunk vs seq out")
+    assert_close(f64(st), f64(s_seq), CHUNK_SEQ_TOL[w.io], f"{name} chunk vs seq state")
 
 
 @pytest.mark.parametrize("path", ["decode", "seq", "chunk"])

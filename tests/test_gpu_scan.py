@@ -13,7 +13,7 @@ import pytest
 import cases
 import oracle
 import workloads
-from gpu_util import (SEQ_STATE_TOL, TOL, assert_close, assert_close_slices, state_tol, bits, dev, dev_i32, ensure_built, f64, head_subproblem, require_gpu,
+from gpu_util import (CHUNK_SEQ_TOL, CHUNK_TOL, SEQ_STATE_TOL, TOL, assert_close, out_tol, assert_close_slices, state_tol, bits, dev, dev_i32, ensure_built, f64, head_subproblem, require_gpu,
                       sentinel)
 
 pytestmark = pytest.mark.gpu
@@ -80,7 +80,7 @@ def check_against_oracle(w, name, out, st, path):
         ref_s.append(s_ref[:, 0])
         got_o.append(og[:, h][:, vsel])
         got_s.append(sg[:, h][:, vsel])
-    assert_close(np.stack(got_o), np.stack(ref_o), TOL[w.io], f"{name} {path} out")
+    assert_close(np.stack(got_o), np.stack(ref_o), out_tol(w.io, path), f"{name} {path} out")
     assert_close(np.stack(got_s), np.stack(ref_s), state_tol(w.io, path), f"{name} {path} final state")
 
 
@@ -182,11 +182,12 @@ def test_chunk_ragged_against_oracle_and_seq(torch, K, H, io, G):
     out_s, st_s, _ = gpu_scan(torch, w, "seq", False)
     o_ref, s_ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io, gate_dtype=w.gate_dtype,
                                a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias, state_in=w.state)
-    e1 = assert_close(f64(out_c), o_ref, TOL[w.io], "chunk out")
-    e2 = assert_close(f64(st_c), s_ref, 2e-2, "chunk state")
+    # fp16: the chunked form on fp16 operands stays within 1e-3 of the oracle
+    e1 = assert_close(f64(out_c), o_ref, 1e-3 if w.io == "f16" else CHUNK_TOL[w.io], "chunk out")
+    e2 = assert_close(f64(st_c), s_ref, CHUNK_TOL[w.io], "chunk state")
     # the chunked form agrees with the sequential form on the same launch inputs
-    e3 = assert_close(f64(out_c), f64(out_s), TOL[w.io], "chunk vs seq out")
-    e4 = assert_close(f64(st_c), f64(st_s), 2e-2, "chunk vs seq state")
+    e3 = assert_close(f64(out_c), f64(out_s), CHUNK_SEQ_TOL[w.io], "chunk vs seq out")
+    e4 = assert_close(f64(st_c), f64(st_s), CHUNK_SEQ_TOL[w.io], "chunk vs seq state")
     print(f"  errors: out {e1:.2e} state {e2:.2e} vs-seq out {e3:.2e} state {e4:.2e}", flush=True)
     empty = np.flatnonzero(w.lengths == 0)
     assert np.array_equal(bits(st_c)[empty], w.state[empty].view(np.int32))
@@ -196,8 +197,8 @@ def test_chunk_matches_seq_at_full_prefill_size(torch):
     w = cases.get("prefill")
     out_c, st_c, _ = gpu_scan(torch, w, "chunk", False)
     out_s, st_s, _ = gpu_scan(torch, w, "seq", False)
-    e1 = assert_close(f64(out_c), f64(out_s), TOL[w.io], "chunk vs seq out")
-    e2 = assert_close(f64(st_c), f64(st_s), 2e-2, "chunk vs seq state")
+    e1 = assert_close(f64(out_c), f64(out_s), CHUNK_SEQ_TOL[w.io], "chunk vs seq out")
+    e2 = assert_close(f64(st_c), f64(st_s), CHUNK_SEQ_TOL[w.io], "chunk vs seq state")
     print(f"  prefill chunk vs seq: out {e1:.2e} state {e2:.2e}", flush=True)
 
 
@@ -226,7 +227,7 @@ def test_chunk_long_sequence_k64(torch, io):
     out_s, st_s, _ = gpu_scan(torch, w, "seq", False)
     o_ref, s_ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io, gate_dtype=w.gate_dtype,
                                a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias, state_in=w.state)
-    e1 = assert_close(f64(out_c), o_ref, TOL[w.io], "chunk out")
-    e2 = assert_close(f64(st_c), s_ref, 2e-2, "chunk state")
-    e3 = assert_close(f64(out_c), f64(out_s), TOL[w.io], "chunk vs seq out")
+    e1 = assert_close(f64(out_c), o_ref, 1e-3 if w.io == "f16" else CHUNK_TOL[w.io], "chunk out")
+    e2 = assert_close(f64(st_c), s_ref, CHUNK_TOL[w.io], "chunk state")
+    e3 = assert_close(f64(out_c), f64(out_s), CHUNK_SEQ_TOL[w.io], "chunk vs seq out")
     print(f"  long k64 {io}: out {e1:.2e} state {e2:.2e} vs-seq {e3:.2e}", flush=True)
