@@ -393,7 +393,9 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     const int local = cid - tab.cstart[b];
     const int t0 = p.offsets[b] + local * CH;
     const int n = min(CH, p.offsets[b + 1] - t0);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
+    // (the wave index is read from the first lane so that the compiler keeps it, and everything
+    // derived from it, in scalar registers)
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4;
     const int pc = lane % LPT, tsub = lane / LPT;
     const TS* const xk = static_cast<const TS*>(p.x.k);
 
@@ -634,7 +636,10 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
     const int seq_start = p.offsets[b], len = p.offsets[b + 1] - seq_start;
     const int cid0 = tab.cstart[b];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+    // (the wave index is read from the first lane so that the compiler keeps it, and everything
+    // derived from it, in scalar registers: wave-dependent buffer resources, loop bounds)
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4,
+              l16 = lane & 15;
     const size_t slot_stride = ((size_t)K * K + (size_t)VT * K);
     float* const slots = reinterpret_cast<float*>(p.ws + p.L.slots);
     auto slot_phi = [&](int s) { return slots + ((size_t)s * p.H + h) * slot_stride; };
@@ -896,8 +901,11 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
                 const f32x4 r_j = *reinterpret_cast<const f32x4*>(&Bf.rk[j0]);
                 float pv4[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    pv4[r] = (j0 + r <= i) ? fexp(fminf(g_i - g_j[r], 0.0f)) * (q_i * r_j[r]) * pt[r] : 0.0f;
+                for (int r = 0; r < 4; ++r) {
+                    // every lane computes the (finite) value and the mask selects it: no divergent branch
+                    const float val = fexp(fminf(g_i - g_j[r], 0.0f)) * (q_i * r_j[r]) * pt[r];
+                    pv4[r] = val * (j0 + r <= i ? 1.0f : 0.0f);
+                }
                 *reinterpret_cast<u32x2*>(&sm.pb[i][32 * (jt >> 1) + 8 * g + 4 * (jt & 1)]) =
                     u32x2{Op<T>::pk(pv4[0], pv4[1]), Op<T>::pk(pv4[2], pv4[3])};
             }
