@@ -220,6 +220,22 @@ __device__ __forceinline__ float sumsq8(u32x4 raw) {
     }
     return s;
 }
+// Inclusive prefix sum over the 64 lanes by DPP: shifts by 1, 2, 4 and 8 inside each 16-lane row
+// (lanes past a row's start read zero), then the row totals through row_bcast:15 (row r's last lane
+// into row r + 1, rows 1 and 3) and row_bcast:31 (lane 31 into rows 2 and 3).
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, BOUND_ZERO));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_f32<0x111, 0xf, true>(x);   // row_shr:1
+    x += dpp_f32<0x112, 0xf, true>(x);   // row_shr:2
+    x += dpp_f32<0x114, 0xf, true>(x);   // row_shr:4
+    x += dpp_f32<0x118, 0xf, true>(x);   // row_shr:8
+    x += dpp_f32<0x142, 0xa, false>(x);  // row_bcast:15
+    x += dpp_f32<0x143, 0xc, false>(x);  // row_bcast:31
+    return x;
+}
 // e^x through the hardware 2^x (about 1 ulp): for decay factors that are rounded to bf16 or scale
 // a whole chunk
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
@@ -367,10 +383,12 @@ __global__ __launch_bounds__(1024) void chunk_index_kernel(ChunkArgs p) {
 
 // ---- tmat: gates, G and the T fragments of every (chunk, head) -----------------------------------
 // k rows are read whole (K/8 lanes per row, 16 bytes each); wave w normalises token rows
-// 16w..16w+15.  A is formed in 16 x 16 blocks by MFMA (wave w: column tile w).  T: the diagonal
-// blocks by substitution (wave w, block w), then wave w walks down its block column,
-// T_iw = -T_ii sum_{w <= m < i} A_im T_mw, which needs only its own earlier blocks and the diagonal
-// ones (one barrier).
+// 16w..16w+15 (wave 0 also forms the gates, whose loads go out first).  A is formed in its ten
+// nonzero 16 x 16 blocks by MFMA, blocks w, w+4, w+8 (row-major) by wave w.  T: the diagonal blocks
+// in fp32 by forward substitution (wave w, block w; lane = column, each solved row updating the rows
+// below it, so the chain is one FMA per row), then wave w walks down its block column,
+// T_iw = -T_ii sum_{w <= m < i} A_im T_mw, on MFMA operands of the I/O type with its earlier blocks
+// kept in accumulators (the operands of the chunk chain are rounded to that type anyway).
 template <typename T, int K>
 __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     using TS = typename T::storage;
@@ -380,7 +398,6 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
         float tm[CH][CH + 4];      // T (fp32)
     } r0;
     __shared__ __align__(16) float am[CH][CH + 4];
-    __shared__ float scr[NW][16][17];
     __shared__ __align__(16) float s_gam[CH], s_beta[CH], s_rk[CH];
 
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws);
@@ -399,6 +416,19 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     const int pc = lane % LPT, tsub = lane / LPT;
     const TS* const xk = static_cast<const TS*>(p.x.k);
 
+    // wave 0: the raw gate inputs first, widened only after the k rows are requested too (so that
+    // the three loads are in flight together)
+    const bool g32 = p.gate_dtype == GDN_F32;
+    uint32_t a_raw = 0u, b_raw = 0u;
+    if (w == 0 && lane < n) {
+        const size_t gi = (size_t)(t0 + lane) * p.H + h;
+        a_raw = g32 ? static_cast<const uint32_t*>(p.a)[gi] : static_cast<const uint16_t*>(p.a)[gi];
+        if (p.b) b_raw = g32 ? static_cast<const uint32_t*>(p.b)[gi] : static_cast<const uint16_t*>(p.b)[gi];
+    }
+    auto widen = [&](uint32_t raw) {
+        return g32 ? __builtin_bit_cast(float, raw)
+                   : p.gate_dtype == GDN_BF16 ? bf16_bits_to_f32((uint16_t)raw) : f16_bits_to_f32((uint16_t)raw);
+    };
     u32x4 kr[NI];
     const bool kin = 8 * pc < p.K;  // keys past the width read as zero
 #pragma unroll
@@ -411,20 +441,11 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     if (w == 0) {  // gates and the cumulative log-decay; padding tokens: no decay, no update
         float ell = 0.0f, beta = 0.0f;
         if (lane < n) {
-            const size_t gi = (size_t)(t0 + lane) * p.H + h;
-            ell = -expf(p.A_log[h]) * softplus_f(load_any(p.a, p.gate_dtype, gi) + p.dt_bias[h]);
-            beta = 1.0f;
-            if (p.b) {
-                beta = load_any(p.b, p.gate_dtype, gi);
-                if (p.flags & GDN_SIGMOID) beta = 1.0f / (1.0f + expf(-beta));
-            }
+            ell = -expf(p.A_log[h]) * softplus_f(widen(a_raw) + p.dt_bias[h]);
+            beta = p.b ? widen(b_raw) : 1.0f;
+            if (p.b && (p.flags & GDN_SIGMOID)) beta = 1.0f / (1.0f + expf(-beta));
         }
-        float gam = ell;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float y = __shfl_up(gam, d);
-            if (lane >= d) gam += y;
-        }
+        const float gam = wave_prefix_sum(ell);
         s_gam[lane] = gam;
         s_beta[lane] = beta;
         float* const gout = reinterpret_cast<float*>(p.ws + p.L.gates) + ch * 3 * CH;
@@ -444,15 +465,17 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
         }
     }
     __syncthreads();
-    {  // A, column tile w, rows it = w..3
-        const int ja = 16 * w + (lane & 15);
-        const float g_ja = s_gam[ja], r_ja = s_rk[ja];
+    {  // A: lower-triangle blocks t = w, w + 4, w + 8 in row-major order (it, jt <= it)
 #pragma unroll 1
-        for (int it = w; it < 4; ++it) {
+        for (int t = w; t < 10; t += NW) {
+            const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+            const int jt = t - it * (it + 1) / 2;
+            const int ja = 16 * jt + (lane & 15);
+            const float g_ja = s_gam[ja], r_ja = s_rk[ja];
             f32x4 a = zero4();
 #pragma unroll
             for (int kk = 0; kk < K; kk += 32)
-                a = Op<T>::mma(frag<T>(&r0.kn[16 * it][kk], K + kPadRow, lane), frag<T>(&r0.kn[16 * w][kk], K + kPadRow, lane), a);
+                a = Op<T>::mma(frag<T>(&r0.kn[16 * it][kk], K + kPadRow, lane), frag<T>(&r0.kn[16 * jt][kk], K + kPadRow, lane), a);
             const int ia = 16 * it + 4 * g;
             const f32x4 g_ia = *reinterpret_cast<const f32x4*>(&s_gam[ia]);
             const f32x4 b_ia = *reinterpret_cast<const f32x4*>(&s_beta[ia]);
@@ -470,37 +493,50 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
         const int cc = lane, o = 16 * w;
         float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float v = (i == cc) ? 1.0f : 0.0f;
+        for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.0f : 0.0f;
 #pragma unroll
-            for (int m = 0; m < i; ++m) v = fmaf(-am[o + i][o + m], x[m], v);
-            x[i] = v;
-        }
+        for (int m = 0; m < 15; ++m)  // x[m] is final: take it out of the rows below
+#pragma unroll
+            for (int i = m + 1; i < 16; ++i) x[i] = fmaf(-am[o + i][o + m], x[m], x[i]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) tm[o + i][o + cc] = x[i];
     }
     __syncthreads();  // diagonal blocks ready
-    // block column w, top down; the wave's own writes are read back by other lanes of the wave
-    for (int i = w + 1; i < 4; ++i) {
-        f32x4 y = zero4();
-        for (int m = w; m < i; ++m)
+    {  // block column w, top down: tc[m] = T_mw in accumulator layout (rows 4g..4g+3, column l%16)
+        const int l16 = lane & 15;
+        f32x4 tc[4];
 #pragma unroll
-            for (int kk = 0; kk < 16; kk += 4)
-                y = mma_f32(am[16 * i + (lane & 15)][16 * m + kk + g], tm[16 * m + kk + g][16 * w + (lane & 15)], y);
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) scr[w][4 * g + r][lane & 15] = y[r];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        f32x4 z = zero4();
+            for (int r = 0; r < 4; ++r) tc[m][r] = m == w ? tm[16 * w + 4 * g + r][16 * w + l16] : 0.0f;
+        // A operand of rows 16 i + l%16 over the 32 columns 16 m .. 16 m + 31 in the split order
+        // {4g..4g+3, 16+4g..16+4g+3}; a half whose block does not contribute is zero
+        auto a_split = [&](const float* row, bool lo, bool hi) {
+            const f32x4 x0 = lo ? *reinterpret_cast<const f32x4*>(row + 4 * g) : zero4();
+            const f32x4 x1 = hi ? *reinterpret_cast<const f32x4*>(row + 16 + 4 * g) : zero4();
+            return __builtin_bit_cast(typename Op<T>::v8, u32x4{Op<T>::pk(x0[0], x0[1]), Op<T>::pk(x0[2], x0[3]),
+                                                                Op<T>::pk(x1[0], x1[1]), Op<T>::pk(x1[2], x1[3])});
+        };
 #pragma unroll
-        for (int kk = 0; kk < 16; kk += 4)
-            z = mma_f32(tm[16 * i + (lane & 15)][16 * i + kk + g], scr[w][kk + g][lane & 15], z);
+        for (int i = 1; i < 4; ++i) {
+            if (i <= w) continue;
+            f32x4 y = zero4();
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tm[16 * i + 4 * g + r][16 * w + (lane & 15)] = -z[r];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int m = 0; m < 4; m += 2) {  // blocks m and m + 1 of sum_{w <= m < i} A_im T_mw
+                const bool u0 = m >= w && m < i, u1 = m + 1 >= w && m + 1 < i;
+                if (!u0 && !u1) continue;
+                y = Op<T>::mma(a_split(&am[16 * i + l16][16 * m], u0, u1),
+                               pack_acc<T>(u0 ? tc[m] : zero4(), u1 ? tc[m + 1] : zero4()), y);
+            }
+            const f32x4 z = Op<T>::mma(a_split(&tm[16 * i + l16][16 * i], true, false), pack_acc<T>(y, zero4()), zero4());
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tc[i][r] = -z[r];
+        }
+#pragma unroll
+        for (int m = 1; m < 4; ++m)
+            if (m > w)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tm[16 * m + 4 * g + r][16 * w + l16] = tc[m][r];
     }
     __syncthreads();  // T complete
     // fragments f = w and w + 4: lane l holds row 16 it + l%16, columns 32 jj + {4g.., 16+4g..}; the
@@ -772,7 +808,7 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
         for (int j = 0; j < NTFW; ++j)
             if (w + NWV * j < NTF) *reinterpret_cast<u32x4*>(&sm.tf[w + NWV * j][8 * lane]) = R.tf[j];
         if (w == 0) {  // (every value part: each reads its own factors)
-            const float gC = __shfl(R.gam, CH - 1);
+            const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, R.gam), CH - 1));
             const float eg = fexp(R.gam);
             Bf.gam[lane] = R.gam;
             Bf.beta[lane] = R.beta;
