@@ -393,12 +393,15 @@ template <typename T, int K>
 __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     using TS = typename T::storage;
     constexpr int LPT = K / 8, TPI = 64 / LPT, NI = 16 / TPI;
+    // A and T are kept as values of the operand type (a 64 x 64 tile in 9 KB each), so that four
+    // or five blocks share a compute unit; the diagonal solve works on them in fp32
     __shared__ __align__(16) union {
-        uint16_t kn[CH][K + kPadRow];  // normalised k rows, until A is formed
-        float tm[CH][CH + 4];      // T (fp32)
+        uint16_t kn[CH][K + kPadRow];  // raw k rows, until A is formed
+        uint16_t tm[CH][CH + 8];       // T
     } r0;
-    __shared__ __align__(16) float am[CH][CH + 4];
+    __shared__ __align__(16) uint16_t am[CH][CH + 8];
     __shared__ __align__(16) float s_gam[CH], s_beta[CH], s_rk[CH];
+    auto to16 = [](float v) { return (uint16_t)(Op<T>::pk(v, 0.0f) & 0xffffu); };
 
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws);
     if (hdr[0] != GDN_OK) return;
@@ -483,7 +486,7 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float e = fexp(fminf(g_ia[r] - g_ja, 0.0f));
-                am[ia + r][ja] = (ja < ia + r) ? (b_ia[r] * r_ia[r] * r_ja) * e * a[r] : 0.0f;
+                am[ia + r][ja] = to16((ja < ia + r) ? (b_ia[r] * r_ia[r] * r_ja) * e * a[r] : 0.0f);
             }
         }
     }
@@ -497,9 +500,9 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
 #pragma unroll
         for (int m = 0; m < 15; ++m)  // x[m] is final: take it out of the rows below
 #pragma unroll
-            for (int i = m + 1; i < 16; ++i) x[i] = fmaf(-am[o + i][o + m], x[m], x[i]);
+            for (int i = m + 1; i < 16; ++i) x[i] = fmaf(-to_f32<T>(am[o + i][o + m]), x[m], x[i]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tm[o + i][o + cc] = x[i];
+        for (int i = 0; i < 16; ++i) tm[o + i][o + cc] = to16(x[i]);
     }
     __syncthreads();  // diagonal blocks ready
     {  // block column w, top down: tc[m] = T_mw in accumulator layout (rows 4g..4g+3, column l%16)
@@ -508,14 +511,13 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) tc[m][r] = m == w ? tm[16 * w + 4 * g + r][16 * w + l16] : 0.0f;
+            for (int r = 0; r < 4; ++r) tc[m][r] = m == w ? to_f32<T>(tm[16 * w + 4 * g + r][16 * w + l16]) : 0.0f;
         // A operand of rows 16 i + l%16 over the 32 columns 16 m .. 16 m + 31 in the split order
         // {4g..4g+3, 16+4g..16+4g+3}; a half whose block does not contribute is zero
-        auto a_split = [&](const float* row, bool lo, bool hi) {
-            const f32x4 x0 = lo ? *reinterpret_cast<const f32x4*>(row + 4 * g) : zero4();
-            const f32x4 x1 = hi ? *reinterpret_cast<const f32x4*>(row + 16 + 4 * g) : zero4();
-            return __builtin_bit_cast(typename Op<T>::v8, u32x4{Op<T>::pk(x0[0], x0[1]), Op<T>::pk(x0[2], x0[3]),
-                                                                Op<T>::pk(x1[0], x1[1]), Op<T>::pk(x1[2], x1[3])});
+        auto a_split = [&](const uint16_t* row, bool lo, bool hi) {
+            const u32x2 x0 = lo ? *reinterpret_cast<const u32x2*>(row + 4 * g) : u32x2{0u, 0u};
+            const u32x2 x1 = hi ? *reinterpret_cast<const u32x2*>(row + 16 + 4 * g) : u32x2{0u, 0u};
+            return __builtin_bit_cast(typename Op<T>::v8, u32x4{x0[0], x0[1], x1[0], x1[1]});
         };
 #pragma unroll
         for (int i = 1; i < 4; ++i) {
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
         for (int m = 1; m < 4; ++m)
             if (m > w)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) tm[16 * m + 4 * g + r][16 * w + l16] = tc[m][r];
+                for (int r = 0; r < 4; ++r) tm[16 * m + 4 * g + r][16 * w + l16] = to16(tc[m][r]);
     }
     __syncthreads();  // T complete
     // fragments f = w and w + 4: lane l holds row 16 it + l%16, columns 32 jj + {4g.., 16+4g..}; the
@@ -546,13 +548,9 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
         const int it = tf_tile(f), jj = tf_blk(f);
         const int i = 16 * it + (lane & 15);
         const int j0 = 32 * jj + 4 * g, j1 = j0 + 16;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[e] = (j0 >> 4) <= it ? tm[i][j0 + e] : 0.0f;
-            v[4 + e] = (j1 >> 4) <= it ? tm[i][j1 + e] : 0.0f;
-        }
-        *reinterpret_cast<u32x4*>(tout + f * 512 + 8 * lane) = pack8<T>(v, 1.0f);
+        const u32x2 x0 = (j0 >> 4) <= it ? *reinterpret_cast<const u32x2*>(&tm[i][j0]) : u32x2{0u, 0u};
+        const u32x2 x1 = (j1 >> 4) <= it ? *reinterpret_cast<const u32x2*>(&tm[i][j1]) : u32x2{0u, 0u};
+        *reinterpret_cast<u32x4*>(tout + f * 512 + 8 * lane) = u32x4{x0[0], x0[1], x1[0], x1[1]};
     }
 }
 
@@ -1134,18 +1132,22 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
 // ---- combine: S_start of every segment, in order ------------------------------------------------
 // K and V are the compiled widths (the slots' layout; one value part).
 // One block per (sequence, head, 8 value rows); a thread owns key column k = t % K of rows
-// t / K + (256 / K) j.  S_start(s+1) = S_start(s) Phi_s + N_s  (rows v: S[v][k] = sum_c S[v][c]
+// t / K + (NTH / K) j.  S_start(s+1) = S_start(s) Phi_s + N_s  (rows v: S[v][k] = sum_c S[v][c]
 // phi[c][k] + N[v][k]), in fp32.  Phi is staged through LDS in tiles of CT rows; the next tile (and
 // the next N rows) are loaded into registers while the current one is used.
+// NTH = 256 threads (more threads per block with fewer rows each measured slower).
+template <int K>
+constexpr int combine_threads() { return 256; }
 template <int K, int V>
-__global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs p) {
+__global__ __launch_bounds__(combine_threads<K>()) void chunk_combine_kernel(ChunkArgs p) {
+    constexpr int NTH = combine_threads<K>();
     constexpr int VR = 8;          // value rows per block
-    constexpr int RG = 256 / K;    // row groups
+    constexpr int RG = NTH / K;    // row groups
     constexpr int RPT = VR / RG;   // rows per thread
     constexpr int CT = K * K <= 16384 ? K : 16384 / K;  // Phi rows per tile
     constexpr int NCT = K / CT;
-    constexpr int NLD = CT * K / (4 * 256);  // 16-byte loads per thread per tile
-    static_assert(256 % K == 0 && VR % RG == 0 && NLD >= 1 && V % VR == 0, "combine tiling");
+    constexpr int NLD = CT * K / (4 * NTH);  // 16-byte loads per thread per tile
+    static_assert(NTH % K == 0 && VR % RG == 0 && NLD >= 1 && V % VR == 0, "combine tiling");
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws);
     if (hdr[0] != GDN_OK) return;
     const Tables tab = tables(p.ws, p.B);
@@ -1178,7 +1180,7 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs p) {
     auto fetch = [&](int sg, int ct) {
         const f32x4* src = reinterpret_cast<const f32x4*>(slot_phi(s0 + sg) + (size_t)ct * CT * K);
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) pre[i] = src[tid + 256 * i];
+        for (int i = 0; i < NLD; ++i) pre[i] = src[tid + NTH * i];
         if (ct == 0) {
             const float* const nst = slot_phi(s0 + sg) + (size_t)K * K;
 #pragma unroll
@@ -1192,7 +1194,7 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs p) {
         for (int ct = 0; ct < NCT; ++ct) {
             __syncthreads();  // the previous tile (and the rows of s) have been read
 #pragma unroll
-            for (int i = 0; i < NLD; ++i) reinterpret_cast<f32x4*>(phs)[tid + 256 * i] = pre[i];
+            for (int i = 0; i < NLD; ++i) reinterpret_cast<f32x4*>(phs)[tid + NTH * i] = pre[i];
             __syncthreads();
             if (ct + 1 < NCT) fetch(sg, ct + 1);
             else if (sg + 2 < nseg) fetch(sg + 1, 0);
@@ -1246,7 +1248,7 @@ hipError_t launch_kv(ChunkArgs p, hipStream_t stream) {
         if (sum_units > 0) {
             p.n_blocks = (int)sum_units;
             hipLaunchKernelGGL((chunk_fused_kernel<T, K, V, kSummary, VTW>), dim3((unsigned)sum_units), dim3(NT), 0, stream, p);
-            hipLaunchKernelGGL((chunk_combine_kernel<K, V>), dim3((unsigned)comb_blocks), dim3(256), 0, stream, p);
+            hipLaunchKernelGGL((chunk_combine_kernel<K, V>), dim3((unsigned)comb_blocks), dim3(combine_threads<K>()), 0, stream, p);
         }
     } else if (sum_units > 0) {
         return hipErrorInvalidConfiguration;  // (segments are never planned for these widths)
