@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 SCAN_SOURCES = ["gated_delta_rule_varlen_amd/csrc/gdn_scan.hip", "gated_delta_rule_varlen_amd/csrc/gdn_device.hpp"]
 STEP_SOURCES = ["gated_delta_rule_varlen_amd/csrc/gdn_decode.hip", "gated_delta_rule_varlen_amd/csrc/gdn_device.hpp"]
+CHUNK_SOURCES = ["gated_delta_rule_varlen_amd/csrc/gdn_chunk.hpp", "gated_delta_rule_varlen_amd/csrc/gdn_device.hpp"]
 
 
 def sizeof(dt: str) -> int:
@@ -200,9 +201,10 @@ def time_path(p: "Path", steps: int, warmup: int):
     return total_ms / steps, scan_ms, used, wall
 
 
-def roofline(w, scan_ms: float, workload: str, kernel: str = "scan_kernel", fused_step: bool = False):
+def roofline(w, scan_ms: float, workload: str, kernel: str = "scan_kernel", fused_step: bool = False,
+             sources=SCAN_SOURCES):
     nbytes = step_bytes(w) if fused_step else scan_bytes(w)
-    traffic = measured_traffic(f"{workload}_step", STEP_SOURCES) if fused_step else measured_traffic(workload)
+    traffic = measured_traffic(f"{workload}_step", STEP_SOURCES) if fused_step else measured_traffic(workload, sources)
     achieved = nbytes / (scan_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -235,13 +237,16 @@ def compute_roofline(w, scan_ms: float, used: str):
     return rec
 
 
-def secondary(torch, wl, steps: int, warmup: int):
-    """One more workload, measured the same way (chunked path when eligible)."""
+def secondary(torch, wl, steps: int, warmup: int, record: str):
+    """One more workload, measured the same way (chunked path when eligible).  The counter traffic of
+    a chunked call is the sum over its kernels (index, tmat, summary, combine, main)."""
     pp = Path(wl, torch, "auto")
     pms, pscan_ms, pused, _ = time_path(pp, steps, warmup)
     rec = {"workload": wl.name, "N": wl.N, "path": pused, "tokens_per_s": round(wl.N / (pms * 1e-3), 1),
            "ms_per_step": round(pms, 4), "scan_ms": round(pscan_ms, 4),
-           "roofline": roofline(wl, pscan_ms, "none", "gdn_scan_varlen call (all its kernels)"), "compute_roofline": compute_roofline(wl, pscan_ms, pused)}
+           "roofline": roofline(wl, pscan_ms, record if pused == "chunk" else "none",
+                                "gdn_scan_varlen call (all its kernels)", sources=CHUNK_SOURCES),
+           "compute_roofline": compute_roofline(wl, pscan_ms, pused)}
     del pp
     torch.cuda.empty_cache()
     return rec
@@ -534,17 +539,19 @@ def cpu_baseline(w, budget_s: float = 12.0):
 
 
 def copy_calibration(torch, steps: int, warmup: int):
-    """A plain device-to-device copy of 1 GiB: known bytes per launch (1 GiB read + 1 GiB written)."""
+    """A plain streaming copy of 1 GiB (1 GiB read + 1 GiB written per launch) through an elementwise
+    kernel, dst = src * 1: the rate a read-once/write-once kernel reaches on this device.  (The
+    runtime's own device-to-device copy, torch's copy_, measured about 20% slower.)"""
     n = 1 << 28
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(warmup):
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
         a.record()
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         b.record()
     torch.cuda.synchronize()
     us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
@@ -617,8 +624,8 @@ def main():
         del p
         torch.cuda.empty_cache()
         # warmups long enough for the clocks to settle (a 2-step warmup reads ~15% slow)
-        line["also"] = {"prefill": secondary(torch, workloads.varlen_prefill(), max(3, args.steps // 10), 20),
-                        "long": secondary(torch, workloads.long_single(), 5, 5),
+        line["also"] = {"prefill": secondary(torch, workloads.varlen_prefill(), max(3, args.steps // 10), 20, "prefill"),
+                        "long": secondary(torch, workloads.long_single(), 5, 5, "long"),
                         "decode_step_fused_vs_two_call": fused_comparison(torch),
                         "speculative_verify_capture": verify_comparison(torch),
                         "mixed_batch": mixed_comparison(torch),
