@@ -72,9 +72,9 @@ def test_chunk_width_against_oracle_and_seq(torch, name):
 
 LONG = {
     # (geometry, lengths): segments at K=128/V=64 and K=64/V=32; one segment per sequence at K=256
-    "k128_v64_segments": (dict(HQ=1, H=2, K=128, V=64, io="bf16"), [3000, 40]),
-    "k64_v32_segments": (dict(HQ=2, H=2, K=64, V=32, io="f16"), [2500, 1, 1100]),
-    "k256_v64_long": (dict(HQ=1, H=2, K=256, V=64, io="bf16"), [1500, 3]),
+    "k128_v64_bf16_segments": (dict(HQ=1, H=2, K=128, V=64, io="bf16"), [3000, 40]),
+    "k64_v32_f16_segments": (dict(HQ=2, H=2, K=64, V=32, io="f16"), [2500, 1, 1100]),
+    "k256_v64_bf16_long": (dict(HQ=1, H=2, K=256, V=64, io="bf16"), [1500, 3]),
 }
 
 
