@@ -177,15 +177,16 @@ class Path:
 EV_EVERY = 8
 
 
-def time_path(p: "Path", steps: int, warmup: int):
+def time_path(p: "Path", steps: int, warmup: int, ev_every: int = EV_EVERY):
     torch = p.torch
     for _ in range(warmup):
         used = p.step()
     torch.cuda.synchronize()
-    # the recurrence launch is bracketed by events on every EV_EVERY-th step of the timed region
-    # (events on every step add a few microseconds to each short step)
+    # the recurrence launch is bracketed by events on every ev_every-th step of the timed region
+    # (events on every step add a few microseconds to each short step; long steps take them on
+    # every step)
     evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for i in range(0, steps, EV_EVERY)}
+           for i in range(0, steps, ev_every)}
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -241,7 +242,7 @@ def secondary(torch, wl, steps: int, warmup: int, record: str):
     """One more workload, measured the same way (chunked path when eligible).  The counter traffic of
     a chunked call is the sum over its kernels (index, tmat, summary, combine, main)."""
     pp = Path(wl, torch, "auto")
-    pms, pscan_ms, pused, _ = time_path(pp, steps, warmup)
+    pms, pscan_ms, pused, _ = time_path(pp, steps, warmup, ev_every=1)
     rec = {"workload": wl.name, "N": wl.N, "path": pused, "tokens_per_s": round(wl.N / (pms * 1e-3), 1),
            "ms_per_step": round(pms, 4), "scan_ms": round(pscan_ms, 4),
            "roofline": roofline(wl, pscan_ms, record if pused == "chunk" else "none",
@@ -625,7 +626,7 @@ def main():
         torch.cuda.empty_cache()
         # warmups long enough for the clocks to settle (a 2-step warmup reads ~15% slow)
         line["also"] = {"prefill": secondary(torch, workloads.varlen_prefill(), max(3, args.steps // 10), 20, "prefill"),
-                        "long": secondary(torch, workloads.long_single(), 5, 5, "long"),
+                        "long": secondary(torch, workloads.long_single(), 10, 10, "long"),
                         "decode_step_fused_vs_two_call": fused_comparison(torch),
                         "speculative_verify_capture": verify_comparison(torch),
                         "mixed_batch": mixed_comparison(torch),
