@@ -149,7 +149,6 @@ gdn_status conv_call(const gdn_conv_desc* d, const void* x, const void* w, const
     if (d->flags & ~(uint32_t)GDN_CONV_SILU) return GDN_ERR_UNSUPPORTED;
     const long long L = (long long)(d->W - 1) * d->D;
     if (L > INT_MAX || (long long)d->B * d->C > INT_MAX) return GDN_ERR_OVERFLOW;
-    if (d->W > 8) return GDN_ERR_UNSUPPORTED;
     if (misaligned(x) || misaligned(w) || misaligned(bias) || misaligned(state_in) || misaligned(y) ||
         misaligned(state_out))
         return GDN_ERR_ALIGN;

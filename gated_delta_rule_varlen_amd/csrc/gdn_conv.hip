@@ -439,6 +439,96 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs p) {
     }
 }
 
+// ---- any width: the compiled kernels above hold the W taps in registers (W <= 8); wider convs
+// take two plain kernels with the same arithmetic in the same order (bias, then the taps, fp32 FMA,
+// the same SiLU and rounding).  The outputs first, one thread per (token, channel), reading the old
+// window; then, in stream order, one thread per (sequence, channel) writes the new window in
+// increasing entry order (reading entry j + len >= j before writing j, so an aliased window is
+// correct) and the capture slots.
+template <typename T, typename S>
+__global__ __launch_bounds__(256) void conv_wide_out_kernel(ConvArgs p, int W) {
+    using TS = typename T::storage;
+    using SS = typename S::storage;
+    __shared__ int s_off[kStagedOffsets];
+    const bool staged = p.B < kStagedOffsets;
+    const bool malformed = check_stage_offsets(p.offsets, p.B, p.N, staged ? s_off : nullptr);
+    report_status(p.dev_status, malformed);
+    if (malformed) return;
+    auto off = [&](int i) { return staged ? s_off[i] : p.offsets[i]; };
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long long)p.N * p.C) return;
+    const int C = p.C, D = p.D, L = p.L;
+    const int t = (int)(idx / C), c = (int)(idx % C);
+    int lo = 0, hi = p.B - 1;  // the sequence of token t: the last b with off(b) <= t
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off(mid) <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    const int b = lo, start = off(b), l = t - start;
+    const TS* x = static_cast<const TS*>(p.x);
+    const TS* w = static_cast<const TS*>(p.w) + (size_t)c * W;
+    const SS* st_in = static_cast<const SS*>(p.state_in);
+    const size_t wrow = ((size_t)b * C + c) * (size_t)L;
+    float acc[1] = {p.bias != nullptr ? to_f32<T>(static_cast<const TS*>(p.bias)[c]) : 0.0f};
+    for (int j = 0; j < W; ++j) {
+        const int m = l - (W - 1 - j) * D;
+        const float xv = m >= 0 ? to_f32<T>(x[(size_t)(start + m) * C + c])
+                                : (st_in ? to_f32<S>(st_in[wrow + (size_t)(L + m)]) : 0.0f);
+        acc[0] = fmaf(to_f32<T>(w[j]), xv, acc[0]);
+    }
+    activate<1>(acc, p.silu);
+    static_cast<TS*>(p.y)[(size_t)t * C + c] = from_f32<T>(acc[0]);
+}
+
+template <typename T, typename S>
+__global__ __launch_bounds__(256) void conv_wide_window_kernel(ConvArgs p) {
+    using TS = typename T::storage;
+    using SS = typename S::storage;
+    const bool malformed = check_stage_offsets(p.offsets, p.B, p.N, nullptr);
+    report_status(p.dev_status, malformed);  // (also when there are no tokens and no output launch)
+    if (malformed) return;
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long long)p.B * p.C) return;
+    const int C = p.C, L = p.L;
+    const int b = (int)(idx / C), c = (int)(idx % C);
+    const int start = p.offsets[b], len = p.offsets[b + 1] - start;
+    const TS* x = static_cast<const TS*>(p.x);
+    const SS* st_in = static_cast<const SS*>(p.state_in);
+    SS* st_out = static_cast<SS*>(p.state_out);
+    const size_t wrow = ((size_t)b * C + c) * (size_t)L;
+    if (st_out != nullptr) {
+        for (int j = 0; j < L; ++j) {
+            const int m = len - L + j;
+            SS v;
+            if (m >= 0) {
+                const TS xs = x[(size_t)(start + m) * C + c];
+                if constexpr (std::is_same<S, T>::value) v = xs;
+                else v = to_f32<T>(xs);  // exact widening into an fp32 window
+            } else {
+                v = st_in ? st_in[wrow + (size_t)(L + m)] : (SS)0;
+            }
+            st_out[wrow + j] = v;
+        }
+    }
+    if (p.cap > 0) {
+        const int n = captured_tokens(p.counts, nullptr, p.cap, b, len);
+        TS* u = static_cast<TS*>(p.updates) + (size_t)b * p.cap * C + c;
+        for (int i = 0; i < p.cap; ++i) u[(size_t)i * C] = i < n ? x[(size_t)(start + i) * C + c] : (TS)0;
+    }
+}
+
+template <typename T, typename S>
+hipError_t launch_wide(const ConvArgs& p, int W, hipStream_t stream) {
+    const long long out_blocks = ((long long)p.N * p.C + 255) / 256;
+    const long long win_blocks = ((long long)p.B * p.C + 255) / 256;
+    if (out_blocks > kMaxBlocks || win_blocks > kMaxBlocks) return hipErrorInvalidConfiguration;
+    if (out_blocks > 0)
+        hipLaunchKernelGGL((conv_wide_out_kernel<T, S>), dim3((unsigned)out_blocks), dim3(256), 0, stream, p, W);
+    hipLaunchKernelGGL((conv_wide_window_kernel<T, S>), dim3((unsigned)win_blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
 template <typename T, typename S, int VEC>
 hipError_t launch_vec(const ConvLaunch& a, hipStream_t stream) {
     ConvArgs p;
@@ -463,6 +553,7 @@ hipError_t launch_vec(const ConvLaunch& a, hipStream_t stream) {
     const int threads = p.n_cvec >= 256 ? 256 : ((p.n_cvec + 63) / 64) * 64;
     p.n_cblk = (p.n_cvec + threads - 1) / threads;
     p.tile = kConvTile;
+    if (a.W > 8) return launch_wide<T, S>(p, a.W, stream);
     const long long n_tiles = ((long long)a.N + p.tile - 1) / p.tile;
     const long long blocks = ((long long)a.B + n_tiles) * p.n_cblk;
     if (blocks > kMaxBlocks) return hipErrorInvalidConfiguration;

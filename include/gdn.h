@@ -91,8 +91,9 @@ typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
  *   state_out  [B, C, L]  state_dtype                  NULL = new window not produced; may alias state_in
  *   offsets    [B+1]      int32                        required
  *   dev_status [1]        int32                        NULL = no status word
- * Constraints: B >= 1, N >= 0, C >= 1, 1 <= W <= 8 (GDN_ERR_UNSUPPORTED above 8), D >= 1,
- * state_dtype is x_dtype or GDN_F32.
+ * Constraints: B >= 1, N >= 0, C >= 1, W >= 1, D >= 1, (W-1)*D and B*C within int32,
+ * state_dtype is x_dtype or GDN_F32.  Widths up to 8 run on kernels that keep the taps in
+ * registers; wider ones on a plain per-element form with the same arithmetic (slower).
  * ---------------------------------------------------------------------------------------------- */
 #define GDN_CONV_SILU 1u
 

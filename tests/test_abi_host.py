@@ -53,7 +53,6 @@ def conv(abi, desc, x=P, w=P, bias=None, sin=None, y=P, sout=None, off=P):
         (dict(C=0), {}, "ERR_SHAPE"),
         (dict(W=0), {}, "ERR_SHAPE"),
         (dict(D=0), {}, "ERR_SHAPE"),
-        (dict(W=9), {}, "ERR_UNSUPPORTED"),
         (dict(x_dtype=7), {}, "ERR_DTYPE"),
         (dict(x_dtype=0, state_dtype=1), {}, "ERR_DTYPE"),
         (dict(flags=2), {}, "ERR_UNSUPPORTED"),
@@ -204,7 +203,7 @@ def conv_capture(abi, desc, cap=4, counts=P, updates=P, **kw):
         ({}, dict(updates=None), "ERR_NULL"),
         ({}, dict(updates=P + 2), "ERR_ALIGN"),
         ({}, dict(cap=2**24), "ERR_OVERFLOW"),  # cap * C beyond int32
-        (dict(W=9), {}, "ERR_UNSUPPORTED"),  # the conv's own checks still apply
+        (dict(D=0), {}, "ERR_SHAPE"),  # the conv's own checks still apply
         ({}, dict(x=None), "ERR_NULL"),
     ],
 )

@@ -53,6 +53,7 @@ CONV_CASES = {
     "f16_w3_d2_f32win": dict(io="f16", W=3, D=2, conv_state_dtype="f32"),
     "f32_w1": dict(io="f32", W=1, D=1),
     "f32_w5_d3_scalar_channels": dict(io="f32", W=5, D=3, K=30, V=30),  # C % 4 != 0: one channel per thread
+    "bf16_w12_d2_wide": dict(io="bf16", W=12, D=2, conv_state_dtype="f32"),  # a width past 8: the per-element form
 }
 
 

@@ -124,3 +124,36 @@ def test_conv_widths_and_dilations(torch, W, D, io, sdt):
     assert np.array_equal(f64(st), st_ref), "the new window is a copy"
     y2, st2 = gpu_conv(torch, w, inplace=True)
     assert np.array_equal(bits(y2), bits(y)) and np.array_equal(bits(st2), bits(st))
+
+
+WIDE = [(W, D, io, sdt) for W in (9, 12, 16) for D in (1, 3) for io, sdt in (("bf16", "f32"), ("f16", "f16"), ("f32", "f32"))]
+
+
+@pytest.mark.parametrize("W,D,io,sdt", WIDE)
+def test_conv_wide_widths(torch, W, D, io, sdt):
+    """Widths past 8 (the pages' conv has no width limit) run on the per-element form: outputs
+    against the oracle, the new window a bit copy, in place bit-identical, with sequences empty,
+    shorter than the window (L = (W-1) D up to 45) and long, and an odd channel count."""
+    lens = [0, 1, 2, 5, 40, 7, 0, 63, 130]
+    w = workloads.make(name=f"conv_wide_w{W}_d{D}_{io}", seed=1300 + 10 * W + D, lengths=lens, HQ=1, H=1, K=32, V=61,
+                       W=W, D=D, io=io, conv_state_dtype=sdt)
+    print(f"[conv wide] W={W} D={D} {io}/{sdt} L={w.L} C={w.C}", flush=True)
+    y, st = gpu_conv(torch, w)
+    y_ref, st_ref = oracle.conv(w.x, w.conv_w, w.offsets, W=w.W, D=w.D, x_dtype=w.io, bias=w.conv_bias,
+                                state_in=w.conv_state, state_dtype=w.conv_state_dtype, silu=w.silu)
+    assert_close(f64(y), y_ref, TOL[w.io], "y")
+    assert np.array_equal(f64(st), st_ref), "the new window is a copy"
+    y2, st2 = gpu_conv(torch, w, inplace=True)
+    assert np.array_equal(bits(y2), bits(y)) and np.array_equal(bits(st2), bits(st))
+
+
+def test_conv_wide_malformed_offsets_write_nothing(torch):
+    w = workloads.make(name="conv_wide_bad", seed=1399, lengths=[3, 0, 9, 4], HQ=1, H=1, K=32, V=64, W=12, D=2,
+                       io="bf16", conv_state_dtype="f32")
+    for case, bad in workloads.malformed_offsets(w.offsets):
+        print(f"[conv wide malformed] {case}", flush=True)
+        status = dev_i32(np.array([12345]))
+        y, st = gpu_conv(torch, w, offsets=bad, dev_status=status)
+        assert int(status.cpu()[0]) == -9
+        assert np.all(bits(y) == bits(sentinel(tuple(y.shape), w.io)))
+        assert np.all(bits(st) == bits(sentinel(tuple(st.shape), w.conv_state_dtype)))
