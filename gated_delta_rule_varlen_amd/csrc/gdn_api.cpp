@@ -86,7 +86,8 @@ gdn_status strided_streams(const gdn_scan_desc* d, const gdn_qkv_streams* s, boo
 // The chunked path sums log-decays, so it needs every decay finite and positive (a decay input with
 // the softplus gate), and it relies on normalised keys for a well-conditioned (I + A); it computes
 // the gates and norms itself, so it runs on fused inputs only; its algebra is that of the rules
-// with the retrieval term and one decay per head.  Built for bf16/fp16 I/O with K = V = 64 or 128.
+// with the retrieval term and one decay per head.  Built for bf16/fp16 I/O with K and V multiples
+// of 8 (K at most 256).
 // It records a capture from its first chunk, so at most 64 slots.  A call without tokens reads no
 // decays (its chunked form only copies the initial states), so there the decay input may be absent.
 bool chunk_eligible(const gdn_scan_desc* d, bool prepared, bool has_decay, int cap) {
