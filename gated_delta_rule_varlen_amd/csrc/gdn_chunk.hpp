@@ -331,7 +331,81 @@ __device__ void block_scan(int n, F val, int32_t* out, int* s_tot, int* s_carry)
 }
 
 // ---- index --------------------------------------------------------------------------------------
+// Batches of fewer than 1024 sequences: one thread per sequence, every table formed in LDS and
+// registers from a single read of the offsets (no table is read back from memory), the four scans
+// in one pass.  Returns -1 (nothing done) for larger batches, else 0, or 1 for malformed offsets.
+__device__ int chunk_index_small(const ChunkArgs& p) {
+    const int B = p.B, i = threadIdx.x, lane = i & 63, wv = i >> 6;
+    if (B >= 1024) return -1;
+    __shared__ int s_off[1025], s_cnt[1024], s_part[16][4];
+    int32_t* hdr = reinterpret_cast<int32_t*>(p.ws);
+    int o = 0;
+    if (i <= B) {
+        o = p.offsets[i];
+        s_off[i] = o;
+    }
+    __syncthreads();
+    int bad = 0;
+    if (i <= B) bad = (i == 0 ? o != 0 : s_off[i - 1] > o) || (i == B && o != p.N);
+    const bool malformed = __syncthreads_or(bad) != 0;
+    report_status(p.dev_status, malformed);
+    if (malformed) {
+        if (i == 0) hdr[0] = GDN_ERR_OFFSETS;
+        return 1;
+    }
+    const Tables tb = tables(p.ws, B);
+    const int sl = p.L.seglen;
+    const int nc = i < B ? (s_off[i + 1] - o + CH - 1) / CH : 0;
+    s_cnt[i] = nc;
+    __syncthreads();
+    // sequences longest first (list scheduling of the long-lived main blocks)
+    int ci_rank = 0;  // chunks of the sequence of rank i
+    if (i < B) {
+        int rank = 0;
+        for (int j = 0; j < B; ++j) {
+            const int cj = s_cnt[j];
+            rank += (cj > nc) || (cj == nc && j < i);
+        }
+        tb.order[rank] = i;
+        tb.nchunk[i] = nc;
+        s_off[rank] = i;  // (the offsets are no longer needed)
+    }
+    __syncthreads();
+    if (i < B) ci_rank = s_cnt[s_off[i]];
+    const int ns = nseg_of(nc, sl);
+    int v[4] = {i < B ? nseg_of(ci_rank, sl) * p.H * p.VS : 0, ns > 1 ? (ns - 1) * p.H : 0, ns > 1 ? ns : 0, nc};
+    int incl[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        incl[e] = v[e];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl[e], d);
+            if (lane >= d) incl[e] += y;
+        }
+        if (lane == 63) s_part[wv][e] = incl[e];
+    }
+    __syncthreads();
+    int32_t* const outs[4] = {tb.ustart, tb.sstart, tb.slot0, tb.cstart};
+    int ex[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        int before = 0;
+        for (int k = 0; k < wv; ++k) before += s_part[k][e];
+        ex[e] = before + incl[e] - v[e];
+        if (i <= B) outs[e][i] = ex[e];  // (thread B: the total)
+    }
+    if (i == B) {  // (the header is read only by kernels launched after this one)
+        hdr[1] = ex[0];
+        hdr[2] = ex[1];
+        hdr[3] = ex[3];
+        hdr[0] = GDN_OK;
+    }
+    return 0;
+}
+
 __global__ __launch_bounds__(1024) void chunk_index_kernel(ChunkArgs p) {
+    if (chunk_index_small(p) >= 0) return;
     const bool malformed = offsets_malformed(p.offsets, p.B, p.N);
     report_status(p.dev_status, malformed);
     int32_t* hdr = reinterpret_cast<int32_t*>(p.ws);
@@ -384,22 +458,26 @@ __global__ __launch_bounds__(1024) void chunk_index_kernel(ChunkArgs p) {
 // ---- tmat: gates, G and the T fragments of every (chunk, head) -----------------------------------
 // k rows are read whole (K/8 lanes per row, 16 bytes each); wave w normalises token rows
 // 16w..16w+15 (wave 0 also forms the gates, whose loads go out first).  A is formed in its ten
-// nonzero 16 x 16 blocks by MFMA, blocks w, w+4, w+8 (row-major) by wave w.  T: the diagonal blocks
-// in fp32 by forward substitution (wave w, block w; lane = column, each solved row updating the rows
-// below it, so the chain is one FMA per row), then wave w walks down its block column,
+// nonzero 16 x 16 blocks by MFMA, blocks w, w+4, w+8 (row-major) by wave w.  T: the four diagonal
+// blocks in fp32 by forward substitution in a single wave (lane = block l/16 and column l%16, so that
+// every lane does useful work; the kernel is bound by vector-ALU issue), then wave w walks down its
+// block column,
 // T_iw = -T_ii sum_{w <= m < i} A_im T_mw, on MFMA operands of the I/O type with its earlier blocks
 // kept in accumulators (the operands of the chunk chain are rounded to that type anyway).
 template <typename T, int K>
 __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     using TS = typename T::storage;
     constexpr int LPT = K / 8, TPI = 64 / LPT, NI = 16 / TPI;
-    // A and T are kept as values of the operand type (a 64 x 64 tile in 9 KB each), so that four
-    // or five blocks share a compute unit; the diagonal solve works on them in fp32
+    // A and T are kept as values of the operand type (a 64 x 64 tile in 9 KB each) in the space of
+    // the k rows, which are dead once A's blocks are in registers: more blocks share a compute unit
     __shared__ __align__(16) union {
         uint16_t kn[CH][K + kPadRow];  // raw k rows, until A is formed
-        uint16_t tm[CH][CH + 8];       // T
+        struct {
+            uint16_t am[CH][CH + 8];  // A
+            uint16_t tm[CH][CH + 8];  // T
+        } at;
     } r0;
-    __shared__ __align__(16) uint16_t am[CH][CH + 8];
+    auto& am = r0.at.am;
     __shared__ __align__(16) float s_gam[CH], s_beta[CH], s_rk[CH];
     auto to16 = [](float v) { return (uint16_t)(Op<T>::pk(v, 0.0f) & 0xffffu); };
 
@@ -468,9 +546,13 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
         }
     }
     __syncthreads();
-    {  // A: lower-triangle blocks t = w, w + 4, w + 8 in row-major order (it, jt <= it)
-#pragma unroll 1
-        for (int t = w; t < 10; t += NW) {
+    {  // A: lower-triangle blocks t = w, w + 4, w + 8 in row-major order (it, jt <= it), held in
+       // registers until every wave is done with the k rows
+        uint16_t av[3][4];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int t = w + NW * j;
+            if (t >= 10) break;
             const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
             const int jt = t - it * (it + 1) / 2;
             const int ja = 16 * jt + (lane & 15);
@@ -486,21 +568,42 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float e = fexp(fminf(g_ia[r] - g_ja, 0.0f));
-                am[ia + r][ja] = to16((ja < ia + r) ? (b_ia[r] * r_ia[r] * r_ja) * e * a[r] : 0.0f);
+                av[j][r] = to16((ja < ia + r) ? (b_ia[r] * r_ia[r] * r_ja) * e * a[r] : 0.0f);
             }
         }
+        __syncthreads();  // k rows dead
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int t = w + NW * j;
+            if (t >= 10) break;
+            const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+            const int jt = t - it * (it + 1) / 2;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) am[16 * it + 4 * g + r][16 * jt + (lane & 15)] = av[j][r];
+        }
     }
-    __syncthreads();  // A ready; k rows dead: T may be written
-    auto& tm = r0.tm;
-    if (lane < 16) {  // diagonal block w by forward substitution, lane = column
-        const int cc = lane, o = 16 * w;
+    __syncthreads();  // A ready
+    auto& tm = r0.at.tm;
+    if (w == (int)(blockIdx.x & 3)) {  // the four diagonal blocks by forward substitution in one wave
+        const int o = 16 * g, cc = lane & 15;  // lane: block g, column l%16 of T
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.0f : 0.0f;
 #pragma unroll
-        for (int m = 0; m < 15; ++m)  // x[m] is final: take it out of the rows below
+        for (int i = 1; i < 16; ++i) {  // row i: x_i -= sum_{m < i} A_im x_m, the newest term last
+            float a[16];
 #pragma unroll
-            for (int i = m + 1; i < 16; ++i) x[i] = fmaf(-to_f32<T>(am[o + i][o + m]), x[m], x[i]);
+            for (int h8 = 0; h8 < (i + 7) / 8; ++h8) {
+                const u32x4 r = *reinterpret_cast<const u32x4*>(&am[o + i][o + 8 * h8]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a[8 * h8 + 2 * e] = to_f32<T>((uint16_t)(r[e] & 0xffffu));
+                    a[8 * h8 + 2 * e + 1] = to_f32<T>((uint16_t)(r[e] >> 16));
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < i; ++m) x[i] = fmaf(-a[m], x[m], x[i]);
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) tm[o + i][o + cc] = to16(x[i]);
     }
