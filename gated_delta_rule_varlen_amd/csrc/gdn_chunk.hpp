@@ -207,16 +207,21 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-// sum of squares of eight 16-bit inputs, fp32 (plain FMAs; v_dot2 would need a bit cast of each
-// vector element, which was compiled to read element 0 every time)
+// sum of squares of eight 16-bit inputs, fp32: one v_dot2 per 32-bit word (the products of two
+// 16-bit values are exact in fp32)
 template <typename T>
 __device__ __forceinline__ float sumsq8(u32x4 raw) {
     float s = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float lo = to_f32<T>((uint16_t)(raw[e] & 0xffffu)), hi = to_f32<T>((uint16_t)(raw[e] >> 16));
-        s = fmaf(lo, lo, s);
-        s = fmaf(hi, hi, s);
+        const uint32_t x = raw[e];  // (a scalar first: each word is then read from its own register)
+        if constexpr (std::is_same<T, F16>::value) {
+            const f16x2 v = __builtin_bit_cast(f16x2, x);
+            s = __builtin_amdgcn_fdot2(v, v, s, false);
+        } else {
+            const bf16x2 v = __builtin_bit_cast(bf16x2, x);
+            s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+        }
     }
     return s;
 }
@@ -239,6 +244,13 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 // e^x through the hardware 2^x (about 1 ulp): for decay factors that are rounded to bf16 or scale
 // a whole chunk
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+// softplus(x) = max(x, 0) + log1p(e^-|x|) on the hardware exp2/log2, with log1p(e) = log(1 + e) e / ((1 + e) - 1)
+// (the quotient cancels the rounding of 1 + e; e itself where 1 + e rounds to 1)
+__device__ __forceinline__ float softplus_hw(float x) {
+    const float e = fexp(-fabsf(x)), u = 1.0f + e;
+    const float l1p = u == 1.0f ? e : __builtin_amdgcn_logf(u) * 0.693147180559945309f * (e / (u - 1.0f));
+    return fmaxf(x, 0.0f) + l1p;
+}
 __device__ __forceinline__ int tf_tile(int f) { return f < 2 ? f : 2 + (f - 2) / 2; }  // token tile of T fragment f
 __device__ __forceinline__ int tf_blk(int f) { return f < 2 ? 0 : (f - 2) % 2; }    // its 32-block
 
@@ -522,9 +534,9 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     if (w == 0) {  // gates and the cumulative log-decay; padding tokens: no decay, no update
         float ell = 0.0f, beta = 0.0f;
         if (lane < n) {
-            ell = -expf(p.A_log[h]) * softplus_f(widen(a_raw) + p.dt_bias[h]);
+            ell = -expf(p.A_log[h]) * softplus_hw(widen(a_raw) + p.dt_bias[h]);
             beta = p.b ? widen(b_raw) : 1.0f;
-            if (p.b && (p.flags & GDN_SIGMOID)) beta = 1.0f / (1.0f + expf(-beta));
+            if (p.b && (p.flags & GDN_SIGMOID)) beta = __builtin_amdgcn_rcpf(1.0f + fexp(-beta));
         }
         const float gam = wave_prefix_sum(ell);
         s_gam[lane] = gam;
