@@ -1032,12 +1032,13 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
         if (c > cb) flush_out(c - 1);
         if (c + 1 < ce) load_rows(c + 1, R);  // in flight during this chunk
 
-        // ---- P = M o (Q K^T) / (|q_i| |k_j|): the ten nonzero 16 x 16 blocks (it, jt <= it), block n by
-        // wave n % NWV, formed transposed (K_jt Q_it^T; lane: 4 consecutive j = 16 jt + 4g + r of row
-        // i = 16 it + l%16)
+        // ---- P = M o (Q K^T) / (|q_i| |k_j|): the ten nonzero 16 x 16 blocks (it, jt <= it), formed
+        // transposed (K_jt Q_it^T; lane: 4 consecutive j = 16 jt + 4g + r of row i = 16 it + l%16).
+        // Block n goes to wave (n + 2) % NWV: the waves with a second block then sit on other SIMDs
+        // than wave 0, which also forms the per-token factors (waves w and w + 4 share a SIMD).
         if constexpr (!SUMMARY) {
 #pragma unroll
-            for (int nb = w; nb < 10; nb += NWV) {
+            for (int nb = (w + NWV - 2 % NWV) % NWV; nb < 10; nb += NWV) {
                 const int it = nb < 1 ? 0 : nb < 3 ? 1 : nb < 6 ? 2 : 3;
                 const int jt = nb - it * (it + 1) / 2;
                 f32x4 pt = zero4();
@@ -1049,11 +1050,16 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
                 const f32x4 g_j = *reinterpret_cast<const f32x4*>(&Bf.gam[j0]);
                 const f32x4 r_j = *reinterpret_cast<const f32x4*>(&Bf.rk[j0]);
                 float pv4[4];
+                if (it == jt) {  // diagonal block: the causal mask (every lane computes a finite value
+                                 // and the mask selects it: no divergent branch)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    // every lane computes the (finite) value and the mask selects it: no divergent branch
-                    const float val = fexp(fminf(g_i - g_j[r], 0.0f)) * (q_i * r_j[r]) * pt[r];
-                    pv4[r] = val * (j0 + r <= i ? 1.0f : 0.0f);
+                    for (int r = 0; r < 4; ++r) {
+                        const float val = fexp(fminf(g_i - g_j[r], 0.0f)) * (q_i * r_j[r]) * pt[r];
+                        pv4[r] = j0 + r <= i ? val : 0.0f;
+                    }
+                } else {  // below the diagonal: j < i, and G does not increase along the chunk
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pv4[r] = fexp(g_i - g_j[r]) * (q_i * r_j[r]) * pt[r];
                 }
                 *reinterpret_cast<u32x2*>(&sm.pb[i][32 * (jt >> 1) + 8 * g + 4 * (jt & 1)]) =
                     u32x2{Op<T>::pk(pv4[0], pv4[1]), Op<T>::pk(pv4[2], pv4[3])};
