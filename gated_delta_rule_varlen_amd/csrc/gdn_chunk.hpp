@@ -243,8 +243,7 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 }
 // e^x through the hardware 2^x (about 1 ulp): for decay factors that are rounded to bf16 or scale
 // a whole chunk
-constexpr float kLog2e = 1.44269504088896341f;
-__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 // softplus(x) = max(x, 0) + log1p(e^-|x|) on the hardware exp2/log2, with log1p(e) = log(1 + e) e / ((1 + e) - 1)
 // (the quotient cancels the rounding of 1 + e; e itself where 1 + e rounds to 1)
 __device__ __forceinline__ float softplus_hw(float x) {
@@ -705,9 +704,8 @@ __device__ __forceinline__ typename Op<T>::v8 frag_t(const uint16_t* tile, int l
 // after it, so one copy serves; the per-token factors are read after that barrier and have two, and
 // so has kt where LDS allows (else the next chunk's kt waits for one more barrier).
 struct ChunkBuf {
-    // per token: G log2(e); b; scale e^G; b e^G / |k|; e^{G_C - G} / |k|; G log2(e) + log2 |k|; 1/|q|;
-    // and e^{G_C}
-    float g2[CH], beta[CH], eg[CH], bx[CH], ud[CH], hk[CH], rq[CH], gc[4];
+    // per token: G; b; scale e^G; b e^G / |k|; e^{G_C - G} / |k|; 1/|k|; 1/|q|; and e^{G_C}
+    float gam[CH], beta[CH], eg[CH], bx[CH], ud[CH], rk[CH], rq[CH], gc[4];
 };
 template <int K, int VT, bool SUMMARY, int NKT, bool SO>
 struct FusedLds {
@@ -925,12 +923,12 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
         if (w == 0) {  // (every value part: each reads its own factors)
             const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, R.gam), CH - 1));
             const float eg = fexp(R.gam);
-            Bf.g2[lane] = R.gam * kLog2e;
+            Bf.gam[lane] = R.gam;
             Bf.beta[lane] = R.beta;
             Bf.eg[lane] = p.scale * eg;
             Bf.bx[lane] = R.beta * eg * R.rk;
             Bf.ud[lane] = std::is_same<T, F16>::value ? fexp(gC - R.gam) : fexp(gC - R.gam) * R.rk;
-            Bf.hk[lane] = R.gam * kLog2e - __builtin_amdgcn_logf(R.rk);  // (1/|k| <= 1e6: finite)
+            Bf.rk[lane] = R.rk;
             if (lane == 0) Bf.gc[0] = fexp(gC);
             // the previous token's G, read by the whole wave (a lane shuffle from an inactive lane
             // would read zero)
@@ -1048,19 +1046,20 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
                 for (int kk = 0; kk < KK; ++kk)
                     pt = Op<T>::mma(frag<T>(&sm.kn[16 * jt][32 * kk], K + kPadRow, lane), frag<T>(&sm.qn[16 * it][32 * kk], K + kPadRow, lane), pt);
                 const int i = 16 * it + l16, j0 = 16 * jt + 4 * g;
-                // e^{G_i - G_j} / (|q_i| |k_j|) as one power of two (the norms are at least 1e-6)
-                const float a_i = Bf.g2[i] + __builtin_amdgcn_logf(Bf.rq[i]);
-                const f32x4 h_j = *reinterpret_cast<const f32x4*>(&Bf.hk[j0]);
+                const float g_i = Bf.gam[i], q_i = Bf.rq[i];
+                const f32x4 g_j = *reinterpret_cast<const f32x4*>(&Bf.gam[j0]);
+                const f32x4 r_j = *reinterpret_cast<const f32x4*>(&Bf.rk[j0]);
                 float pv4[4];
-                if (it == jt) {  // diagonal block: the causal mask selects (what it drops may be inf)
+                if (it == jt) {  // diagonal block: the causal mask (every lane computes a finite value
+                                 // and the mask selects it: no divergent branch)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float val = __builtin_amdgcn_exp2f(a_i - h_j[r]) * pt[r];
+                        const float val = fexp(fminf(g_i - g_j[r], 0.0f)) * (q_i * r_j[r]) * pt[r];
                         pv4[r] = j0 + r <= i ? val : 0.0f;
                     }
                 } else {  // below the diagonal: j < i, and G does not increase along the chunk
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) pv4[r] = __builtin_amdgcn_exp2f(a_i - h_j[r]) * pt[r];
+                    for (int r = 0; r < 4; ++r) pv4[r] = fexp(g_i - g_j[r]) * (q_i * r_j[r]) * pt[r];
                 }
                 *reinterpret_cast<u32x2*>(&sm.pb[i][32 * (jt >> 1) + 8 * g + 4 * (jt & 1)]) =
                     u32x2{Op<T>::pk(pv4[0], pv4[1]), Op<T>::pk(pv4[2], pv4[3])};
