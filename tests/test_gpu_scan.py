@@ -4,7 +4,8 @@ Every path (DECODE, SEQ) runs in both input modes (fused: norms and gates in-ker
 from gdn_prepare_qk_gates) on the five workloads at full size, in the launch configuration the
 benchmark uses (plus the benchmark's speculative verification step); the oracle computes sampled
 heads and columns of the same launch.  Outputs use
-the dtype tolerance, the final fp32 state 1e-4 for fp32 I/O and 2e-2 otherwise."""
+the dtype tolerance (1e-4 fp32, 2e-2 half) and the final fp32 state 1e-4 on the token-sequential
+paths; the chunked form uses its own tolerances for both (bf16 2e-2, fp16 1.5e-3)."""
 import dataclasses
 
 import numpy as np
@@ -13,7 +14,7 @@ import pytest
 import cases
 import oracle
 import workloads
-from gpu_util import (CHUNK_SEQ_TOL, CHUNK_TOL, SEQ_STATE_TOL, TOL, assert_close, out_tol, assert_close_slices, state_tol, bits, dev, dev_i32, ensure_built, f64, head_subproblem, require_gpu,
+from gpu_util import (CHUNK_SEQ_TOL, CHUNK_SLICE_TOL, CHUNK_TOL, SEQ_STATE_TOL, TOL, assert_close, out_tol, assert_close_slices, state_tol, bits, dev, dev_i32, ensure_built, f64, head_subproblem, require_gpu,
                       sentinel)
 
 pytestmark = pytest.mark.gpu
@@ -191,6 +192,41 @@ def test_chunk_ragged_against_oracle_and_seq(torch, K, H, io, G):
     print(f"  errors: out {e1:.2e} state {e2:.2e} vs-seq out {e3:.2e} state {e4:.2e}", flush=True)
     empty = np.flatnonzero(w.lengths == 0)
     assert np.array_equal(bits(st_c)[empty], w.state[empty].view(np.int32))
+
+
+@pytest.mark.parametrize("B", [1023, 1024, 1500])
+def test_chunk_many_sequences_against_oracle_and_seq(torch, B):
+    # the chunk tables are formed in LDS by one thread per sequence below 1024 sequences and by the
+    # looped block scans from 1024 on: both forms, at and around the boundary, with zero-length
+    # sequences, one-token sequences and sequences of one and two chunks
+    rng = np.random.default_rng(900 + B)
+    lengths = rng.integers(0, 100, size=B)
+    lengths[rng.choice(B, size=B // 10, replace=False)] = 0
+    lengths[rng.choice(B, size=B // 20, replace=False)] = 1
+    w = workloads.make(name=f"chunk_many_b{B}", seed=901 + B, lengths=lengths, HQ=1, H=2, K=64, V=64, io="bf16",
+                       conv_state_dtype="f32")
+    print(f"[chunk many] B={B} N={w.N}", flush=True)
+    status = torch.full((1,), 777, dtype=torch.int32, device="cuda")
+    out_c, st_c, used = gpu_scan(torch, w, "chunk", False, dev_status=status)
+    assert used == "chunk" and int(status.item()) == 0
+    out_s, st_s, _ = gpu_scan(torch, w, "seq", False)
+    o_ref, s_ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io, gate_dtype=w.gate_dtype,
+                               a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias, state_in=w.state)
+    e1 = assert_close(f64(out_c), o_ref, CHUNK_TOL[w.io], "chunk out")
+    e2 = assert_close(f64(st_c), s_ref, CHUNK_TOL[w.io], "chunk state")
+    assert_close_slices(f64(out_c), o_ref, w.lengths, CHUNK_SLICE_TOL[w.io], "chunk out")
+    e3 = assert_close(f64(out_c), f64(out_s), CHUNK_SEQ_TOL[w.io], "chunk vs seq out")
+    e4 = assert_close(f64(st_c), f64(st_s), CHUNK_SEQ_TOL[w.io], "chunk vs seq state")
+    print(f"  errors: out {e1:.2e} state {e2:.2e} vs-seq out {e3:.2e} state {e4:.2e}", flush=True)
+    empty = np.flatnonzero(w.lengths == 0)
+    assert np.array_equal(bits(st_c)[empty], w.state[empty].view(np.int32))
+    # malformed offsets on either form of the tables: nothing is written
+    for case, bad in workloads.malformed_offsets(w.offsets):
+        print(f"  malformed {case}", flush=True)
+        out, st, _ = gpu_scan(torch, w, "chunk", False, offsets=bad, dev_status=status)
+        assert int(status.item()) == -9, case
+        assert np.all(bits(out) == bits(sentinel(tuple(out.shape), w.io))), case
+        assert np.all(bits(st) == bits(sentinel(tuple(st.shape), "f32"))), case
 
 
 def test_chunk_matches_seq_at_full_prefill_size(torch):
