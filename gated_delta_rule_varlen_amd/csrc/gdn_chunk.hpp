@@ -176,6 +176,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: each lane names 8 bytes (four 16-bit elements) of LDS; within each group of 16
+// lanes, lane i receives element i%4 of the reads of lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+}
 
 // MFMA operands of an I/O type: bf16 I/O runs on bf16 operands (v_mfma_f32_16x16x32_bf16) and fp16
 // I/O on fp16 operands (v_mfma_f32_16x16x32_f16, same rate), so the raw q, k and v rows are
@@ -700,7 +706,7 @@ __device__ __forceinline__ typename Op<T>::v8 frag_t(const uint16_t* tile, int l
     return *reinterpret_cast<const typename Op<T>::v8*>(tile + idx * ld + 8 * ((4 * jj + (lane >> 4)) ^ ((idx >> kSwz) & 7)));
 }
 
-// kn, qn and vt are last read before a chunk's middle barrier and are written for the next chunk
+// kn, qn and vr are last read before a chunk's middle barrier and are written for the next chunk
 // after it, so one copy serves; the per-token factors are read after that barrier and have two, and
 // so has kt where LDS allows (else the next chunk's kt waits for one more barrier).
 struct ChunkBuf {
@@ -711,7 +717,7 @@ template <int K, int VT, bool SUMMARY, int NKT, bool SO>
 struct FusedLds {
     uint16_t kn[CH][K + kPadRow];
     uint16_t qn[SUMMARY ? 1 : CH][K + kPadRow];
-    uint16_t vt[VT][CH + kPadT];
+    uint16_t vr[CH][VT + kPadRow];  // v rows as loaded (read transposed by ds_read_b64_tr_b16)
     uint16_t tf[NTF][512];  // T fragments (lane order), read before the middle barrier
     uint16_t kt[NKT][K][CH + kPadT];
     ChunkBuf buf[2];
@@ -981,20 +987,9 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
             }
         }
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
+        for (int i = 0; i < NV; ++i) {  // v rows as loaded: 16 bytes a lane
             const int ti = RPW * w + TPV * i + vsub;
-            if constexpr (TPV == 4) {
-                const u32x4 y = transpose_rows4(R.v[i]);
-                const int r0 = 8 * pv + 2 * vsub, t0 = RPW * w + TPV * i;
-                *reinterpret_cast<u32x2*>(&sm.vt[r0][tpos(r0, t0)]) =
-                    u32x2{(y[0] & 0xffffu) | (y[1] << 16), (y[2] & 0xffffu) | (y[3] << 16)};
-                *reinterpret_cast<u32x2*>(&sm.vt[r0 + 1][tpos(r0 + 1, t0)]) =
-                    u32x2{(y[0] >> 16) | (y[1] & 0xffff0000u), (y[2] >> 16) | (y[3] & 0xffff0000u)};
-            } else {
-                const int tp = tpos(8 * pv, ti);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sm.vt[8 * pv + e][tp] = half_of(R.v[i], e);
-            }
+            *reinterpret_cast<u32x4*>(&sm.vr[ti][8 * pv]) = R.v[i];
         }
     };
 
@@ -1102,10 +1097,12 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
             const f32x4 bxv = *reinterpret_cast<const f32x4*>(&Bf.bx[i0]);
 #pragma unroll
             for (int ct = 0; ct < VTW; ++ct) {
-                const int cc = col_of(ct);
-                const u32x2 vr = *reinterpret_cast<const u32x2*>(&sm.vt[cc][tpos(cc, i0)]);
-                const float vv[4] = {to_f32<T>((uint16_t)(vr.x & 0xffffu)), to_f32<T>((uint16_t)(vr.x >> 16)),
-                                     to_f32<T>((uint16_t)(vr.y & 0xffffu)), to_f32<T>((uint16_t)(vr.y >> 16))};
+                // tokens i0 .. i0+3 of column 16 (VTW w + ct) + l%16 from the row-major v tile: within
+                // each 16-lane group the transposing read hands lane i element i%4 of the four lanes
+                // 4k + i/4 (k = 0..3), so lane s reads token i0 + s/4, columns + 4 (s%4) .. + 3
+                const v4i16 tv = lds_read_tr16(&sm.vr[i0 + (l16 >> 2)][16 * (VTW * w + ct) + 4 * (l16 & 3)]);
+                const float vv[4] = {to_f32<T>((uint16_t)tv[0]), to_f32<T>((uint16_t)tv[1]), to_f32<T>((uint16_t)tv[2]),
+                                     to_f32<T>((uint16_t)tv[3])};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) ks[it][ct][r] = fmaf(bet[r], vv[r], -bxv[r] * ks[it][ct][r]);
             }
