@@ -713,13 +713,16 @@ struct ChunkBuf {
     // per token: G; b; scale e^G; b e^G / |k|; e^{G_C - G} / |k|; 1/|k|; 1/|q|; and e^{G_C}
     float gam[CH], beta[CH], eg[CH], bx[CH], ud[CH], rk[CH], rq[CH], gc[4];
 };
-template <int K, int VT, bool SUMMARY, int NKT, bool SO>
+// TRK (bf16 operands): K^T is read from the k rows themselves through the transposing read, so the k
+// rows take NKT copies and there is no transposed tile; on fp16 operands K^T holds the normalised
+// rows and has a tile of its own (NKT copies).
+template <int K, int VT, bool SUMMARY, int NKT, bool SO, bool TRK>
 struct FusedLds {
-    uint16_t kn[CH][K + kPadRow];
+    uint16_t kn[TRK ? NKT : 1][CH][K + kPadRow];
     uint16_t qn[SUMMARY ? 1 : CH][K + kPadRow];
     uint16_t vr[CH][VT + kPadRow];  // v rows as loaded (read transposed by ds_read_b64_tr_b16)
     uint16_t tf[NTF][512];  // T fragments (lane order), read before the middle barrier
-    uint16_t kt[NKT][K][CH + kPadT];
+    uint16_t kt[TRK ? 1 : NKT][TRK ? 1 : K][CH + kPadT];
     ChunkBuf buf[2];
     uint16_t pb[SUMMARY ? 1 : CH][CH + kPadT];
     uint16_t ob[SUMMARY || !SO ? 1 : CH][VT + 8];  // output rows of the previous chunk, stored whole
@@ -727,11 +730,11 @@ struct FusedLds {
 // LDS of one block: two kt buffers and staged output rows while they fit, else one kt buffer, and
 // then output rows stored straight from the registers (K = 256 with 128-column value parts).
 constexpr size_t kLdsBytes = 160 * 1024;
-template <int K, int VT, bool SUMMARY>
+template <int K, int VT, bool SUMMARY, bool TRK>
 struct LdsPlan {
-    static constexpr int NKT = sizeof(FusedLds<K, VT, SUMMARY, 2, true>) <= kLdsBytes ? 2 : 1;
-    static constexpr bool SO = sizeof(FusedLds<K, VT, SUMMARY, NKT, true>) <= kLdsBytes;
-    using Lds = FusedLds<K, VT, SUMMARY, NKT, SO>;
+    static constexpr int NKT = sizeof(FusedLds<K, VT, SUMMARY, 2, true, TRK>) <= kLdsBytes ? 2 : 1;
+    static constexpr bool SO = sizeof(FusedLds<K, VT, SUMMARY, NKT, true, TRK>) <= kLdsBytes;
+    using Lds = FusedLds<K, VT, SUMMARY, NKT, SO, TRK>;
     static_assert(sizeof(Lds) <= kLdsBytes, "LDS per block");
 };
 // voffset of a buffer access that is to read zero or write nothing (past every range used here:
@@ -759,7 +762,8 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
     constexpr int LPV = VT / 8, TPV = 64 / LPV;
     static_assert(RPW % TPI == 0 && RPW % TPV == 0, "staging tiles");
     constexpr int NI = RPW / TPI, NV = RPW / TPV;
-    using Plan = LdsPlan<K, VT, SUMMARY>;
+    constexpr bool TRK = std::is_same<T, BF16>::value;
+    using Plan = LdsPlan<K, VT, SUMMARY, TRK>;
     constexpr int NKT = Plan::NKT;
     constexpr bool SO = Plan::SO;
     __shared__ __align__(16) typename Plan::Lds sm;
@@ -921,7 +925,19 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
         R.rk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgt, (2 * CH + lane) * 4, 0, 0));
     };
     // raw rows, transposes, norms and per-token factors of chunk c into buffer Bf
-    auto stage = [&](int c, const Rows& R, ChunkBuf& Bf, uint16_t (&kt)[K][CH + kPadT]) {
+    // K^T operand from the row-major k rows (bf16 operands): keys 16 kt + l%16, the tokens of 32-block
+    // jj in the split order.  Within each 16-lane group g, lane s names 8 bytes of token
+    // 32 jj + 4g + s/4 (then 16 tokens on) at the split slots of keys 16 kt + 4(s%4) .. +3; the
+    // transposing read hands each key's four tokens to that key's lane.
+    auto kt_frag = [&](const uint16_t (&kr)[CH][K + kPadRow], int kt, int jj) -> OpV {
+        const int col = 32 * (kt >> 1) + 8 * (l16 & 3) + 4 * (kt & 1);
+        const v4i16 lo = lds_read_tr16(&kr[32 * jj + 4 * g + (l16 >> 2)][col]);
+        const v4i16 hi = lds_read_tr16(&kr[32 * jj + 16 + 4 * g + (l16 >> 2)][col]);
+        return __builtin_bit_cast(OpV, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto stage = [&](int c, const Rows& R, ChunkBuf& Bf, int kbuf) {
+        auto& knb = sm.kn[TRK ? kbuf : 0];
+        auto& kt = sm.kt[TRK ? 0 : kbuf];
         const bool cap_chunk = CAPTURE && c == 0 && captured > 0;
 #pragma unroll
         for (int j = 0; j < NTFW; ++j)
@@ -945,30 +961,33 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
         for (int i = 0; i < NI; ++i) {
             const int ti = RPW * w + TPI * i + tsub;
             const u32x4 kb = R.k[i];
-            *reinterpret_cast<u32x2*>(&sm.kn[ti][ks0]) = u32x2{kb[0], kb[1]};
-            *reinterpret_cast<u32x2*>(&sm.kn[ti][ks0 + 8]) = u32x2{kb[2], kb[3]};
-            // K^T: raw rows on bf16 operands (1/|k| goes with U); on fp16 operands the rows are
-            // normalised here, so that U's factor stays within 1 whatever |k| is
-            u32x4 ktb = kb;
-            if constexpr (std::is_same<T, F16>::value) {
-                const float rk = rsqrtf(group_sum<LPT>(sumsq8<T>(kb)) + 1e-12f);
-                float kf[8];
-                unpack8<T>(kb, kf);
-                ktb = pack8<T>(kf, rk);
-            }
-            if constexpr (TPI == 4) {
-                // lanes pc, pc + 16, pc + 32, pc + 48 hold four consecutive tokens: after the
-                // transpose, row tsub has keys 8 pc + 2 tsub and + 1 of all four (8 bytes per key)
-                const u32x4 y = transpose_rows4(ktb);
-                const int r0 = 8 * pc + 2 * tsub, t0 = RPW * w + TPI * i;
-                *reinterpret_cast<u32x2*>(&kt[r0][tpos(r0, t0)]) =
-                    u32x2{(y[0] & 0xffffu) | (y[1] << 16), (y[2] & 0xffffu) | (y[3] << 16)};
-                *reinterpret_cast<u32x2*>(&kt[r0 + 1][tpos(r0 + 1, t0)]) =
-                    u32x2{(y[0] >> 16) | (y[1] & 0xffff0000u), (y[2] >> 16) | (y[3] & 0xffff0000u)};
-            } else {
-                const int tp = tpos(8 * pc, ti);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kt[8 * pc + e][tp] = half_of(ktb, e);
+            *reinterpret_cast<u32x2*>(&knb[ti][ks0]) = u32x2{kb[0], kb[1]};
+            *reinterpret_cast<u32x2*>(&knb[ti][ks0 + 8]) = u32x2{kb[2], kb[3]};
+            // K^T: raw rows on bf16 operands (1/|k| goes with U), read from the k rows; on fp16
+            // operands the rows are normalised here, so that U's factor stays within 1 whatever |k|
+            // is, and transposed into a tile of their own
+            if constexpr (!TRK) {
+                u32x4 ktb = kb;
+                if constexpr (std::is_same<T, F16>::value) {
+                    const float rk = rsqrtf(group_sum<LPT>(sumsq8<T>(kb)) + 1e-12f);
+                    float kf[8];
+                    unpack8<T>(kb, kf);
+                    ktb = pack8<T>(kf, rk);
+                }
+                if constexpr (TPI == 4) {
+                    // lanes pc, pc + 16, pc + 32, pc + 48 hold four consecutive tokens: after the
+                    // transpose, row tsub has keys 8 pc + 2 tsub and + 1 of all four (8 bytes per key)
+                    const u32x4 y = transpose_rows4(ktb);
+                    const int r0 = 8 * pc + 2 * tsub, t0 = RPW * w + TPI * i;
+                    *reinterpret_cast<u32x2*>(&kt[r0][tpos(r0, t0)]) =
+                        u32x2{(y[0] & 0xffffu) | (y[1] << 16), (y[2] & 0xffffu) | (y[3] << 16)};
+                    *reinterpret_cast<u32x2*>(&kt[r0 + 1][tpos(r0 + 1, t0)]) =
+                        u32x2{(y[0] >> 16) | (y[1] & 0xffff0000u), (y[2] >> 16) | (y[3] & 0xffff0000u)};
+                } else {
+                    const int tp = tpos(8 * pc, ti);
+    #pragma unroll
+                    for (int e = 0; e < 8; ++e) kt[8 * pc + e][tp] = half_of(ktb, e);
+                }
             }
             if constexpr (!SUMMARY) {
                 if (cap_chunk && ti < captured && h % p.G == 0 && vp == 0) {  // (uniform over the row's lanes)
@@ -1018,10 +1037,11 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
         }
     };
 
-    // One chunk; Bf and ktf hold it, Bn and ktn receive the next one (the buffers alternate; with
-    // one kt buffer ktf and ktn are the same)
+    // One chunk; Bf and K^T buffer kc hold it, Bn and buffer kx receive the next one (the buffers
+    // alternate; with one K^T buffer kc and kx are the same)
     Rows R;
-    auto step = [&](int c, ChunkBuf& Bf, ChunkBuf& Bn, uint16_t (&ktf)[K][CH + kPadT], uint16_t (&ktn)[K][CH + kPadT]) {
+    auto step = [&](int c, ChunkBuf& Bf, ChunkBuf& Bn, int kc, int kx) {
+        const auto& knc = sm.kn[TRK ? kc : 0];
         const int t0 = seq_start + c * CH, n = min(CH, len - c * CH);
         const bool cap_chunk = CAPTURE && c == 0 && captured > 0;
         if (c > cb) flush_out(c - 1);
@@ -1039,7 +1059,7 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
                 f32x4 pt = zero4();
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    pt = Op<T>::mma(frag<T>(&sm.kn[16 * jt][32 * kk], K + kPadRow, lane), frag<T>(&sm.qn[16 * it][32 * kk], K + kPadRow, lane), pt);
+                    pt = Op<T>::mma(frag<T>(&knc[16 * jt][32 * kk], K + kPadRow, lane), frag<T>(&sm.qn[16 * it][32 * kk], K + kPadRow, lane), pt);
                 const int i = 16 * it + l16, j0 = 16 * jt + 4 * g;
                 const float g_i = Bf.gam[i], q_i = Bf.rq[i];
                 const f32x4 g_j = *reinterpret_cast<const f32x4*>(&Bf.gam[j0]);
@@ -1079,7 +1099,7 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
             }
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const OpV kf = frag<T>(&sm.kn[16 * it][32 * kk], K + kPadRow, lane);
+                const OpV kf = frag<T>(&knc[16 * it][32 * kk], K + kPadRow, lane);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) ks[it][ct] = Op<T>::mma(kf, sbf[kk][ct], ks[it][ct]);
                 if constexpr (!SUMMARY) {
@@ -1190,8 +1210,8 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
             const float gC = Bf.gc[0];
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const OpV a0 = frag_t<T>(&ktf[0][0], CH + kPadT, 16 * kt, 0, lane);
-                const OpV a1 = frag_t<T>(&ktf[0][0], CH + kPadT, 16 * kt, 1, lane);
+                const OpV a0 = TRK ? kt_frag(knc, kt, 0) : frag_t<T>(&sm.kt[kc][0][0], CH + kPadT, 16 * kt, 0, lane);
+                const OpV a1 = TRK ? kt_frag(knc, kt, 1) : frag_t<T>(&sm.kt[kc][0][0], CH + kPadT, 16 * kt, 1, lane);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     f32x4 s = sacc[kt][ct] * gC;
@@ -1203,13 +1223,13 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
         // the next chunk into the other buffer (last read before the previous barrier); a single kt
         // buffer is free once every wave has updated its state
         if constexpr (NKT == 1) __syncthreads();
-        if (c + 1 < ce) stage(c + 1, R, Bn, ktn);
+        if (c + 1 < ce) stage(c + 1, R, Bn, kx);
         __syncthreads();
     };
 
     if (cb < ce) {
         load_rows(cb, R);
-        stage(cb, R, sm.buf[0], sm.kt[0]);
+        stage(cb, R, sm.buf[0], 0);
     }
     // nothing may be in flight when the loop starts: the compiler then has to wait in the loop only
     // for what the loop itself issued
@@ -1217,7 +1237,7 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
     __syncthreads();
     for (int c = cb; c < ce; ++c) {
         const int bi = (c - cb) & 1;
-        step(c, sm.buf[bi], sm.buf[bi ^ 1], sm.kt[NKT == 2 ? bi : 0], sm.kt[NKT == 2 ? bi ^ 1 : 0]);
+        step(c, sm.buf[bi], sm.buf[bi ^ 1], NKT == 2 ? bi : 0, NKT == 2 ? bi ^ 1 : 0);
     }
     if (cb < ce) flush_out(ce - 1);  // after the last step's barrier
 
