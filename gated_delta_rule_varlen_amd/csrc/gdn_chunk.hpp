@@ -706,9 +706,10 @@ __device__ __forceinline__ typename Op<T>::v8 frag_t(const uint16_t* tile, int l
     return *reinterpret_cast<const typename Op<T>::v8*>(tile + idx * ld + 8 * ((4 * jj + (lane >> 4)) ^ ((idx >> kSwz) & 7)));
 }
 
-// kn, qn and vr are last read before a chunk's middle barrier and are written for the next chunk
-// after it, so one copy serves; the per-token factors are read after that barrier and have two, and
-// so has kt where LDS allows (else the next chunk's kt waits for one more barrier).
+// qn and vr are last read before a chunk's middle barrier and are written for the next chunk after
+// it, so one copy serves; the per-token factors are read after that barrier and have two, and so has
+// the source of K^T (kn on bf16 operands, kt on fp16 ones) where LDS allows (else the next chunk's
+// copy waits for one more barrier).
 struct ChunkBuf {
     // per token: G; b; scale e^G; b e^G / |k|; e^{G_C - G} / |k|; 1/|k|; 1/|q|; and e^{G_C}
     float gam[CH], beta[CH], eg[CH], bx[CH], ud[CH], rk[CH], rq[CH], gc[4];
@@ -1153,8 +1154,8 @@ __global__ __launch_bounds__(64 * (VT / (16 * VTW))) void chunk_fused_kernel(Chu
                 for (int ct = 0; ct < NCT; ++ct) ua[it][ct] = Op<T>::mma(tf[f], rb[jj][ct], ua[it][ct]);
             }
         }
-        // P is complete, and kn, qn and vt of this chunk have been read for the last time (the next
-        // chunk's rows are staged into them after the state update)
+        // P is complete, and qn, vr and (on fp16 operands) kn of this chunk have been read for the
+        // last time (the next chunk's rows are staged into them after the state update)
         __syncthreads();
         if constexpr (!SUMMARY) {
             // O^T = (S0 Q^T) diag(scale e^G / |q|) + scale U^T P^T (the first factor is eg / |q|).
