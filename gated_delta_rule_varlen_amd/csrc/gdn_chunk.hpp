@@ -17,8 +17,8 @@
 //   index    one block: checks the offsets (nothing is written anywhere when they are malformed)
 //            and builds the tables (chunks per sequence, sequences longest first, segments).
 //   tmat     one block per (chunk, head), fully parallel: the gates and G, A by MFMA and
-//            T = (I + A)^{-1} by blocked inversion, stored as the six 16 x 32 bf16 operand
-//            fragments the chain reads (6 KB), plus G and b (512 B).  This is the only per-chunk
+//            T = (I + A)^{-1} by blocked inversion, stored as the six 16 x 32 operand fragments
+//            the chain reads (6 KB), plus G, b and 1/|k| (768 B).  This is the only per-chunk
 //            data that goes through memory.
 //   summary  (long sequences only, below)
 //   combine  (long sequences only, below)
@@ -29,11 +29,12 @@
 //            supplies inner elements in the order {4g..4g+3, 16+4g..16+4g+3} (g = lane/16) of each
 //            32-block, so A operands are read in that same order ("split" fragments) and K S0^T,
 //            Q S0^T, T R, P U and K^T U chain from accumulator to operand in registers.  P is formed
-//            by each wave directly in that operand order.  The raw q and k rows as bf16 operands
-//            (their norms scale per-token factors instead; k also transposed) and the transposed v
-//            of the next chunk are staged while the current one is in use, and the next chunk's
-//            rows and T fragments are in flight meanwhile: two barriers per chunk (three where
-//            LDS holds one transposed-k buffer only).
+//            by each wave directly in that operand order.  The raw q, k and v rows of the next
+//            chunk (the q and k norms scale per-token factors instead) are staged as loaded while
+//            the current one is in use, and the next chunk's rows and T fragments are in flight
+//            meanwhile; K^T and R's columns of v are read from the row tiles through the
+//            transposing LDS read (on fp16 operands K^T is a transposed tile of normalised rows):
+//            two barriers per chunk (three where LDS holds one copy of the K^T source only).
 // Widths: the key width runs on the next of 64, 128 and 256 and the value width in parts of the
 // next of 32, 64 and 128 columns (parts of 128 past that), with keys and columns past the real
 // widths zero; loads past them read zero and stores past them are dropped.
@@ -677,11 +678,13 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
 
 // ---- summary and main -----------------------------------------------------------------------------
 // LDS layouts of one chunk (all 16-bit elements):
-//   kn, qn  [token][key]: the raw k and q rows as bf16 operands (the L2 norms 1/|k|, 1/|q| scale
+//   kn, qn  [token][key]: the raw k and q rows as operands (the L2 norms 1/|k|, 1/|q| scale
 //           per-token factors instead), keys of every 32-block in the split order (physical slot
 //           8g + e holds key 4g + e for e < 4 and 16 + 4g + e - 4 otherwise), so a split fragment
-//           is one 16-byte read; products between two such rows are unchanged.
-//   kt, vt  [key or value column][token]: transposed, tokens of every 32-block in the split order,
+//           is one 16-byte read; products between two such rows are unchanged.  Four consecutive
+//           keys share 8 contiguous bytes, which is what the transposing read of K^T takes.
+//   vr      [token][value column]: the v rows as loaded.
+//   kt      [key][token] (fp16 operands): transposed, tokens of every 32-block in the split order,
 //           in 16-byte units (8 tokens = one lane group's split fragment) placed at unit u ^ (idx/8 % 8)
 //           so that the stores of one row-major lane (8 consecutive indices) spread over the banks.
 //   pb      P, [row i][column j] with the columns in the split order.
