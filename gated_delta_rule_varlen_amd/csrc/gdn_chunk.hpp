@@ -731,8 +731,9 @@ struct FusedLds {
     uint16_t pb[SUMMARY ? 1 : CH][CH + kPadT];
     uint16_t ob[SUMMARY || !SO ? 1 : CH][VT + 8];  // output rows of the previous chunk, stored whole
 };
-// LDS of one block: two kt buffers and staged output rows while they fit, else one kt buffer, and
-// then output rows stored straight from the registers (K = 256 with 128-column value parts).
+// LDS of one block: two copies of the K^T source and staged output rows while they fit, else one
+// copy, and then output rows stored straight from the registers (K = 256 with 128-column value
+// parts on fp16 operands).
 constexpr size_t kLdsBytes = 160 * 1024;
 template <int K, int VT, bool SUMMARY, bool TRK>
 struct LdsPlan {
