@@ -503,7 +503,9 @@ __global__ __launch_bounds__(256) void chunk_tmat_kernel(ChunkArgs p) {
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.ws);
     if (hdr[0] != GDN_OK) return;
     const Tables tab = tables(p.ws, p.B);
-    const int blk = xcd_remap((int)blockIdx.x, p.n_blocks, p.G);
+    // the H heads of a chunk on one XCD: they read the same gate rows (one cache line serves several
+    // heads) and, G at a time, the same k rows
+    const int blk = xcd_remap((int)blockIdx.x, p.n_blocks, p.H);
     const int cid = blk / p.H, h = blk % p.H, kh = h / p.G;
     if (cid >= hdr[3]) return;
     const int b = find_start(tab.cstart, p.B, cid);
@@ -1295,7 +1297,9 @@ __global__ __launch_bounds__(combine_threads<K>()) void chunk_combine_kernel(Chu
     if (hdr[0] != GDN_OK) return;
     const Tables tab = tables(p.ws, p.B);
     constexpr int NVT = V / VR;
-    const int blk = blockIdx.x;
+    // the NVT blocks of a (sequence, head) on one XCD: each reads every Phi of the head, which its
+    // L2 then serves once
+    const int blk = xcd_remap((int)blockIdx.x, (int)gridDim.x, NVT);
     const int vt = blk % NVT, bh = blk / NVT;
     const int h = bh % p.H, b = bh / p.H;
     const int nseg = nseg_of(tab.nchunk[b], p.L.seglen);
