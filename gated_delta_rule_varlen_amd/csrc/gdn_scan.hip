@@ -241,6 +241,14 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
         if (ntok >= 2 && ntok <= TSH && full_tile && p.state_in != nullptr && p.state_out != nullptr) {
             const int tid = (int)threadIdx.x;
             const int vb0 = vt * NW * WC;  // first column of the block
+            // the state tile first: its loads are in flight while the tokens are staged
+            f32x4 sc[CPL][EPL / 4];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const float* sp = p.state_in + (col0 + vbase + c) * Kr;
+#pragma unroll
+                for (int i = 0; i < EPL / 4; ++i) sc[c][i] = ld_row4<KX, NT>(sp, 4 * (gl + LPC * i), Kr);
+            }
             // (1) token operands, once per block: 32 threads per token, EPT elements each
             for (int tb = 0; tb < ntok; tb += 2 * NW) {
                 const int t = tb + tid / 32, j = tid % 32;
@@ -344,13 +352,6 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(ScanArgs p) {
             // a block-uniform scale c (the product of the decays so far), so that a token's update is
             // one fused multiply-add per element.  When c would leave [1e-30, 1e30] (including a zero
             // decay) it is folded into s' first.
-            f32x4 sc[CPL][EPL / 4];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const float* sp = p.state_in + (col0 + vbase + c) * Kr;
-#pragma unroll
-                for (int i = 0; i < EPL / 4; ++i) sc[c][i] = ld_row4<KX, NT>(sp, 4 * (gl + LPC * i), Kr);
-            }
             const int lc = vbase - vb0;
             float cs = 1.0f;
 #pragma unroll
