@@ -252,6 +252,25 @@ def test_chunk_rejects_ineligible_inputs(torch):
     assert ei.value.status == -6
 
 
+def test_chunk_segments_with_partial_block_rounds(torch):
+    """Three sequences (6000, 900 and 2500 tokens) at H = 12, G = 3, K = V = 128: the first and the
+    last are cut into segments (6 and 3 of 16 chunks) and the second is not, and the tmat and combine
+    grids end in a partial round of the per-XCD block grouping (12 heads of a chunk; 16 combine
+    blocks of a head), whose blocks keep their index.  Against the oracle and the sequential form."""
+    w = workloads.make(name="chunk_seg_h12", seed=143, lengths=[6000, 900, 2500], HQ=4, H=12, K=128, V=128, io="bf16",
+                       conv_state_dtype="f32", state_std=0.1)
+    out_c, st_c, used = gpu_scan(torch, w, "chunk", False)
+    assert used == "chunk"
+    out_s, st_s, _ = gpu_scan(torch, w, "seq", False)
+    o_ref, s_ref = oracle.scan(w.qkv, w.offsets, HQ=w.HQ, H=w.H, K=w.K, V=w.V, qkv_dtype=w.io, gate_dtype=w.gate_dtype,
+                               a=w.a, b=w.b, A_log=w.A_log, dt_bias=w.dt_bias, state_in=w.state)
+    e1 = assert_close(f64(out_c), o_ref, CHUNK_TOL[w.io], "chunk out")
+    e2 = assert_close(f64(st_c), s_ref, CHUNK_TOL[w.io], "chunk state")
+    e3 = assert_close(f64(out_c), f64(out_s), CHUNK_SEQ_TOL[w.io], "chunk vs seq out")
+    e4 = assert_close(f64(st_c), f64(st_s), CHUNK_SEQ_TOL[w.io], "chunk vs seq state")
+    print(f"  segments h12: out {e1:.2e} state {e2:.2e} vs-seq {e3:.2e} / {e4:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("io", ["bf16", "f16"])
 def test_chunk_long_sequence_k64(torch, io):
     """One 8192-token sequence (128 chunks in one serial chain) at K = V = 64, both half types:
